@@ -1,0 +1,143 @@
+"""MI355X (gfx950) lightning indexer + top-k token selector.
+
+Thin Python binding over libdsaidx.so (include/dsaidx.h).  Every step of the
+computation runs in the library's HIP kernels; this module only checks
+tensor shapes, allocates outputs and workspace with torch on the inputs'
+device, and passes pointers and the current HIP stream.
+
+    indexer_prefill(q, k, w, topk, q_scale=None, k_scale=None, want_scores=False)
+    indexer_decode_paged(q, w, k_cache, k_scale, block_table, context_lens, topk, max_context_len=None)
+    topk_select(scores, topk, row_len=None)
+
+Input formats: fp32 tensors; bf16 as torch.bfloat16 or int16/uint16 bit
+patterns; OCP FP8 E4M3 as torch.float8_e4m3fn or uint8 codes with fp32
+per-row scales.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+
+__all__ = ["indexer_prefill", "indexer_decode_paged", "topk_select", "dtype_code", "F32", "BF16", "FP8_E4M3"]
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def indexer_prefill(q, k, w, topk: int, q_scale=None, k_scale=None, want_scores: bool = False,
+                    want_topk_score: bool = True):
+    """Top-k causal history positions of every token of B sequences.
+
+    q [B,L,H,D], k [B,L,D], w [B,L,H] fp32 (+ q_scale [B,L,H], k_scale [B,L]
+    fp32 for fp8).  Returns (idx int32 [B,L,topk], score fp32 [B,L,topk] or
+    None, scores fp32 [B,L,L] or None)."""
+    lib = _lib.load()
+    B, L, H, D = q.shape
+    if tuple(k.shape) != (B, L, D) or tuple(w.shape) != (B, L, H):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} w{tuple(w.shape)}")
+    dt = dtype_code(q)
+    if dtype_code(k) != dt:
+        raise ValueError("q and k must share a format")
+    for name, t in (("q", q), ("k", k), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale)):
+        if t is not None:
+            _dev(t, name)
+    dev = q.device
+    idx = torch.empty((B, L, topk), dtype=torch.int32, device=dev)
+    val = torch.empty((B, L, topk), dtype=torch.float32, device=dev) if want_topk_score else None
+    scores = torch.empty((B, L, L), dtype=torch.float32, device=dev) if want_scores else None
+    nws = lib.indexer_prefill_workspace_bytes(B, L, H, D, topk, dt, 1 if want_scores else 0)
+    ws = _workspace(nws, dev)
+    st = lib.indexer_prefill(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), dt, _ptr(w), B, L, H, D, topk,
+                             _ptr(idx), _ptr(val), _ptr(scores), _ptr(ws), nws, _stream(dev))
+    _lib.check(st, "indexer_prefill")
+    return idx, val, scores
+
+
+def indexer_decode_paged(q, w, k_cache, k_scale, block_table, context_lens, topk: int,
+                         max_context_len: int | None = None, want_topk_score: bool = True,
+                         workspace: torch.Tensor | None = None):
+    """Top-k context positions of B decode queries over a paged fp8 cache.
+
+    q [B,H,D] bf16, w [B,H] fp32, k_cache [P,page,D] fp8 codes, k_scale
+    [P,page] fp32, block_table [B,max_pages] int32, context_lens [B] int32.
+    ``max_context_len`` bounds context_lens (default: max_pages * page).
+    Returns (idx int32 [B,topk], score fp32 [B,topk] or None)."""
+    lib = _lib.load()
+    B, H, D = q.shape
+    P, page, Dk = k_cache.shape
+    if Dk != D or tuple(k_scale.shape) != (P, page) or tuple(w.shape) != (B, H):
+        raise ValueError("shape mismatch")
+    if block_table.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_table / context_lens shape mismatch")
+    for name, t in (("q", q), ("w", w), ("k_cache", k_cache), ("k_scale", k_scale),
+                    ("block_table", block_table), ("context_lens", context_lens)):
+        _dev(t, name)
+    mpp = block_table.shape[1]
+    mcl = mpp * page if max_context_len is None else int(max_context_len)
+    dev = q.device
+    idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    val = torch.empty((B, topk), dtype=torch.float32, device=dev) if want_topk_score else None
+    nws = lib.indexer_decode_paged_workspace_bytes(B, mcl, H, D, topk)
+    ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, dev)
+    st = lib.indexer_decode_paged(_ptr(q), dtype_code(q), _ptr(w), _ptr(k_cache), _ptr(k_scale),
+                                  _ptr(block_table), mpp, _ptr(context_lens), mcl, B, H, D, page, P, topk,
+                                  _ptr(idx), _ptr(val), _ptr(ws), nws, _stream(dev))
+    _lib.check(st, "indexer_decode_paged")
+    return idx, val
+
+
+def decode_workspace_bytes(B: int, max_context_len: int, H: int, D: int, topk: int) -> int:
+    return _lib.load().indexer_decode_paged_workspace_bytes(B, max_context_len, H, D, topk)
+
+
+def topk_select(scores, topk: int, row_len=None, want_values: bool = True):
+    """Top-k of each row of a [rows, cols] fp32 matrix (row r valid up to
+    row_len[r]).  Returns (idx int32 [rows,topk], values fp32 or None)."""
+    lib = _lib.load()
+    if scores.dim() != 2 or scores.dtype != torch.float32:
+        raise ValueError("scores must be a 2-D fp32 tensor")
+    if scores.stride(1) != 1:
+        raise ValueError("scores rows must be contiguous")
+    rows, cols = scores.shape
+    dev = scores.device
+    if row_len is not None:
+        _dev(row_len, "row_len")
+    idx = torch.empty((rows, topk), dtype=torch.int32, device=dev)
+    val = torch.empty((rows, topk), dtype=torch.float32, device=dev) if want_values else None
+    nws = lib.topk_select_workspace_bytes(rows, cols, topk)
+    ws = _workspace(nws, dev)
+    st = lib.topk_select(_ptr(scores), rows, cols, scores.stride(0), _ptr(row_len), topk, _ptr(idx), _ptr(val),
+                         _ptr(ws), nws, _stream(dev))
+    _lib.check(st, "topk_select")
+    return idx, val

@@ -1,0 +1,250 @@
+// C ABI of the lightning-indexer library: argument checks (all on the host,
+// before any launch), workspace sizing and kernel dispatch.  The entry points
+// are documented in include/dsaidx.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "dsaidx.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[320];
+
+dsaidx_status fail(dsaidx_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+dsaidx_status hip_fail(hipError_t e, const char* what) {
+    return fail(DSAIDX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int kMaxTopk = 2048;
+constexpr int kMaxL = 131072;
+constexpr int kMaxSelectCols = 4194304;
+
+bool prefill_is_fused(int dtype, int H, int D) {
+    return (dtype == DSAIDX_BF16 || dtype == DSAIDX_FP8_E4M3) && D == 128 && H % 16 == 0 && H >= 16 && H <= 64;
+}
+
+size_t decode_score_stride(int max_ctx) { return (size_t)((max_ctx + 63) / 64) * 64; }
+
+}  // namespace
+
+extern "C" {
+
+int dsaidx_version(void) { return 100; }
+
+const char* dsaidx_status_string(int s) {
+    switch (s) {
+        case DSAIDX_OK: return "ok";
+        case DSAIDX_ERR_NULL: return "required pointer is NULL";
+        case DSAIDX_ERR_SHAPE: return "invalid or inconsistent size";
+        case DSAIDX_ERR_DTYPE: return "unknown dtype";
+        case DSAIDX_ERR_UNSUPPORTED: return "outside the supported ranges";
+        case DSAIDX_ERR_WORKSPACE: return "workspace too small";
+        case DSAIDX_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* dsaidx_last_error(void) { return g_err; }
+
+size_t topk_select_workspace_bytes(int rows, int cols, int topk) {
+    (void)rows; (void)cols; (void)topk;
+    return 0;
+}
+
+dsaidx_status topk_select(const float* scores, int rows, int cols, int64_t row_stride,
+                          const int32_t* row_len, int topk, int32_t* idx_out, float* val_out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace; (void)workspace_bytes;
+    g_err[0] = 0;
+    if (!scores) return fail(DSAIDX_ERR_NULL, "scores is NULL");
+    if (!idx_out) return fail(DSAIDX_ERR_NULL, "idx_out is NULL");
+    if (rows < 1 || cols < 1 || topk < 1) return fail(DSAIDX_ERR_SHAPE, "rows=%d cols=%d topk=%d must be >= 1", rows, cols, topk);
+    if (row_stride < cols) return fail(DSAIDX_ERR_SHAPE, "row_stride=%lld < cols=%d", (long long)row_stride, cols);
+    if (topk > kMaxTopk) return fail(DSAIDX_ERR_UNSUPPORTED, "topk=%d > %d", topk, kMaxTopk);
+    if (cols > kMaxSelectCols) return fail(DSAIDX_ERR_UNSUPPORTED, "cols=%d > %d", cols, kMaxSelectCols);
+    dsaidx::SelectArgs a{};
+    a.scores = scores;
+    a.row_stride = row_stride;
+    a.cols = cols;
+    a.row_len = row_len;
+    a.causal_L = 0;
+    a.hist = nullptr;
+    a.topk = topk;
+    a.idx_out = idx_out;
+    a.val_out = val_out;
+    hipError_t e = dsaidx::launch_topk_select(a, rows, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "topk_select");
+    return DSAIDX_OK;
+}
+
+size_t indexer_prefill_workspace_bytes(int B, int L, int H, int D, int topk, int qk_dtype, int want_scores) {
+    (void)topk;
+    if (B < 1 || L < 1) return 0;
+    if (prefill_is_fused(qk_dtype, H, D) || want_scores) return 0;
+    return (size_t)B * (size_t)L * (size_t)L * sizeof(float);
+}
+
+dsaidx_status indexer_prefill(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                              int qk_dtype, const float* w, int B, int L, int H, int D, int topk,
+                              int32_t* topk_idx, float* topk_score, float* scores,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!q) return fail(DSAIDX_ERR_NULL, "q is NULL");
+    if (!k) return fail(DSAIDX_ERR_NULL, "k is NULL");
+    if (!w) return fail(DSAIDX_ERR_NULL, "w is NULL");
+    if (!topk_idx) return fail(DSAIDX_ERR_NULL, "topk_idx is NULL");
+    if (qk_dtype != DSAIDX_F32 && qk_dtype != DSAIDX_BF16 && qk_dtype != DSAIDX_FP8_E4M3)
+        return fail(DSAIDX_ERR_DTYPE, "qk_dtype=%d", qk_dtype);
+    if (qk_dtype == DSAIDX_FP8_E4M3) {
+        if (!q_scale) return fail(DSAIDX_ERR_NULL, "q_scale is NULL for fp8 inputs");
+        if (!k_scale) return fail(DSAIDX_ERR_NULL, "k_scale is NULL for fp8 inputs");
+    } else if (q_scale || k_scale) {
+        return fail(DSAIDX_ERR_SHAPE, "q_scale/k_scale must be NULL unless qk_dtype is FP8");
+    }
+    if (B < 1 || L < 1 || H < 1 || D < 1 || topk < 1)
+        return fail(DSAIDX_ERR_SHAPE, "B=%d L=%d H=%d D=%d topk=%d must be >= 1", B, L, H, D, topk);
+    if (L > kMaxL) return fail(DSAIDX_ERR_UNSUPPORTED, "L=%d > %d", L, kMaxL);
+    if (H % 4 != 0 || H > 64) return fail(DSAIDX_ERR_UNSUPPORTED, "H=%d (multiple of 4 in [4, 64])", H);
+    if (D != 32 && D != 64 && D != 128) return fail(DSAIDX_ERR_UNSUPPORTED, "D=%d (32, 64 or 128)", D);
+    if (topk > kMaxTopk) return fail(DSAIDX_ERR_UNSUPPORTED, "topk=%d > %d", topk, kMaxTopk);
+    if (!aligned16(q) || !aligned16(k)) return fail(DSAIDX_ERR_UNSUPPORTED, "q and k must be 16-byte aligned");
+    if ((size_t)B * (size_t)L > (size_t)0x7FFFFFFF) return fail(DSAIDX_ERR_UNSUPPORTED, "B*L too large");
+
+    dsaidx::PrefillArgs a{};
+    a.q = q;
+    a.q_scale = q_scale;
+    a.k = k;
+    a.k_scale = k_scale;
+    a.w = w;
+    a.B = B;
+    a.L = L;
+    a.H = H;
+    a.D = D;
+    a.topk = topk;
+    a.inv_sqrt_d = 1.0f / sqrtf((float)D);
+    a.idx_out = topk_idx;
+    a.val_out = topk_score;
+    a.scores = scores;
+    hipStream_t st = (hipStream_t)stream;
+
+    if (prefill_is_fused(qk_dtype, H, D)) {
+        hipError_t e = dsaidx::launch_prefill_fused(a, qk_dtype, st);
+        if (e != hipSuccess) return hip_fail(e, "indexer_prefill (fused)");
+        return DSAIDX_OK;
+    }
+    float* mat = scores;
+    if (!mat) {
+        const size_t need = indexer_prefill_workspace_bytes(B, L, H, D, topk, qk_dtype, 0);
+        if (!workspace || workspace_bytes < need)
+            return fail(DSAIDX_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+        mat = reinterpret_cast<float*>(workspace);
+    }
+    hipError_t e = dsaidx::launch_prefill_scores_generic(a, qk_dtype, mat, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer_prefill (scores)");
+    dsaidx::SelectArgs s{};
+    s.scores = mat;
+    s.row_stride = L;
+    s.cols = L;
+    s.row_len = nullptr;
+    s.causal_L = L;
+    s.hist = nullptr;
+    s.topk = topk;
+    s.idx_out = topk_idx;
+    s.val_out = topk_score;
+    e = dsaidx::launch_topk_select(s, B * L, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer_prefill (select)");
+    return DSAIDX_OK;
+}
+
+size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, int D, int topk) {
+    (void)H; (void)D; (void)topk;
+    if (B < 1 || max_context_len < 0) return 0;
+    return (size_t)B * decode_score_stride(max_context_len) * sizeof(float) +
+           (size_t)B * dsaidx::kHistBins * sizeof(uint32_t);
+}
+
+dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
+                                   const uint8_t* k_cache, const float* k_scale,
+                                   const int32_t* block_table, int max_pages_per_seq,
+                                   const int32_t* context_lens, int max_context_len,
+                                   int B, int H, int D, int page_size, int num_pages, int topk,
+                                   int32_t* topk_idx, float* topk_score,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!q) return fail(DSAIDX_ERR_NULL, "q is NULL");
+    if (!w) return fail(DSAIDX_ERR_NULL, "w is NULL");
+    if (!k_cache) return fail(DSAIDX_ERR_NULL, "k_cache is NULL");
+    if (!k_scale) return fail(DSAIDX_ERR_NULL, "k_scale is NULL");
+    if (!block_table) return fail(DSAIDX_ERR_NULL, "block_table is NULL");
+    if (!context_lens) return fail(DSAIDX_ERR_NULL, "context_lens is NULL");
+    if (!topk_idx) return fail(DSAIDX_ERR_NULL, "topk_idx is NULL");
+    if (q_dtype != DSAIDX_F32 && q_dtype != DSAIDX_BF16 && q_dtype != DSAIDX_FP8_E4M3)
+        return fail(DSAIDX_ERR_DTYPE, "q_dtype=%d", q_dtype);
+    if (B < 1 || H < 1 || D < 1 || page_size < 1 || num_pages < 1 || max_pages_per_seq < 1 || topk < 1 ||
+        max_context_len < 0)
+        return fail(DSAIDX_ERR_SHAPE, "B=%d H=%d D=%d page_size=%d num_pages=%d max_pages_per_seq=%d topk=%d "
+                    "max_context_len=%d", B, H, D, page_size, num_pages, max_pages_per_seq, topk, max_context_len);
+    if ((int64_t)max_context_len > (int64_t)max_pages_per_seq * page_size)
+        return fail(DSAIDX_ERR_SHAPE, "max_context_len=%d > max_pages_per_seq*page_size=%lld", max_context_len,
+                    (long long)max_pages_per_seq * page_size);
+    if (q_dtype != DSAIDX_BF16) return fail(DSAIDX_ERR_UNSUPPORTED, "decode queries must be bf16");
+    if (H % 16 != 0 || H > 64) return fail(DSAIDX_ERR_UNSUPPORTED, "H=%d (16, 32, 48 or 64)", H);
+    if (D != 128) return fail(DSAIDX_ERR_UNSUPPORTED, "D=%d (128)", D);
+    if (page_size != 64) return fail(DSAIDX_ERR_UNSUPPORTED, "page_size=%d (64)", page_size);
+    if (topk > kMaxTopk) return fail(DSAIDX_ERR_UNSUPPORTED, "topk=%d > %d", topk, kMaxTopk);
+    if (max_context_len > kMaxSelectCols) return fail(DSAIDX_ERR_UNSUPPORTED, "max_context_len too large");
+    if (!aligned16(q) || !aligned16(k_cache)) return fail(DSAIDX_ERR_UNSUPPORTED, "q and k_cache must be 16-byte aligned");
+    const size_t need = indexer_decode_paged_workspace_bytes(B, max_context_len, H, D, topk);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSAIDX_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+
+    hipStream_t st = (hipStream_t)stream;
+    const size_t stride = decode_score_stride(max_context_len);
+    float* sc = reinterpret_cast<float*>(workspace);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(workspace) + (size_t)B * stride * sizeof(float));
+    hipError_t e = dsaidx::launch_zero_u32(hist, (size_t)B * dsaidx::kHistBins, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (clear)");
+    if (max_context_len > 0) {
+        dsaidx::DecodeArgs d{};
+        d.q = reinterpret_cast<const uint16_t*>(q);
+        d.w = w;
+        d.k_cache = k_cache;
+        d.k_scale = k_scale;
+        d.block_table = block_table;
+        d.max_pages = max_pages_per_seq;
+        d.context_lens = context_lens;
+        d.max_ctx = max_context_len;
+        d.B = B;
+        d.inv_sqrt_d = 1.0f / sqrtf((float)D);
+        d.scores = sc;
+        d.score_stride = (int64_t)stride;
+        d.hist = hist;
+        e = dsaidx::launch_decode_scan(d, H, max_context_len, st);
+        if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (scan)");
+    }
+    dsaidx::SelectArgs s{};
+    s.scores = sc;
+    s.row_stride = (int64_t)stride;
+    s.cols = max_context_len > 0 ? max_context_len : 1;
+    s.row_len = context_lens;
+    s.causal_L = 0;
+    s.hist = hist;
+    s.topk = topk;
+    s.idx_out = topk_idx;
+    s.val_out = topk_score;
+    e = dsaidx::launch_topk_select(s, B, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (select)");
+    return DSAIDX_OK;
+}
+
+}  // extern "C"

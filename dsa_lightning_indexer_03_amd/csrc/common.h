@@ -1,0 +1,70 @@
+// Device helpers shared by the gfx950 kernels of the lightning-indexer library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsaidx {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Order-preserving map of an fp32 score to an unsigned key: a larger key is a
+// larger score, -0.0 maps to the key of +0.0 so both zeros tie.  -inf maps to
+// 0x007FFFFF, so every non-NaN score has a key > 0.
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    u = (u == 0x80000000u) ? 0u : u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of `mask` below the calling lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        uint32_t o = __shfl_up(v, d, kWave);
+        if (l >= d) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+// Wave-uniform value from lane 0 (tells the compiler it is uniform).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Two OCP E4M3 codes (bytes 2,3 of `packed` if HI else bytes 0,1) -> two
+// bf16 values, exact (every E4M3 value is representable in bf16).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(int packed) {
+    v2bf r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+}  // namespace dsaidx

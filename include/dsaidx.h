@@ -1,0 +1,189 @@
+/*
+ * dsaidx.h -- C ABI of the MI355X (gfx950) lightning-indexer library.
+ *
+ * The DeepSeek Sparse Attention lightning indexer scores, for every query
+ * token t and every history token s, the relevance
+ *
+ *     I[t,s] = sum_{i<H} w[t,i] * ReLU( q[t,i] . k[s] / sqrt(D) )
+ *
+ * with H index heads on the query side and ONE D-wide key per token shared by
+ * all heads, and keeps the top-k positions s of each query (the "token
+ * selector").  Formula: "From formula to code -- DeepSeek-V3.2 lightning
+ * indexer", section 2.1 (core formula) and "Lightning Indexer explained",
+ * section 4 (scoring formula; multi-head on the query side only).  Selection:
+ * "Lightning Indexer explained", section 1 (top-k of k = 2048 positions) and
+ * section 2.3 (at most min(k, #history) positions come back).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array argument is a DEVICE pointer owned by the caller, row-major
+ *   and contiguous unless a stride is given.  The library allocates nothing
+ *   and keeps no state between calls; scratch memory is the caller's
+ *   `workspace` (size from the matching *_workspace_bytes query; it may be
+ *   NULL when that size is 0).
+ * - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *   enqueue work and return; results are valid after the caller synchronises
+ *   the stream.
+ * - Scores are fp32.  A selected position's score is the fp32 score of that
+ *   position.  Padding slots hold index -1 and score -inf.
+ * - Tie rule: among equal scores the lower position wins (-0.0 equals +0.0).
+ *   The order of the selected positions inside a row is unspecified; the
+ *   valid entries of a row come first, then the padding.
+ * - Errors: every argument check runs on the host before any launch; a
+ *   non-OK status means nothing was enqueued and no output was written.
+ *   DSAIDX_ERR_HIP means a launch failed (text in dsaidx_last_error()).
+ *   The library never aborts, exits or prints.
+ * - Undefined behaviour (not checked): NaN inputs, device arrays shorter than
+ *   stated, block-table entries outside [0, num_pages), context lengths
+ *   outside [0, max_pages_per_seq * page_size], negative fp8 scales.
+ *
+ * Input formats (dsaidx_dtype)
+ * ----------------------------
+ *   DSAIDX_F32      IEEE binary32.
+ *   DSAIDX_BF16     bfloat16 bit patterns (uint16).
+ *   DSAIDX_FP8_E4M3 OCP FP8 E4M3FN codes (uint8: bias 7, max 448, no Inf,
+ *                   S.1111.111 = NaN).  Each row carries an fp32 scale: the
+ *                   value of a code is decode(code) * scale.  The pages keep
+ *                   the indexer keys in FP8 ("Lightning Indexer explained",
+ *                   section 5; "Study MLA Indexer", data-flow diagram); the
+ *                   per-row scale is this library's storage convention.
+ */
+#ifndef DSAIDX_H
+#define DSAIDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSAIDX_OK = 0,
+    DSAIDX_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    DSAIDX_ERR_SHAPE = 2,       /* a size is non-positive or inconsistent         */
+    DSAIDX_ERR_DTYPE = 3,       /* unknown dtype code                             */
+    DSAIDX_ERR_UNSUPPORTED = 4, /* valid request outside the supported ranges     */
+    DSAIDX_ERR_WORKSPACE = 5,   /* workspace smaller than the query returned      */
+    DSAIDX_ERR_HIP = 6          /* a HIP launch failed                            */
+} dsaidx_status;
+
+typedef enum {
+    DSAIDX_F32 = 0,
+    DSAIDX_BF16 = 1,
+    DSAIDX_FP8_E4M3 = 2
+} dsaidx_dtype;
+
+/*
+ * indexer_prefill -- score every causal pair of B sequences of L tokens and
+ * select the top-k history positions of every token.
+ *
+ * Passage: the core formula ("From formula to code", section 2.1) evaluated
+ * for all query tokens at once, with the causal mask of that page's listing
+ * (section 3: the lower-triangular mask keeps s <= t; masked scores are -inf)
+ * and its top-k over the masked rows.  Row t therefore has t+1 valid
+ * positions; rows with t+1 <= topk return all of them, then -1 padding.
+ *
+ *   q         [B][L][H][D] in qk_dtype
+ *   q_scale   [B][L][H] fp32 when qk_dtype is FP8 (one scale per query-head
+ *             row), else must be NULL
+ *   k         [B][L][D] in qk_dtype (one key per token, shared by all heads)
+ *   k_scale   [B][L] fp32 when qk_dtype is FP8, else must be NULL
+ *   w         [B][L][H] fp32 head weights (any finite values)
+ *   topk_idx  out [B][L][topk] int32
+ *   topk_score out [B][L][topk] fp32, or NULL
+ *   scores    out [B][L][L] fp32 full score matrix (-inf above the diagonal),
+ *             or NULL.  Large L costs B*L*L*4 bytes of HBM writes; the fused
+ *             path never writes it unless asked.
+ *
+ * Supported: 1 <= B, 1 <= L <= 131072, H a multiple of 4 in [4, 64],
+ * D in {32, 64, 128}, 1 <= topk <= 2048.  bf16/fp8 with D = 128 and H a
+ * multiple of 16 take the fused MFMA path (no workspace); other shapes score
+ * into a B*L*L fp32 matrix (the `scores` output if given, else workspace)
+ * and select from it.
+ */
+dsaidx_status indexer_prefill(const void* q, const float* q_scale,
+                              const void* k, const float* k_scale,
+                              int qk_dtype, const float* w,
+                              int B, int L, int H, int D, int topk,
+                              int32_t* topk_idx, float* topk_score, float* scores,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+size_t indexer_prefill_workspace_bytes(int B, int L, int H, int D, int topk, int qk_dtype,
+                                       int want_scores);
+
+/*
+ * indexer_decode_paged -- one decode step for B queries, each scoring its
+ * whole cached context.
+ *
+ * Passage: "Lightning Indexer explained", section 2 (decode walkthrough): the
+ * current query is dotted against every row of the indexer key cache, giving
+ * one score per history position, then top-k; section 2.3: at most
+ * min(k, context) positions.  Query b sits at position context_lens[b]-1 and
+ * sees the positions s in [0, context_lens[b]).  Logical position s of query
+ * b lives in page block_table[b][s / page_size], slot s % page_size of the
+ * shared page pool (paging is this library's layout of that cache).
+ *
+ *   q            [B][H][D] bf16 (q_dtype must be DSAIDX_BF16)
+ *   w            [B][H] fp32
+ *   k_cache      [num_pages][page_size][D] FP8 E4M3 codes
+ *   k_scale      [num_pages][page_size] fp32, one scale per cached token
+ *   block_table  [B][max_pages_per_seq] int32 page ids
+ *   context_lens [B] int32, each in [0, max_context_len]
+ *   max_context_len  host-side upper bound of context_lens (sizes the launch
+ *                and the workspace); <= max_pages_per_seq * page_size
+ *   topk_idx     out [B][topk] int32;  topk_score out [B][topk] fp32 or NULL
+ *
+ * Supported: H a multiple of 16 in [16, 64], D = 128, page_size = 64,
+ * 1 <= topk <= 2048, max_context_len <= 131072 (larger needs no change but
+ * is untested).
+ */
+dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
+                                   const uint8_t* k_cache, const float* k_scale,
+                                   const int32_t* block_table, int max_pages_per_seq,
+                                   const int32_t* context_lens, int max_context_len,
+                                   int B, int H, int D, int page_size, int num_pages, int topk,
+                                   int32_t* topk_idx, float* topk_score,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, int D, int topk);
+
+/*
+ * topk_select -- the token selector on its own: top-k of each row of a score
+ * matrix.
+ *
+ * Passage: the top-k step of "From formula to code", section 3 (top-k over
+ * the masked score rows) with the tie and short-row rules above.  Row r's
+ * valid entries are its first row_len[r] columns (all `cols` if row_len is
+ * NULL); entries past that are never read.
+ *
+ *   scores   [rows] rows of `cols` fp32 values, row r starting at
+ *            scores + r * row_stride (row_stride >= cols, in elements)
+ *   row_len  [rows] int32 in [0, cols], or NULL
+ *   idx_out  out [rows][topk] int32;  val_out out [rows][topk] fp32 or NULL
+ *
+ * Supported: 1 <= rows, 1 <= cols <= 4194304, 1 <= topk <= 2048.
+ */
+dsaidx_status topk_select(const float* scores, int rows, int cols, int64_t row_stride,
+                          const int32_t* row_len, int topk,
+                          int32_t* idx_out, float* val_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+size_t topk_select_workspace_bytes(int rows, int cols, int topk);
+
+/* Static text for a status code. */
+const char* dsaidx_status_string(int status);
+
+/* Detail of the last non-OK status returned on the calling thread
+ * (which argument, which limit, or the HIP error string).  Thread-local,
+ * valid until the next call on the same thread. */
+const char* dsaidx_last_error(void);
+
+/* Library version as an integer: major * 10000 + minor * 100 + patch. */
+int dsaidx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSAIDX_H */

@@ -1,0 +1,117 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and every argument check fires on the host before any HIP
+call (so these run on a CPU-only machine)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsaidx.h")
+LIB = os.path.join(ROOT, "dsa_lightning_indexer_03_amd", "libdsaidx.so")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, WS = 0, 1, 2, 3, 4, 5
+P = 4096  # a fake, 16-byte aligned, non-NULL device address (never dereferenced)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libdsaidx.so not built")
+    from dsa_lightning_indexer_03_amd import _lib
+    return _lib.load(LIB)
+
+
+def test_header_declares_the_three_entry_points():
+    fns = header_functions()
+    for name in ("indexer_prefill", "indexer_decode_paged", "topk_select"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported(lib):
+    fns = header_functions()
+    assert len(fns) >= 9
+    for name in fns:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(fns) <= exported
+    from dsa_lightning_indexer_03_amd import _lib
+    assert set(fns) == set(_lib.SIGNATURES)
+
+
+def test_status_strings(lib):
+    assert lib.dsaidx_status_string(0) == b"ok"
+    for s in range(1, 7):
+        assert lib.dsaidx_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.dsaidx_version() >= 100
+
+
+def prefill(lib, q=P, qs=None, k=P, ks=None, dt=1, w=P, B=1, L=64, H=16, D=128, topk=8,
+            idx=P, val=None, sc=None, ws=None, nws=0):
+    return lib.indexer_prefill(q, qs, k, ks, dt, w, B, L, H, D, topk, idx, val, sc, ws, nws, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(w=None), NULL), (dict(idx=None), NULL),
+    (dict(dt=7), DTYPE), (dict(dt=2), NULL), (dict(dt=2, qs=P), NULL), (dict(qs=P), SHAPE),
+    (dict(B=0), SHAPE), (dict(L=0), SHAPE), (dict(H=0), SHAPE), (dict(topk=0), SHAPE),
+    (dict(L=131073), UNSUP), (dict(H=6), UNSUP), (dict(H=68), UNSUP), (dict(D=96), UNSUP),
+    (dict(topk=2049), UNSUP), (dict(q=P + 4), UNSUP),
+    (dict(dt=0, H=4, D=32), WS), (dict(dt=0, H=4, D=32, ws=P, nws=64 * 64 * 4 - 1), WS),
+])
+def test_prefill_rejects_before_launch(lib, kw, status):
+    assert prefill(lib, **kw) == status
+    assert lib.dsaidx_last_error()  # a detail message is set
+
+
+def test_prefill_workspace_query(lib):
+    assert lib.indexer_prefill_workspace_bytes(1, 8192, 64, 128, 2048, 2, 0) == 0   # fused
+    assert lib.indexer_prefill_workspace_bytes(2, 256, 4, 32, 16, 0, 0) == 2 * 256 * 256 * 4
+    assert lib.indexer_prefill_workspace_bytes(2, 256, 4, 32, 16, 0, 1) == 0
+
+
+def decode(lib, q=P, qd=1, w=P, kc=P, ks=P, bt=P, mpp=4, cl=P, mcl=256, B=2, H=64, D=128, ps=64,
+           npg=8, topk=16, idx=P, val=None, ws=P, nws=None):
+    if nws is None:
+        nws = lib.indexer_decode_paged_workspace_bytes(B, mcl, H, D, topk)
+    return lib.indexer_decode_paged(q, qd, w, kc, ks, bt, mpp, cl, mcl, B, H, D, ps, npg, topk, idx, val,
+                                    ws, nws, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(w=None), NULL), (dict(kc=None), NULL), (dict(ks=None), NULL),
+    (dict(bt=None), NULL), (dict(cl=None), NULL), (dict(idx=None), NULL),
+    (dict(qd=9), DTYPE), (dict(qd=0), UNSUP), (dict(qd=2), UNSUP),
+    (dict(B=0), SHAPE), (dict(mcl=-1), SHAPE), (dict(mcl=257), SHAPE), (dict(npg=0), SHAPE),
+    (dict(H=8), UNSUP), (dict(D=64), UNSUP), (dict(ps=32, mcl=128), UNSUP), (dict(topk=4096), UNSUP),
+    (dict(ws=None), WS), (dict(nws=100), WS), (dict(kc=P + 8), UNSUP),
+])
+def test_decode_rejects_before_launch(lib, kw, status):
+    assert decode(lib, **kw) == status
+
+
+def test_decode_workspace_query(lib):
+    n = lib.indexer_decode_paged_workspace_bytes(64, 131072, 64, 128, 2048)
+    assert n == 64 * 131072 * 4 + 64 * 2048 * 4
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 4, 100, 100, None, 8, P, None), NULL),
+    ((P, 4, 100, 100, None, 8, None, None), NULL),
+    ((P, 0, 100, 100, None, 8, P, None), SHAPE),
+    ((P, 4, 100, 99, None, 8, P, None), SHAPE),
+    ((P, 4, 100, 100, None, 0, P, None), SHAPE),
+    ((P, 4, 100, 100, None, 2049, P, None), UNSUP),
+    ((P, 4, 4194305, 4194305, None, 8, P, None), UNSUP),
+])
+def test_topk_select_rejects_before_launch(lib, args, status):
+    assert lib.topk_select(*args, None, 0, None) == status

@@ -1,0 +1,126 @@
+"""GPU parity of indexer_decode_paged against the fp64 oracle: scattered and
+contiguous page tables, contexts shorter than k, partial last pages, the
+full fp8 code range, and layout independence (a permuted page table gives
+bit-identical results to the identity layout)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import run_decode, run_prefill, say
+from oracle import indexer
+from oracle.check import check_topk_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def parity(d, K, name="", queries=None, max_context_len=None):
+    B = d["q"].shape[0]
+    say(f"decode {name}: B={B} ctx={d['context_lens'][:8].tolist()} H={d['H']} K={K}")
+    gi, gv = run_decode(d, K, max_context_len)
+    qs = range(B) if queries is None else queries
+    swaps = 0
+    for b in qs:
+        o = indexer.decode_scores(d, b)
+        swaps += check_topk_rows(gi[b:b + 1], gv[b:b + 1], o[None], [o.size], K, where=f"{name} q{b}")
+    say(f"  ok, near-tie swaps={swaps}")
+    return gi, gv
+
+
+def test_small_scattered_pages():
+    d = synth.decode_inputs(5, [100, 64, 130, 30, 1], 64, 128, seed=500, permute=True)
+    parity(d, 50, "small")
+
+
+@pytest.mark.parametrize("H", [16, 32, 48, 64])
+def test_head_counts(H):
+    d = synth.decode_inputs(3, [5000, 4097, 4095], H, 128, seed=510 + H, permute=True)
+    parity(d, 256, f"H={H}")
+
+
+def test_long_context_k2048():
+    d = synth.decode_inputs(4, [20000, 9000, 2048, 2047], 64, 128, seed=520, permute=True)
+    gi, _ = parity(d, 2048, "long")
+    assert np.all(gi[3, 2047:] == -1) and sorted(gi[3, :2047].tolist()) == list(range(2047))
+
+
+def test_permuted_equals_identity_bitwise():
+    d1 = synth.decode_inputs(3, [3000, 700, 5000], 64, 128, seed=530, permute=True)
+    ps = 64
+    rows_c, rows_s, bt = [], [], np.zeros_like(d1["block_table"])
+    off = 0
+    for b in range(3):
+        n = -(-int(d1["context_lens"][b]) // ps)
+        for j in range(n):
+            p = d1["block_table"][b, j]
+            rows_c.append(d1["k_cache"][p])
+            rows_s.append(d1["k_scale"][p])
+            bt[b, j] = off + j
+        off += n
+    d2 = dict(d1, k_cache=np.stack(rows_c), k_scale=np.stack(rows_s), block_table=bt)
+    i1, v1 = run_decode(d1, 300)
+    i2, v2 = run_decode(d2, 300)
+    for b in range(3):
+        o1 = np.argsort(i1[b])
+        o2 = np.argsort(i2[b])
+        assert np.array_equal(i1[b][o1], i2[b][o2])
+        assert np.array_equal(v1[b][o1].view(np.uint32), v2[b][o2].view(np.uint32))
+
+
+def test_every_fp8_code_decodes():
+    """A cache whose 256 tokens hold each E4M3 code (except the two NaNs,
+    replaced by 0) in dim 0; the query is +1 on head 0 and -1 on head 1
+    in dim 0, so every code's value reaches a score through one ReLU."""
+    H, D, K = 16, 128, 2048
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0xFF]] = 0
+    kc = np.zeros((4, 64, D), np.uint8)
+    kc.reshape(256, D)[:, 0] = codes
+    ks = np.full((4, 64), 0.5, np.float32)
+    q = np.zeros((1, H, D), np.float32)
+    q[0, 0, 0], q[0, 1, 0] = 1.0, -1.0
+    w = np.zeros((1, H), np.float32)
+    w[0, :2] = 1.0
+    d = dict(q=synth.to_bf16_bits(q), w=w, k_cache=kc, k_scale=ks,
+             block_table=np.arange(4, dtype=np.int32)[None], context_lens=np.array([256], np.int32),
+             page_size=64, q_dtype="bf16", H=H)
+    parity(d, K, "fp8 codes")
+
+
+def test_max_context_bound_smaller_than_table():
+    d = synth.decode_inputs(2, [500, 300], 64, 128, seed=540, permute=True, max_pages_per_seq=20)
+    parity(d, 100, "bound", max_context_len=512)
+
+
+def test_prefill_row_matches_decode_of_prefix():
+    """Row t of an fp8 prefill and a decode with ctx = t+1 over the same keys
+    agree within tolerance (the query rows are fp8 values, exactly bf16)."""
+    L, H, D, K = 700, 64, 128, 64
+    inp = synth.prefill_inputs(1, L, H, D, "fp8", seed=550)
+    inp["q_scale"][:] = 1.0   # query values are then fp8 codes, exactly bf16
+    gi, gv, gs = run_prefill(inp, K, want_scores=True)
+    from oracle import formats
+    for t in (63, 64, 699):
+        qv = formats.decode(inp["q"][0, t], "fp8", inp["q_scale"][0, t]).astype(np.float32)
+        qb = synth.to_bf16_bits(qv)
+        assert np.array_equal(synth.gen.bf16_bits_to_f32(qb), qv)  # exact in bf16
+        ctx = t + 1
+        npg = -(-ctx // 64)
+        kc = np.zeros((npg, 64, D), np.uint8)
+        ks = np.ones((npg, 64), np.float32)
+        kc.reshape(-1, D)[:ctx] = inp["k"][0, :ctx]
+        ks.reshape(-1)[:ctx] = inp["k_scale"][0, :ctx]
+        d = dict(q=qb[None], w=inp["w"][0, t:t + 1], k_cache=kc, k_scale=ks,
+                 block_table=np.arange(npg, dtype=np.int32)[None], context_lens=np.array([ctx], np.int32),
+                 page_size=64, q_dtype="bf16", H=H)
+        di, dv = run_decode(d, K)
+        o = indexer.decode_scores(d, 0)
+        check_topk_rows(di, dv, o[None], [ctx], K, where=f"decode t={t}")
+        check_topk_rows(gi[0, t:t + 1], gv[0, t:t + 1], gs[0, t:t + 1, :ctx].astype(np.float64), [ctx], K,
+                        where=f"prefill-vs-gpu-scores t={t}")

@@ -1,0 +1,93 @@
+"""GPU parity of the standalone selector (topk_select) against the oracle's
+full sort.  Selection over identical fp32 inputs is integer work: the sets
+and the returned values must match exactly."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+import dsa_lightning_indexer_03_amd as dsa  # noqa: E402
+from oracle import indexer  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run(scores, K, row_len=None):
+    idx, val = dsa.topk_select(dev(scores), K, row_len=None if row_len is None else dev(row_len))
+    torch.cuda.synchronize()
+    return host(idx), host(val)
+
+
+def compare(scores, K, row_len=None, name=""):
+    say(f"topk_select {name}: rows={scores.shape[0]} cols={scores.shape[1]} K={K}")
+    gi, gv = run(scores, K, row_len)
+    oi, ov = indexer.topk_rows(scores, row_len, K)
+    for r in range(scores.shape[0]):
+        n = scores.shape[1] if row_len is None else int(row_len[r])
+        m = min(K, n)
+        assert np.all(gi[r, m:] == -1) and np.all(np.isneginf(gv[r, m:])), (name, r)
+        assert sorted(gi[r, :m].tolist()) == sorted(oi[r, :m].tolist()), (name, r)
+        # values are the input scores of the returned positions (-0.0 == +0.0)
+        assert np.array_equal(gv[r, :m], scores[r, gi[r, :m]]), (name, r)
+
+
+def test_random_rows():
+    rng = np.random.default_rng(100)
+    compare(rng.standard_normal((8, 5000)).astype(np.float32), 100, name="random")
+
+
+def test_row_lengths_including_empty_and_short():
+    rng = np.random.default_rng(101)
+    s = rng.standard_normal((7, 3000)).astype(np.float32)
+    rl = np.array([0, 1, 99, 100, 101, 2999, 3000], np.int32)
+    compare(s, 100, rl, name="row_len")
+
+
+def test_tie_heavy_rows():
+    rng = np.random.default_rng(102)
+    s = np.round(rng.standard_normal((6, 20000)), 1).astype(np.float32)
+    compare(s, 2048, name="ties")
+
+
+def test_signed_zeros_tie():
+    rng = np.random.default_rng(103)
+    s = rng.choice(np.array([-0.0, 0.0, 0.0, 1.0, -1.0], np.float32), size=(4, 9000)).astype(np.float32)
+    compare(s, 2048, name="zeros")
+
+
+def test_huge_exact_tie_uses_lowest_positions():
+    s = np.ones((2, 40000), np.float32)
+    s[1, 5] = 2.0
+    gi, _ = run(s, 2048)
+    assert sorted(gi[0].tolist()) == list(range(2048))
+    assert sorted(gi[1].tolist()) == list(range(2048))
+    compare(s, 2048, name="huge tie")
+
+
+def test_crowded_bin_beyond_lds():
+    rng = np.random.default_rng(104)
+    s = rng.standard_normal((3, 60000)).astype(np.float32)
+    s[:, ::2] = 0.75 + rng.integers(0, 4, size=(3, 30000)).astype(np.float32) * 1e-6
+    compare(s, 2048, name="crowded")
+
+
+def test_long_rows_and_infinities():
+    rng = np.random.default_rng(105)
+    s = rng.standard_normal((4, 131072)).astype(np.float32)
+    s[0, :100000] = -np.inf
+    s[1, ::3] = -np.inf
+    compare(s, 2048, name="long")
+
+
+def test_all_k_values_small():
+    rng = np.random.default_rng(106)
+    s = rng.standard_normal((3, 777)).astype(np.float32)
+    for K in (1, 2, 7, 64, 776, 777, 778, 2048):
+        compare(s, K, name=f"K={K}")
