@@ -1,0 +1,225 @@
+"""Throughput of the lightning indexer on one MI355X.
+
+Headline: indexer score + top-k pairs/s of the fused fp8 prefill at
+L = 32768 (B=1, H=64, D=128, k=2048, OCP e4m3 with per-row fp32 scales,
+causal); a step is one indexer_prefill call over inputs already resident in
+HBM.  Alongside, in the same JSON line: paged-decode K-cache GB/s for the
+64 x 131072 contiguous workload and the 128-query scattered-page workload,
+the roofline of the dominant kernel, and the CPU oracle timed on a bounded
+sample of the headline workload (whose rows are also parity-checked against
+the GPU output).
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "indexer score+top-k pairs/s (prefill L=32K) and decode K-cache GB/s"
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def up(torch, a, dev):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(dev)
+
+
+def time_calls(torch, fn, steps, warmup):
+    """Runs fn warmup times, then `steps` times with a HIP event pair around
+    each call on the current stream (the stream the library launches on).
+    Returns per-call milliseconds and the wall time of the timed region."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in evs], wall
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return int(info[0]["num_threads"]), info[0].get("internal_api", "blas")
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0)), "unknown"
+
+
+def cpu_baseline_prefill(inp, K, gpu_idx, gpu_val, seconds):
+    """The oracle as it stands on a time-bounded, seeded sample of rows of
+    the headline workload; the sampled rows are also checked against the
+    GPU's output of the timed run."""
+    from oracle import indexer
+    from oracle.check import check_topk_rows
+
+    L = inp["q"].shape[1]
+    rng = np.random.default_rng(12345)
+    first = [0, K - 2, K - 1, K, L - 1]
+    rest = [int(x) for x in rng.permutation(L) if int(x) not in first]
+    order = first + rest
+    done, pairs, t_oracle = [], 0, 0.0
+    chunk = 16
+    i = 0
+    while i < len(order) and t_oracle < seconds:
+        rows = np.array(order[i:i + chunk])
+        t0 = time.perf_counter()
+        oi, ov, osc = indexer.prefill(inp, K, rows=rows, want_scores=True)
+        t_oracle += time.perf_counter() - t0
+        check_topk_rows(gpu_idx[rows], gpu_val[rows], osc[0], rows + 1, K, where="bench prefill sample")
+        done += rows.tolist()
+        pairs += int((rows + 1).sum())
+        i += chunk
+    threads, api = blas_threads()
+    return {"value": pairs / t_oracle, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done)} seeded rows of the L=32768 fp8 workload (incl. t=0,{K-2},{K-1},{K},{L-1}); "
+                      f"{pairs} causal pairs scored + full-sort top-k in {t_oracle:.1f} s, numpy fp64 with "
+                      f"{threads} {api} threads; every sampled row parity-checked against the GPU output"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dsa_lightning_indexer_03_amd as dsa
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    # ---------------- headline: fused fp8 prefill, L = 32768 ----------------
+    cfg = synth.CONFIGS[3]
+    L, H, D, K = cfg["L"], cfg["H"], cfg["D"], cfg["topk"]
+    t0 = time.perf_counter()
+    inp = synth.config_inputs(3)
+    log(f"generated prefill inputs in {time.perf_counter() - t0:.1f} s")
+    q, k, w = up(torch, inp["q"], dev), up(torch, inp["k"], dev), up(torch, inp["w"], dev)
+    qs, ks = up(torch, inp["q_scale"], dev), up(torch, inp["k_scale"], dev)
+    out = {}
+
+    def step():
+        out["r"] = dsa.indexer_prefill(q, k, w, K, q_scale=qs, k_scale=ks)
+
+    ms, wall = time_calls(torch, step, args.steps, args.warmup)
+    pairs = L * (L + 1) // 2
+    ms_avg = float(np.mean(ms))
+    flops = 2.0 * H * D * pairs
+    achieved = flops / (ms_avg * 1e-3) / 1e12
+    log(f"prefill: {ms_avg:.3f} ms/step (min {min(ms):.3f}), {pairs / (ms_avg * 1e-3):.4g} pairs/s, "
+        f"{achieved:.1f} TFLOP/s")
+
+    gpu_idx = out["r"][0].cpu().numpy()[0]
+    gpu_val = out["r"][1].cpu().numpy()[0]
+
+    result = {
+        "metric": METRIC,
+        "value": pairs / (ms_avg * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_avg,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": "prefill B=1 L=32768 H=64 D=128 k=2048, fp8 e4m3 q/k with per-row fp32 scales, "
+                               "causal s<=t, fused score+top-k (no [L,L] in HBM)",
+                   "batch": 1, "L": L, "H": H, "D": D, "topk": K, "seed": 3},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None,
+                     "kernel": "prefill_fused_kernel<fp8,H=64>",
+                     "work": f"2*H*D flop per causal pair x {pairs} pairs = {flops:.4g} flop per launch"},
+        "wall_s_timed": wall,
+    }
+    del q, k, w, qs, ks, out
+    torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # ---------------- decode: contiguous and scattered pages ----------------
+    if not args.no_decode:
+        dec = {}
+        for n in (4, 5):
+            c = synth.CONFIGS[n]
+            t0 = time.perf_counter()
+            d = synth.config_inputs(n)
+            log(f"generated decode workload {n} in {time.perf_counter() - t0:.1f} s")
+            args_d = [up(torch, d[x], dev) for x in ("q", "w", "k_cache", "k_scale", "block_table", "context_lens")]
+            mcl = d["max_pages_per_seq"] * d["page_size"]
+            ws = torch.empty(dsa.decode_workspace_bytes(c["B"], mcl, c["H"], c["D"], c["topk"]),
+                             dtype=torch.uint8, device=dev)
+
+            def dstep():
+                dsa.indexer_decode_paged(*args_d, c["topk"], max_context_len=mcl, workspace=ws)
+
+            dms, _ = time_calls(torch, dstep, max(args.steps, 10), args.warmup)
+            nbytes = int(d["context_lens"].astype(np.int64).sum()) * (c["D"] + 4)
+            gbs = nbytes / (np.mean(dms) * 1e-3) / 1e9
+            log(f"decode {n}: {np.mean(dms) * 1e3:.1f} us/call, {gbs:.0f} GB/s")
+            dec[f"workload_{n}"] = {
+                "what": ("64 queries x 131072-token contiguous fp8 cache" if n == 4 else
+                         "128 queries, ctx ~ U[4096,131072], 64-token pages scattered by a seeded permutation"),
+                "kcache_bytes": nbytes, "us_per_call": float(np.mean(dms) * 1e3), "GB/s": gbs,
+                "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "topk": c["topk"],
+            }
+            del args_d, ws
+            torch.cuda.empty_cache()
+        result["decode"] = dec
+
+    # ---------------- CPU oracle baseline (rank 0, N=1) ----------------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefill(inp, K, gpu_idx, gpu_val, args.cpu_seconds)
+        log(f"cpu baseline: {result['cpu_baseline']['value']:.4g} pairs/s")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
