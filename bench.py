@@ -109,6 +109,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true", help="skip the prefill headline (profiling aid)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (for counter calibration)")
     args = ap.parse_args()
@@ -127,54 +128,57 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
 
+    result = {"metric": METRIC, "decode_only": True}
+    inp = gpu_idx = gpu_val = None
     # ---------------- headline: fused fp8 prefill, L = 32768 ----------------
-    cfg = synth.CONFIGS[3]
-    L, H, D, K = cfg["L"], cfg["H"], cfg["D"], cfg["topk"]
-    t0 = time.perf_counter()
-    inp = synth.config_inputs(3)
-    log(f"generated prefill inputs in {time.perf_counter() - t0:.1f} s")
-    q, k, w = up(torch, inp["q"], dev), up(torch, inp["k"], dev), up(torch, inp["w"], dev)
-    qs, ks = up(torch, inp["q_scale"], dev), up(torch, inp["k_scale"], dev)
-    out = {}
+    if not args.decode_only:
+        cfg = synth.CONFIGS[3]
+        L, H, D, K = cfg["L"], cfg["H"], cfg["D"], cfg["topk"]
+        t0 = time.perf_counter()
+        inp = synth.config_inputs(3)
+        log(f"generated prefill inputs in {time.perf_counter() - t0:.1f} s")
+        q, k, w = up(torch, inp["q"], dev), up(torch, inp["k"], dev), up(torch, inp["w"], dev)
+        qs, ks = up(torch, inp["q_scale"], dev), up(torch, inp["k_scale"], dev)
+        out = {}
 
-    def step():
-        out["r"] = dsa.indexer_prefill(q, k, w, K, q_scale=qs, k_scale=ks)
+        def step():
+            out["r"] = dsa.indexer_prefill(q, k, w, K, q_scale=qs, k_scale=ks)
 
-    ms, wall = time_calls(torch, step, args.steps, args.warmup)
-    pairs = L * (L + 1) // 2
-    ms_avg = float(np.mean(ms))
-    flops = 2.0 * H * D * pairs
-    achieved = flops / (ms_avg * 1e-3) / 1e12
-    log(f"prefill: {ms_avg:.3f} ms/step (min {min(ms):.3f}), {pairs / (ms_avg * 1e-3):.4g} pairs/s, "
-        f"{achieved:.1f} TFLOP/s")
+        ms, wall = time_calls(torch, step, args.steps, args.warmup)
+        pairs = L * (L + 1) // 2
+        ms_avg = float(np.mean(ms))
+        flops = 2.0 * H * D * pairs
+        achieved = flops / (ms_avg * 1e-3) / 1e12
+        log(f"prefill: {ms_avg:.3f} ms/step (min {min(ms):.3f}), {pairs / (ms_avg * 1e-3):.4g} pairs/s, "
+            f"{achieved:.1f} TFLOP/s")
 
-    gpu_idx = out["r"][0].cpu().numpy()[0]
-    gpu_val = out["r"][1].cpu().numpy()[0]
+        gpu_idx = out["r"][0].cpu().numpy()[0]
+        gpu_val = out["r"][1].cpu().numpy()[0]
 
-    result = {
-        "metric": METRIC,
-        "value": pairs / (ms_avg * 1e-3),
-        "unit": "pairs/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_avg,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8_e4m3",
-        "data": "synthetic",
-        "config": {"workload": "prefill B=1 L=32768 H=64 D=128 k=2048, fp8 e4m3 q/k with per-row fp32 scales, "
-                               "causal s<=t, fused score+top-k (no [L,L] in HBM)",
-                   "batch": 1, "L": L, "H": H, "D": D, "topk": K, "seed": 3},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None,
-                     "kernel": "prefill_fused_kernel<fp8,H=64>",
-                     "work": f"2*H*D flop per causal pair x {pairs} pairs = {flops:.4g} flop per launch"},
-        "wall_s_timed": wall,
-    }
-    del q, k, w, qs, ks, out
-    torch.cuda.empty_cache()
+        result = {
+            "metric": METRIC,
+            "value": pairs / (ms_avg * 1e-3),
+            "unit": "pairs/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": ms_avg,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "fp8_e4m3",
+            "data": "synthetic",
+            "config": {"workload": "prefill B=1 L=32768 H=64 D=128 k=2048, fp8 e4m3 q/k with per-row fp32 scales, "
+                                   "causal s<=t, fused score+top-k (no [L,L] in HBM)",
+                       "batch": 1, "L": L, "H": H, "D": D, "topk": K, "seed": 3},
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None,
+                         "kernel": "prefill_fused_kernel<fp8,H=64>",
+                         "work": f"2*H*D flop per causal pair x {pairs} pairs = {flops:.4g} flop per launch"},
+            "wall_s_timed": wall,
+        }
+        del q, k, w, qs, ks, out
+        torch.cuda.empty_cache()
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -214,7 +218,7 @@ def main():
         result["decode"] = dec
 
     # ---------------- CPU oracle baseline (rank 0, N=1) ----------------
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.decode_only:
         result["cpu_baseline"] = cpu_baseline_prefill(inp, K, gpu_idx, gpu_val, args.cpu_seconds)
         log(f"cpu baseline: {result['cpu_baseline']['value']:.4g} pairs/s")
 

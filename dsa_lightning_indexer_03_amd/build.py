@@ -29,6 +29,8 @@ FLAGS = [
     "-fPIC",
     "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: no accvgpr copies around the epilogues
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
     f"-I{INCLUDE}",

@@ -169,8 +169,11 @@ dsaidx_status indexer_prefill(const void* q, const float* q_scale, const void* k
 size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, int D, int topk) {
     (void)H; (void)D; (void)topk;
     if (B < 1 || max_context_len < 0) return 0;
-    return (size_t)B * decode_score_stride(max_context_len) * sizeof(float) +
-           (size_t)B * dsaidx::kHistBins * sizeof(uint32_t);
+    // scores, candidate scores, candidate positions: [B][stride] each;
+    // first-digit histogram [B][2048]; two counters per query.
+    // per-query page prefix [B+1].
+    return (size_t)B * decode_score_stride(max_context_len) * 12u +
+           (size_t)B * (dsaidx::kHistBins + dsaidx::kCtrlStride) * sizeof(uint32_t) + (size_t)(B + 1) * sizeof(int32_t);
 }
 
 dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
@@ -204,16 +207,23 @@ dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
     if (topk > kMaxTopk) return fail(DSAIDX_ERR_UNSUPPORTED, "topk=%d > %d", topk, kMaxTopk);
     if (max_context_len > kMaxSelectCols) return fail(DSAIDX_ERR_UNSUPPORTED, "max_context_len too large");
     if (!aligned16(q) || !aligned16(k_cache)) return fail(DSAIDX_ERR_UNSUPPORTED, "q and k_cache must be 16-byte aligned");
+    if (!aligned16(workspace)) return fail(DSAIDX_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
     const size_t need = indexer_decode_paged_workspace_bytes(B, max_context_len, H, D, topk);
     if (!workspace || workspace_bytes < need)
         return fail(DSAIDX_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
 
     hipStream_t st = (hipStream_t)stream;
     const size_t stride = decode_score_stride(max_context_len);
-    float* sc = reinterpret_cast<float*>(workspace);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(workspace) + (size_t)B * stride * sizeof(float));
-    hipError_t e = dsaidx::launch_zero_u32(hist, (size_t)B * dsaidx::kHistBins, st);
-    if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (clear)");
+    char* wp = reinterpret_cast<char*>(workspace);
+    float* sc = reinterpret_cast<float*>(wp);
+    float* cand_score = reinterpret_cast<float*>(wp + (size_t)B * stride * 4);
+    int32_t* cand_pos = reinterpret_cast<int32_t*>(wp + (size_t)B * stride * 8);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(wp + (size_t)B * stride * 12);
+    uint32_t* ctrl = hist + (size_t)B * dsaidx::kHistBins;   // [B][kCtrlStride]
+    uint32_t* pre_count = ctrl;
+    uint32_t* cand_n = ctrl + 1;
+    int32_t* prefix = reinterpret_cast<int32_t*>(ctrl + (size_t)B * dsaidx::kCtrlStride);
+    hipError_t e;
     if (max_context_len > 0) {
         dsaidx::DecodeArgs d{};
         d.q = reinterpret_cast<const uint16_t*>(q);
@@ -229,16 +239,43 @@ dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
         d.scores = sc;
         d.score_stride = (int64_t)stride;
         d.hist = hist;
+        d.prefix = prefix;
         e = dsaidx::launch_decode_scan(d, H, max_context_len, st);
         if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (scan)");
+        dsaidx::DecodeFilterArgs f{};
+        f.scores = sc;
+        f.stride = (int64_t)stride;
+        f.context_lens = context_lens;
+        f.max_ctx = max_context_len;
+        f.hist = hist;
+        f.pre_count = pre_count;
+        f.cand_n = cand_n;
+        f.cand_score = cand_score;
+        f.cand_pos = cand_pos;
+        f.B = B;
+        f.topk = topk;
+        f.idx_out = topk_idx;
+        f.val_out = topk_score;
+        e = dsaidx::launch_decode_filter(f, st);
+        if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (filter)");
+    } else {
+        e = dsaidx::launch_zero_u32(hist, (size_t)B * (dsaidx::kHistBins + dsaidx::kCtrlStride), st);
+        if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (clear)");
     }
+    // Exact finish among the candidates of the k-th score's first digit.
     dsaidx::SelectArgs s{};
-    s.scores = sc;
+    s.scores = cand_score;
     s.row_stride = (int64_t)stride;
-    s.cols = max_context_len > 0 ? max_context_len : 1;
-    s.row_len = context_lens;
+    s.cols = (int)(stride > 0 ? stride : 1);
+    s.row_len = reinterpret_cast<const int32_t*>(cand_n);
+    s.counter_stride = dsaidx::kCtrlStride;
+    s.level0_bin = max_context_len > 0 ? ctrl + 2 : nullptr;
     s.causal_L = 0;
-    s.hist = hist;
+    s.pos = cand_pos;
+    s.hist = nullptr;
+    s.pre_count = pre_count;
+    s.total = context_lens;
+    s.total_max = max_context_len;
     s.topk = topk;
     s.idx_out = topk_idx;
     s.val_out = topk_score;

@@ -56,6 +56,11 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
     return v;
 }
 
+// max(x, 0) on the bit pattern: one integer max, and -0.0 (INT_MIN as an
+// integer) maps to +0.0.  An IEEE float max would need its input quieted
+// first (an extra instruction) since MFMA results are not known canonical.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Wave-uniform value from lane 0 (tells the compiler it is uniform).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

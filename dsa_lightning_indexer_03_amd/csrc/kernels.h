@@ -8,20 +8,43 @@
 namespace dsaidx {
 
 constexpr int kHistBins = 2048;        // first radix digit: score key bits [31:21]
-constexpr int kDecodeSplit = 4096;     // tokens per decode workgroup
-constexpr int kFusedTokensPerBlock = 4;
-constexpr int kFusedCap = 4096;        // per-row candidate buffer (entries)
+constexpr int kCtrlStride = 64;        // u32 words between per-query counters (own cache lines)
 
 struct SelectArgs {
     const float* scores;
     int64_t row_stride;
     int cols;
-    const int32_t* row_len;   // nullable
-    int causal_L;             // > 0: row r has (r % causal_L) + 1 valid entries
-    const uint32_t* hist;     // nullable [rows][kHistBins] first-digit histogram
+    const int32_t* row_len;   // nullable: entries of row r = row_len[r * counter_stride] (else cols)
+    int causal_L;             // > 0: row r has (r % causal_L) + 1 entries
+    const int32_t* pos;       // nullable [rows][row_stride]: position of each entry (else its column)
+    const uint32_t* hist;     // nullable [rows][kHistBins] first-digit histogram of the entries
+    const uint32_t* level0_bin;  // nullable [rows * counter_stride]: every entry of row r has first
+                                 // digit level0_bin[r * counter_stride] (the histogram is then skipped)
+    int counter_stride;       // element stride of row_len and pre_count (0 means 1)
+    const uint32_t* pre_count;  // nullable: output slots [0, pre_count[r * counter_stride]) already hold selected
+                                // positions that outrank every entry of the row
+    const int32_t* total;     // nullable [rows]: valid positions of the row, clamped to [0, total_max];
+    int total_max;            //   the row returns min(topk, total) positions (default: its entry count)
     int topk;
     int32_t* idx_out;
     float* val_out;           // nullable
+};
+
+struct DecodeFilterArgs {
+    const float* scores;      // [B][stride]
+    int64_t stride;
+    const int32_t* context_lens;
+    int max_ctx;
+    const uint32_t* hist;     // [B][kHistBins]
+    uint32_t* pre_count;      // [B * kCtrlStride] entries emitted straight to the output; word 2 of
+                              // each query's block receives the first digit of its k-th score
+    uint32_t* cand_n;         // [B * kCtrlStride] entries sent to the candidate list
+    float* cand_score;        // [B][stride]
+    int32_t* cand_pos;        // [B][stride]
+    int B;
+    int topk;
+    int32_t* idx_out;
+    float* val_out;
 };
 
 struct DecodeArgs {
@@ -37,7 +60,8 @@ struct DecodeArgs {
     float inv_sqrt_d;
     float* scores;            // [B][score_stride]
     int64_t score_stride;
-    uint32_t* hist;           // [B][kHistBins]
+    uint32_t* hist;           // [B][kHistBins], then [B][kCtrlStride] per-query counters
+    int32_t* prefix;          // [B+1] exclusive prefix of per-query page counts
 };
 
 struct PrefillArgs {
@@ -58,6 +82,8 @@ size_t topk_select_smem_bytes();
 hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
 hipError_t launch_decode_scan(const DecodeArgs& a, int H, int max_ctx, hipStream_t stream);
+hipError_t launch_decode_filter(const DecodeFilterArgs& a, hipStream_t stream);
+constexpr int kFilterChunk = 8192;     // entries per filter workgroup
 hipError_t launch_prefill_scores_generic(const PrefillArgs& a, int dtype, float* out, hipStream_t stream);
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream);
 

@@ -9,8 +9,11 @@
 // causal half; D = 128 and H is a multiple of 16.
 //
 // Layout of the work:
-// * workgroup = 4 independent waves; wave w owns query token t = 4*blk + w and
+// * workgroup = W independent waves; wave w owns query token t = W*blk + w and
 //   all 16*HB of its heads.  Blocks are issued heaviest (largest t) first.
+//   For L <= 65536 positions fit 16 bits: W = 8 waves (two per SIMD, so one
+//   wave's MFMAs overlap the other's VALU epilogue) with 3072-entry buffers;
+//   longer sequences use W = 4 with 4096-entry buffers and 32-bit positions.
 // * the token's queries sit in registers as MFMA A operands for the whole
 //   scan (head on M);  keys stream through registers as B operands (key on
 //   N), 16 keys per subtile, 64 keys per step.  No LDS is used for keys and
@@ -25,8 +28,8 @@
 //   positive scale, and the key's fp8 scale is applied once per key after
 //   the head sum), then a cross-lane reduce-scatter leaves lane l with the
 //   score of key s0 + l.
-// * streaming top-k per wave: a per-row candidate buffer of 4096 (key,
-//   position) pairs in LDS, filled in position order.  A score enters the
+// * streaming top-k per wave: a per-row candidate buffer of (key, position)
+//   pairs in LDS, filled in position order.  A score enters the
 //   buffer only if its order-preserving key beats the row threshold.  When
 //   the buffer nears capacity it is compacted: one radix digit below the
 //   buffer's common key prefix locates the bin of the k-th largest key, the
@@ -35,6 +38,8 @@
 //   always holds every entry that can still be in the row's top k.  At the
 //   end an exact radix select over the buffer finds the k-th largest key and
 //   ties at that key go to the lowest positions.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -43,9 +48,14 @@ namespace dsaidx {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kT = kFusedTokensPerBlock;  // waves (= tokens) per workgroup
-constexpr int kCap = kFusedCap;
-constexpr int kWaveSmemWords = 2 * kCap + 256;
+
+template <bool POS16>
+struct BufCfg {
+    using Pos = typename std::conditional<POS16, uint16_t, uint32_t>::type;
+    static constexpr int kWaves = POS16 ? 8 : 4;      // waves (= tokens) per workgroup
+    static constexpr int kCap = POS16 ? 3072 : 4096;  // candidates per row
+    static constexpr size_t kWaveBytes = (size_t)kCap * (4 + sizeof(Pos)) + 256 * 4;
+};
 
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 #pragma unroll
@@ -68,15 +78,17 @@ __device__ __forceinline__ float reduce_scatter4(const float v[4]) {
 }
 
 // Per-wave candidate buffer in LDS.
+template <typename Pos>
 struct RowBuf {
     uint32_t* key;
-    uint32_t* pos;
+    Pos* pos;
     uint32_t* hist;  // 256 bins
 };
 
 // Histogram of the 8-bit (or narrower) digit (key >> shift) & mask over the
 // buffer entries whose key matches (key & pm) == pv.
-__device__ __forceinline__ void wave_hist(const RowBuf& rb, int n, uint32_t pm, uint32_t pv,
+template <typename Pos>
+__device__ __forceinline__ void wave_hist(const RowBuf<Pos>& rb, int n, uint32_t pm, uint32_t pv,
                                           int shift, uint32_t dmask) {
     const int l = lane_id();
 #pragma unroll
@@ -91,7 +103,8 @@ __device__ __forceinline__ void wave_hist(const RowBuf& rb, int n, uint32_t pm, 
 
 // Bin (counting down from the top) where the running count reaches `need`.
 // Returns the bin; *above = count in bins above it.
-__device__ __forceinline__ uint32_t wave_find_bin(const RowBuf& rb, uint32_t need, uint32_t* above,
+template <typename Pos>
+__device__ __forceinline__ uint32_t wave_find_bin(const RowBuf<Pos>& rb, uint32_t need, uint32_t* above,
                                                   uint32_t* in_bin) {
     const int l = lane_id();
     uint32_t c[4];
@@ -116,7 +129,8 @@ __device__ __forceinline__ uint32_t wave_find_bin(const RowBuf& rb, uint32_t nee
 }
 
 // Common leading bits of all buffer keys: returns their count; *pv = value.
-__device__ __forceinline__ int wave_common_prefix(const RowBuf& rb, int n, uint32_t* pv) {
+template <typename Pos>
+__device__ __forceinline__ int wave_common_prefix(const RowBuf<Pos>& rb, int n, uint32_t* pv) {
     uint32_t o = 0u, a = 0xFFFFFFFFu;
     for (int j = lane_id(); j < n; j += kWave) {
         const uint32_t k = rb.key[j];
@@ -134,7 +148,8 @@ __device__ __forceinline__ int wave_common_prefix(const RowBuf& rb, int n, uint3
 // Exact k-th largest key of the buffer: returns kappa, *ties = how many
 // entries equal to kappa belong to the top `need` (the rest of the top are
 // strictly greater).
-__device__ uint32_t wave_kth_key(const RowBuf& rb, int n, uint32_t need, uint32_t* ties) {
+template <typename Pos>
+__device__ uint32_t wave_kth_key(const RowBuf<Pos>& rb, int n, uint32_t need, uint32_t* ties) {
     uint32_t pv;
     const int cp = wave_common_prefix(rb, n, &pv);
     uint32_t pm = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
@@ -157,7 +172,8 @@ __device__ uint32_t wave_kth_key(const RowBuf& rb, int n, uint32_t need, uint32_
 
 // Drops buffer entries that cannot be in the top k.  Returns the new count
 // and the new append threshold (append iff key > *thr).
-__device__ int wave_compact(const RowBuf& rb, int n, uint32_t K, uint32_t* thr) {
+template <typename Pos>
+__device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* thr, int cap) {
     const int l = lane_id();
     uint32_t pv;
     const int cp = wave_common_prefix(rb, n, &pv);
@@ -175,7 +191,7 @@ __device__ int wave_compact(const RowBuf& rb, int n, uint32_t K, uint32_t* thr) 
         const uint32_t b = wave_find_bin(rb, K, &above, &inb);
         lo_edge = pv | (b << shift);
         // Too many entries would survive (a crowded bin): fall back to exact.
-        if (above + inb > (uint32_t)(kCap - 1024)) exact = true;
+        if (above + inb > (uint32_t)(cap - 512)) exact = true;
     } else {
         exact = true;  // all keys equal
     }
@@ -187,7 +203,7 @@ __device__ int wave_compact(const RowBuf& rb, int n, uint32_t K, uint32_t* thr) 
         const int j = j0 + l;
         const bool ok = j < n;
         const uint32_t k = ok ? rb.key[j] : 0u;
-        const uint32_t p = ok ? rb.pos[j] : 0u;
+        const Pos p = ok ? rb.pos[j] : (Pos)0;
         bool keep;
         if (exact) {
             const bool eq = ok && k == kappa;
@@ -213,7 +229,8 @@ __device__ int wave_compact(const RowBuf& rb, int n, uint32_t K, uint32_t* thr) 
 
 // Writes the exact top K of the buffer (or all of it when n <= K) to the
 // output row, then the -1 / -inf padding.
-__device__ void wave_emit(const RowBuf& rb, int n, int K, int32_t* idx, float* val) {
+template <typename Pos>
+__device__ void wave_emit(const RowBuf<Pos>& rb, int n, int K, int32_t* idx, float* val) {
     const int l = lane_id();
     if (n <= K) {
         for (int j = l; j < K; j += kWave) {
@@ -316,26 +333,31 @@ struct Operands<1> {
     static constexpr int kRowBytes = kD * 2;
 };
 
-template <int DT, int HB>
-__global__ void __launch_bounds__(kT * kWave)
+template <int DT, int HB, bool POS16>
+__global__ void __launch_bounds__(BufCfg<POS16>::kWaves * kWave)
 prefill_fused_kernel(PrefillArgs a) {
-    extern __shared__ __align__(16) uint32_t smem[];
+    extern __shared__ __align__(16) unsigned char smem_raw[];
     using Op = Operands<DT>;
+    using Cfg = BufCfg<POS16>;
+    using Pos = typename Cfg::Pos;
+    constexpr int W = Cfg::kWaves;
+    constexpr int CAP = Cfg::kCap;
     constexpr int H = 16 * HB;
     const int L = a.L;
-    const int nblk = (L + kT - 1) / kT;
+    const int nblk = (L + W - 1) / W;
     const int b = blockIdx.x % a.B;
     const int blk = nblk - 1 - (int)(blockIdx.x / a.B);  // heaviest first
     const int wave = threadIdx.x / kWave;
-    const int t = blk * kT + wave;
+    const int t = blk * W + wave;
     if (t >= L) return;
     const int lane = lane_id();
     const int n = lane & 15, g = lane >> 4;
 
-    RowBuf rb;
-    rb.key = smem + wave * kWaveSmemWords;
-    rb.pos = rb.key + kCap;
-    rb.hist = rb.pos + kCap;
+    RowBuf<Pos> rb;
+    unsigned char* wbase = smem_raw + wave * Cfg::kWaveBytes;
+    rb.key = reinterpret_cast<uint32_t*>(wbase);
+    rb.hist = reinterpret_cast<uint32_t*>(wbase + (size_t)CAP * 4);
+    rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)CAP * 4 + 256 * 4);
 
     const size_t row_t = (size_t)b * L + t;
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * L * Op::kRowBytes;
@@ -355,33 +377,48 @@ prefill_fused_kernel(PrefillArgs a) {
     const float* kscale = DT == 2 ? a.k_scale + (size_t)b * L : nullptr;
     float* srow = a.scores ? a.scores + row_t * L : nullptr;
 
-    int nb = 0;           // candidates in the buffer (wave-uniform)
-    uint32_t thr = 0u;    // append iff key > thr
-    const int last = t / 64;
-    for (int chunk = 0; chunk <= last; ++chunk) {
-        const int s0 = chunk * 64;
-        typename Op::Bt Bk[4];
+    auto load_chunk = [&](int s0, typename Op::Bt (&Bk)[4], float& ksc) {
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             int s = s0 + 16 * st + n;
             s = s < L ? s : L - 1;
             Op::load_b(Bk[st], kbase + (size_t)s * Op::kRowBytes, g);
         }
-        float ksc = 1.f;
         if constexpr (DT == 2) {
             const int s = s0 + lane;
             ksc = kscale[s < L ? s : L - 1];
         }
+    };
+
+    int nb = 0;           // candidates in the buffer (wave-uniform)
+    uint32_t thr = 0u;    // append iff key > thr
+    const int last = t / 64;
+    typename Op::Bt Bn[4];
+    float ksn = 1.f;
+    load_chunk(0, Bn, ksn);
+    for (int chunk = 0; chunk <= last; ++chunk) {
+        const int s0 = chunk * 64;
+        typename Op::Bt Bk[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) Bk[st] = Bn[st];
+        const float ksc = ksn;
+        if constexpr (DT == 2) {
+            if (chunk < last) load_chunk(s0 + 64, Bn, ksn);   // prefetch the next chunk's keys
+        }
+        v4f acc[4][HB];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) Op::template mma<HB>(acc[st], Aq, Bk[st]);
+        if constexpr (DT != 2) {
+            if (chunk < last) load_chunk(s0 + 64, Bn, ksn);
+        }
         float part[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            v4f acc[HB];
-            Op::template mma<HB>(acc, Aq, Bk[st]);
             float p = 0.f;
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p = fmaf(c[hb][i], fmaxf(acc[hb][i], 0.f), p);
+                for (int i = 0; i < 4; ++i) p = fmaf(c[hb][i], relu(acc[st][hb][i]), p);
             part[st] = p;
         }
         const float score = reduce_scatter4(part) * ksc;
@@ -394,12 +431,12 @@ prefill_fused_kernel(PrefillArgs a) {
         if (app) {
             const int o = nb + lanes_below(m);
             rb.key[o] = key;
-            rb.pos[o] = (uint32_t)s;
+            rb.pos[o] = (Pos)s;
         }
         nb += __builtin_popcountll(m);
-        if (nb > kCap - kWave) {
+        if (nb > CAP - kWave) {
             __builtin_amdgcn_wave_barrier();
-            nb = wave_compact(rb, nb, (uint32_t)a.topk, &thr);
+            nb = wave_compact(rb, nb, (uint32_t)a.topk, &thr, CAP);
         }
     }
     if (srow) {
@@ -409,20 +446,26 @@ prefill_fused_kernel(PrefillArgs a) {
     wave_emit(rb, nb, a.topk, a.idx_out + row_t * a.topk, a.val_out ? a.val_out + row_t * a.topk : nullptr);
 }
 
-template <int DT, int HB>
+template <int DT, int HB, bool POS16>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
-    const size_t smem = (size_t)kT * kWaveSmemWords * sizeof(uint32_t);
+    using Cfg = BufCfg<POS16>;
+    const size_t smem = (size_t)Cfg::kWaves * Cfg::kWaveBytes;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_fused_kernel<DT, HB>,
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_fused_kernel<DT, HB, POS16>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    const int nblk = (a.L + kT - 1) / kT;
-    hipLaunchKernelGGL((prefill_fused_kernel<DT, HB>), dim3((unsigned)(nblk * a.B)), dim3(kT * kWave), smem,
-                       stream, a);
+    const int nblk = (a.L + Cfg::kWaves - 1) / Cfg::kWaves;
+    hipLaunchKernelGGL((prefill_fused_kernel<DT, HB, POS16>), dim3((unsigned)(nblk * a.B)),
+                       dim3(Cfg::kWaves * kWave), smem, stream, a);
     return hipGetLastError();
+}
+
+template <int DT, int HB>
+hipError_t launch_pos(const PrefillArgs& a, hipStream_t stream) {
+    return a.L <= 65536 ? launch_one<DT, HB, true>(a, stream) : launch_one<DT, HB, false>(a, stream);
 }
 
 }  // namespace
@@ -431,17 +474,17 @@ hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t str
     const int hb = a.H / 16;
     if (dtype == 2) {
         switch (hb) {
-            case 1: return launch_one<2, 1>(a, stream);
-            case 2: return launch_one<2, 2>(a, stream);
-            case 3: return launch_one<2, 3>(a, stream);
-            case 4: return launch_one<2, 4>(a, stream);
+            case 1: return launch_pos<2, 1>(a, stream);
+            case 2: return launch_pos<2, 2>(a, stream);
+            case 3: return launch_pos<2, 3>(a, stream);
+            case 4: return launch_pos<2, 4>(a, stream);
         }
     } else if (dtype == 1) {
         switch (hb) {
-            case 1: return launch_one<1, 1>(a, stream);
-            case 2: return launch_one<1, 2>(a, stream);
-            case 3: return launch_one<1, 3>(a, stream);
-            case 4: return launch_one<1, 4>(a, stream);
+            case 1: return launch_pos<1, 1>(a, stream);
+            case 2: return launch_pos<1, 2>(a, stream);
+            case 3: return launch_pos<1, 3>(a, stream);
+            case 4: return launch_pos<1, 4>(a, stream);
         }
     }
     return hipErrorInvalidValue;

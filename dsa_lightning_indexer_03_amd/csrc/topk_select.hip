@@ -118,48 +118,71 @@ topk_select_kernel(SelectArgs a) {
     const int row = blockIdx.x;
     const int t = threadIdx.x;
     const float* src = a.scores + (int64_t)row * a.row_stride;
+    const int32_t* psrc = a.pos ? a.pos + (int64_t)row * a.row_stride : nullptr;
     int n = a.cols;
     if (a.causal_L > 0) n = (row % a.causal_L) + 1;
-    else if (a.row_len) n = a.row_len[row];
+    const int64_t cstride = a.counter_stride > 0 ? a.counter_stride : 1;
+    if (a.causal_L <= 0 && a.row_len) n = a.row_len[row * cstride];
     n = n < 0 ? 0 : (n > a.cols ? a.cols : n);
     const int K = a.topk;
-    int32_t* idx_out = a.idx_out + (int64_t)row * K;
-    float* val_out = a.val_out ? a.val_out + (int64_t)row * K : nullptr;
-    const int R = n < K ? n : K;
+    // Output slots [0, G) were filled by the producer; this row returns
+    // min(K, total) positions in all, R of them chosen here among n entries.
+    const int G = a.pre_count ? (int)min(a.pre_count[row * cstride], (uint32_t)K) : 0;
+    int total = n;
+    if (a.total) {
+        total = a.total[row];
+        total = total < 0 ? 0 : (total > a.total_max ? a.total_max : total);
+    }
+    const int Rtot = total < K ? total : K;
+    int R = Rtot - G;
+    R = R < 0 ? 0 : (R > n ? n : R);
+    int32_t* idx_out = a.idx_out + (int64_t)row * K + G;
+    float* val_out = a.val_out ? a.val_out + (int64_t)row * K + G : nullptr;
 
-    if (R == n) {  // every valid entry is selected
-        for (int j = t; j < K; j += kThreads) {
-            idx_out[j] = j < n ? j : -1;
-            if (val_out) val_out[j] = j < n ? src[j] : -INFINITY;
+    if (R == n) {  // every entry is selected
+        for (int j = t; j < n; j += kThreads) {
+            idx_out[j] = psrc ? psrc[j] : j;
+            if (val_out) val_out[j] = src[j];
+        }
+        for (int j = G + n + t; j < K; j += kThreads) {
+            a.idx_out[(int64_t)row * K + j] = -1;
+            if (a.val_out) a.val_out[(int64_t)row * K + j] = -INFINITY;
         }
         return;
     }
-
-    // ---- level-0 histogram ----
-    if (a.hist) {
-        const uint32_t* h = a.hist + (int64_t)row * kBins;
-        for (int b = t; b < kBins; b += kThreads) sh.hist[b] = h[b];
-    } else {
-        for (int b = t; b < kBins; b += kThreads) sh.hist[b] = 0;
-        __syncthreads();
-        for (int j = t; j < n; j += kThreads) atomicAdd(&sh.hist[score_key(src[j]) >> 21], 1u);
-    }
-    if (t == 0) {
-        sh.out_n = 0;
-        sh.cand_n = 0;
-    }
-    __syncthreads();
 
     uint32_t need = (uint32_t)R;
     uint32_t pk = 0, mk = 0, pi = 0, mi = 0;  // fixed prefix (value, mask) of key and ~pos
     bool in_lds = false;
     int level = 0;
+    const bool known0 = a.level0_bin != nullptr;
+    if (t == 0) {
+        sh.out_n = 0;
+        sh.cand_n = 0;
+    }
+    // ---- level-0 histogram (unless every entry's first digit is known) ----
+    if (a.hist) {
+        const uint32_t* h = a.hist + (int64_t)row * kBins;
+        for (int b = t; b < kBins; b += kThreads) sh.hist[b] = h[b];
+    } else if (!known0) {
+        for (int b = t; b < kBins; b += kThreads) sh.hist[b] = 0;
+        __syncthreads();
+        for (int j = t; j < n; j += kThreads) atomicAdd(&sh.hist[score_key(src[j]) >> 21], 1u);
+    }
+    __syncthreads();
+
     for (;;) {
         const Level lv = kLevels[level];
-        find_bin(sh, 1 << lv.bits, need);
-        const uint32_t b = sh.bin;
-        need -= sh.above;
-        const uint32_t cnt = sh.hist[b];
+        uint32_t b, cnt;
+        if (known0 && level == 0) {
+            b = a.level0_bin[row * cstride];
+            cnt = (uint32_t)n;
+        } else {
+            find_bin(sh, 1 << lv.bits, need);
+            b = sh.bin;
+            need -= sh.above;
+            cnt = sh.hist[b];
+        }
         const uint32_t fm = ((1u << lv.bits) - 1u) << lv.shift;
         if (lv.on_idx) { pi |= b << lv.shift; mi |= fm; }
         else           { pk |= b << lv.shift; mk |= fm; }
@@ -171,11 +194,12 @@ topk_select_kernel(SelectArgs a) {
                 const int j = j0 + t;
                 const bool ok = j < n;
                 const float v = ok ? src[j] : 0.f;
-                const uint32_t key = score_key(v), np = ~(uint32_t)j;
+                const uint32_t p = ok ? (psrc ? (uint32_t)psrc[j] : (uint32_t)j) : 0u;
+                const uint32_t key = score_key(v), np = ~p;
                 const uint32_t kt = key & mk, it = np & mi;
                 const bool above = ok && (kt > pk || (kt == pk && it > pi));
                 const bool tie = ok && kt == pk && it == pi;
-                emit(sh, above, (uint32_t)j, v, idx_out, val_out, (uint32_t)R);
+                emit(sh, above, p, v, idx_out, val_out, (uint32_t)R);
                 uint64_t m = wave_ballot(tie);
                 if (m) {
                     uint32_t base = 0;
@@ -185,7 +209,7 @@ topk_select_kernel(SelectArgs a) {
                     const uint32_t o = base + (uint32_t)lanes_below(m);
                     if (tie && o < (uint32_t)kCap) {
                         sh.cand_key[o] = key;
-                        sh.cand_pos[o] = (uint32_t)j;
+                        sh.cand_pos[o] = p;
                     }
                 }
             }
@@ -207,7 +231,8 @@ topk_select_kernel(SelectArgs a) {
             }
         } else {
             for (int j = t; j < n; j += kThreads) {
-                const uint32_t key = score_key(src[j]), np = ~(uint32_t)j;
+                const uint32_t key = score_key(src[j]);
+                const uint32_t np = ~(psrc ? (uint32_t)psrc[j] : (uint32_t)j);
                 if ((key & mk) == pk && (np & mi) == pi) atomicAdd(&sh.hist[level_digit(nx, key, np)], 1u);
             }
         }
@@ -231,9 +256,9 @@ topk_select_kernel(SelectArgs a) {
         }
     }
     __syncthreads();
-    for (int j = R + t; j < K; j += kThreads) {
-        idx_out[j] = -1;
-        if (val_out) val_out[j] = -INFINITY;
+    for (int j = Rtot + t; j < K; j += kThreads) {
+        a.idx_out[(int64_t)row * K + j] = -1;
+        if (a.val_out) a.val_out[(int64_t)row * K + j] = -INFINITY;
     }
 }
 

@@ -101,7 +101,7 @@ def test_decode_rejects_before_launch(lib, kw, status):
 
 def test_decode_workspace_query(lib):
     n = lib.indexer_decode_paged_workspace_bytes(64, 131072, 64, 128, 2048)
-    assert n == 64 * 131072 * 4 + 64 * 2048 * 4
+    assert n == 64 * 131072 * 12 + 64 * (2048 + 64) * 4 + 65 * 4
 
 
 @pytest.mark.parametrize("args,status", [

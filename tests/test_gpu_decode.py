@@ -124,3 +124,25 @@ def test_prefill_row_matches_decode_of_prefix():
         check_topk_rows(di, dv, o[None], [ctx], K, where=f"decode t={t}")
         check_topk_rows(gi[0, t:t + 1], gv[0, t:t + 1], gs[0, t:t + 1, :ctx].astype(np.float64), [ctx], K,
                         where=f"prefill-vs-gpu-scores t={t}")
+
+
+def test_ragged_contexts_with_empty_queries():
+    d = synth.decode_inputs(9, [0, 5000, 0, 64, 65, 0, 131, 4096, 1], 64, 128, seed=560, permute=True)
+    gi, gv = parity(d, 100, "ragged")
+    for b in (0, 2, 5):
+        assert np.all(gi[b] == -1) and np.all(np.isneginf(gv[b]))
+
+
+def test_all_contexts_empty():
+    d = synth.decode_inputs(3, [0, 0, 0], 16, 128, seed=561, permute=False, extra_pages=2, max_pages_per_seq=4)
+    gi, gv = run_decode(d, 64)
+    assert np.all(gi == -1) and np.all(np.isneginf(gv))
+
+
+def test_many_queries_short_contexts():
+    """More queries than waves in the persistent grid have pages: every
+    wave share boundary falls inside some query."""
+    rng = np.random.default_rng(562)
+    ctx = rng.integers(1, 700, size=300).tolist()
+    d = synth.decode_inputs(300, ctx, 16, 128, seed=562, permute=True)
+    parity(d, 128, "many", queries=range(0, 300, 7))

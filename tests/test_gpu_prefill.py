@@ -124,3 +124,15 @@ def test_tie_heavy_keys_fused(dtype):
 def test_tie_heavy_generic():
     inp = synth.tie_heavy_prefill(1, 500, 4, 32, "f32", seed=4001, n_proto=3)
     parity(inp, 40, want_scores=True, name="ties generic")
+
+
+@pytest.mark.parametrize("L", [65536, 66000])
+def test_fused_long_sequences_sampled(L):
+    """Both candidate-buffer layouts (16-bit positions up to L = 65536, 32-bit
+    beyond), checked on sampled rows including the first and last."""
+    inp = synth.prefill_inputs(1, L, 16, 128, "fp8", seed=5000 + L)
+    rows = np.array([0, 2046, 2047, 2048, 40000, 65535, L - 1])
+    say(f"prefill long L={L}")
+    gi, gv, _ = run_prefill(inp, 2048)
+    _, _, osc = indexer.prefill(inp, 2048, rows=rows, want_scores=True)
+    check_topk_rows(gi[0][rows], gv[0][rows], osc[0], rows + 1, 2048, where=f"long L={L}")
