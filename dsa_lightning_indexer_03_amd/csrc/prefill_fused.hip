@@ -49,6 +49,14 @@ namespace {
 
 constexpr int kD = 128;
 
+#ifndef DSAIDX_PREFILL_DEPTH
+#define DSAIDX_PREFILL_DEPTH 1   // key chunks in flight ahead of the one multiplied (1 or 2)
+#endif
+#ifndef DSAIDX_PREFILL_STAGED
+#define DSAIDX_PREFILL_STAGED 1  // fp8 with L <= 65536: stage keys through LDS
+#endif
+constexpr int kPrefetch = DSAIDX_PREFILL_DEPTH >= 2 ? 2 : 1;
+
 template <bool POS16>
 struct BufCfg {
     using Pos = typename std::conditional<POS16, uint16_t, uint32_t>::type;
@@ -56,17 +64,6 @@ struct BufCfg {
     static constexpr int kCap = POS16 ? 3072 : 4096;  // candidates per row
     static constexpr size_t kWaveBytes = (size_t)kCap * (4 + sizeof(Pos)) + 256 * 4;
 };
-
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v |= __shfl_xor(v, d, kWave);
-    return v;
-}
-__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v &= __shfl_xor(v, d, kWave);
-    return v;
-}
 
 __device__ __forceinline__ float reduce_scatter4(const float v[4]) {
     auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[2]), false, false);
@@ -85,6 +82,36 @@ struct RowBuf {
     uint32_t* hist;  // 256 bins
 };
 
+// The buffer routines below walk the buffer 256 entries per step, lane l
+// holding entries 256*step + 4*l .. +3 (one 16-byte key read, one 8- or
+// 16-byte position read), so each step keeps four independent LDS reads in
+// flight instead of one.  Buffer capacities are multiples of 256.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+template <typename Pos>
+struct Pos4 { Pos v[4]; };
+
+template <typename Pos>
+__device__ __forceinline__ Pos4<Pos> read_pos4(const Pos* p) {
+    Pos4<Pos> r;
+    if constexpr (sizeof(Pos) == 2) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        r.v[0] = (Pos)(u.x & 0xFFFF); r.v[1] = (Pos)(u.x >> 16);
+        r.v[2] = (Pos)(u.y & 0xFFFF); r.v[3] = (Pos)(u.y >> 16);
+    } else {
+        const v4u u = *reinterpret_cast<const v4u*>(p);
+        r.v[0] = (Pos)u[0]; r.v[1] = (Pos)u[1]; r.v[2] = (Pos)u[2]; r.v[3] = (Pos)u[3];
+    }
+    return r;
+}
+
+// Exclusive prefix over the wave of a per-lane count (counts < 2^16).
+__device__ __forceinline__ uint32_t wave_excl(uint32_t v, uint32_t* total) {
+    const uint32_t inc = wave_incl_scan(v);
+    *total = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+    return inc - v;
+}
+
 // Histogram of the 8-bit (or narrower) digit (key >> shift) & mask over the
 // buffer entries whose key matches (key & pm) == pv.
 template <typename Pos>
@@ -94,9 +121,12 @@ __device__ __forceinline__ void wave_hist(const RowBuf<Pos>& rb, int n, uint32_t
 #pragma unroll
     for (int i = 0; i < 4; ++i) rb.hist[l + 64 * i] = 0u;
     __builtin_amdgcn_wave_barrier();
-    for (int j = l; j < n; j += kWave) {
-        const uint32_t k = rb.key[j];
-        if ((k & pm) == pv) atomicAdd(&rb.hist[(k >> shift) & dmask], 1u);
+    for (int j0 = 0; j0 < n; j0 += 256) {
+        const int j = j0 + 4 * l;
+        const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (j + e < n && (k[e] & pm) == pv) atomicAdd(&rb.hist[(k[e] >> shift) & dmask], 1u);
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -123,19 +153,22 @@ __device__ __forceinline__ uint32_t wave_find_bin(const RowBuf<Pos>& rb, uint32_
     const uint64_t m = wave_ballot(hit >= 0);
     const int src = __builtin_ctzll(m);
     const int bin = 255 - 4 * l - (hit < 0 ? 0 : hit);
-    *above = __shfl(ab, src, kWave);
-    *in_bin = __shfl(cnt, src, kWave);
-    return (uint32_t)__shfl(bin, src, kWave);
+    *above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
+    *in_bin = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
+    return (uint32_t)__builtin_amdgcn_readlane(bin, src);
 }
 
 // Common leading bits of all buffer keys: returns their count; *pv = value.
 template <typename Pos>
 __device__ __forceinline__ int wave_common_prefix(const RowBuf<Pos>& rb, int n, uint32_t* pv) {
     uint32_t o = 0u, a = 0xFFFFFFFFu;
-    for (int j = lane_id(); j < n; j += kWave) {
-        const uint32_t k = rb.key[j];
-        o |= k;
-        a &= k;
+    const int l = lane_id();
+    for (int j0 = 0; j0 < n; j0 += 256) {
+        const int j = j0 + 4 * l;
+        const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (j + e < n) { o |= k[e]; a &= k[e]; }
     }
     o = wave_or(o);
     a = wave_and(a);
@@ -170,14 +203,69 @@ __device__ uint32_t wave_kth_key(const RowBuf<Pos>& rb, int n, uint32_t need, ui
     return pv;
 }
 
+// One stable pass over the buffer keeping, in position order, every entry
+// with key > hi_key, and the first `ties` entries with key == hi_key ... or,
+// when exact is false, every entry with key >= lo_edge.  Kept entries go to
+// the buffer front (in place) or, if idx != nullptr, to the output row.
+template <typename Pos>
+__device__ int wave_keep_pass(const RowBuf<Pos>& rb, int n, bool exact, uint32_t kappa, uint32_t ties,
+                              uint32_t lo_edge, int32_t* idx, float* val, int limit) {
+    const int l = lane_id();
+    int wpos = 0;
+    uint32_t tie_seen = 0;
+    for (int j0 = 0; j0 < n; j0 += 256) {
+        const int j = j0 + 4 * l;
+        const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
+        const Pos4<Pos> p = read_pos4(rb.pos + j);
+        bool keep[4];
+        if (exact) {
+            uint32_t eqc = 0;
+            bool eq[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { eq[e] = j + e < n && k[e] == kappa; eqc += eq[e]; }
+            uint32_t eq_tot;
+            uint32_t rank = tie_seen + wave_excl(eqc, &eq_tot);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                keep[e] = (j + e < n) && (k[e] > kappa || (eq[e] && rank < ties));
+                rank += eq[e];
+            }
+            tie_seen += eq_tot;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) keep[e] = j + e < n && k[e] >= lo_edge;
+        }
+        const uint32_t kc = (uint32_t)keep[0] + keep[1] + keep[2] + keep[3];
+        uint32_t k_tot;
+        int o = wpos + (int)wave_excl(kc, &k_tot);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (keep[e]) {
+                if (idx) {
+                    if (o < limit) {
+                        idx[o] = (int32_t)p.v[e];
+                        if (val) val[o] = key_score(k[e]);
+                    }
+                } else {
+                    rb.key[o] = k[e];
+                    rb.pos[o] = p.v[e];
+                }
+                ++o;
+            }
+        }
+        wpos += (int)k_tot;
+    }
+    __builtin_amdgcn_wave_barrier();
+    return wpos;
+}
+
 // Drops buffer entries that cannot be in the top k.  Returns the new count
 // and the new append threshold (append iff key > *thr).
 template <typename Pos>
 __device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* thr, int cap) {
-    const int l = lane_id();
     uint32_t pv;
     const int cp = wave_common_prefix(rb, n, &pv);
-    uint32_t lo_edge;  // keep keys >= lo_edge
+    uint32_t lo_edge = 0;  // keep keys >= lo_edge
     bool exact = false;
     uint32_t kappa = 0, ties = 0;
     if (cp < 32) {
@@ -191,40 +279,14 @@ __device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* 
         const uint32_t b = wave_find_bin(rb, K, &above, &inb);
         lo_edge = pv | (b << shift);
         // Too many entries would survive (a crowded bin): fall back to exact.
-        if (above + inb > (uint32_t)(cap - 512)) exact = true;
+        if (above + inb > (uint32_t)(cap - 256)) exact = true;
     } else {
         exact = true;  // all keys equal
     }
     if (exact) kappa = wave_kth_key(rb, n, K, &ties);
-
-    int wpos = 0;
-    uint32_t tie_seen = 0;
-    for (int j0 = 0; j0 < n; j0 += kWave) {
-        const int j = j0 + l;
-        const bool ok = j < n;
-        const uint32_t k = ok ? rb.key[j] : 0u;
-        const Pos p = ok ? rb.pos[j] : (Pos)0;
-        bool keep;
-        if (exact) {
-            const bool eq = ok && k == kappa;
-            const uint64_t me = wave_ballot(eq);
-            const uint32_t rank = tie_seen + (uint32_t)lanes_below(me);
-            keep = ok && (k > kappa || (eq && rank < ties));
-            tie_seen += (uint32_t)__builtin_popcountll(me);
-        } else {
-            keep = ok && k >= lo_edge;
-        }
-        const uint64_t m = wave_ballot(keep);
-        if (keep) {
-            const int o = wpos + lanes_below(m);
-            rb.key[o] = k;
-            rb.pos[o] = p;
-        }
-        wpos += __builtin_popcountll(m);
-    }
-    __builtin_amdgcn_wave_barrier();
+    const int kept = wave_keep_pass(rb, n, exact, kappa, ties, lo_edge, (int32_t*)nullptr, (float*)nullptr, 0);
     *thr = exact ? kappa : (lo_edge == 0u ? 0u : lo_edge - 1u);
-    return wpos;
+    return kept;
 }
 
 // Writes the exact top K of the buffer (or all of it when n <= K) to the
@@ -246,25 +308,7 @@ __device__ void wave_emit(const RowBuf<Pos>& rb, int n, int K, int32_t* idx, flo
     }
     uint32_t ties;
     const uint32_t kappa = wave_kth_key(rb, n, (uint32_t)K, &ties);
-    int wpos = 0;
-    uint32_t tie_seen = 0;
-    for (int j0 = 0; j0 < n; j0 += kWave) {
-        const int j = j0 + l;
-        const bool ok = j < n;
-        const uint32_t k = ok ? rb.key[j] : 0u;
-        const bool eq = ok && k == kappa;
-        const uint64_t me = wave_ballot(eq);
-        const uint32_t rank = tie_seen + (uint32_t)lanes_below(me);
-        const bool keep = ok && (k > kappa || (eq && rank < ties));
-        tie_seen += (uint32_t)__builtin_popcountll(me);
-        const uint64_t m = wave_ballot(keep);
-        const int o = wpos + lanes_below(m);
-        if (keep && o < K) {  // exactly K entries are kept
-            idx[o] = (int32_t)rb.pos[j];
-            if (val) val[o] = key_score(k);
-        }
-        wpos += __builtin_popcountll(m);
-    }
+    wave_keep_pass(rb, n, true, kappa, ties, 0u, idx, val, K);
 }
 
 template <int DT>  // 1 = bf16, 2 = fp8 e4m3
@@ -364,62 +408,133 @@ prefill_fused_kernel(PrefillArgs a) {
     typename Op::template A<HB> Aq;
     Op::template load_a<HB>(Aq, reinterpret_cast<const uint8_t*>(a.q) + row_t * H * Op::kRowBytes, n, g);
 
+    // Head coefficients of the lane's accumulator rows: c = w * q_scale / sqrt(D)
+    // (fp8) or w / sqrt(D) (bf16).  The fp8 epilogue uses the identity
+    //   sum_i c_i max(S_i, 0) = 1/2 sum_i c_i |S_i| + 1/2 sum_i c_i S_i,
+    // so its coefficients carry the 1/2.
+    constexpr float kHalf = DT == 2 ? 0.5f : 1.0f;
     float c[HB][4];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = 16 * hb + 4 * g + i;
-            float cf = a.w[row_t * H + h] * a.inv_sqrt_d;
+            float cf = a.w[row_t * H + h] * (a.inv_sqrt_d * kHalf);
             if constexpr (DT == 2) cf *= a.q_scale[row_t * H + h];
             c[hb][i] = cf;
         }
+
+    // fp8: the linear half 1/2 sum_i c_i S_i = u . k with u = sum_i c_i q_i (in
+    // code units) is one more MFMA block.  u (fp32) is split into six fp8
+    // pieces with power-of-two scales, piece p = e4m3(r_p / 2^e_p), r_{p+1} =
+    // r_p - piece_p * 2^e_p; each piece shrinks the largest residual by 2^4,
+    // so the dropped remainder is below 2^-24 of max|u|.  Pieces 0..3 sit in
+    // rows 0, 4, 8, 12 of the extra A block and pieces 4, 5 in rows 1, 5, so
+    // every lane group folds at most two of them into its partial sum.
+    v8i Alin = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    float lin0 = 0.f, lin1 = 0.f;
+    if constexpr (DT == 2) {
+        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + row_t * H * kD;
+        const int tu = __builtin_amdgcn_readfirstlane((int)row_t);
+        float u0 = 0.f, u1 = 0.f;  // dims 2*lane, 2*lane+1
+        for (int h = 0; h < H; ++h) {
+            const float ch = a.w[(size_t)tu * H + h] * a.q_scale[(size_t)tu * H + h] * (a.inv_sqrt_d * 0.5f);
+            const int two = (int)*reinterpret_cast<const uint16_t*>(qrow + (size_t)h * kD + 2 * lane);
+            const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(two, false);
+            u0 = fmaf(ch, f[0], u0);
+            u1 = fmaf(ch, f[1], u1);
+        }
+        uint8_t* pieces = reinterpret_cast<uint8_t*>(rb.hist);  // 6 x 128 bytes of scratch
+        float sc[6];
+#pragma unroll
+        for (int pc = 0; pc < 6; ++pc) {
+            float m = fmaxf(fabsf(u0), fabsf(u1));
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+            // smallest power of two >= m / 448, so every |r / scale| <= 448
+            const bool live = m > 1e-30f;  // a vanishing residual ends the pieces
+            const float scale = live ? ldexpf(1.0f, __builtin_amdgcn_frexp_expf(m * (1.0f / 448.0f))) : 0.f;
+            const float inv = live ? 1.0f / scale : 0.f;
+            const int code = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * inv, u1 * inv, 0, false);
+            const auto dec = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+            u0 -= dec[0] * scale;
+            u1 -= dec[1] * scale;
+            *reinterpret_cast<uint16_t*>(pieces + pc * kD + 2 * lane) = (uint16_t)(code & 0xFFFF);
+            sc[pc] = scale;
+        }
+        __builtin_amdgcn_wave_barrier();
+        // lane (row n, group g) of the extra A block
+        int pc_of_row = -1;
+        if ((n & 3) == 0) pc_of_row = n >> 2;               // rows 0, 4, 8, 12 -> pieces 0..3
+        else if (n == 1 || n == 5) pc_of_row = 4 + (n >> 2);  // rows 1, 5 -> pieces 4, 5
+        if (pc_of_row >= 0) {
+            const v4i lo = *reinterpret_cast<const v4i*>(pieces + pc_of_row * kD + 32 * g);
+            const v4i hi = *reinterpret_cast<const v4i*>(pieces + pc_of_row * kD + 32 * g + 16);
+            Alin = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        // output rows 4g (piece g) and 4g+1 (piece 4+g for g < 2)
+        lin0 = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
+        lin1 = g == 0 ? sc[4] : g == 1 ? sc[5] : 0.f;
+        __builtin_amdgcn_wave_barrier();
+    }
+    (void)Alin; (void)lin0; (void)lin1;
+
     const float* kscale = DT == 2 ? a.k_scale + (size_t)b * L : nullptr;
     float* srow = a.scores ? a.scores + row_t * L : nullptr;
 
     auto load_chunk = [&](int s0, typename Op::Bt (&Bk)[4], float& ksc) {
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            int s = s0 + 16 * st + n;
-            s = s < L ? s : L - 1;
+            const int s = min(s0 + 16 * st + n, L - 1);
             Op::load_b(Bk[st], kbase + (size_t)s * Op::kRowBytes, g);
         }
         if constexpr (DT == 2) {
-            const int s = s0 + lane;
-            ksc = kscale[s < L ? s : L - 1];
+            ksc = kscale[min(s0 + lane, L - 1)];
         }
     };
 
     int nb = 0;           // candidates in the buffer (wave-uniform)
     uint32_t thr = 0u;    // append iff key > thr
     const int last = t / 64;
-    typename Op::Bt Bn[4];
-    float ksn = 1.f;
-    load_chunk(0, Bn, ksn);
-    for (int chunk = 0; chunk <= last; ++chunk) {
+
+    // One step over the 64 keys of `chunk`, held in `cur`; the next chunk's
+    // keys are loaded into `nxt` first.  Called with alternating buffers.
+    auto step = [&](int chunk, typename Op::Bt (&cur)[4], float ksc, typename Op::Bt (&nxt)[4], float& ksn) {
         const int s0 = chunk * 64;
-        typename Op::Bt Bk[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) Bk[st] = Bn[st];
-        const float ksc = ksn;
-        if constexpr (DT == 2) {
-            if (chunk < last) load_chunk(s0 + 64, Bn, ksn);   // prefetch the next chunk's keys
-        }
-        v4f acc[4][HB];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) Op::template mma<HB>(acc[st], Aq, Bk[st]);
-        if constexpr (DT != 2) {
-            if (chunk < last) load_chunk(s0 + 64, Bn, ksn);
-        }
+        if (chunk + kPrefetch <= last) load_chunk(s0 + 64 * kPrefetch, nxt, ksn);
         float part[4];
+        if constexpr (DT == 2) {
+            v4f acc[4][HB], accl[4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            float p = 0.f;
+            for (int st = 0; st < 4; ++st) {
+                Op::template mma<HB>(acc[st], Aq, cur[st]);
+                const v8i bb = v8i{cur[st].lo[0], cur[st].lo[1], cur[st].lo[2], cur[st].lo[3],
+                                   cur[st].hi[0], cur[st].hi[1], cur[st].hi[2], cur[st].hi[3]};
+                accl[st] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Alin, bb, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                              0, 0, 0, 0, 0, 0);
+            }
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb)
+            for (int st = 0; st < 4; ++st) {
+                float pp = fmaf(lin0, accl[st][0], lin1 * accl[st][1]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p = fmaf(c[hb][i], relu(acc[st][hb][i]), p);
-            part[st] = p;
+                for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pp = fmaf(c[hb][i], fabsf(acc[st][hb][i]), pp);
+                part[st] = pp;
+            }
+        } else {
+            v4f acc[4][HB];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) Op::template mma<HB>(acc[st], Aq, cur[st]);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                float pp = 0.f;
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pp = fmaf(c[hb][i], relu(acc[st][hb][i]), pp);
+                part[st] = pp;
+            }
         }
         const float score = reduce_scatter4(part) * ksc;
         const int s = s0 + lane;
@@ -438,7 +553,28 @@ prefill_fused_kernel(PrefillArgs a) {
             __builtin_amdgcn_wave_barrier();
             nb = wave_compact(rb, nb, (uint32_t)a.topk, &thr, CAP);
         }
+    };
+
+#if DSAIDX_PREFILL_DEPTH >= 2
+    // keys two chunks ahead are in flight: three buffers in rotation
+    typename Op::Bt bx[4], by[4], bz[4];
+    float kx = 1.f, ky = 1.f, kz = 1.f;
+    load_chunk(0, bx, kx);
+    if (last >= 1) load_chunk(64, by, ky);
+    for (int chunk = 0; chunk <= last; chunk += 3) {
+        step(chunk, bx, kx, bz, kz);
+        if (chunk + 1 <= last) step(chunk + 1, by, ky, bx, kx);
+        if (chunk + 2 <= last) step(chunk + 2, bz, kz, by, ky);
     }
+#else
+    typename Op::Bt bx[4], by[4];
+    float kx = 1.f, ky = 1.f;
+    load_chunk(0, bx, kx);
+    for (int chunk = 0; chunk <= last; chunk += 2) {
+        step(chunk, bx, kx, by, ky);
+        if (chunk + 1 <= last) step(chunk + 1, by, ky, bx, kx);
+    }
+#endif
     if (srow) {
         for (int s = (last + 1) * 64 + lane; s < L; s += kWave) srow[s] = -INFINITY;
     }
@@ -463,8 +599,239 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// fp8, L <= 65536: keys staged through LDS.
+//
+// The 8 waves of a workgroup (8 consecutive tokens, all with the same last
+// 64-key chunk) walk the chunks in lockstep: every 64-key chunk (8 KB of fp8
+// rows) is fetched from L2 once per workgroup with direct global->LDS loads
+// (no VGPRs in flight), double-buffered, one barrier per chunk.  Rows are
+// stored with their 16-byte segments XOR-swizzled by (row & 7) so the MFMA
+// operand reads (16 rows at a 128-byte stride) spread over the LDS banks.
+// Everything else -- operands, epilogue, per-wave candidate buffers -- is as
+// in the kernel above.
+// ---------------------------------------------------------------------------
+constexpr int kStagedWaves = 8;
+constexpr int kStagedCap = 2560;   // candidates per row; 8 rows + 3 key chunks fit in 160 KB
+constexpr int kStages = 3;
+constexpr size_t kStagedWaveBytes = (size_t)kStagedCap * 6 + 256 * 4;
+constexpr size_t kStageBytes = 64 * kD;  // one chunk of fp8 keys
+
+template <int HB>
+__global__ void __launch_bounds__(kStagedWaves * kWave)
+prefill_fused_fp8_staged_kernel(PrefillArgs a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    __shared__ uint32_t flags[3];
+    using Op = Operands<2>;
+    using Pos = uint16_t;
+    constexpr int W = kStagedWaves;
+    constexpr int CAP = kStagedCap;
+    constexpr int H = 16 * HB;
+    const int L = a.L;
+    const int nblk = (L + W - 1) / W;
+    const int b = blockIdx.x % a.B;
+    const int blk = nblk - 1 - (int)(blockIdx.x / a.B);  // heaviest first
+    const int wave = threadIdx.x / kWave;
+    const int t_raw = blk * W + wave;
+    const bool live = t_raw < L;        // waves past the end only help stage keys
+    const int t = live ? t_raw : L - 1;
+    const int lane = lane_id();
+    const int n = lane & 15, g = lane >> 4;
+
+    RowBuf<Pos> rb;
+    unsigned char* wbase = smem_raw + kStages * kStageBytes + wave * kStagedWaveBytes;
+    rb.key = reinterpret_cast<uint32_t*>(wbase);
+    rb.hist = reinterpret_cast<uint32_t*>(wbase + (size_t)CAP * 4);
+    rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)CAP * 4 + 256 * 4);
+
+    const size_t row_t = (size_t)b * L + t;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * L * kD;
+    typename Op::template A<HB> Aq;
+    Op::template load_a<HB>(Aq, reinterpret_cast<const uint8_t*>(a.q) + row_t * H * kD, n, g);
+
+    float c[HB][4];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 16 * hb + 4 * g + i;
+            c[hb][i] = a.w[row_t * H + h] * a.q_scale[row_t * H + h] * (a.inv_sqrt_d * 0.5f);
+        }
+    // Linear half on the MFMA: u = sum_i c_i q_i split into six fp8 pieces
+    // (see the kernel above).
+    v8i Alin = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    float lin0, lin1;
+    {
+        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + row_t * H * kD;
+        const int tu = __builtin_amdgcn_readfirstlane((int)row_t);
+        float u0 = 0.f, u1 = 0.f;
+        for (int h = 0; h < H; ++h) {
+            const float ch = a.w[(size_t)tu * H + h] * a.q_scale[(size_t)tu * H + h] * (a.inv_sqrt_d * 0.5f);
+            const int two = (int)*reinterpret_cast<const uint16_t*>(qrow + (size_t)h * kD + 2 * lane);
+            const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(two, false);
+            u0 = fmaf(ch, f[0], u0);
+            u1 = fmaf(ch, f[1], u1);
+        }
+        uint8_t* pieces = reinterpret_cast<uint8_t*>(rb.hist);
+        float sc[6];
+#pragma unroll
+        for (int pc = 0; pc < 6; ++pc) {
+            float m = fmaxf(fabsf(u0), fabsf(u1));
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+            const bool on = m > 1e-30f;
+            const float scale = on ? ldexpf(1.0f, __builtin_amdgcn_frexp_expf(m * (1.0f / 448.0f))) : 0.f;
+            const float inv = on ? 1.0f / scale : 0.f;
+            const int code = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * inv, u1 * inv, 0, false);
+            const auto dec = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+            u0 -= dec[0] * scale;
+            u1 -= dec[1] * scale;
+            *reinterpret_cast<uint16_t*>(pieces + pc * kD + 2 * lane) = (uint16_t)(code & 0xFFFF);
+            sc[pc] = scale;
+        }
+        __builtin_amdgcn_wave_barrier();
+        int pc_of_row = -1;
+        if ((n & 3) == 0) pc_of_row = n >> 2;
+        else if (n == 1 || n == 5) pc_of_row = 4 + (n >> 2);
+        if (pc_of_row >= 0) {
+            const v4i lo = *reinterpret_cast<const v4i*>(pieces + pc_of_row * kD + 32 * g);
+            const v4i hi = *reinterpret_cast<const v4i*>(pieces + pc_of_row * kD + 32 * g + 16);
+            Alin = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        lin0 = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
+        lin1 = g == 0 ? sc[4] : g == 1 ? sc[5] : 0.f;
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    const float* kscale = a.k_scale + (size_t)b * L;
+    float* srow = (a.scores && live) ? a.scores + row_t * L : nullptr;
+    const int last = (min(blk * W + W - 1, L - 1)) / 64;   // same for every wave of the block
+
+    // Thread i of the block stages 16 bytes: LDS slot i = (row i/8, segment
+    // i%8) holds global segment (i%8) ^ (row & 7) of that row.
+    const int srow_i = threadIdx.x >> 3;
+    const int sseg = (threadIdx.x & 7) ^ (srow_i & 7);
+    auto stage_chunk = [&](int chunk, unsigned char* dst) {
+        const int r = min(chunk * 64 + srow_i, L - 1);
+        const uint8_t* src = kbase + (size_t)r * kD + 16 * sseg;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 1024 * wave),
+                                         16, 0, 0);
+    };
+    // Swizzled byte offset of (row r, 16-byte segment j) inside a stage.
+    auto soff = [](int r, int j) { return r * kD + 16 * (j ^ (r & 7)); };
+
+    int nb = 0;
+    uint32_t thr = 0u;
+
+    // Software pipeline at half-chunk (32-key) granularity: the MFMAs of the
+    // next half run on the matrix cores while the VALU finishes the epilogue
+    // of the current one.  Chunk c lives in stage buffer c % 3; at the top of
+    // chunk c (after the barrier) chunk c+1 has landed and every wave is done
+    // reading chunk c-1, whose buffer receives chunk c+2.
+    struct HalfAcc { v4f s[2][HB]; v4f l[2]; };
+    auto mma_half = [&](int chunk, int half, HalfAcc& A_) {
+        const unsigned char* cur = smem_raw + (chunk % kStages) * kStageBytes;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int r = 16 * (2 * half + q) + n;
+            const v4i lo = *reinterpret_cast<const v4i*>(cur + soff(r, 2 * g));
+            const v4i hi = *reinterpret_cast<const v4i*>(cur + soff(r, 2 * g + 1));
+            const v8i bb = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+                A_.s[q][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq.a[hb], bb, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                               0, 0, 0, 0, 0, 0);
+            A_.l[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Alin, bb, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                         0, 0, 0, 0, 0, 0);
+        }
+    };
+    auto epi_half = [&](const HalfAcc& A_, float& p0, float& p1) {
+        float pp[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            float x = fmaf(lin0, A_.l[q][0], lin1 * A_.l[q][1]);
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x = fmaf(c[hb][i], fabsf(A_.s[q][hb][i]), x);
+            pp[q] = x;
+        }
+        p0 = pp[0];
+        p1 = pp[1];
+    };
+    auto finish = [&](int chunk, const float (&part)[4], float ks) {
+        const float score = reduce_scatter4(part) * ks;
+        const int s = chunk * 64 + lane;
+        const bool valid = live && s <= t;
+        if (srow && s < L) srow[s] = valid ? score : -INFINITY;
+        const uint32_t key = score_key(score);
+        const bool app = valid && key > thr;
+        const uint64_t m = wave_ballot(app);
+        if (app) {
+            const int o = nb + lanes_below(m);
+            rb.key[o] = key;
+            rb.pos[o] = (Pos)s;
+        }
+        nb += __builtin_popcountll(m);
+        // Near capacity: ask every wave to compact at the next barrier.
+        if (nb > CAP - 2 * kWave && lane == 0) flags[chunk % 3] = 1u;
+    };
+
+    HalfAcc h0, h1;
+    if (threadIdx.x < 3) flags[threadIdx.x] = 0u;
+    stage_chunk(0, smem_raw);
+    if (last >= 1) stage_chunk(1, smem_raw + kStageBytes);
+    __builtin_amdgcn_s_waitcnt(0x0F71);  // vmcnt(1): chunk 0 landed (chunk 1 may be in flight)
+    __syncthreads();
+    mma_half(0, 0, h0);
+    float ksn = kscale[min(lane, L - 1)];
+    for (int chunk = 0; chunk <= last; ++chunk) {
+        const float ks = ksn;
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): chunk c+1 (and this chunk's scales) landed
+        __syncthreads();
+        ksn = kscale[min(chunk * 64 + 64 + lane, L - 1)];
+        // Cooperative compaction: a flag raised in chunk c-1 makes every wave
+        // compact now, so the block pays one stall per event.  Flags rotate
+        // over three slots: set in chunk c, read in c+1, cleared in c+2.
+        if (chunk >= 1 && flags[(chunk - 1) % 3] != 0u) {
+            if (nb > a.topk) nb = wave_compact(rb, nb, (uint32_t)a.topk, &thr, CAP);
+        }
+        if (threadIdx.x == 0 && chunk >= 2) flags[(chunk - 2) % 3] = 0u;
+        if (chunk + 2 <= last) stage_chunk(chunk + 2, smem_raw + ((chunk + 2) % kStages) * kStageBytes);
+        float part[4];
+        mma_half(chunk, 1, h1);                 // second half of chunk c
+        epi_half(h0, part[0], part[1]);         // first half of chunk c
+        if (chunk + 1 <= last) mma_half(chunk + 1, 0, h0);  // first half of chunk c+1
+        epi_half(h1, part[2], part[3]);         // second half of chunk c
+        finish(chunk, part, ks);
+    }
+    if (!live) return;
+    if (srow) {
+        for (int s = (last + 1) * 64 + lane; s < L; s += kWave) srow[s] = -INFINITY;
+    }
+    __builtin_amdgcn_wave_barrier();
+    wave_emit(rb, nb, a.topk, a.idx_out + row_t * a.topk, a.val_out ? a.val_out + row_t * a.topk : nullptr);
+}
+
+template <int HB>
+hipError_t launch_fp8_staged(const PrefillArgs& a, hipStream_t stream) {
+    const size_t smem = kStages * kStageBytes + (size_t)kStagedWaves * kStagedWaveBytes;
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_fused_fp8_staged_kernel<HB>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const int nblk = (a.L + kStagedWaves - 1) / kStagedWaves;
+    hipLaunchKernelGGL((prefill_fused_fp8_staged_kernel<HB>), dim3((unsigned)(nblk * a.B)),
+                       dim3(kStagedWaves * kWave), smem, stream, a);
+    return hipGetLastError();
+}
+
 template <int DT, int HB>
 hipError_t launch_pos(const PrefillArgs& a, hipStream_t stream) {
+    if (DSAIDX_PREFILL_STAGED && DT == 2 && a.L <= 65536) return launch_fp8_staged<HB>(a, stream);
     return a.L <= 65536 ? launch_one<DT, HB, true>(a, stream) : launch_one<DT, HB, false>(a, stream);
 }
 
