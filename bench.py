@@ -29,6 +29,23 @@ METRIC = "indexer score+top-k pairs/s (prefill L=32K) and decode K-cache GB/s"
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
+# HBM traffic per launch from two rocprofv3 counter passes (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch) over `bench.py --steps 2 --warmup 1
+# --no-cpu-baseline --copy-calibration`.  Each counter is scaled by what it
+# reads for a 1 GiB device-to-device copy (FETCH_SIZE 524314.9 KiB, WRITE_SIZE
+# 1048576.0 KiB).  A record applies only while the kernel's sources hash to
+# the value it was taken at; otherwise traffic is reported as null.
+COPY_FETCH_FACTOR = 1048576.0 / 524314.9
+COPY_WRITE_FACTOR = 1048576.0 / 1048576.0
+COUNTERS = {
+    "prefill": {"sources": ["csrc/prefill_fused.hip", "csrc/common.h", "csrc/kernels.h", "build.py"],
+                "sha256": "6705b4346a9f3c88696e606659e824d8c7521660ef1788fcd0d7ccd91e30fe11",
+                "fetch_kib": 256810.1, "write_kib": 524313.8},
+    "decode_scan": {"sources": ["csrc/decode_paged.hip", "csrc/common.h", "csrc/kernels.h", "build.py"],
+                    "sha256": "f1f72e2c99d4b56ea7fccbab380bd69e670a7608ef222fbdfec606a09c75feca",
+                    "fetch_kib": 549458.5, "write_kib": 33168.8},
+}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -57,6 +74,21 @@ def time_calls(torch, fn, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return [a.elapsed_time(b) for a, b in evs], wall
+
+
+def measured_traffic(name):
+    """Calibrated HBM bytes per launch of kernel `name`, or None when its
+    sources changed since the counters were taken."""
+    import hashlib
+    rec = COUNTERS[name]
+    pkg = os.path.join(ROOT, "dsa_lightning_indexer_03_amd")
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(pkg, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec["sha256"]:
+        return None
+    return (rec["fetch_kib"] * COPY_FETCH_FACTOR + rec["write_kib"] * COPY_WRITE_FACTOR) * 1024.0
 
 
 def blas_threads():
@@ -172,8 +204,9 @@ def main():
                                    "causal s<=t, fused score+top-k (no [L,L] in HBM)",
                        "batch": 1, "L": L, "H": H, "D": D, "topk": K, "seed": 3},
             "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                         "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None,
-                         "kernel": "prefill_fused_kernel<fp8,H=64>",
+                         "frac": achieved / PEAK_FP8_TFLOPS, "traffic": measured_traffic("prefill"),
+                         "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+                         "kernel": "prefill_fused_fp8_staged_kernel<4>",
                          "work": f"2*H*D flop per causal pair x {pairs} pairs = {flops:.4g} flop per launch"},
             "wall_s_timed": wall,
         }
@@ -215,6 +248,7 @@ def main():
             }
             del args_d, ws
             torch.cuda.empty_cache()
+        dec["scan_traffic_bytes_per_call"] = measured_traffic("decode_scan")
         result["decode"] = dec
 
     # ---------------- CPU oracle baseline (rank 0, N=1) ----------------

@@ -6,9 +6,9 @@
 // bound by the cache bytes it streams (128 fp8 bytes + a 4-byte scale per
 // position), so the kernel is laid out for HBM:
 //
-// * grid = (ceil(max_ctx / 4096), B): each workgroup scans a 4096-position
-//   split of one query's context; each of its 4 waves takes whole 64-token
-//   pages, page by page.
+// * persistent grid: the (query, page) pairs of all queries form one list
+//   that is cut into equal shares, one per resident workgroup; each of a
+//   workgroup's 4 waves takes whole 64-token pages (details at the kernel).
 // * A page's 16-key subtile is 16 rows x 128 B = 2 KB contiguous; lane
 //   (n = lane % 16, g = lane / 16) loads the 32 bytes [32g, 32g+32) of row n
 //   with two 16-byte loads, so a wave's loads are fully coalesced.

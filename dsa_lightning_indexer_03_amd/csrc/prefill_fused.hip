@@ -2,7 +2,7 @@
 // + streaming top-k, with the [L, L] score matrix kept out of HBM.
 //
 // What is computed: for every token t and history position s <= t,
-// I[t,s] = sum_i w[t,i] * ReLU(q[t,i] . k[s] / sqrt(D))  ("From formula to
+// I[t,s] = sum_i w[t,i] * ReLU(q[t,i] . k[s] / sqrt(D))  ("From principle to
 // code", section 2.1; one shared key per token, "Lightning Indexer
 // explained", section 4), then the top-k positions of row t by (I desc,
 // s asc).  As a contraction this is Q[L*H, D] x K[L, D]^T restricted to the

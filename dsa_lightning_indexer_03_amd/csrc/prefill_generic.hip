@@ -1,7 +1,7 @@
 // Materialising prefill scorer for the shapes the fused MFMA path does not
 // cover (fp32 inputs, small H or D).  Writes the full causal score matrix
 // I[b][t][s] (-inf for s > t, the masking of the tutorial listing in "From
-// formula to code", section 3); the selector then runs over its rows.
+// principle to code", section 3); the selector then runs over its rows.
 //
 // Workgroup = 4 waves = 4 query tokens x 64 keys: wave w owns token t, lane l
 // owns key s = s_base + l.  The 64 keys of the tile are decoded once into LDS

@@ -8,7 +8,7 @@
  *
  * with H index heads on the query side and ONE D-wide key per token shared by
  * all heads, and keeps the top-k positions s of each query (the "token
- * selector").  Formula: "From formula to code -- DeepSeek-V3.2 lightning
+ * selector").  Formula: "From principle to code -- DeepSeek-V3.2 lightning
  * indexer", section 2.1 (core formula) and "Lightning Indexer explained",
  * section 4 (scoring formula; multi-head on the query side only).  Selection:
  * "Lightning Indexer explained", section 1 (top-k of k = 2048 positions) and
@@ -78,7 +78,7 @@ typedef enum {
  * indexer_prefill -- score every causal pair of B sequences of L tokens and
  * select the top-k history positions of every token.
  *
- * Passage: the core formula ("From formula to code", section 2.1) evaluated
+ * Passage: the core formula ("From principle to code", section 2.1) evaluated
  * for all query tokens at once, with the causal mask of that page's listing
  * (section 3: the lower-triangular mask keeps s <= t; masked scores are -inf)
  * and its top-k over the masked rows.  Row t therefore has t+1 valid
@@ -152,7 +152,7 @@ size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, i
  * topk_select -- the token selector on its own: top-k of each row of a score
  * matrix.
  *
- * Passage: the top-k step of "From formula to code", section 3 (top-k over
+ * Passage: the top-k step of "From principle to code", section 3 (top-k over
  * the masked score rows) with the tie and short-row rules above.  Row r's
  * valid entries are its first row_len[r] columns (all `cols` if row_len is
  * NULL); entries past that are never read.

@@ -10,7 +10,7 @@ Definition followed, step by step, in the order the pages give it:
    the query side only, the key is row s of the indexer cache; Study MLA
    Indexer, data flow: one d_idx-wide key per token.)
 3. Scale by 1/sqrt(D) and apply ReLU:  r = max(S / sqrt(D), 0).
-   (From formula to code -- DeepSeek-V3.2 lightning indexer, section 2.1
+   (From principle to code -- DeepSeek-V3.2 lightning indexer, section 2.1
    "core formula": the scaled dot product goes through ReLU; Study MLA
    Indexer, data flow: logits carry the 1/sqrt(d_idx) factor.  The second
    page's formula omits the factor; the reading taken is that it is present,
