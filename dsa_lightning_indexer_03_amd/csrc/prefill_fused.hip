@@ -615,7 +615,8 @@ constexpr int kStagedWaves = 8;
 constexpr int kStagedCap = 2560;   // candidates per row; 8 rows + 3 key chunks fit in 160 KB
 constexpr int kStages = 3;
 constexpr size_t kStagedWaveBytes = (size_t)kStagedCap * 6 + 256 * 4;
-constexpr size_t kStageBytes = 64 * kD;  // one chunk of fp8 keys
+constexpr size_t kStageKeyBytes = 64 * kD;                 // one chunk of fp8 keys ...
+constexpr size_t kStageBytes = kStageKeyBytes + 64 * 4;   // ... and their fp32 scales
 
 template <int HB>
 __global__ void __launch_bounds__(kStagedWaves * kWave)
@@ -707,15 +708,23 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     float* srow = (a.scores && live) ? a.scores + row_t * L : nullptr;
     const int last = (min(blk * W + W - 1, L - 1)) / 64;   // same for every wave of the block
 
-    // Thread i of the block stages 16 bytes: LDS slot i = (row i/8, segment
-    // i%8) holds global segment (i%8) ^ (row & 7) of that row.
+    // Staging of chunk c into stage buffer c % 3: thread i of the block
+    // copies 16 key bytes (LDS slot i = row i/8, segment i%8 holds global
+    // segment (i%8) ^ (row & 7) of that row) and wave 0 also copies the
+    // chunk's 64 key scales.  Rows past the end are clamped to L-1; they
+    // only ever feed masked scores.
     const int srow_i = threadIdx.x >> 3;
     const int sseg = (threadIdx.x & 7) ^ (srow_i & 7);
-    auto stage_chunk = [&](int chunk, unsigned char* dst) {
+    auto stage_chunk = [&](int chunk) {
+        unsigned char* dst = smem_raw + (chunk % kStages) * kStageBytes;
         const int r = min(chunk * 64 + srow_i, L - 1);
         const uint8_t* src = kbase + (size_t)r * kD + 16 * sseg;
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 1024 * wave),
                                          16, 0, 0);
+        if (wave == 0)
+            __builtin_amdgcn_global_load_lds(kscale + min(chunk * 64 + lane, L - 1),
+                                             (__attribute__((address_space(3))) void*)(dst + kStageKeyBytes),
+                                             4, 0, 0);
     };
     // Swizzled byte offset of (row r, 16-byte segment j) inside a stage.
     auto soff = [](int r, int j) { return r * kD + 16 * (j ^ (r & 7)); };
@@ -723,25 +732,36 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     int nb = 0;
     uint32_t thr = 0u;
 
-    // Software pipeline at half-chunk (32-key) granularity: the MFMAs of the
-    // next half run on the matrix cores while the VALU finishes the epilogue
-    // of the current one.  Chunk c lives in stage buffer c % 3; at the top of
-    // chunk c (after the barrier) chunk c+1 has landed and every wave is done
-    // reading chunk c-1, whose buffer receives chunk c+2.
+    // Pipeline.  Chunk c is loaded two chunks ahead (its stage buffer frees up
+    // once every wave is past chunk c-3) and waited for at the top of chunk c,
+    // so a load has two chunk-times to arrive.  Within a chunk the work runs
+    // at half-chunk (32-key) granularity: while the matrix cores multiply one
+    // half, the VALU runs the epilogue of the previous one.  Issue is in order
+    // within a wave and the two waves of a SIMD run in step (one barrier per
+    // chunk), so the overlap has to come from within each wave: each region
+    // below is branch-free and places a few independent epilogue
+    // instructions after every MFMA.
     struct HalfAcc { v4f s[2][HB]; v4f l[2]; };
-    auto mma_half = [&](int chunk, int half, HalfAcc& A_) {
+    struct HalfB { v8i b[2]; };
+    auto load_b = [&](int chunk, int half, HalfB& B_) {
         const unsigned char* cur = smem_raw + (chunk % kStages) * kStageBytes;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int r = 16 * (2 * half + q) + n;
             const v4i lo = *reinterpret_cast<const v4i*>(cur + soff(r, 2 * g));
             const v4i hi = *reinterpret_cast<const v4i*>(cur + soff(r, 2 * g + 1));
-            const v8i bb = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            B_.b[q] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    };
+    auto mma_half = [&](const HalfB& B_, HalfAcc& A_) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb)
-                A_.s[q][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq.a[hb], bb, v4f{0.f, 0.f, 0.f, 0.f},
+                A_.s[q][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq.a[hb], B_.b[q],
+                                                                               v4f{0.f, 0.f, 0.f, 0.f},
                                                                                0, 0, 0, 0, 0, 0);
-            A_.l[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Alin, bb, v4f{0.f, 0.f, 0.f, 0.f},
+            A_.l[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Alin, B_.b[q], v4f{0.f, 0.f, 0.f, 0.f},
                                                                          0, 0, 0, 0, 0, 0);
         }
     };
@@ -758,6 +778,23 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         }
         p0 = pp[0];
         p1 = pp[1];
+    };
+    // Scheduling pattern of one region: `nds` operand reads, then one MFMA
+    // followed by a few VALU instructions, for every MFMA of the half.
+    auto region_pattern = [](auto nds) {
+        (void)nds;
+        if constexpr (decltype(nds)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(nds)::value, 0);
+#pragma unroll
+        for (int i = 0; i < (HB + 1) * 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+    };
+    // Scale of key chunk*64 + lane; read while chunk's buffer is still owned
+    // (before the barrier that lets chunk+3 overwrite it).
+    auto load_ks = [&](int chunk) {
+        return *reinterpret_cast<const float*>(smem_raw + (chunk % kStages) * kStageBytes + kStageKeyBytes +
+                                               4 * lane);
     };
     auto finish = [&](int chunk, const float (&part)[4], float ks) {
         const float score = reduce_scatter4(part) * ks;
@@ -777,34 +814,64 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         if (nb > CAP - 2 * kWave && lane == 0) flags[chunk % 3] = 1u;
     };
 
-    HalfAcc h0, h1;
+    HalfAcc hA, hB;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        hB.l[q] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) hB.s[q][hb] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    HalfB bA, bB;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float ks_prev = 0.f;
     if (threadIdx.x < 3) flags[threadIdx.x] = 0u;
-    stage_chunk(0, smem_raw);
-    if (last >= 1) stage_chunk(1, smem_raw + kStageBytes);
-    __builtin_amdgcn_s_waitcnt(0x0F71);  // vmcnt(1): chunk 0 landed (chunk 1 may be in flight)
-    __syncthreads();
-    mma_half(0, 0, h0);
-    float ksn = kscale[min(lane, L - 1)];
+    stage_chunk(0);
+    stage_chunk(1);
     for (int chunk = 0; chunk <= last; ++chunk) {
-        const float ks = ksn;
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): chunk c+1 (and this chunk's scales) landed
+        // This wave's copies of chunk c have landed once at most its copies
+        // of chunk c+1 are in flight (loads complete in issue order); the
+        // barrier then makes every wave's copies visible.  With the score
+        // matrix requested, the row's stores share the counter: wait for all.
+        if (a.scores) __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
+        else if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F72);       // vmcnt(2)
+        else __builtin_amdgcn_s_waitcnt(0x0F71);                      // vmcnt(1)
         __syncthreads();
-        ksn = kscale[min(chunk * 64 + 64 + lane, L - 1)];
-        // Cooperative compaction: a flag raised in chunk c-1 makes every wave
-        // compact now, so the block pays one stall per event.  Flags rotate
-        // over three slots: set in chunk c, read in c+1, cleared in c+2.
-        if (chunk >= 1 && flags[(chunk - 1) % 3] != 0u) {
+        // Cooperative compaction: a flag raised by the appends of chunk c-2
+        // (made during iteration c-1) makes every wave compact now, before its
+        // next appends, so the block pays one stall per event.  Slot j % 3
+        // belongs to the appends of chunk j: set in iteration j+1, read in
+        // j+2, cleared in j+3 (each step separated by a barrier).
+        if (chunk >= 2 && flags[(chunk - 2) % 3] != 0u) {
             if (nb > a.topk) nb = wave_compact(rb, nb, (uint32_t)a.topk, &thr, CAP);
         }
-        if (threadIdx.x == 0 && chunk >= 2) flags[(chunk - 2) % 3] = 0u;
-        if (chunk + 2 <= last) stage_chunk(chunk + 2, smem_raw + ((chunk + 2) % kStages) * kStageBytes);
-        float part[4];
-        mma_half(chunk, 1, h1);                 // second half of chunk c
-        epi_half(h0, part[0], part[1]);         // first half of chunk c
-        if (chunk + 1 <= last) mma_half(chunk + 1, 0, h0);  // first half of chunk c+1
-        epi_half(h1, part[2], part[3]);         // second half of chunk c
-        finish(chunk, part, ks);
+        if (threadIdx.x == 0 && chunk >= 3) flags[(chunk - 3) % 3] = 0u;
+        // Chunk c+2 goes to the buffer chunk c-1 used.  Past the last chunk
+        // the copy is a clamped dummy, so every chunk issues the same loads.
+        stage_chunk(chunk + 2);
+        // Region 1: first half of chunk c on the MFMA, epilogue of the second
+        // half of chunk c-1 (zeros before the first chunk).
+        // The second half's operands are read here too, a region ahead.
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(chunk, 0, bA);
+        load_b(chunk, 1, bB);
+        mma_half(bA, hA);
+        epi_half(hB, part[2], part[3]);
+        // keep this epilogue here (it would otherwise sink into the branch below)
+        asm volatile("" : "+v"(part[2]), "+v"(part[3]));
+        region_pattern(std::integral_constant<int, 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if (chunk >= 1) finish(chunk - 1, part, ks_prev);
+        // Region 2: second half of chunk c on the MFMA, epilogue of its first half.
+        __builtin_amdgcn_sched_barrier(0);
+        mma_half(bB, hB);
+        epi_half(hA, part[0], part[1]);
+        region_pattern(std::integral_constant<int, 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        ks_prev = load_ks(chunk);
     }
+    epi_half(hB, part[2], part[3]);
+    finish(last, part, ks_prev);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no LDS copy may still be in flight at exit
     if (!live) return;
     if (srow) {
         for (int s = (last + 1) * 64 + lane; s < L; s += kWave) srow[s] = -INFINITY;
