@@ -112,10 +112,20 @@ __device__ __forceinline__ uint32_t wave_excl(uint32_t v, uint32_t* total) {
     return inc - v;
 }
 
-// Histogram of the 8-bit (or narrower) digit (key >> shift) & mask over the
-// buffer entries whose key matches (key & pm) == pv.
+// Position as an unsigned value of the buffer's position width, inverted so
+// that a lower position compares larger.
 template <typename Pos>
-__device__ __forceinline__ void wave_hist(const RowBuf<Pos>& rb, int n, uint32_t pm, uint32_t pv,
+__device__ __forceinline__ uint32_t inv_pos(Pos p) {
+    return (uint32_t)(Pos)~p;
+}
+
+// Histogram of an 8-bit (or narrower) digit over matching buffer entries.
+// BY_POS = false: digit (key >> shift) & dmask of the entries whose key has
+//   (key & pm) == pv.
+// BY_POS = true: digit of the inverted position of the entries whose key
+//   equals kappa and whose inverted position has (ipos & pm) == pv.
+template <bool BY_POS, typename Pos>
+__device__ __forceinline__ void wave_hist(const RowBuf<Pos>& rb, int n, uint32_t kappa, uint32_t pm, uint32_t pv,
                                           int shift, uint32_t dmask) {
     const int l = lane_id();
 #pragma unroll
@@ -124,9 +134,18 @@ __device__ __forceinline__ void wave_hist(const RowBuf<Pos>& rb, int n, uint32_t
     for (int j0 = 0; j0 < n; j0 += 256) {
         const int j = j0 + 4 * l;
         const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
+        if constexpr (BY_POS) {
+            const Pos4<Pos> p = read_pos4(rb.pos + j);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (j + e < n && (k[e] & pm) == pv) atomicAdd(&rb.hist[(k[e] >> shift) & dmask], 1u);
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t ip = inv_pos(p.v[e]);
+                if (j + e < n && k[e] == kappa && (ip & pm) == pv) atomicAdd(&rb.hist[(ip >> shift) & dmask], 1u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j + e < n && (k[e] & pm) == pv) atomicAdd(&rb.hist[(k[e] >> shift) & dmask], 1u);
+        }
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -178,21 +197,22 @@ __device__ __forceinline__ int wave_common_prefix(const RowBuf<Pos>& rb, int n, 
     return cp;
 }
 
-// Exact k-th largest key of the buffer: returns kappa, *ties = how many
-// entries equal to kappa belong to the top `need` (the rest of the top are
-// strictly greater).
+// Exact `need`-th largest key of the buffer (1 <= need <= n): returns kappa;
+// *ties = how many entries equal to kappa belong to the top `need` (the rest
+// of the top are strictly greater); *eq = how many entries equal kappa.
 template <typename Pos>
-__device__ uint32_t wave_kth_key(const RowBuf<Pos>& rb, int n, uint32_t need, uint32_t* ties) {
+__device__ uint32_t wave_kth_key(const RowBuf<Pos>& rb, int n, uint32_t need, uint32_t* ties, uint32_t* eq) {
     uint32_t pv;
     const int cp = wave_common_prefix(rb, n, &pv);
     uint32_t pm = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
     int hi = 32 - cp;
+    uint32_t inb = (uint32_t)n;  // all keys equal when no digit is left
     while (hi > 0) {
         const int width = hi < 8 ? hi : 8;
         const int shift = hi - width;
         const uint32_t dmask = (1u << width) - 1u;
-        wave_hist(rb, n, pm, pv, shift, dmask);
-        uint32_t above, inb;
+        wave_hist<false>(rb, n, 0u, pm, pv, shift, dmask);
+        uint32_t above;
         const uint32_t b = wave_find_bin(rb, need, &above, &inb);
         need -= above;
         pv |= b << shift;
@@ -200,41 +220,47 @@ __device__ uint32_t wave_kth_key(const RowBuf<Pos>& rb, int n, uint32_t need, ui
         hi = shift;
     }
     *ties = need;
+    *eq = inb;
     return pv;
 }
 
-// One stable pass over the buffer keeping, in position order, every entry
-// with key > hi_key, and the first `ties` entries with key == hi_key ... or,
-// when exact is false, every entry with key >= lo_edge.  Kept entries go to
-// the buffer front (in place) or, if idx != nullptr, to the output row.
+// Tie break at the k-th key: among the entries whose key equals kappa, the
+// `ties` lowest positions win (1 <= ties <= count of such entries).  Returns
+// the largest winning position; an entry with key kappa wins iff its
+// position is <= the result.  Radix select on inverted positions.
 template <typename Pos>
-__device__ int wave_keep_pass(const RowBuf<Pos>& rb, int n, bool exact, uint32_t kappa, uint32_t ties,
+__device__ uint32_t wave_tie_cut(const RowBuf<Pos>& rb, int n, uint32_t kappa, uint32_t ties) {
+    uint32_t pm = 0u, pv = 0u, need = ties;
+    for (int hi = 8 * (int)sizeof(Pos); hi > 0; hi -= 8) {
+        const int shift = hi - 8;
+        wave_hist<true>(rb, n, kappa, pm, pv, shift, 0xFFu);
+        uint32_t above, inb;
+        const uint32_t b = wave_find_bin(rb, need, &above, &inb);
+        need -= above;
+        pv |= b << shift;
+        pm |= 0xFFu << shift;
+    }
+    return inv_pos((Pos)pv);
+}
+
+// One stable pass over the buffer keeping, in buffer order, every entry with
+// key > kappa or (key == kappa and position <= pos_cut) when exact, else
+// every entry with key >= lo_edge.  Kept entries go to the buffer front (in
+// place) or, if idx != nullptr, to the output row.
+template <typename Pos>
+__device__ int wave_keep_pass(const RowBuf<Pos>& rb, int n, bool exact, uint32_t kappa, uint32_t pos_cut,
                               uint32_t lo_edge, int32_t* idx, float* val, int limit) {
     const int l = lane_id();
     int wpos = 0;
-    uint32_t tie_seen = 0;
     for (int j0 = 0; j0 < n; j0 += 256) {
         const int j = j0 + 4 * l;
         const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
         const Pos4<Pos> p = read_pos4(rb.pos + j);
         bool keep[4];
-        if (exact) {
-            uint32_t eqc = 0;
-            bool eq[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { eq[e] = j + e < n && k[e] == kappa; eqc += eq[e]; }
-            uint32_t eq_tot;
-            uint32_t rank = tie_seen + wave_excl(eqc, &eq_tot);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                keep[e] = (j + e < n) && (k[e] > kappa || (eq[e] && rank < ties));
-                rank += eq[e];
-            }
-            tie_seen += eq_tot;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) keep[e] = j + e < n && k[e] >= lo_edge;
-        }
+        for (int e = 0; e < 4; ++e)
+            keep[e] = j + e < n &&
+                      (exact ? (k[e] > kappa || (k[e] == kappa && (uint32_t)p.v[e] <= pos_cut)) : k[e] >= lo_edge);
         const uint32_t kc = (uint32_t)keep[0] + keep[1] + keep[2] + keep[3];
         uint32_t k_tot;
         int o = wpos + (int)wave_excl(kc, &k_tot);
@@ -259,22 +285,33 @@ __device__ int wave_keep_pass(const RowBuf<Pos>& rb, int n, bool exact, uint32_t
     return wpos;
 }
 
-// Drops buffer entries that cannot be in the top k.  Returns the new count
-// and the new append threshold (append iff key > *thr).
+// Exact cut of the buffer to its top K by (key desc, position asc): returns
+// kappa and the position cut for wave_keep_pass.
+template <typename Pos>
+__device__ __forceinline__ uint32_t wave_exact_cut(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* pos_cut) {
+    uint32_t ties, eq;
+    const uint32_t kappa = wave_kth_key(rb, n, K, &ties, &eq);
+    *pos_cut = eq > ties ? wave_tie_cut(rb, n, kappa, ties) : 0xFFFFFFFFu;
+    return kappa;
+}
+
+// Drops buffer entries that cannot be in the top K (n > K).  Returns the new
+// count and the new append floor (append iff key > *thr).  Entries equal to
+// the cut key stay admissible: in an out-of-order scan a later one may have
+// a lower position.
 template <typename Pos>
 __device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* thr, int cap) {
     uint32_t pv;
     const int cp = wave_common_prefix(rb, n, &pv);
     uint32_t lo_edge = 0;  // keep keys >= lo_edge
     bool exact = false;
-    uint32_t kappa = 0, ties = 0;
     if (cp < 32) {
         const int hi = 32 - cp;
         const int width = hi < 8 ? hi : 8;
         const int shift = hi - width;
         const uint32_t dmask = (1u << width) - 1u;
         const uint32_t pm = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
-        wave_hist(rb, n, pm, pv, shift, dmask);
+        wave_hist<false>(rb, n, 0u, pm, pv, shift, dmask);
         uint32_t above, inb;
         const uint32_t b = wave_find_bin(rb, K, &above, &inb);
         lo_edge = pv | (b << shift);
@@ -283,14 +320,39 @@ __device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* 
     } else {
         exact = true;  // all keys equal
     }
-    if (exact) kappa = wave_kth_key(rb, n, K, &ties);
-    const int kept = wave_keep_pass(rb, n, exact, kappa, ties, lo_edge, (int32_t*)nullptr, (float*)nullptr, 0);
-    *thr = exact ? kappa : (lo_edge == 0u ? 0u : lo_edge - 1u);
+    uint32_t kappa = 0, pos_cut = 0;
+    if (exact) kappa = wave_exact_cut(rb, n, K, &pos_cut);
+    const int kept = wave_keep_pass(rb, n, exact, kappa, pos_cut, lo_edge, (int32_t*)nullptr, (float*)nullptr, 0);
+    const uint32_t fl = exact ? kappa : lo_edge;
+    *thr = fl == 0u ? 0u : fl - 1u;
     return kept;
 }
 
-// Writes the exact top K of the buffer (or all of it when n <= K) to the
-// output row, then the -1 / -inf padding.
+// Speculative floor: keeps the entries whose key is at least the lower edge
+// of the radix bin (one digit below the common prefix) that holds the r-th
+// largest key, and returns that edge (<= the r-th largest key).  1 <= r <= n.
+template <typename Pos>
+__device__ int wave_floor(const RowBuf<Pos>& rb, int n, uint32_t r, uint32_t* floor_key) {
+    uint32_t pv;
+    const int cp = wave_common_prefix(rb, n, &pv);
+    uint32_t lo_edge = pv;
+    if (cp < 32) {
+        const int hi = 32 - cp;
+        const int width = hi < 8 ? hi : 8;
+        const int shift = hi - width;
+        const uint32_t dmask = (1u << width) - 1u;
+        const uint32_t pm = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
+        wave_hist<false>(rb, n, 0u, pm, pv, shift, dmask);
+        uint32_t above, inb;
+        const uint32_t b = wave_find_bin(rb, r, &above, &inb);
+        lo_edge = pv | (b << shift);
+    }
+    *floor_key = lo_edge;
+    return wave_keep_pass(rb, n, false, 0u, 0u, lo_edge, (int32_t*)nullptr, (float*)nullptr, 0);
+}
+
+// Writes the exact top K of the buffer by (key desc, position asc) -- or all
+// of it when n <= K -- to the output row, then the -1 / -inf padding.
 template <typename Pos>
 __device__ void wave_emit(const RowBuf<Pos>& rb, int n, int K, int32_t* idx, float* val) {
     const int l = lane_id();
@@ -306,9 +368,9 @@ __device__ void wave_emit(const RowBuf<Pos>& rb, int n, int K, int32_t* idx, flo
         }
         return;
     }
-    uint32_t ties;
-    const uint32_t kappa = wave_kth_key(rb, n, (uint32_t)K, &ties);
-    wave_keep_pass(rb, n, true, kappa, ties, 0u, idx, val, K);
+    uint32_t pos_cut;
+    const uint32_t kappa = wave_exact_cut(rb, n, (uint32_t)K, &pos_cut);
+    wave_keep_pass(rb, n, true, kappa, pos_cut, 0u, idx, val, K);
 }
 
 template <int DT>  // 1 = bf16, 2 = fp8 e4m3
@@ -614,7 +676,9 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
 constexpr int kStagedWaves = 8;
 constexpr int kStagedCap = 2560;   // candidates per row; 8 rows + 3 key chunks fit in 160 KB
 constexpr int kStages = 3;
-constexpr size_t kStagedWaveBytes = (size_t)kStagedCap * 6 + 256 * 4;
+// per wave: keys [CAP + 64] u32, histogram [256] u32, positions [CAP + 64] u16; the
+// 64 slots past CAP take the writes of lanes that do not append
+constexpr size_t kStagedWaveBytes = (size_t)(kStagedCap + kWave) * 6 + 256 * 4;
 constexpr size_t kStageKeyBytes = 64 * kD;                 // one chunk of fp8 keys ...
 constexpr size_t kStageBytes = kStageKeyBytes + 64 * 4;   // ... and their fp32 scales
 
@@ -622,7 +686,7 @@ template <int HB>
 __global__ void __launch_bounds__(kStagedWaves * kWave)
 prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    __shared__ uint32_t flags[3];
+    __shared__ uint32_t flags[4];  // [0..2] compaction requests, [3] rescan request
     using Op = Operands<2>;
     using Pos = uint16_t;
     constexpr int W = kStagedWaves;
@@ -642,8 +706,8 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     RowBuf<Pos> rb;
     unsigned char* wbase = smem_raw + kStages * kStageBytes + wave * kStagedWaveBytes;
     rb.key = reinterpret_cast<uint32_t*>(wbase);
-    rb.hist = reinterpret_cast<uint32_t*>(wbase + (size_t)CAP * 4);
-    rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)CAP * 4 + 256 * 4);
+    rb.hist = reinterpret_cast<uint32_t*>(wbase + (size_t)(CAP + kWave) * 4);
+    rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)(CAP + kWave) * 4 + 256 * 4);
 
     const size_t row_t = (size_t)b * L + t;
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * L * kD;
@@ -708,15 +772,34 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     float* srow = (a.scores && live) ? a.scores + row_t * L : nullptr;
     const int last = (min(blk * W + W - 1, L - 1)) / 64;   // same for every wave of the block
 
-    // Staging of chunk c into stage buffer c % 3: thread i of the block
-    // copies 16 key bytes (LDS slot i = row i/8, segment i%8 holds global
-    // segment (i%8) ^ (row & 7) of that row) and wave 0 also copies the
-    // chunk's 64 key scales.  Rows past the end are clamped to L-1; they
+    // Chunk order.  When the block spans at least 32 chunks, a strided sample
+    // (chunks 16i+15, i < S) is scored first; the rest follow in increasing
+    // order.  After the sample each long row sets a speculative floor: the
+    // lower edge of the radix bin holding the r-th largest sampled key, with
+    // r five standard deviations above the expected number of sampled keys
+    // at or above the row's k-th largest.  Keys below the floor are never
+    // appended.  The floor is verified at the end: if fewer than k keys of
+    // the row cleared it, some of the top k may have been dropped and the row
+    // is scanned again without a floor.  Otherwise every dropped key lies
+    // below the k-th largest and the selection is exact.
+    const int S = last + 1 >= 32 ? (last + 1) / 16 : 0;
+    auto chunk_at = [&](int i) -> int {
+        i = min(i, last);  // the stage copies issued past the end re-read the last chunk
+        if (i < S) return 16 * i + 15;
+        const int j = i - S;
+        return j < 15 * S ? j + j / 15 : j + S;
+    };
+
+    // Stage slot i % 3 receives the i-th chunk of the order: thread x of the
+    // block copies 16 key bytes (LDS slot x = row x/8, segment x%8 holds
+    // global segment (x%8) ^ (row & 7) of that row) and wave 0 also copies
+    // the chunk's 64 key scales.  Rows past the end are clamped to L-1; they
     // only ever feed masked scores.
     const int srow_i = threadIdx.x >> 3;
     const int sseg = (threadIdx.x & 7) ^ (srow_i & 7);
-    auto stage_chunk = [&](int chunk) {
-        unsigned char* dst = smem_raw + (chunk % kStages) * kStageBytes;
+    auto stage_chunk = [&](int i) {
+        unsigned char* dst = smem_raw + (i % kStages) * kStageBytes;
+        const int chunk = chunk_at(i);
         const int r = min(chunk * 64 + srow_i, L - 1);
         const uint8_t* src = kbase + (size_t)r * kD + 16 * sseg;
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 1024 * wave),
@@ -729,22 +812,30 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     // Swizzled byte offset of (row r, 16-byte segment j) inside a stage.
     auto soff = [](int r, int j) { return r * kD + 16 * (j ^ (r & 7)); };
 
+    const int K = a.topk;
     int nb = 0;
     uint32_t thr = 0u;
+    bool active = live;   // this wave scores and appends in the current pass
+    bool floored = false; // a speculative floor is in force
+    uint32_t r_spec = 0;  // rank of the floor in the sample (0: no floor)
+    if (live && S >= 2 && t + 1 > 2 * K) {
+        const float ec = 64.f * (float)S * (float)K / (float)(t + 1);
+        r_spec = (uint32_t)ceilf(ec + 5.f * sqrtf(ec) + 8.f);
+    }
 
-    // Pipeline.  Chunk c is loaded two chunks ahead (its stage buffer frees up
-    // once every wave is past chunk c-3) and waited for at the top of chunk c,
-    // so a load has two chunk-times to arrive.  Within a chunk the work runs
-    // at half-chunk (32-key) granularity: while the matrix cores multiply one
-    // half, the VALU runs the epilogue of the previous one.  Issue is in order
-    // within a wave and the two waves of a SIMD run in step (one barrier per
-    // chunk), so the overlap has to come from within each wave: each region
-    // below is branch-free and places a few independent epilogue
-    // instructions after every MFMA.
+    // Pipeline.  The i-th chunk is loaded two chunks ahead (its stage slot
+    // frees up once every wave is past chunk i-3) and waited for at the top of
+    // iteration i, so a load has two chunk-times to arrive.  Within a chunk
+    // the work runs at half-chunk (32-key) granularity: while the matrix cores
+    // multiply one half, the VALU runs the epilogue of the previous one.
+    // Issue is in order within a wave and the waves of a SIMD run in step
+    // (one barrier per chunk), so the overlap has to come from within each
+    // wave: each region below is branch-free and places a few independent
+    // epilogue instructions after every MFMA.
     struct HalfAcc { v4f s[2][HB]; v4f l[2]; };
     struct HalfB { v8i b[2]; };
-    auto load_b = [&](int chunk, int half, HalfB& B_) {
-        const unsigned char* cur = smem_raw + (chunk % kStages) * kStageBytes;
+    auto load_b = [&](int i, int half, HalfB& B_) {
+        const unsigned char* cur = smem_raw + (i % kStages) * kStageBytes;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int r = 16 * (2 * half + q) + n;
@@ -779,105 +870,155 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         p0 = pp[0];
         p1 = pp[1];
     };
-    // Scheduling pattern of one region: `nds` operand reads, then one MFMA
-    // followed by a few VALU instructions, for every MFMA of the half.
-    auto region_pattern = [](auto nds) {
-        (void)nds;
-        if constexpr (decltype(nds)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(nds)::value, 0);
+    // Scheduling pattern of one region: one MFMA followed by a few VALU
+    // instructions, for every MFMA of the half.
+    auto region_pattern = []() {
 #pragma unroll
         for (int i = 0; i < (HB + 1) * 2; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
     };
-    // Scale of key chunk*64 + lane; read while chunk's buffer is still owned
-    // (before the barrier that lets chunk+3 overwrite it).
-    auto load_ks = [&](int chunk) {
-        return *reinterpret_cast<const float*>(smem_raw + (chunk % kStages) * kStageBytes + kStageKeyBytes +
-                                               4 * lane);
+    // Scale of key (i-th chunk)*64 + lane; read while the chunk's slot is
+    // still owned (before the barrier that lets chunk i+3 overwrite it).
+    auto load_ks = [&](int i) {
+        return *reinterpret_cast<const float*>(smem_raw + (i % kStages) * kStageBytes + kStageKeyBytes + 4 * lane);
     };
-    auto finish = [&](int chunk, const float (&part)[4], float ks) {
-        const float score = reduce_scatter4(part) * ks;
+    // Appends the i-th chunk's scores above the floor, in lane order.  Branch
+    // free: lanes that do not append write a slot of their own past CAP.
+    auto finish = [&](int chunk, const float (&part)[4], float ks, float& score) {
+        score = reduce_scatter4(part) * ks;
         const int s = chunk * 64 + lane;
-        const bool valid = live && s <= t;
-        if (srow && s < L) srow[s] = valid ? score : -INFINITY;
+        const bool valid = active && s <= t;
         const uint32_t key = score_key(score);
         const bool app = valid && key > thr;
         const uint64_t m = wave_ballot(app);
-        if (app) {
-            const int o = nb + lanes_below(m);
-            rb.key[o] = key;
-            rb.pos[o] = (Pos)s;
-        }
+        int below = lanes_below(m);
+        asm volatile("" : "+v"(below));  // computed by every lane: keeps the select branch-free
+        const int o = app ? nb + below : CAP + lane;
+        rb.key[o] = key;
+        rb.pos[o] = (Pos)s;
         nb += __builtin_popcountll(m);
-        // Near capacity: ask every wave to compact at the next barrier.
-        if (nb > CAP - 2 * kWave && lane == 0) flags[chunk % 3] = 1u;
+    };
+    // The rest of an append step: the optional score-matrix row and the
+    // compaction request when the buffer nears capacity.
+    auto finish_tail = [&](int i, int chunk, float score) {
+        if (srow && active) {
+            const int s = chunk * 64 + lane;
+            if (s < L) srow[s] = s <= t ? score : -INFINITY;
+        }
+        if (active && nb > CAP - 2 * kWave && lane == 0) flags[i % 3] = 1u;
     };
 
-    HalfAcc hA, hB;
+    if (threadIdx.x == 0) flags[3] = 0u;
+    for (int pass = 0;; ++pass) {
+        HalfAcc hA, hB;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        hB.l[q] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 2; ++q) {
+            hB.l[q] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) hB.s[q][hb] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-    HalfB bA, bB;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-    float ks_prev = 0.f;
-    if (threadIdx.x < 3) flags[threadIdx.x] = 0u;
-    stage_chunk(0);
-    stage_chunk(1);
-    for (int chunk = 0; chunk <= last; ++chunk) {
-        // This wave's copies of chunk c have landed once at most its copies
-        // of chunk c+1 are in flight (loads complete in issue order); the
-        // barrier then makes every wave's copies visible.  With the score
-        // matrix requested, the row's stores share the counter: wait for all.
-        if (a.scores) __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
-        else if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F72);       // vmcnt(2)
-        else __builtin_amdgcn_s_waitcnt(0x0F71);                      // vmcnt(1)
-        __syncthreads();
-        // Cooperative compaction: a flag raised by the appends of chunk c-2
-        // (made during iteration c-1) makes every wave compact now, before its
-        // next appends, so the block pays one stall per event.  Slot j % 3
-        // belongs to the appends of chunk j: set in iteration j+1, read in
-        // j+2, cleared in j+3 (each step separated by a barrier).
-        if (chunk >= 2 && flags[(chunk - 2) % 3] != 0u) {
-            if (nb > a.topk) nb = wave_compact(rb, nb, (uint32_t)a.topk, &thr, CAP);
+            for (int hb = 0; hb < HB; ++hb) hB.s[q][hb] = v4f{0.f, 0.f, 0.f, 0.f};
         }
-        if (threadIdx.x == 0 && chunk >= 3) flags[(chunk - 3) % 3] = 0u;
-        // Chunk c+2 goes to the buffer chunk c-1 used.  Past the last chunk
-        // the copy is a clamped dummy, so every chunk issues the same loads.
-        stage_chunk(chunk + 2);
-        // Region 1: first half of chunk c on the MFMA, epilogue of the second
-        // half of chunk c-1 (zeros before the first chunk).
-        // The second half's operands are read here too, a region ahead.
-        __builtin_amdgcn_sched_barrier(0);
-        load_b(chunk, 0, bA);
-        load_b(chunk, 1, bB);
-        mma_half(bA, hA);
+        HalfB bA, bB;
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        float ks_prev = 0.f;
+        int chunk_prev = 0;  // chunk id of the previous iteration
+        if (threadIdx.x < 3) flags[threadIdx.x] = 0u;
+        stage_chunk(0);
+        stage_chunk(1);
+        for (int i = 0; i <= last; ++i) {
+            // This wave's copies of chunk i have landed once at most its copies
+            // of chunk i+1 are in flight (loads complete in issue order); the
+            // barrier then makes every wave's copies visible.  With the score
+            // matrix requested, the row's stores share the counter: wait for all.
+            if (a.scores) __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
+            else if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F72);       // vmcnt(2)
+            else __builtin_amdgcn_s_waitcnt(0x0F71);                      // vmcnt(1)
+            __syncthreads();
+            // Compaction request of the appends of the (i-2)-th chunk (made
+            // during iteration i-1); acted on below, after region 1.  Slot
+            // j % 3 belongs to the appends of the j-th chunk: set in iteration
+            // j+1, read in j+2, cleared in j+3 (each step separated by a barrier).
+            const bool want_compact = i >= 2 && flags[(i - 2) % 3] != 0u;
+            if (threadIdx.x == 0 && i >= 3) flags[(i - 3) % 3] = 0u;
+            // Chunk i+2 goes to the slot chunk i-1 used.  Past the last chunk
+            // the copy is a clamped dummy, so every chunk issues the same loads.
+            stage_chunk(i + 2);
+            // Region 1: first half of chunk i on the MFMA, epilogue of the
+            // second half of chunk i-1 (zeros before the first chunk).  The
+            // second half's operands are read here too, a region ahead.
+            __builtin_amdgcn_sched_barrier(0);
+            load_b(i, 0, bA);
+            load_b(i, 1, bB);
+            mma_half(bA, hA);
+            epi_half(hB, part[2], part[3]);
+            // keep this epilogue here (it would otherwise sink into a branch below)
+            asm volatile("" : "+v"(part[2]), "+v"(part[3]));
+            region_pattern();
+            __builtin_amdgcn_sched_barrier(0);
+            // Buffer maintenance, before the appends of chunk i-1.  The
+            // sample's appends (chunks 0..S-1 of the order) end in iteration
+            // S: set the speculative floor before any other append.
+            if (i == S + 1 && r_spec != 0u && active && (uint32_t)nb > r_spec) {
+                uint32_t fl;
+                nb = wave_floor(rb, nb, r_spec, &fl);
+                thr = fl == 0u ? 0u : fl - 1u;
+                floored = true;
+            }
+            // Cooperative compaction: a request from any wave makes every
+            // wave compact now, so the block pays one stall per event.
+            if (want_compact && active && nb > K) nb = wave_compact(rb, nb, (uint32_t)K, &thr, CAP);
+            // Region 2: second half of chunk i on the MFMA, epilogue of its
+            // first half, and the appends of chunk i-1 (discarded before the
+            // first chunk: nothing is valid yet).
+            const float fin_part[4] = {part[0], part[1], part[2], part[3]};
+            const int chunk_cur = chunk_at(i);
+            const bool fin_on = i >= 1;
+            const bool was_active = active;
+            active = active && fin_on;
+            float fin_score;
+            const int nb0 = nb;
+            __builtin_amdgcn_sched_barrier(0);
+            mma_half(bB, hB);
+            epi_half(hA, part[0], part[1]);
+            finish(chunk_prev, fin_part, ks_prev, fin_score);
+            asm volatile("" : "+v"(part[0]), "+v"(part[1]), "+v"(fin_score));
+            region_pattern();
+            __builtin_amdgcn_sched_barrier(0);
+            active = was_active;
+            if (!fin_on) nb = nb0;
+            if (fin_on) finish_tail(i - 1, chunk_prev, fin_score);
+            ks_prev = load_ks(i);
+            chunk_prev = chunk_cur;
+        }
         epi_half(hB, part[2], part[3]);
-        // keep this epilogue here (it would otherwise sink into the branch below)
-        asm volatile("" : "+v"(part[2]), "+v"(part[3]));
-        region_pattern(std::integral_constant<int, 0>{});
-        __builtin_amdgcn_sched_barrier(0);
-        if (chunk >= 1) finish(chunk - 1, part, ks_prev);
-        // Region 2: second half of chunk c on the MFMA, epilogue of its first half.
-        __builtin_amdgcn_sched_barrier(0);
-        mma_half(bB, hB);
-        epi_half(hA, part[0], part[1]);
-        region_pattern(std::integral_constant<int, 0>{});
-        __builtin_amdgcn_sched_barrier(0);
-        ks_prev = load_ks(chunk);
+        {
+            float fin_score;
+            finish(chunk_prev, part, ks_prev, fin_score);
+            finish_tail(last, chunk_prev, fin_score);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // no stage copy may still be in flight
+        if (pass == 1) break;
+        // Verification of the floor (see above); any failing row makes the
+        // whole block scan again, with only the failing waves appending.
+        const bool redo = active && floored && nb < K;
+        if (redo && lane == 0) flags[3] = 1u;
+        __syncthreads();
+        if (flags[3] == 0u) break;
+        active = redo;
+        if (redo) {
+            nb = 0;
+            thr = 0u;
+            floored = false;
+        }
+        r_spec = 0u;
     }
-    epi_half(hB, part[2], part[3]);
-    finish(last, part, ks_prev);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // no LDS copy may still be in flight at exit
     if (!live) return;
     if (srow) {
         for (int s = (last + 1) * 64 + lane; s < L; s += kWave) srow[s] = -INFINITY;
     }
     __builtin_amdgcn_wave_barrier();
-    wave_emit(rb, nb, a.topk, a.idx_out + row_t * a.topk, a.val_out ? a.val_out + row_t * a.topk : nullptr);
+    wave_emit(rb, nb, K, a.idx_out + row_t * K, a.val_out ? a.val_out + row_t * K : nullptr);
 }
 
 template <int HB>

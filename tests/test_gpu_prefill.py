@@ -126,6 +126,47 @@ def test_tie_heavy_generic():
     parity(inp, 40, want_scores=True, name="ties generic")
 
 
+def test_fused_small_k_long_rows_sampled():
+    """Long rows with a small k: the fp8 kernel's candidate buffer is cut down
+    many times per row, under a floor set from a strided sample of chunks."""
+    L, K = 8192, 64
+    inp = synth.prefill_inputs(1, L, 16, 128, "fp8", seed=5500)
+    rows = np.array([0, 63, 64, 2047, 2048, 4095, 5000, 8190, 8191])
+    parity(inp, K, rows=rows, name="small k long rows")
+
+
+def test_fused_floor_rescan_when_sample_holds_the_top():
+    """Keys at positions 1024 j + [960, 1024) -- the strided chunks a long row
+    of the fp8 kernel scores first -- score far above every other key, so the
+    floor each long row sets from that sample lies above its k-th score: the
+    check at the end of the scan fails and the row is scanned again.  The
+    selection must still be exact."""
+    L, H, D, K = 4096, 16, 128, 256
+    rng = np.random.default_rng(6000)
+    q0 = rng.standard_normal(D).astype(np.float32)
+    q = np.broadcast_to(q0, (1, L, H, D)).copy()
+    k = rng.standard_normal((1, L, D)).astype(np.float32)
+    hot = (np.arange(L) // 64) % 16 == 15
+    k[0, hot] = 2.0 * q0[None, :] + 0.1 * rng.standard_normal((int(hot.sum()), D)).astype(np.float32)
+    w = synth.softmax_weights(rng.standard_normal((1, L, H)))
+    qc, qs = synth.quantize_fp8_rows(q)
+    kc, ks = synth.quantize_fp8_rows(k)
+    inp = dict(q=qc, q_scale=qs, k=kc, k_scale=ks, w=w, dtype="fp8")
+    rows = np.array([0, 255, 256, 1983, 1984, 2047, 2048, 3000, 4094, 4095])
+    gi, _ = parity(inp, K, rows=rows, name="floor rescan")
+    hot_pos = np.flatnonzero(hot)
+    assert set(gi[0, 4095].tolist()) == set(hot_pos.tolist())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_tie_heavy_long_rows_sampled(dtype):
+    """Exact ties on long rows: ties at the k-th score go to the lowest
+    positions even though the fp8 kernel scores a row's chunks out of order."""
+    inp = synth.tie_heavy_prefill(1, 6000, 16, 128, dtype, seed=4100, n_proto=4)
+    rows = np.array([0, 511, 512, 2100, 4000, 5999])
+    parity(inp, 512, rows=rows, name="ties long rows")
+
+
 @pytest.mark.parametrize("L", [65536, 66000])
 def test_fused_long_sequences_sampled(L):
     """Both candidate-buffer layouts (16-bit positions up to L = 65536, 32-bit
