@@ -668,7 +668,7 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
 // 64-key chunk) walk the chunks in lockstep: every 64-key chunk (8 KB of fp8
 // rows) is fetched from L2 once per workgroup with direct global->LDS loads
 // (no VGPRs in flight), double-buffered, one barrier per chunk.  Rows are
-// stored with their 16-byte segments XOR-swizzled by (row & 7) so the MFMA
+// stored with their 16-byte segments XOR-swizzled by ((row >> 1) & 7) so the MFMA
 // operand reads (16 rows at a 128-byte stride) spread over the LDS banks.
 // Everything else -- operands, epilogue, per-wave candidate buffers -- is as
 // in the kernel above.
@@ -792,11 +792,11 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
 
     // Stage slot i % 3 receives the i-th chunk of the order: thread x of the
     // block copies 16 key bytes (LDS slot x = row x/8, segment x%8 holds
-    // global segment (x%8) ^ (row & 7) of that row) and wave 0 also copies
+    // global segment (x%8) ^ ((row >> 1) & 7) of that row) and wave 0 also copies
     // the chunk's 64 key scales.  Rows past the end are clamped to L-1; they
     // only ever feed masked scores.
     const int srow_i = threadIdx.x >> 3;
-    const int sseg = (threadIdx.x & 7) ^ (srow_i & 7);
+    const int sseg = (threadIdx.x & 7) ^ ((srow_i >> 1) & 7);
     auto stage_chunk = [&](int i) {
         unsigned char* dst = smem_raw + (i % kStages) * kStageBytes;
         const int chunk = chunk_at(i);
@@ -810,7 +810,9 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
                                              4, 0, 0);
     };
     // Swizzled byte offset of (row r, 16-byte segment j) inside a stage.
-    auto soff = [](int r, int j) { return r * kD + 16 * (j ^ (r & 7)); };
+    // Rows r and r+1 share a swizzle value and lie in opposite bank halves,
+    // so the 16 rows one operand read touches use all 64 banks once.
+    auto soff = [](int r, int j) { return r * kD + 16 * (j ^ ((r >> 1) & 7)); };
 
     const int K = a.topk;
     int nb = 0;
@@ -823,9 +825,10 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         r_spec = (uint32_t)ceilf(ec + 5.f * sqrtf(ec) + 8.f);
     }
 
-    // Pipeline.  The i-th chunk is loaded two chunks ahead (its stage slot
-    // frees up once every wave is past chunk i-3) and waited for at the top of
-    // iteration i, so a load has two chunk-times to arrive.  Within a chunk
+    // Pipeline.  The i-th chunk is copied three chunks ahead into the slot
+    // of chunk i-3 (free once every wave has read that chunk into registers)
+    // and waited for at the barrier in the middle of iteration i-1, so a copy
+    // has about two chunk-times to arrive.  Within a chunk
     // the work runs at half-chunk (32-key) granularity: while the matrix cores
     // multiply one half, the VALU runs the epilogue of the previous one.
     // Issue is in order within a wave and the waves of a SIMD run in step
@@ -872,11 +875,16 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     };
     // Scheduling pattern of one region: one MFMA followed by a few VALU
     // instructions, for every MFMA of the half.
-    auto region_pattern = []() {
+    auto region_pattern = [](auto lead_ds, auto nvalu) {
+        (void)lead_ds; (void)nvalu;
+        if constexpr (decltype(lead_ds)::value) {  // operand reads first: their latency hides under the MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
 #pragma unroll
         for (int i = 0; i < (HB + 1) * 2; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
         }
     };
     // Scale of key (i-th chunk)*64 + lane; read while the chunk's slot is
@@ -926,36 +934,46 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         if (threadIdx.x < 3) flags[threadIdx.x] = 0u;
         stage_chunk(0);
         stage_chunk(1);
+        stage_chunk(2);
+        // chunk 0 landed: at most this wave's copies of chunks 1 and 2 in flight
+        if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F74);                // vmcnt(4)
+        else __builtin_amdgcn_s_waitcnt(0x0F72);                          // vmcnt(2)
+        __syncthreads();
+        load_b(0, 0, bA);
         for (int i = 0; i <= last; ++i) {
-            // This wave's copies of chunk i have landed once at most its copies
-            // of chunk i+1 are in flight (loads complete in issue order); the
-            // barrier then makes every wave's copies visible.  With the score
-            // matrix requested, the row's stores share the counter: wait for all.
+            // Region 1: first half of chunk i on the MFMA (operands read during
+            // the previous region 2), epilogue of the second half of chunk
+            // i-1 (zeros before the first chunk); the second half's operands
+            // and the chunk's key scales are read here, before the barrier
+            // that releases the chunk's stage slot.
+            __builtin_amdgcn_sched_barrier(0);
+            mma_half(bA, hA);
+            epi_half(hB, part[2], part[3]);
+            load_b(i, 1, bB);
+            const float ks_cur = load_ks(i);
+            // keep this epilogue here (it would otherwise sink into a branch below)
+            asm volatile("" : "+v"(part[2]), "+v"(part[3]));
+            region_pattern(std::true_type{}, std::integral_constant<int, 4>{});
+            __builtin_amdgcn_sched_barrier(0);
+            // This wave's copies of chunk i+1 have landed once at most its
+            // copies of chunk i+2 are in flight (loads complete in issue
+            // order); the barrier then makes every wave's copies visible and
+            // certifies that every wave is done reading chunk i's slot.  With
+            // the score matrix requested, the row's stores share the counter:
+            // wait for all.
             if (a.scores) __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
             else if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F72);       // vmcnt(2)
             else __builtin_amdgcn_s_waitcnt(0x0F71);                      // vmcnt(1)
             __syncthreads();
             // Compaction request of the appends of the (i-2)-th chunk (made
-            // during iteration i-1); acted on below, after region 1.  Slot
-            // j % 3 belongs to the appends of the j-th chunk: set in iteration
-            // j+1, read in j+2, cleared in j+3 (each step separated by a barrier).
+            // during iteration i-1).  Slot j % 3 belongs to the appends of the
+            // j-th chunk: set in iteration j+1, read in j+2, cleared in j+3
+            // (each step separated by a barrier).
             const bool want_compact = i >= 2 && flags[(i - 2) % 3] != 0u;
             if (threadIdx.x == 0 && i >= 3) flags[(i - 3) % 3] = 0u;
-            // Chunk i+2 goes to the slot chunk i-1 used.  Past the last chunk
-            // the copy is a clamped dummy, so every chunk issues the same loads.
-            stage_chunk(i + 2);
-            // Region 1: first half of chunk i on the MFMA, epilogue of the
-            // second half of chunk i-1 (zeros before the first chunk).  The
-            // second half's operands are read here too, a region ahead.
-            __builtin_amdgcn_sched_barrier(0);
-            load_b(i, 0, bA);
-            load_b(i, 1, bB);
-            mma_half(bA, hA);
-            epi_half(hB, part[2], part[3]);
-            // keep this epilogue here (it would otherwise sink into a branch below)
-            asm volatile("" : "+v"(part[2]), "+v"(part[3]));
-            region_pattern();
-            __builtin_amdgcn_sched_barrier(0);
+            // Chunk i+3 goes to chunk i's slot.  Past the last chunk the copy
+            // is a clamped dummy, so every chunk issues the same loads.
+            stage_chunk(i + 3);
             // Buffer maintenance, before the appends of chunk i-1.  The
             // sample's appends (chunks 0..S-1 of the order) end in iteration
             // S: set the speculative floor before any other append.
@@ -969,8 +987,9 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             // wave compact now, so the block pays one stall per event.
             if (want_compact && active && nb > K) nb = wave_compact(rb, nb, (uint32_t)K, &thr, CAP);
             // Region 2: second half of chunk i on the MFMA, epilogue of its
-            // first half, and the appends of chunk i-1 (discarded before the
-            // first chunk: nothing is valid yet).
+            // first half, the appends of chunk i-1 (discarded before the first
+            // chunk: nothing is valid yet) and the first-half operands of
+            // chunk i+1 (landed, per the barrier above).
             const float fin_part[4] = {part[0], part[1], part[2], part[3]};
             const int chunk_cur = chunk_at(i);
             const bool fin_on = i >= 1;
@@ -982,13 +1001,14 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             mma_half(bB, hB);
             epi_half(hA, part[0], part[1]);
             finish(chunk_prev, fin_part, ks_prev, fin_score);
+            load_b(i + 1, 0, bA);
             asm volatile("" : "+v"(part[0]), "+v"(part[1]), "+v"(fin_score));
-            region_pattern();
+            region_pattern(std::true_type{}, std::integral_constant<int, 6>{});
             __builtin_amdgcn_sched_barrier(0);
             active = was_active;
             if (!fin_on) nb = nb0;
             if (fin_on) finish_tail(i - 1, chunk_prev, fin_score);
-            ks_prev = load_ks(i);
+            ks_prev = ks_cur;
             chunk_prev = chunk_cur;
         }
         epi_half(hB, part[2], part[3]);
@@ -997,7 +1017,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             finish(chunk_prev, part, ks_prev, fin_score);
             finish_tail(last, chunk_prev, fin_score);
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // no stage copy may still be in flight
+        __builtin_amdgcn_s_waitcnt(0x0000);  // no stage copy or LDS read may still be in flight
         if (pass == 1) break;
         // Verification of the floor (see above); any failing row makes the
         // whole block scan again, with only the failing waves appending.
