@@ -34,6 +34,8 @@ bool prefill_is_fused(int dtype, int H, int D) {
 }
 
 size_t decode_score_stride(int max_ctx) { return (size_t)((max_ctx + 63) / 64) * 64; }
+// Bound on one query's sampled keys: at most one page in 32, 64 keys each.
+size_t decode_sample_words(int max_ctx) { return (size_t)(((max_ctx + 63) / 64 + 31) / 32) * 64; }
 
 }  // namespace
 
@@ -169,11 +171,13 @@ dsaidx_status indexer_prefill(const void* q, const float* q_scale, const void* k
 size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, int D, int topk) {
     (void)H; (void)D; (void)topk;
     if (B < 1 || max_context_len < 0) return 0;
-    // scores, candidate scores, candidate positions: [B][stride] each;
-    // first-digit histogram [B][2048]; two counters per query.
-    // per-query page prefix [B+1].
-    return (size_t)B * decode_score_stride(max_context_len) * 12u +
-           (size_t)B * (dsaidx::kHistBins + dsaidx::kCtrlStride) * sizeof(uint32_t) + (size_t)(B + 1) * sizeof(int32_t);
+    // candidate scores and positions: [B][stride] each; per-query counters
+    // [B][kCtrlStride]; sampled keys [B][decode_sample_words]; page and
+    // sampled-page prefixes [B+1] each.
+    return (size_t)B * decode_score_stride(max_context_len) * 8u +
+           (size_t)B * dsaidx::kCtrlStride * sizeof(uint32_t) +
+           (size_t)B * decode_sample_words(max_context_len) * sizeof(uint32_t) +
+           (size_t)(B + 1) * 2 * sizeof(int32_t);
 }
 
 dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
@@ -215,14 +219,12 @@ dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
     hipStream_t st = (hipStream_t)stream;
     const size_t stride = decode_score_stride(max_context_len);
     char* wp = reinterpret_cast<char*>(workspace);
-    float* sc = reinterpret_cast<float*>(wp);
-    float* cand_score = reinterpret_cast<float*>(wp + (size_t)B * stride * 4);
-    int32_t* cand_pos = reinterpret_cast<int32_t*>(wp + (size_t)B * stride * 8);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(wp + (size_t)B * stride * 12);
-    uint32_t* ctrl = hist + (size_t)B * dsaidx::kHistBins;   // [B][kCtrlStride]
-    uint32_t* pre_count = ctrl;
-    uint32_t* cand_n = ctrl + 1;
-    int32_t* prefix = reinterpret_cast<int32_t*>(ctrl + (size_t)B * dsaidx::kCtrlStride);
+    float* cand_score = reinterpret_cast<float*>(wp);
+    int32_t* cand_pos = reinterpret_cast<int32_t*>(wp + (size_t)B * stride * 4);
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(wp + (size_t)B * stride * 8);  // [B][kCtrlStride]
+    uint32_t* sample_key = ctrl + (size_t)B * dsaidx::kCtrlStride;
+    int32_t* prefix = reinterpret_cast<int32_t*>(sample_key + (size_t)B * decode_sample_words(max_context_len));
+    int32_t* sprefix = prefix + (B + 1);
     hipError_t e;
     if (max_context_len > 0) {
         dsaidx::DecodeArgs d{};
@@ -235,45 +237,34 @@ dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
         d.context_lens = context_lens;
         d.max_ctx = max_context_len;
         d.B = B;
+        d.topk = topk;
         d.inv_sqrt_d = 1.0f / sqrtf((float)D);
-        d.scores = sc;
-        d.score_stride = (int64_t)stride;
-        d.hist = hist;
+        d.ctrl = ctrl;
+        d.sample_key = sample_key;
         d.prefix = prefix;
-        e = dsaidx::launch_decode_scan(d, H, max_context_len, st);
+        d.sprefix = sprefix;
+        d.cand_score = cand_score;
+        d.cand_pos = cand_pos;
+        d.cand_stride = (int64_t)stride;
+        e = dsaidx::launch_decode_scan(d, H, st);
         if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (scan)");
-        dsaidx::DecodeFilterArgs f{};
-        f.scores = sc;
-        f.stride = (int64_t)stride;
-        f.context_lens = context_lens;
-        f.max_ctx = max_context_len;
-        f.hist = hist;
-        f.pre_count = pre_count;
-        f.cand_n = cand_n;
-        f.cand_score = cand_score;
-        f.cand_pos = cand_pos;
-        f.B = B;
-        f.topk = topk;
-        f.idx_out = topk_idx;
-        f.val_out = topk_score;
-        e = dsaidx::launch_decode_filter(f, st);
-        if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (filter)");
     } else {
-        e = dsaidx::launch_zero_u32(hist, (size_t)B * (dsaidx::kHistBins + dsaidx::kCtrlStride), st);
+        e = dsaidx::launch_zero_u32(ctrl, (size_t)B * dsaidx::kCtrlStride, st);
         if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (clear)");
     }
-    // Exact finish among the candidates of the k-th score's first digit.
+    // Exact selection over each query's candidates (every score that can
+    // be selected is among them).
     dsaidx::SelectArgs s{};
     s.scores = cand_score;
     s.row_stride = (int64_t)stride;
     s.cols = (int)(stride > 0 ? stride : 1);
-    s.row_len = reinterpret_cast<const int32_t*>(cand_n);
+    s.row_len = reinterpret_cast<const int32_t*>(ctrl + 1);
     s.counter_stride = dsaidx::kCtrlStride;
-    s.level0_bin = max_context_len > 0 ? ctrl + 2 : nullptr;
+    s.level0_bin = nullptr;
     s.causal_L = 0;
     s.pos = cand_pos;
     s.hist = nullptr;
-    s.pre_count = pre_count;
+    s.pre_count = nullptr;
     s.total = context_lens;
     s.total_max = max_context_len;
     s.topk = topk;

@@ -4,7 +4,7 @@
 // (the decode walkthrough of "Lightning Indexer explained", section 2: one
 // dot of the current query against the whole indexer cache).  The scan is
 // bound by the cache bytes it streams (128 fp8 bytes + a 4-byte scale per
-// position), so the kernel is laid out for HBM:
+// position), so the kernels are laid out for HBM:
 //
 // * persistent grid: the (query, page) pairs of all queries form one list
 //   that is cut into equal shares, one per resident workgroup; each of a
@@ -22,10 +22,24 @@
 //   c[h] * max(S, 0) with c = w / sqrt(D), then a 4-way cross-lane
 //   reduce-scatter (permlane32/permlane16 swaps) that leaves lane l holding
 //   the score of key s0 + l of the 64-key page; times the key's fp32 scale.
-// * Scores go to a [B][stride] fp32 workspace (4 bytes written per 132
-//   bytes read) and into a per-workgroup LDS histogram of the first radix
-//   digit, flushed to a per-query global histogram that the selector uses
-//   to skip its first pass.
+//
+// Writes, not reads, set the price of keeping scores: a score stream of 4 B
+// per 132 B read, interleaved with the cache reads, costs about a fifth of
+// the scan.  So the scan writes only candidates:
+//
+// 1. A sample pass scores a strided sample of every long query's pages (one
+//    page in kSampleStride, from a per-query offset) and stores the sampled
+//    score keys.
+// 2. A floor kernel takes, per query, the r-th largest sampled key to 22
+//    bits (two radix digits), with r five standard deviations above the
+//    expected number of sampled scores at or above the query's k-th largest.
+// 3. The main pass scores every position and writes only the scores whose
+//    key reaches the query's floor, to the query's candidate list.
+// 4. Verification: if at least min(k, context) scores reached the floor,
+//    the k-th largest score is among them (and so is every score tied with
+//    it, since the floor is a key threshold), so the selection over the
+//    candidates is exact.  Otherwise a repair pass rescores the query in
+//    full.
 #include "common.h"
 #include "kernels.h"
 
@@ -36,6 +50,9 @@ namespace {
 constexpr int kD = 128;
 constexpr int kPage = 64;
 constexpr int kThreadsDec = 256;
+constexpr int kPrefixLds = 2048;   // queries whose page prefix is searched in LDS
+constexpr int kSampleStride = 32;  // one sampled page in this many
+constexpr int kCandBuf = 1024;     // per-wave LDS candidate buffer (score, position) pairs
 
 #ifndef DSAIDX_DECODE_NT
 #define DSAIDX_DECODE_NT 0  // 1: non-temporal (streaming) loads of the key cache
@@ -67,67 +84,94 @@ __device__ __forceinline__ float reduce_scatter4(const float v[4]) {
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Prologue: per-query page counts -> exclusive prefix over queries (the
-// global page list the scan walks; workgroup 0), and clears the histograms
-// and per-query counters (all workgroups, 16-byte stores).
+__device__ __forceinline__ int clamp_ctx(int ctx, int max_ctx) {
+    return ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
+}
+
+// Sampling of query b: pages sample_offset(b) + kSampleStride * i for
+// i < sampled_pages(ctx).  Only queries with context >= 4k and at least two
+// sampling strides of pages are sampled; the count is the same for every
+// offset (pages o + 32 i < np for all o < 32 when i < (np - 32) / 32 + 1).
+__device__ __forceinline__ int sample_offset(int b) {
+    return (int)(((uint32_t)b * 0x9E3779B1u) >> 27);  // in [0, 32)
+}
+__device__ __forceinline__ int sampled_pages(int ctx, int topk) {
+    const int np = (ctx + kPage - 1) / kPage;
+    if (ctx < 4 * topk || np < 2 * kSampleStride) return 0;
+    return (np - kSampleStride) / kSampleStride + 1;
+}
+
+// Prologue: per-query page counts and sampled-page counts -> exclusive
+// prefixes over queries (workgroup 0), and clears the per-query counters
+// (all workgroups, 16-byte stores).
 __global__ void __launch_bounds__(1024)
 decode_prologue_kernel(DecodeArgs a) {
-    __shared__ uint32_t wtot[16];
-    __shared__ uint32_t carry;
+    __shared__ uint32_t wtot[2][16];
+    __shared__ uint32_t carry[2];
     const int t = threadIdx.x;
-    const size_t nz4 = (size_t)a.B * (kHistBins + kCtrlStride) / 4;
-    v4i* z = reinterpret_cast<v4i*>(a.hist);
+    const size_t nz4 = (size_t)a.B * kCtrlStride / 4;
+    v4i* z = reinterpret_cast<v4i*>(a.ctrl);
     for (size_t i = (size_t)blockIdx.x * 1024 + t; i < nz4; i += (size_t)gridDim.x * 1024) z[i] = v4i{0, 0, 0, 0};
     if (blockIdx.x != 0) return;
-    if (t == 0) carry = 0;
+    if (t < 2) carry[t] = 0;
     __syncthreads();
     for (int b0 = 0; b0 < a.B; b0 += 1024) {
         const int b = b0 + t;
-        uint32_t np = 0;
+        uint32_t np = 0, ns = 0;
         if (b < a.B) {
-            int ctx = a.context_lens[b];
-            ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+            const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
             np = (uint32_t)((ctx + kPage - 1) / kPage);
+            ns = (uint32_t)sampled_pages(ctx, a.topk);
         }
-        const uint32_t incl = wave_incl_scan(np);
-        if (lane_id() == kWave - 1) wtot[t / kWave] = incl;
+        const uint32_t ip = wave_incl_scan(np), is = wave_incl_scan(ns);
+        if (lane_id() == kWave - 1) { wtot[0][t / kWave] = ip; wtot[1][t / kWave] = is; }
         __syncthreads();
-        uint32_t run = carry + incl - np;
-        for (int w = 0; w < t / kWave; ++w) run += wtot[w];
-        if (b < a.B) a.prefix[b] = (int32_t)run;
+        uint32_t rp = carry[0] + ip - np, rs = carry[1] + is - ns;
+        for (int w = 0; w < t / kWave; ++w) { rp += wtot[0][w]; rs += wtot[1][w]; }
+        if (b < a.B) { a.prefix[b] = (int32_t)rp; a.sprefix[b] = (int32_t)rs; }
         __syncthreads();
-        if (t == 1023) carry = run + np;
+        if (t == 1023) { carry[0] = rp + np; carry[1] = rs + ns; }
         __syncthreads();
     }
-    if (t == 0) a.prefix[a.B] = (int32_t)carry;
+    if (t == 0) { a.prefix[a.B] = (int32_t)carry[0]; a.sprefix[a.B] = (int32_t)carry[1]; }
 }
 
 // The scan.  A persistent grid (one resident round of workgroups): the
-// global list of (query, page) pairs, query-major, is cut into equal
-// contiguous shares, one per workgroup, so ragged context lengths leave no
-// tail of idle CUs.  Inside a share the 4 waves take interleaved pages
-// (wave w: pages w, w+4, ...), so a workgroup streams 32 KB of adjacent
-// cache per step.  Each wave keeps the next page's loads in flight while it
-// multiplies the current one; the (query, position, page id) of its next 64
-// pages sit one per lane, so no load waits on a block-table read.  Query
-// operands are reloaded only when a wave's pages cross into the next query;
-// each wave keeps its own LDS histogram of the first radix digit, flushed to
-// the query's global histogram on every query change and at the end.
+// global list of (query, page) pairs -- every page of every query in the
+// main pass, the sampled pages in the sample pass -- query-major, is cut into
+// equal contiguous shares, one per workgroup, so ragged context lengths
+// leave no tail of idle CUs.  Inside a share the 4 waves take interleaved
+// pages (wave w: pages w, w+4, ...).  Each wave keeps two pages of loads in
+// flight while it multiplies the current one; the (query, position, page id)
+// of its next 64 pages sit one per lane, so no load waits on a block-table
+// read.  Query operands are reloaded only when a wave's pages cross into the
+// next query.  Sample pass: every score key is stored, at the page's slot
+// in the sample list.  Main pass: scores whose key reaches the query's floor
+// go to the wave's LDS candidate buffer, flushed to the query's candidate
+// list.
 template <int HB>
 __global__ void __launch_bounds__(kThreadsDec)
 decode_scan_kernel(DecodeArgs a) {
-    __shared__ uint32_t hist_all[kThreadsDec / kWave][kHistBins];
+    __shared__ uint32_t lds_wave[kThreadsDec / kWave][2 * kCandBuf];  // candidate buffer
+    __shared__ int32_t prefix_lds[kPrefixLds];
     constexpr int NW = kThreadsDec / kWave;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int n = lane & 15, g = lane >> 4;
     constexpr int H = HB * 16;
-    uint32_t* hist = hist_all[wave];
-#pragma unroll
-    for (int i = 0; i < kHistBins / kWave; ++i) hist[lane + kWave * i] = 0u;
+    const bool sample = a.sample != 0;
+    float* cbuf_s = reinterpret_cast<float*>(lds_wave[wave]);
+    int32_t* cbuf_p = reinterpret_cast<int32_t*>(lds_wave[wave] + kCandBuf);
 
-    const int32_t* prefix = a.prefix;
-    const int P = prefix[a.B];
+    // The page prefix over queries goes to LDS when it fits: the searches
+    // below then cost LDS round trips instead of dependent global loads.
+    const int32_t* prefix = sample ? a.sprefix : a.prefix;
+    const bool pre_in_lds = a.B + 1 <= kPrefixLds;
+    if (pre_in_lds)
+        for (int i = threadIdx.x; i <= a.B; i += kThreadsDec) prefix_lds[i] = prefix[i];
+    __syncthreads();
+    auto prefix_at = [&](int i) -> int { return pre_in_lds ? prefix_lds[i] : prefix[i]; };
+    const int P = prefix_at(a.B);
     const int64_t G = gridDim.x;
     const int share_begin = (int)((int64_t)blockIdx.x * P / G);
     const int share_end = (int)((int64_t)(blockIdx.x + 1) * P / G);
@@ -141,7 +185,7 @@ decode_scan_kernel(DecodeArgs a) {
         const int p0 = share_begin + wave;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (prefix[mid] <= p0) lo = mid; else hi = mid;
+            if (prefix_at(mid) <= p0) lo = mid; else hi = mid;
         }
     }
     // Per-lane description of pages k0 .. k0+63 of this wave.
@@ -152,14 +196,18 @@ decode_scan_kernel(DecodeArgs a) {
         qb = -1; pos0 = 0; pid = 0;
         if (k < nk) {
             int bb = walk_b;
-            while (prefix[bb + 1] <= gp) ++bb;
-            const int j = gp - prefix[bb];
+            while (prefix_at(bb + 1) <= gp) ++bb;
+            int j = gp - prefix_at(bb);
+            if (sample) j = sample_offset(bb) + kSampleStride * j;
             qb = bb;
             pos0 = j * kPage;
             pid = a.block_table[(size_t)bb * a.max_pages + j];
         }
         const int last = min(63, nk - 1 - k0);
         if (last >= 0) walk_b = __builtin_amdgcn_readlane(qb, last);
+        // Settle the table loads here (once per 64 pages): left pending, they
+        // would make every later step wait for its own prefetches too.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     };
 
     const uint32_t lane_off = (uint32_t)(n * kD + 32 * g);
@@ -177,17 +225,22 @@ decode_scan_kernel(DecodeArgs a) {
     v8bf A[HB][4];
     float c[HB][4];
     int qcur = -1, ctx_cur = 0;
-    float* out = nullptr;
-    auto flush = [&](int qb) {
-        uint32_t* gh = a.hist + (size_t)qb * kHistBins;
-#pragma unroll 4
-        for (int i = 0; i < kHistBins / kWave; ++i) {
-            const uint32_t v = hist[lane + kWave * i];
-            if (v) {
-                atomicAdd(&gh[lane + kWave * i], v);
-                hist[lane + kWave * i] = 0u;
-            }
+    uint32_t floor_key = 0u;  // main pass: candidates have key >= floor_key
+    int nbuf = 0;             // main pass: entries in the wave's candidate buffer
+    uint32_t* cand_n = a.ctrl + 1;  // word 1 of each query's counter block
+    auto flush_cand = [&](int qb) {
+        if (nbuf == 0) return;
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&cand_n[(size_t)qb * kCtrlStride], (uint32_t)nbuf);
+        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+        float* cs = a.cand_score + (size_t)qb * a.cand_stride + base;
+        int32_t* cp = a.cand_pos + (size_t)qb * a.cand_stride + base;
+        for (int j = lane; j < nbuf; j += kWave) {
+            cs[j] = cbuf_s[j];
+            cp[j] = cbuf_p[j];
         }
+        __builtin_amdgcn_wave_barrier();
+        nbuf = 0;
     };
 
     int cq, cpos, cpid;   // lanes: pages k0 .. k0+63
@@ -195,26 +248,29 @@ decode_scan_kernel(DecodeArgs a) {
     describe(0, cq, cpos, cpid);
     describe(64, nq, npos, npid);
 
-    // One pipeline step: prefetch page k+1 into `nxt`, multiply page k held
-    // in `cur`.  Called with the two buffers alternating, so no copies.
-    auto step = [&](int k, v4i (&cur)[4][2], float ks_c, v4i (&nxt)[4][2], float& ks_n) {
+    // One pipeline step: prefetch page k+2 into `pre`, multiply page k held
+    // in `cur` (page k+1 is in flight meanwhile).  Called with three buffers
+    // rotating, so no copies.
+    auto step = [&](int k, v4i (&cur)[4][2], float ks_c, v4i (&pre)[4][2], float& ks_p) {
         const int i = k & 63;
         const int pb = __builtin_amdgcn_readlane(cq, i);
         const int ppos = __builtin_amdgcn_readlane(cpos, i);
-        if (k + 1 < nk) {
-            const int pid = i < 63 ? __builtin_amdgcn_readlane(cpid, i + 1) : __builtin_amdgcn_readlane(npid, 0);
-            load_page(pid, nxt, ks_n);
+        {
+            // Unconditional, so every path issues the same loads and the wait
+            // for `cur` can leave two pages in flight; past the end of the
+            // share the current page is fetched again (unused).
+            const int pid_n = i < 62 ? __builtin_amdgcn_readlane(cpid, i + 2) : __builtin_amdgcn_readlane(npid, i - 62);
+            const int pid = k + 2 < nk ? pid_n : __builtin_amdgcn_readlane(cpid, i);
+            load_page(pid, pre, ks_p);
         }
         if (i == 63) {  // roll the page descriptions forward
             cq = nq; cpos = npos; cpid = npid;
             describe(k + 65, nq, npos, npid);
         }
         if (pb != qcur) {  // entering a new query
-            if (qcur >= 0) flush(qcur);
+            if (qcur >= 0 && !sample) flush_cand(qcur);
             qcur = pb;
-            int ctx = a.context_lens[pb];
-            ctx_cur = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-            out = a.scores + (size_t)pb * a.score_stride;
+            ctx_cur = clamp_ctx(a.context_lens[pb], a.max_ctx);
             const uint16_t* qb = a.q + (size_t)pb * H * kD;
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb)
@@ -226,6 +282,11 @@ decode_scan_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii)
                     c[hb][ii] = a.w[(size_t)pb * H + 16 * hb + 4 * g + ii] * a.inv_sqrt_d;
+            if (!sample) floor_key = a.ctrl[(size_t)pb * kCtrlStride + 2];
+            // Settle the query loads here, on this rare path: otherwise the
+            // common path after it inherits their pending count and waits
+            // for every page load in flight at each step.
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
         float part[4];
 #pragma unroll
@@ -250,141 +311,183 @@ decode_scan_kernel(DecodeArgs a) {
         }
         const float score = reduce_scatter4(part) * ks_c;
         const int s = ppos + lane;
-        if (s < ctx_cur) {
-            out[s] = score;
-            atomicAdd(&hist[score_key(score) >> 21], 1u);
+        const uint32_t key = score_key(score);
+        if (sample) {
+            a.sample_key[(size_t)(share_begin + wave + NW * k) * kPage + lane] = key;
+        } else {
+            if (nbuf > kCandBuf - kWave) flush_cand(qcur);
+            const bool take = s < ctx_cur && key >= floor_key;
+            const uint64_t m = wave_ballot(take);
+            if (take) {
+                const int o = nbuf + lanes_below(m);
+                cbuf_s[o] = score;
+                cbuf_p[o] = s;
+            }
+            nbuf += __builtin_popcountll(m);
         }
     };
 
-    v4i bx[4][2], by[4][2];
-    float kx = 0.f, ky = 0.f;
-    load_page(__builtin_amdgcn_readlane(cpid, 0), bx, kx);
-    for (int k = 0; k < nk; k += 2) {
-        step(k, bx, kx, by, ky);
-        if (k + 1 < nk) step(k + 1, by, ky, bx, kx);
+    v4i b0[4][2], b1[4][2], b2[4][2];
+    float k0 = 0.f, k1 = 0.f, k2 = 0.f;
+    load_page(__builtin_amdgcn_readlane(cpid, 0), b0, k0);
+    load_page(__builtin_amdgcn_readlane(cpid, nk > 1 ? 1 : 0), b1, k1);
+    for (int k = 0; k < nk; k += 3) {
+        step(k, b0, k0, b2, k2);
+        if (k + 1 < nk) step(k + 1, b1, k1, b0, k0);
+        if (k + 2 < nk) step(k + 2, b2, k2, b1, k1);
     }
-    if (qcur >= 0) flush(qcur);
+    if (qcur >= 0 && !sample) flush_cand(qcur);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the final page prefetches (unused) settle before exit
 }
 
-// Selection, pass 1 of 2: with the first-digit histogram of the whole row
-// known, the digit b1 of the k-th largest score follows; every score whose
-// digit is above b1 is selected outright (written to the output), the ones
-// in bin b1 go to a per-query candidate list for the exact finish.  Many
-// workgroups per query, so the row is read at full chip bandwidth.
-__global__ void __launch_bounds__(256)
-decode_filter_kernel(DecodeFilterArgs a) {
-    constexpr int kPer = kFilterChunk / 256;  // entries per thread
-    __shared__ uint32_t wtot[4];
-    __shared__ int s_bin;
-    __shared__ uint32_t s_base_above, s_base_tie;
-    const int b = blockIdx.y;
-    int ctx = a.context_lens[b];
-    ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-    const int j0 = blockIdx.x * kFilterChunk;
-    if (j0 >= ctx) return;
-    const int K = a.topk;
+// Bin of the 2048-bin LDS histogram h (256 threads) where the count from
+// the top reaches r; also the count in the bins above it.  With r == 0 it
+// returns the total count in *above and bin -1.
+__device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint32_t* above, uint32_t* red) {
     const int t = threadIdx.x;
-    const int w = t / kWave;
-
-    // Block-wide exclusive prefix sum (4 waves) of one value per thread.
-    auto block_scan = [&](uint32_t v, uint32_t* total) -> uint32_t {
-        const uint32_t incl = wave_incl_scan(v);
-        __syncthreads();
-        if (lane_id() == kWave - 1) wtot[w] = incl;
-        __syncthreads();
-        uint32_t run = incl - v;
-        for (int i = 0; i < w; ++i) run += wtot[i];
-        *total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
-        return run;
-    };
-
-    int b1 = -1;  // ctx <= K: every entry is selected
-    if (ctx > K) {
-        const uint32_t* h = a.hist + (size_t)b * kHistBins;
-        uint32_t c[8], loc = 0;
+    constexpr int kPer = kHistBins / 256;
+    const uint32_t* hl = h + kHistBins - kPer * (t + 1);  // thread t: bins from the top, ascending
+    uint32_t loc = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { c[i] = h[kHistBins - 1 - 8 * t - i]; loc += c[i]; }
-        uint32_t tot;
-        uint32_t run = block_scan(loc, &tot);
-        const uint32_t need = (uint32_t)K;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (run < need && need <= run + c[i]) s_bin = kHistBins - 1 - 8 * t - i;
-            run += c[i];
+    for (int i = 0; i < kPer; ++i) loc += hl[i];
+    const uint32_t incl = wave_incl_scan(loc);
+    if (lane_id() == kWave - 1) red[t / kWave] = incl;
+    __syncthreads();
+    uint32_t run = incl - loc;
+    for (int w = 0; w < t / kWave; ++w) run += red[w];
+    const uint32_t total = red[0] + red[1] + red[2] + red[3];
+    if (r == 0) {
+        __syncthreads();
+        *above = total;
+        return -1;
+    }
+    if (t == 0) red[4] = 0xFFFFFFFFu;
+    __syncthreads();
+    for (int i = kPer - 1; i >= 0; --i) {
+        const uint32_t cnt = hl[i];
+        if (run < r && r <= run + cnt) {
+            red[4] = (uint32_t)(kHistBins - kPer * (t + 1) + i);
+            red[5] = run;
         }
-        __syncthreads();
-        b1 = s_bin;
-    }
-    if (blockIdx.x == 0 && t == 0) a.pre_count[(size_t)b * kCtrlStride + 2] = (uint32_t)b1;
-    const float* sc = a.scores + (size_t)b * a.stride;
-    const int j1 = min(ctx, j0 + kFilterChunk);
-    // Entry j0 + i*256 + t: thread t, step i.  Output positions are handed
-    // out per (step, wave) in step-major order, so each wave's stores of one
-    // step go to consecutive slots.
-    __shared__ uint32_t cnt[kPer][4];
-    float v[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int j = j0 + i * 256 + t;
-        v[i] = j < j1 ? sc[j] : -INFINITY;
-    }
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int j = j0 + i * 256 + t;
-        const int d = j < j1 ? (int)(score_key(v[i]) >> 21) : -2;
-        const uint32_t na = (uint32_t)__builtin_popcountll(wave_ballot(d > b1));
-        const uint32_t nt = (uint32_t)__builtin_popcountll(wave_ballot(d == b1));
-        if (lane_id() == 0) cnt[i][w] = na | (nt << 16);
+        run += cnt;
     }
     __syncthreads();
-    if (w == 0) {  // exclusive prefix over the kPer*4 (step, wave) counts
-        const int l = lane_id();
-        const uint32_t c0 = cnt[(2 * l) / 4][(2 * l) % 4], c1 = cnt[(2 * l + 1) / 4][(2 * l + 1) % 4];
-        const uint32_t incl = wave_incl_scan(c0 + c1);
-        const uint32_t tot = __shfl(incl, kWave - 1, kWave);
-        uint32_t ba = 0, bt = 0;
-        if (l == 0) {
-            ba = (tot & 0xFFFFu) ? atomicAdd(&a.pre_count[(size_t)b * kCtrlStride], tot & 0xFFFFu) : 0u;
-            bt = (tot >> 16) ? atomicAdd(&a.cand_n[(size_t)b * kCtrlStride], tot >> 16) : 0u;
-        }
-        ba = __shfl(ba, 0, kWave);
-        bt = __shfl(bt, 0, kWave);
-        const uint32_t e0 = incl - c0 - c1, e1 = incl - c1;
-        cnt[(2 * l) / 4][(2 * l) % 4] = e0;
-        cnt[(2 * l + 1) / 4][(2 * l + 1) % 4] = e1;
-        if (l == 0) { s_base_above = ba; s_base_tie = bt; }
+    const int bin = (int)red[4];
+    *above = red[5];
+    __syncthreads();
+    return bin;
+}
+
+// Floor of query b: the r-th largest key of its sample, cut to its top 22
+// bits (first digit by histogram, then the next 11 bits inside that bin).
+// Not sampled, or r beyond the sample: the floor stays 0 and every score of
+// the query is a candidate.
+__global__ void __launch_bounds__(256)
+decode_floor_kernel(DecodeArgs a) {
+    __shared__ uint32_t h[kHistBins];
+    __shared__ uint32_t red[8];
+    const int b = blockIdx.x, t = threadIdx.x;
+    const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
+    const int ns = sampled_pages(ctx, a.topk);
+    if (ns == 0) return;
+    const uint32_t* keys = a.sample_key + (size_t)a.sprefix[b] * kPage;
+    const int off = sample_offset(b);
+    const int n_all = ns * kPage;
+    auto valid = [&](int e) { return (off + kSampleStride * (e / kPage)) * kPage + e % kPage < ctx; };
+    for (int i = t; i < kHistBins; i += 256) h[i] = 0u;
+    __syncthreads();
+    for (int e = t; e < n_all; e += 256)
+        if (valid(e)) atomicAdd(&h[keys[e] >> 21], 1u);
+    __syncthreads();
+    uint32_t m = 0;
+    bin_from_top(h, 0, &m, red);
+    const float ex = (float)m * (float)a.topk / (float)ctx;
+    const uint32_t r = (uint32_t)ceilf(ex + 5.f * sqrtf(ex) + 8.f);
+    if (r >= m) return;
+    uint32_t above1 = 0;
+    const int bin1 = bin_from_top(h, r, &above1, red);
+    for (int i = t; i < kHistBins; i += 256) h[i] = 0u;
+    __syncthreads();
+    for (int e = t; e < n_all; e += 256) {
+        const uint32_t key = keys[e];
+        if (valid(e) && (int)(key >> 21) == bin1) atomicAdd(&h[(key >> 10) & (kHistBins - 1)], 1u);
     }
     __syncthreads();
-    const uint32_t ba = s_base_above, bt = s_base_tie;
-    int32_t* io = a.idx_out + (size_t)b * K;
-    float* vo = a.val_out ? a.val_out + (size_t)b * K : nullptr;
-    float* cs = a.cand_score + (size_t)b * a.stride;
-    int32_t* cp = a.cand_pos + (size_t)b * a.stride;
+    uint32_t above2 = 0;
+    const int bin2 = bin_from_top(h, r - above1, &above2, red);
+    if (t == 0) a.ctrl[(size_t)b * kCtrlStride + 2] = ((uint32_t)bin1 << 21) | ((uint32_t)bin2 << 10);
+}
+
+// Repair pass, one workgroup per query: a query whose candidate count fell
+// short of min(k, context) -- its sample floor lay above its k-th largest
+// score -- is rescored in full, every position becoming a candidate.  Plain
+// per-key dot products on the VALU: slow, and reached only by inputs whose
+// sampled pages score unlike the rest of their context.
+__global__ void __launch_bounds__(256)
+decode_repair_kernel(DecodeArgs a, int H) {
+    __shared__ float qs[64 * kD];
+    __shared__ float cs[64];
+    const int b = blockIdx.x;
+    const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
+    uint32_t* cnt = a.ctrl + (size_t)b * kCtrlStride + 1;
+    const uint32_t need = (uint32_t)min(a.topk, ctx);
+    if (*cnt >= need) return;
+    const int t = threadIdx.x;
+    for (int i = t; i < H * kD; i += 256)
+        qs[i] = __uint_as_float((uint32_t)a.q[(size_t)b * H * kD + i] << 16);
+    for (int i = t; i < H; i += 256) cs[i] = a.w[(size_t)b * H + i] * a.inv_sqrt_d;
+    __syncthreads();
+    float* out_s = a.cand_score + (size_t)b * a.cand_stride;
+    int32_t* out_p = a.cand_pos + (size_t)b * a.cand_stride;
+    for (int s = t; s < ctx; s += 256) {
+        const int page = a.block_table[(size_t)b * a.max_pages + s / kPage];
+        const uint8_t* row = a.k_cache + ((size_t)page * kPage + (s % kPage)) * kD;
+        float kf[kD];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int j = j0 + i * 256 + t;
-        const int d = j < j1 ? (int)(score_key(v[i]) >> 21) : -2;
-        const uint64_t ma = wave_ballot(d > b1), mt = wave_ballot(d == b1);
-        const uint32_t off = cnt[i][w];
-        if (d > b1) {
-            const uint32_t o = ba + (off & 0xFFFFu) + (uint32_t)lanes_below(ma);
-            if (o < (uint32_t)K) {
-                io[o] = j;
-                if (vo) vo[o] = v[i];
-            }
-        } else if (d == b1) {
-            const uint32_t o = bt + (off >> 16) + (uint32_t)lanes_below(mt);
-            if (o < (uint32_t)a.stride) {
-                cs[o] = v[i];
-                cp[o] = j;
-            }
+        for (int d = 0; d < kD; d += 2) {
+            const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)*reinterpret_cast<const uint16_t*>(row + d), false);
+            kf[d] = f[0];
+            kf[d + 1] = f[1];
         }
+        float acc = 0.f;
+        for (int h = 0; h < H; ++h) {
+            float dot = 0.f;
+#pragma unroll
+            for (int d = 0; d < kD; ++d) dot = fmaf(qs[h * kD + d], kf[d], dot);
+            acc = fmaf(cs[h], fmaxf(dot, 0.f), acc);
+        }
+        out_s[s] = acc * a.k_scale[(size_t)page * kPage + (s % kPage)];
+        out_p[s] = s;
     }
+    __syncthreads();
+    if (t == 0) *cnt = (uint32_t)ctx;
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = 0u;
+}
+
+template <int HB>
+hipError_t launch_scan_pass(const DecodeArgs& a, int64_t max_pages, hipStream_t stream) {
+    // One resident round of workgroups (occupancy queried once per process).
+    static int resident = 0;
+    hipError_t e;
+    if (resident == 0) {
+        int dev = 0, per_cu = 0, cus = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)decode_scan_kernel<HB>,
+                                                               kThreadsDec, 0)) != hipSuccess)
+            return e;
+        resident = (per_cu < 1 ? 1 : per_cu) * cus;
+    }
+    // Never more workgroups than pages; the kernel tolerates empty shares.
+    int64_t grid = resident;
+    if (grid > max_pages) grid = max_pages;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(decode_scan_kernel<HB>, dim3((unsigned)grid), dim3(kThreadsDec), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -397,46 +500,35 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_decode_filter(const DecodeFilterArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.max_ctx + kFilterChunk - 1) / kFilterChunk), (unsigned)a.B);
-    hipLaunchKernelGGL(decode_filter_kernel, grid, dim3(256), 0, stream, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_decode_scan(const DecodeArgs& a, int H, int max_ctx, hipStream_t stream) {
-    (void)max_ctx;
+hipError_t launch_decode_scan(const DecodeArgs& a_in, int H, hipStream_t stream) {
     {
-        const size_t nz4 = (size_t)a.B * (kHistBins + kCtrlStride) / 4;
+        const size_t nz4 = (size_t)a_in.B * kCtrlStride / 4;
         size_t blocks = (nz4 + 4095) / 4096;
         blocks = blocks < 1 ? 1 : (blocks > 256 ? 256 : blocks);
-        hipLaunchKernelGGL(decode_prologue_kernel, dim3((unsigned)blocks), dim3(1024), 0, stream, a);
+        hipLaunchKernelGGL(decode_prologue_kernel, dim3((unsigned)blocks), dim3(1024), 0, stream, a_in);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // One resident round of workgroups (occupancy queried once per process).
-    static int resident[5] = {0, 0, 0, 0, 0};
     const int hb = H / 16;
     if (hb < 1 || hb > 4) return hipErrorInvalidValue;
-    const void* fn = hb == 1 ? (const void*)decode_scan_kernel<1> : hb == 2 ? (const void*)decode_scan_kernel<2>
-                   : hb == 3 ? (const void*)decode_scan_kernel<3> : (const void*)decode_scan_kernel<4>;
-    if (resident[hb] == 0) {
-        int dev = 0, per_cu = 0, cus = 0;
-        if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreadsDec, 0)) != hipSuccess) return e;
-        resident[hb] = (per_cu < 1 ? 1 : per_cu) * cus;
+    const int64_t max_pages = (int64_t)a_in.B * ((a_in.max_ctx + kPage - 1) / kPage);
+    for (int pass = 0; pass < 2; ++pass) {
+        DecodeArgs a = a_in;
+        a.sample = pass == 0 ? 1 : 0;
+        const int64_t pages = pass == 0 ? (max_pages + kSampleStride - 1) / kSampleStride : max_pages;
+        switch (hb) {
+            case 1: e = launch_scan_pass<1>(a, pages, stream); break;
+            case 2: e = launch_scan_pass<2>(a, pages, stream); break;
+            case 3: e = launch_scan_pass<3>(a, pages, stream); break;
+            default: e = launch_scan_pass<4>(a, pages, stream); break;
+        }
+        if (e != hipSuccess) return e;
+        if (pass == 0) {
+            hipLaunchKernelGGL(decode_floor_kernel, dim3((unsigned)a_in.B), dim3(256), 0, stream, a_in);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
-    // Never more workgroups than pages; the kernel tolerates empty shares.
-    const int64_t max_pages = (int64_t)a.B * ((a.max_ctx + kPage - 1) / kPage);
-    int64_t grid = resident[hb];
-    if (grid > max_pages) grid = max_pages;
-    if (grid < 1) grid = 1;
-    switch (hb) {
-        case 1: hipLaunchKernelGGL(decode_scan_kernel<1>, dim3((unsigned)grid), dim3(kThreadsDec), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL(decode_scan_kernel<2>, dim3((unsigned)grid), dim3(kThreadsDec), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL(decode_scan_kernel<3>, dim3((unsigned)grid), dim3(kThreadsDec), 0, stream, a); break;
-        default: hipLaunchKernelGGL(decode_scan_kernel<4>, dim3((unsigned)grid), dim3(kThreadsDec), 0, stream, a); break;
-    }
+    hipLaunchKernelGGL(decode_repair_kernel, dim3((unsigned)a_in.B), dim3(256), 0, stream, a_in, H);
     return hipGetLastError();
 }
 

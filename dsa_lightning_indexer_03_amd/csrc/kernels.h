@@ -30,23 +30,6 @@ struct SelectArgs {
     float* val_out;           // nullable
 };
 
-struct DecodeFilterArgs {
-    const float* scores;      // [B][stride]
-    int64_t stride;
-    const int32_t* context_lens;
-    int max_ctx;
-    const uint32_t* hist;     // [B][kHistBins]
-    uint32_t* pre_count;      // [B * kCtrlStride] entries emitted straight to the output; word 2 of
-                              // each query's block receives the first digit of its k-th score
-    uint32_t* cand_n;         // [B * kCtrlStride] entries sent to the candidate list
-    float* cand_score;        // [B][stride]
-    int32_t* cand_pos;        // [B][stride]
-    int B;
-    int topk;
-    int32_t* idx_out;
-    float* val_out;
-};
-
 struct DecodeArgs {
     const uint16_t* q;        // [B][H][D] bf16
     const float* w;           // [B][H]
@@ -57,11 +40,16 @@ struct DecodeArgs {
     const int32_t* context_lens;
     int max_ctx;              // context lengths are clamped to [0, max_ctx]
     int B;
+    int topk;
     float inv_sqrt_d;
-    float* scores;            // [B][score_stride]
-    int64_t score_stride;
-    uint32_t* hist;           // [B][kHistBins], then [B][kCtrlStride] per-query counters
+    int sample;               // set per pass by the launcher: 1 = sample pass, 0 = main pass
+    uint32_t* ctrl;           // [B][kCtrlStride] per-query words: 1 = candidate count, 2 = floor key
+    uint32_t* sample_key;     // [sampled pages][64] score keys of the sampled pages
     int32_t* prefix;          // [B+1] exclusive prefix of per-query page counts
+    int32_t* sprefix;         // [B+1] exclusive prefix of per-query sampled-page counts
+    float* cand_score;        // [B][cand_stride] candidate scores
+    int32_t* cand_pos;        // [B][cand_stride] candidate positions
+    int64_t cand_stride;      // >= max_ctx
 };
 
 struct PrefillArgs {
@@ -81,9 +69,7 @@ struct PrefillArgs {
 size_t topk_select_smem_bytes();
 hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
-hipError_t launch_decode_scan(const DecodeArgs& a, int H, int max_ctx, hipStream_t stream);
-hipError_t launch_decode_filter(const DecodeFilterArgs& a, hipStream_t stream);
-constexpr int kFilterChunk = 8192;     // entries per filter workgroup
+hipError_t launch_decode_scan(const DecodeArgs& a, int H, hipStream_t stream);
 hipError_t launch_prefill_scores_generic(const PrefillArgs& a, int dtype, float* out, hipStream_t stream);
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream);
 

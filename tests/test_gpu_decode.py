@@ -1,13 +1,15 @@
 """GPU parity of indexer_decode_paged against the fp64 oracle: scattered and
 contiguous page tables, contexts shorter than k, partial last pages, the
-full fp8 code range, and layout independence (a permuted page table gives
-bit-identical results to the identity layout)."""
+full fp8 code range, layout independence (a permuted page table gives
+bit-identical results to the identity layout), a sampled candidate floor
+that overshoots (full rescoring), and all-tied scores."""
 import numpy as np
 import pytest
 import torch
 
+import dsa_lightning_indexer_03_amd as dsa
 import synth
-from gpu_util import run_decode, run_prefill, say
+from gpu_util import dev, host, run_decode, run_prefill, say
 from oracle import indexer
 from oracle.check import check_topk_rows
 
@@ -146,3 +148,58 @@ def test_many_queries_short_contexts():
     ctx = rng.integers(1, 700, size=300).tolist()
     d = synth.decode_inputs(300, ctx, 16, 128, seed=562, permute=True)
     parity(d, 128, "many", queries=range(0, 300, 7))
+
+
+def sampled_logical_pages(b, ctx, K, page=64, stride=32):
+    """Logical pages the decode scan scores first, to set a query's candidate
+    floor: one page in `stride` from a per-query offset (a multiplicative
+    hash of the query index), for queries with ctx >= 4k spanning at least
+    two strides of pages."""
+    npg = -(-ctx // page)
+    if ctx < 4 * K or npg < 2 * stride:
+        return []
+    off = ((b * 0x9E3779B1) & 0xFFFFFFFF) >> 27
+    return [off + stride * i for i in range((npg - stride) // stride + 1)]
+
+
+def test_floor_overshoot_is_repaired():
+    """Key scales of the sampled pages raised 50x: the floor taken from the
+    sample lies far above each query's k-th largest score, fewer than k
+    scores reach it, and the query is rescored in full.  The result still
+    matches the oracle, and the query's candidate count (word 1 of its
+    counter block in the workspace) equals its context."""
+    K = 512
+    ctx = [9000, 5000, 300]
+    d = synth.decode_inputs(3, ctx, 64, 128, seed=570, permute=True)
+    hot = 0
+    for b in range(3):
+        for j in sampled_logical_pages(b, ctx[b], K):
+            d["k_scale"][d["block_table"][b, j]] *= 50.0
+            hot += 1
+    assert hot > 0
+    B, mcl = 3, 9000
+    stride = -(-mcl // 64) * 64
+    ws = torch.zeros(dsa.decode_workspace_bytes(B, mcl, 64, 128, K), dtype=torch.uint8, device="cuda")
+    gi, gv = dsa.indexer_decode_paged(dev(d["q"]), dev(d["w"]), dev(d["k_cache"]), dev(d["k_scale"]),
+                                      dev(d["block_table"]), dev(d["context_lens"]), K,
+                                      max_context_len=mcl, workspace=ws)
+    torch.cuda.synchronize()
+    gi, gv = host(gi), host(gv)
+    for b in range(B):
+        o = indexer.decode_scores(d, b)
+        check_topk_rows(gi[b:b + 1], gv[b:b + 1], o[None], [o.size], K, where=f"overshoot q{b}")
+    ctrl = host(ws[B * stride * 8:B * stride * 8 + B * 64 * 4]).view(np.uint32).reshape(B, 64)
+    say(f"  candidate counts {ctrl[:, 1].tolist()}")
+    assert ctrl[0, 1] == ctx[0] and ctrl[1, 1] == ctx[1] and ctrl[2, 1] == ctx[2]
+
+
+def test_constant_scores_long_context():
+    """Every key zero: all scores tie at 0, the sampled floor admits every
+    position, and the ties go to the lowest positions."""
+    K = 2048
+    d = synth.decode_inputs(2, [20000, 9000], 16, 128, seed=571, permute=True)
+    d["k_cache"][:] = 0
+    gi, gv = run_decode(d, K)
+    for b in range(2):
+        assert np.array_equal(np.sort(gi[b]), np.arange(K)), f"q{b}: ties not broken toward low positions"
+        assert np.all(gv[b] == 0.0)
