@@ -340,12 +340,15 @@ decode_scan_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // the final page prefetches (unused) settle before exit
 }
 
-// Bin of the 2048-bin LDS histogram h (256 threads) where the count from
-// the top reaches r; also the count in the bins above it.  With r == 0 it
-// returns the total count in *above and bin -1.
+constexpr int kFloorThreads = 1024;
+constexpr int kFloorWaves = kFloorThreads / kWave;
+
+// Bin of the 2048-bin LDS histogram h (kFloorThreads threads) where the
+// count from the top reaches r; also the count in the bins above it.  With
+// r == 0 it returns the total count in *above and bin -1.
 __device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint32_t* above, uint32_t* red) {
     const int t = threadIdx.x;
-    constexpr int kPer = kHistBins / 256;
+    constexpr int kPer = kHistBins / kFloorThreads;
     const uint32_t* hl = h + kHistBins - kPer * (t + 1);  // thread t: bins from the top, ascending
     uint32_t loc = 0;
 #pragma unroll
@@ -353,27 +356,32 @@ __device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint3
     const uint32_t incl = wave_incl_scan(loc);
     if (lane_id() == kWave - 1) red[t / kWave] = incl;
     __syncthreads();
-    uint32_t run = incl - loc;
-    for (int w = 0; w < t / kWave; ++w) run += red[w];
-    const uint32_t total = red[0] + red[1] + red[2] + red[3];
+    uint32_t run = incl - loc, total = 0;
+#pragma unroll
+    for (int w = 0; w < kFloorWaves; ++w) {
+        const uint32_t v = red[w];
+        total += v;
+        if (w < t / kWave) run += v;
+    }
     if (r == 0) {
         __syncthreads();
         *above = total;
         return -1;
     }
-    if (t == 0) red[4] = 0xFFFFFFFFu;
+    if (t == 0) red[kFloorWaves] = 0xFFFFFFFFu;
     __syncthreads();
+#pragma unroll
     for (int i = kPer - 1; i >= 0; --i) {
         const uint32_t cnt = hl[i];
         if (run < r && r <= run + cnt) {
-            red[4] = (uint32_t)(kHistBins - kPer * (t + 1) + i);
-            red[5] = run;
+            red[kFloorWaves] = (uint32_t)(kHistBins - kPer * (t + 1) + i);
+            red[kFloorWaves + 1] = run;
         }
         run += cnt;
     }
     __syncthreads();
-    const int bin = (int)red[4];
-    *above = red[5];
+    const int bin = (int)red[kFloorWaves];
+    *above = red[kFloorWaves + 1];
     __syncthreads();
     return bin;
 }
@@ -381,11 +389,13 @@ __device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint3
 // Floor of query b: the r-th largest key of its sample, cut to its top 22
 // bits (first digit by histogram, then the next 11 bits inside that bin).
 // Not sampled, or r beyond the sample: the floor stays 0 and every score of
-// the query is a candidate.
-__global__ void __launch_bounds__(256)
+// the query is a candidate.  Each thread issues its key loads of a round
+// together, before the histogram updates.
+__global__ void __launch_bounds__(kFloorThreads)
 decode_floor_kernel(DecodeArgs a) {
     __shared__ uint32_t h[kHistBins];
-    __shared__ uint32_t red[8];
+    __shared__ uint32_t red[kFloorWaves + 2];
+    constexpr int U = 4;  // keys per thread per round
     const int b = blockIdx.x, t = threadIdx.x;
     const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
     const int ns = sampled_pages(ctx, a.topk);
@@ -393,12 +403,29 @@ decode_floor_kernel(DecodeArgs a) {
     const uint32_t* keys = a.sample_key + (size_t)a.sprefix[b] * kPage;
     const int off = sample_offset(b);
     const int n_all = ns * kPage;
-    auto valid = [&](int e) { return (off + kSampleStride * (e / kPage)) * kPage + e % kPage < ctx; };
-    for (int i = t; i < kHistBins; i += 256) h[i] = 0u;
-    __syncthreads();
-    for (int e = t; e < n_all; e += 256)
-        if (valid(e)) atomicAdd(&h[keys[e] >> 21], 1u);
-    __syncthreads();
+    auto valid = [&](int e) { return e < n_all && (off + kSampleStride * (e / kPage)) * kPage + e % kPage < ctx; };
+    // pass over the sample: histogram of digit (key >> shift) & 2047 of the
+    // keys whose top bits (key >> 21) equal `sel` (all keys when sel < 0)
+    auto pass = [&](int shift, int sel) {
+        for (int i = t; i < kHistBins; i += kFloorThreads) h[i] = 0u;
+        __syncthreads();
+        for (int e0 = 0; e0 < n_all; e0 += U * kFloorThreads) {
+            uint32_t kk[U];
+            bool vv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + u * kFloorThreads + t;
+                vv[u] = valid(e);
+                kk[u] = vv[u] ? keys[e] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (vv[u] && (sel < 0 || (int)(kk[u] >> 21) == sel))
+                    atomicAdd(&h[(kk[u] >> shift) & (kHistBins - 1)], 1u);
+        }
+        __syncthreads();
+    };
+    pass(21, -1);
     uint32_t m = 0;
     bin_from_top(h, 0, &m, red);
     const float ex = (float)m * (float)a.topk / (float)ctx;
@@ -406,13 +433,7 @@ decode_floor_kernel(DecodeArgs a) {
     if (r >= m) return;
     uint32_t above1 = 0;
     const int bin1 = bin_from_top(h, r, &above1, red);
-    for (int i = t; i < kHistBins; i += 256) h[i] = 0u;
-    __syncthreads();
-    for (int e = t; e < n_all; e += 256) {
-        const uint32_t key = keys[e];
-        if (valid(e) && (int)(key >> 21) == bin1) atomicAdd(&h[(key >> 10) & (kHistBins - 1)], 1u);
-    }
-    __syncthreads();
+    pass(10, bin1);
     uint32_t above2 = 0;
     const int bin2 = bin_from_top(h, r - above1, &above2, red);
     if (t == 0) a.ctrl[(size_t)b * kCtrlStride + 2] = ((uint32_t)bin1 << 21) | ((uint32_t)bin2 << 10);
@@ -524,7 +545,7 @@ hipError_t launch_decode_scan(const DecodeArgs& a_in, int H, hipStream_t stream)
         }
         if (e != hipSuccess) return e;
         if (pass == 0) {
-            hipLaunchKernelGGL(decode_floor_kernel, dim3((unsigned)a_in.B), dim3(256), 0, stream, a_in);
+            hipLaunchKernelGGL(decode_floor_kernel, dim3((unsigned)a_in.B), dim3(kFloorThreads), 0, stream, a_in);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }

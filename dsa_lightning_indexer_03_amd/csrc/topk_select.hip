@@ -8,12 +8,14 @@
 // the selected set is every entry with composite >= C*.
 //
 // Digits, most significant first:  key[31:21], key[20:10], key[9:0],
-// ~pos[21:11], ~pos[10:0].  The first digit's histogram may be supplied by
-// the producer of the scores (the decode scan builds it on the fly);
-// otherwise one pass over the row builds it.  As soon as the entries that
-// still tie with the chosen prefix fit in LDS, one pass over the row writes
-// every entry above the prefix straight to the output and copies the tied
-// ones to LDS; the remaining digits are then resolved in LDS.
+// ~pos[21:11], ~pos[10:0].  A row that fits in LDS is read once, into LDS,
+// and every digit is resolved there.  Otherwise the first digit's histogram
+// is supplied by the producer of the scores or built by one pass over the
+// row, and as soon as the entries that still tie with the chosen prefix fit
+// in LDS, one pass over the row writes every entry above the prefix straight
+// to the output and copies the tied ones to LDS; the remaining digits are
+// then resolved in LDS.  The descent stops at the first digit where the
+// entries tied with the prefix exactly fill the remaining slots.
 #include "common.h"
 #include "kernels.h"
 
@@ -139,12 +141,12 @@ topk_select_kernel(SelectArgs a) {
     int32_t* idx_out = a.idx_out + (int64_t)row * K + G;
     float* val_out = a.val_out ? a.val_out + (int64_t)row * K + G : nullptr;
 
-    if (R == n) {  // every entry is selected
-        for (int j = t; j < n; j += kThreads) {
+    if (R == n || R == 0) {  // every entry, or none, is selected
+        for (int j = t; j < R; j += kThreads) {
             idx_out[j] = psrc ? psrc[j] : j;
             if (val_out) val_out[j] = src[j];
         }
-        for (int j = G + n + t; j < K; j += kThreads) {
+        for (int j = G + R + t; j < K; j += kThreads) {
             a.idx_out[(int64_t)row * K + j] = -1;
             if (a.val_out) a.val_out[(int64_t)row * K + j] = -INFINITY;
         }
@@ -161,7 +163,34 @@ topk_select_kernel(SelectArgs a) {
         sh.cand_n = 0;
     }
     // ---- level-0 histogram (unless every entry's first digit is known) ----
-    if (a.hist) {
+    if (!known0 && n <= kCap) {
+        // The whole row goes to LDS, read once (U loads per thread in flight).
+        constexpr int U = 4;
+        for (int b = t; b < kBins; b += kThreads) sh.hist[b] = 0;
+        if (t == 0) sh.cand_n = (uint32_t)n;
+        __syncthreads();
+        for (int j0 = 0; j0 < n; j0 += U * kThreads) {
+            float v[U];
+            uint32_t p[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = j0 + u * kThreads + t;
+                v[u] = j < n ? src[j] : 0.f;
+                p[u] = j < n ? (psrc ? (uint32_t)psrc[j] : (uint32_t)j) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = j0 + u * kThreads + t;
+                if (j < n) {
+                    const uint32_t key = score_key(v[u]);
+                    sh.cand_key[j] = key;
+                    sh.cand_pos[j] = p[u];
+                    atomicAdd(&sh.hist[key >> 21], 1u);
+                }
+            }
+        }
+        in_lds = true;
+    } else if (a.hist) {
         const uint32_t* h = a.hist + (int64_t)row * kBins;
         for (int b = t; b < kBins; b += kThreads) sh.hist[b] = h[b];
     } else if (!known0) {
@@ -216,7 +245,8 @@ topk_select_kernel(SelectArgs a) {
             in_lds = true;
             __syncthreads();
         }
-        if (level == 4) break;
+        // Every entry tied with the prefix is selected: no finer digit matters.
+        if (level == 4 || (in_lds && cnt == need)) break;
         ++level;
 
         // Histogram of the next digit over the entries matching the prefix.
@@ -239,7 +269,8 @@ topk_select_kernel(SelectArgs a) {
         __syncthreads();
     }
 
-    // Composite fully fixed: C* = (pk, pi).  Emit the LDS entries >= C*.
+    // Prefix (pk under mk, pi under mi) fixed far enough: every LDS entry at
+    // or above it is selected.
     {
         const int cn = min((int)sh.cand_n, kCap);
         for (int j0 = 0; j0 < cn; j0 += kThreads) {
@@ -249,8 +280,8 @@ topk_select_kernel(SelectArgs a) {
             if (j < cn) {
                 key = sh.cand_key[j];
                 pos = sh.cand_pos[j];
-                const uint32_t np = ~pos;
-                take = key > pk || (key == pk && (np & mi) >= pi);
+                const uint32_t kt = key & mk, it = ~pos & mi;
+                take = kt > pk || (kt == pk && it >= pi);
             }
             emit(sh, take, pos, key_score(key), idx_out, val_out, (uint32_t)R);
         }
