@@ -92,7 +92,8 @@ dsaidx_status topk_select(const float* scores, int rows, int cols, int64_t row_s
 size_t indexer_prefill_workspace_bytes(int B, int L, int H, int D, int topk, int qk_dtype, int want_scores) {
     (void)topk;
     if (B < 1 || L < 1) return 0;
-    if (prefill_is_fused(qk_dtype, H, D) || want_scores) return 0;
+    if (prefill_is_fused(qk_dtype, H, D)) return dsaidx::prefill_fused_workspace_bytes(B, L, qk_dtype);
+    if (want_scores) return 0;
     return (size_t)B * (size_t)L * (size_t)L * sizeof(float);
 }
 
@@ -140,6 +141,11 @@ dsaidx_status indexer_prefill(const void* q, const float* q_scale, const void* k
     hipStream_t st = (hipStream_t)stream;
 
     if (prefill_is_fused(qk_dtype, H, D)) {
+        const size_t need = dsaidx::prefill_fused_workspace_bytes(B, L, qk_dtype);
+        if (need > 0 && (!workspace || workspace_bytes < need))
+            return fail(DSAIDX_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+        if (need > 0 && !aligned16(workspace)) return fail(DSAIDX_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+        a.workspace = workspace;
         hipError_t e = dsaidx::launch_prefill_fused(a, qk_dtype, st);
         if (e != hipSuccess) return hip_fail(e, "indexer_prefill (fused)");
         return DSAIDX_OK;

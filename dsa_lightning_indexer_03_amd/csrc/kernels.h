@@ -64,6 +64,11 @@ struct PrefillArgs {
     int32_t* idx_out;
     float* val_out;           // nullable
     float* scores;            // nullable [B][L][L]
+    void* workspace;          // prefill_fused_workspace_bytes(B, L, dtype) bytes (fused path)
+    // set by the fused launcher from the workspace:
+    float* ks_adj;            // [B][Lpad] key scales times 2^Pk
+    uint8_t* kexp;            // [B][Lpad] E8M0 bytes 127 - Pk, lane-major within each 64-key chunk
+    int Lpad;                 // L rounded up to a multiple of 64
 };
 
 size_t topk_select_smem_bytes();
@@ -72,5 +77,6 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
 hipError_t launch_decode_scan(const DecodeArgs& a, int H, hipStream_t stream);
 hipError_t launch_prefill_scores_generic(const PrefillArgs& a, int dtype, float* out, hipStream_t stream);
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream);
+size_t prefill_fused_workspace_bytes(int B, int L, int dtype);
 
 }  // namespace dsaidx

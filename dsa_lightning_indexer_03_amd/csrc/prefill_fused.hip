@@ -23,7 +23,9 @@
 //   16 heads x 16 keys; bf16: four v_mfma_f32_16x16x32_bf16.  The contraction
 //   dimension is split the same way on both operands: lane group g owns the
 //   dims [32g, 32g+32).
-// * epilogue in registers: c[t,h] * max(S, 0) summed over the lane's heads,
+// * epilogue (kernel below; the fp8 kernel with staged keys further down
+//   sums the heads on the matrix cores instead, see there): in registers,
+//   c[t,h] * max(S, 0) summed over the lane's heads,
 //   with c = w * q_scale / sqrt(D) (exact refactoring: ReLU commutes with a
 //   positive scale, and the key's fp8 scale is applied once per key after
 //   the head sum), then a cross-lane reduce-scatter leaves lane l with the
@@ -87,6 +89,9 @@ struct RowBuf {
 // 16-byte position read), so each step keeps four independent LDS reads in
 // flight instead of one.  Buffer capacities are multiples of 256.
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 template <typename Pos>
 struct Pos4 { Pos v[4]; };
@@ -662,16 +667,28 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// fp8, L <= 65536: keys staged through LDS.
+// fp8, L <= 65536: keys staged through LDS, head sums on the matrix cores.
 //
 // The 8 waves of a workgroup (8 consecutive tokens, all with the same last
 // 64-key chunk) walk the chunks in lockstep: every 64-key chunk (8 KB of fp8
 // rows) is fetched from L2 once per workgroup with direct global->LDS loads
-// (no VGPRs in flight), double-buffered, one barrier per chunk.  Rows are
-// stored with their 16-byte segments XOR-swizzled by ((row >> 1) & 7) so the MFMA
-// operand reads (16 rows at a 128-byte stride) spread over the LDS banks.
-// Everything else -- operands, epilogue, per-wave candidate buffers -- is as
-// in the kernel above.
+// (no VGPRs in flight), triple-buffered, one barrier per chunk.  Rows are
+// stored with their 16-byte segments XOR-swizzled by ((row >> 1) & 7) so the
+// MFMA operand reads (16 rows at a 128-byte stride) spread over the LDS banks.
+//
+// Epilogue.  The score of key s is sum_h c_h max(S_h, 0) times the key's
+// scale, with c_h = w_h * q_scale_h / sqrt(D) and S_h the dot product of the
+// fp8 values.  |S_h| <= |q_h|_1 * max_d |k_d| <= 2^Pq * 2^Pk, with Pq taken
+// per token and Pk per key (a pre-pass over the keys), so the score MFMAs,
+// run with the E8M0 operand scales 2^-Pq (A) and 2^-Pk (B), leave every
+// value in [-1, 1].  There the conversion to f16 with its [0, 1] clamp is
+// max(S, 0) itself, rounded to nearest (relative error <= 2^-11 down to
+// 2^-14 of the bound), and the weighted sum over heads is one more MFMA
+// (f16, 16x16x32) with the weights c_h * 2^E as its A operand.  Its weights
+// for subtile st sit in the rows 4st..4st+3 only, so the four subtiles of a
+// chunk accumulate into one tile whose element 0 in lane l is the score of
+// key 64*chunk + l: no cross-lane reduction.  The factor 2^(Pq - E) and the
+// key's scale times 2^Pk finish the score.
 // ---------------------------------------------------------------------------
 constexpr int kStagedWaves = 8;
 constexpr int kStagedCap = 2560;   // candidates per row; 8 rows + 3 key chunks fit in 160 KB
@@ -679,8 +696,40 @@ constexpr int kStages = 3;
 // per wave: keys [CAP + 64] u32, histogram [256] u32, positions [CAP + 64] u16; the
 // 64 slots past CAP take the writes of lanes that do not append
 constexpr size_t kStagedWaveBytes = (size_t)(kStagedCap + kWave) * 6 + 256 * 4;
-constexpr size_t kStageKeyBytes = 64 * kD;                 // one chunk of fp8 keys ...
-constexpr size_t kStageBytes = kStageKeyBytes + 64 * 4;   // ... and their fp32 scales
+constexpr size_t kStageKeyBytes = 64 * kD;                 // one chunk of fp8 keys,
+constexpr size_t kStageScaleOff = kStageKeyBytes;          // their fp32 scales times 2^Pk,
+constexpr size_t kStageExpOff = kStageKeyBytes + 64 * 4;   // their E8M0 bytes (64 used of 256)
+constexpr size_t kStageBytes = kStageExpOff + 256;
+
+// Key pre-pass: for key s of sequence b (positions up to the 64-padded
+// length; rows past the end repeat row L-1, as the staged copies do):
+// 2^Pk >= max_d |k_d| (Pk = 0 for a zero row), ks_adj = k_scale * 2^Pk and
+// the E8M0 byte 127 - Pk, stored at 64*chunk + 4*(s % 16) + (s % 64) / 16 so
+// that lane n of a chunk finds the bytes of its four subtiles in one word.
+__global__ void __launch_bounds__(256)
+prefill_key_exp_kernel(PrefillArgs a) {
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int Lp = a.Lpad;
+    if (gi >= (int64_t)a.B * Lp) return;
+    const int b = (int)(gi / Lp), s = (int)(gi % Lp);
+    const int sr = s < a.L ? s : a.L - 1;
+    const uint8_t* row = reinterpret_cast<const uint8_t*>(a.k) + ((size_t)b * a.L + sr) * kD;
+    uint32_t mx = 0;
+#pragma unroll
+    for (int c = 0; c < kD / 16; ++c) {
+        const v4i v = *reinterpret_cast<const v4i*>(row + 16 * c);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t x = (uint32_t)v[d] & 0x7F7F7F7Fu;  // magnitudes: e4m3 orders like its bits
+            mx = max(mx, max(max(x & 0xFFu, (x >> 8) & 0xFFu), max((x >> 16) & 0xFFu, x >> 24)));
+        }
+    }
+    const float vmax = __builtin_amdgcn_cvt_f32_fp8((int)mx, 0);
+    const int pk = vmax > 0.f ? __builtin_amdgcn_frexp_expf(vmax) : 0;  // 2^pk > vmax
+    a.ks_adj[gi] = ldexpf(a.k_scale[(size_t)b * a.L + sr], pk);
+    const int c = s / 64, n = s % 16, q = (s % 64) / 16;
+    a.kexp[(size_t)b * Lp + 64 * c + 4 * n + q] = (uint8_t)(127 - pk);
+}
 
 template <int HB>
 __global__ void __launch_bounds__(kStagedWaves * kWave)
@@ -714,61 +763,66 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     typename Op::template A<HB> Aq;
     Op::template load_a<HB>(Aq, reinterpret_cast<const uint8_t*>(a.q) + row_t * H * kD, n, g);
 
-    float c[HB][4];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 16 * hb + 4 * g + i;
-            c[hb][i] = a.w[row_t * H + h] * a.q_scale[row_t * H + h] * (a.inv_sqrt_d * 0.5f);
-        }
-    // Linear half on the MFMA: u = sum_i c_i q_i split into six fp8 pieces
-    // (see the kernel above).
-    v8i Alin = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    float lin0, lin1;
+    // Head weights as the A operand of the f16 head-sum MFMA x (x < NX), in
+    // the contraction order k = 8g + j: head 32x + 4g + j for j < 4, head
+    // 32x + 16 + 4g + (j - 4) for j >= 4; subtile st uses rows 4st..4st+3.
+    constexpr int NX = (HB + 1) / 2;
+    v8h Wh[4][NX];
+    float Fscale;  // 2^(Pq - E)
+    int sa;        // E8M0 A scale of the score MFMAs: 127 - Pq
     {
-        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + row_t * H * kD;
-        const int tu = __builtin_amdgcn_readfirstlane((int)row_t);
-        float u0 = 0.f, u1 = 0.f;
-        for (int h = 0; h < H; ++h) {
-            const float ch = a.w[(size_t)tu * H + h] * a.q_scale[(size_t)tu * H + h] * (a.inv_sqrt_d * 0.5f);
-            const int two = (int)*reinterpret_cast<const uint16_t*>(qrow + (size_t)h * kD + 2 * lane);
-            const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(two, false);
-            u0 = fmaf(ch, f[0], u0);
-            u1 = fmaf(ch, f[1], u1);
-        }
-        uint8_t* pieces = reinterpret_cast<uint8_t*>(rb.hist);
-        float sc[6];
+        // 2^Pq >= max_h |q_h|_1 (fp8 values): lane (m, g) sums its 32 bytes of
+        // head 16hb + m, the four lane groups of a row add up, max over rows.
+        float l1 = 0.f;
 #pragma unroll
-        for (int pc = 0; pc < 6; ++pc) {
-            float m = fmaxf(fabsf(u0), fabsf(u1));
+        for (int hb = 0; hb < HB; ++hb) {
+            float sabs = 0.f;
 #pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
-            const bool on = m > 1e-30f;
-            const float scale = on ? ldexpf(1.0f, __builtin_amdgcn_frexp_expf(m * (1.0f / 448.0f))) : 0.f;
-            const float inv = on ? 1.0f / scale : 0.f;
-            const int code = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * inv, u1 * inv, 0, false);
-            const auto dec = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
-            u0 -= dec[0] * scale;
-            u1 -= dec[1] * scale;
-            *reinterpret_cast<uint16_t*>(pieces + pc * kD + 2 * lane) = (uint16_t)(code & 0xFFFF);
-            sc[pc] = scale;
+            for (int d = 0; d < 8; ++d) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(Aq.a[hb][d], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(Aq.a[hb][d], true);
+                sabs += (fabsf(lo[0]) + fabsf(lo[1])) + (fabsf(hi[0]) + fabsf(hi[1]));
+            }
+            sabs += __shfl_xor(sabs, 16, kWave);
+            sabs += __shfl_xor(sabs, 32, kWave);
+            l1 = fmaxf(l1, sabs);
         }
-        __builtin_amdgcn_wave_barrier();
-        int pc_of_row = -1;
-        if ((n & 3) == 0) pc_of_row = n >> 2;
-        else if (n == 1 || n == 5) pc_of_row = 4 + (n >> 2);
-        if (pc_of_row >= 0) {
-            const v4i lo = *reinterpret_cast<const v4i*>(pieces + pc_of_row * kD + 32 * g);
-            const v4i hi = *reinterpret_cast<const v4i*>(pieces + pc_of_row * kD + 32 * g + 16);
-            Alin = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int d = 8; d >= 1; d >>= 1) l1 = fmaxf(l1, __shfl_xor(l1, d, kWave));
+        const int Pq = l1 > 0.f ? __builtin_amdgcn_frexp_expf(l1) : 0;  // 2^Pq > l1
+        sa = 127 - Pq;
+        float cf[HB][4];
+        float mx = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 16 * hb + 4 * g + i;
+                cf[hb][i] = a.w[row_t * H + h] * a.q_scale[row_t * H + h] * a.inv_sqrt_d;
+                mx = fmaxf(mx, fabsf(cf[hb][i]));
+            }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
+        int E = mx > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
+        E = E < -60 ? -60 : (E > 100 ? 100 : E);
+        Fscale = ldexpf(1.0f, Pq - E);
+        // lane (m, g) of the weight operand: row m = n, contraction group g
+        const int own_st = n >> 2;
+#pragma unroll
+        for (int x = 0; x < NX; ++x) {
+            v8h wv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int hb = 2 * x + (j >> 2);
+                wv[j] = hb < HB ? (_Float16)ldexpf(cf[hb < HB ? hb : 0][j & 3], E) : (_Float16)0.f;
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st) Wh[st][x] = st == own_st ? wv : v8h{0, 0, 0, 0, 0, 0, 0, 0};
         }
-        lin0 = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
-        lin1 = g == 0 ? sc[4] : g == 1 ? sc[5] : 0.f;
-        __builtin_amdgcn_wave_barrier();
     }
 
-    const float* kscale = a.k_scale + (size_t)b * L;
+    const float* ksadj = a.ks_adj + (size_t)b * a.Lpad;
+    const uint8_t* kexp = a.kexp + (size_t)b * a.Lpad;
     float* srow = (a.scores && live) ? a.scores + row_t * L : nullptr;
     const int last = (min(blk * W + W - 1, L - 1)) / 64;   // same for every wave of the block
 
@@ -792,9 +846,10 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
 
     // Stage slot i % 3 receives the i-th chunk of the order: thread x of the
     // block copies 16 key bytes (LDS slot x = row x/8, segment x%8 holds
-    // global segment (x%8) ^ ((row >> 1) & 7) of that row) and wave 0 also copies
-    // the chunk's 64 key scales.  Rows past the end are clamped to L-1; they
-    // only ever feed masked scores.
+    // global segment (x%8) ^ ((row >> 1) & 7) of that row), wave 0 also copies
+    // the chunk's 64 adjusted key scales and wave 1 its 64 E8M0 bytes (lanes
+    // 16..63 repeat them into the unused tail).  Rows past the end are
+    // clamped to L-1; they only ever feed masked scores.
     const int srow_i = threadIdx.x >> 3;
     const int sseg = (threadIdx.x & 7) ^ ((srow_i >> 1) & 7);
     auto stage_chunk = [&](int i) {
@@ -805,8 +860,12 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 1024 * wave),
                                          16, 0, 0);
         if (wave == 0)
-            __builtin_amdgcn_global_load_lds(kscale + min(chunk * 64 + lane, L - 1),
-                                             (__attribute__((address_space(3))) void*)(dst + kStageKeyBytes),
+            __builtin_amdgcn_global_load_lds(ksadj + chunk * 64 + lane,
+                                             (__attribute__((address_space(3))) void*)(dst + kStageScaleOff),
+                                             4, 0, 0);
+        if (wave == 1)
+            __builtin_amdgcn_global_load_lds(kexp + chunk * 64 + 4 * (lane & 15),
+                                             (__attribute__((address_space(3))) void*)(dst + kStageExpOff),
                                              4, 0, 0);
     };
     // Swizzled byte offset of (row r, 16-byte segment j) inside a stage.
@@ -828,14 +887,13 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     // Pipeline.  The i-th chunk is copied three chunks ahead into the slot
     // of chunk i-3 (free once every wave has read that chunk into registers)
     // and waited for at the barrier in the middle of iteration i-1, so a copy
-    // has about two chunk-times to arrive.  Within a chunk
-    // the work runs at half-chunk (32-key) granularity: while the matrix cores
-    // multiply one half, the VALU runs the epilogue of the previous one.
-    // Issue is in order within a wave and the waves of a SIMD run in step
-    // (one barrier per chunk), so the overlap has to come from within each
-    // wave: each region below is branch-free and places a few independent
-    // epilogue instructions after every MFMA.
-    struct HalfAcc { v4f s[2][HB]; v4f l[2]; };
+    // has about two chunk-times to arrive.  Within a chunk the work runs at
+    // half-chunk (32-key) granularity: while the matrix cores multiply one
+    // half, the head sums of the previous one are formed.  Issue is in order
+    // within a wave and the waves of a SIMD run in step (one barrier per
+    // chunk), so the overlap has to come from within each wave: each region
+    // below is branch-free and interleaves its instructions step by step.
+    struct HalfAcc { v4f s[2][HB]; };
     struct HalfB { v8i b[2]; };
     auto load_b = [&](int i, int half, HalfB& B_) {
         const unsigned char* cur = smem_raw + (i % kStages) * kStageBytes;
@@ -847,66 +905,115 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             B_.b[q] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
     };
-    auto mma_half = [&](const HalfB& B_, HalfAcc& A_) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb)
-                A_.s[q][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq.a[hb], B_.b[q],
-                                                                               v4f{0.f, 0.f, 0.f, 0.f},
-                                                                               0, 0, 0, 0, 0, 0);
-            A_.l[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Alin, B_.b[q], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                         0, 0, 0, 0, 0, 0);
-        }
-    };
-    auto epi_half = [&](const HalfAcc& A_, float& p0, float& p1) {
-        float pp[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            float x = fmaf(lin0, A_.l[q][0], lin1 * A_.l[q][1]);
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x = fmaf(c[hb][i], fabsf(A_.s[q][hb][i]), x);
-            pp[q] = x;
-        }
-        p0 = pp[0];
-        p1 = pp[1];
-    };
-    // Scheduling pattern of one region: one MFMA followed by a few VALU
-    // instructions, for every MFMA of the half.
-    auto region_pattern = [](auto lead_ds, auto nvalu) {
-        (void)lead_ds; (void)nvalu;
-        if constexpr (decltype(lead_ds)::value) {  // operand reads first: their latency hides under the MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < (HB + 1) * 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
-        }
-    };
-    // Scale of key (i-th chunk)*64 + lane; read while the chunk's slot is
-    // still owned (before the barrier that lets chunk i+3 overwrite it).
+    // Adjusted scale of key (i-th chunk)*64 + lane, and the E8M0 bytes of
+    // the lane's four subtile keys; read while the chunk's slot is still
+    // owned (before the barrier that lets chunk i+3 overwrite it).
     auto load_ks = [&](int i) {
-        return *reinterpret_cast<const float*>(smem_raw + (i % kStages) * kStageBytes + kStageKeyBytes + 4 * lane);
+        return *reinterpret_cast<const float*>(smem_raw + (i % kStages) * kStageBytes + kStageScaleOff + 4 * lane);
     };
-    // Appends the i-th chunk's scores above the floor, in lane order.  Branch
-    // free: lanes that do not append write a slot of their own past CAP.
-    auto finish = [&](int chunk, const float (&part)[4], float ks, float& score) {
-        score = reduce_scatter4(part) * ks;
-        const int s = chunk * 64 + lane;
-        const bool valid = active && s <= t;
-        const uint32_t key = score_key(score);
-        const bool app = valid && key > thr;
-        const uint64_t m = wave_ballot(app);
-        int below = lanes_below(m);
-        asm volatile("" : "+v"(below));  // computed by every lane: keeps the select branch-free
-        const int o = app ? nb + below : CAP + lane;
-        rb.key[o] = key;
-        rb.pos[o] = (Pos)s;
-        nb += __builtin_popcountll(m);
+    auto load_sb = [&](int i) {
+        return *reinterpret_cast<const int*>(smem_raw + (i % kStages) * kStageBytes + kStageExpOff + 4 * n);
+    };
+    // Score MFMA of subtile 2*MH + q (q in {0, 1}) and head block hb.
+    auto score_mma = [&](auto mh, int q, int hb, const HalfB& B_, int sb) -> v4f {
+        constexpr int s0 = 2 * decltype(mh)::value;
+        if (q == 0)
+            return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq.a[hb], B_.b[0], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                      0, 0, 0, sa, s0, sb);
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq.a[hb], B_.b[1], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                  0, 0, 0, sa, s0 + 1, sb);
+    };
+    // Conversion j2 (of 4) of the B operand of head MFMA x for subtile q of
+    // half A_: the pair of heads (hb = 2x + j2/2, i = 2(j2%2), +1) as f16,
+    // clamped to [0, 1].
+    auto cvt_pair = [&](const HalfAcc& A_, int q, int x, int j2) -> v2h {
+        const int hb = 2 * x + (j2 >> 1);
+        if (hb >= HB) return v2h{0, 0};
+        const v2f f = v2f{A_.s[q][hb][2 * (j2 & 1)], A_.s[q][hb][2 * (j2 & 1) + 1]};
+        const v2h r = __builtin_convertvector(f, v2h);
+        return __builtin_elementwise_min(__builtin_elementwise_max(r, v2h{0, 0}), v2h{1, 1});
+    };
+    // One region: the 2*HB score MFMAs of half MH (operands B_, results mm)
+    // and the head sums of half EH of the previous results ep (added to P),
+    // interleaved step by step.  Step k issues score MFMA k, then its share
+    // of the head-sum work (items: four conversions, then the head MFMA they
+    // feed), then extra(k).  The scheduling barrier after each step keeps
+    // the VALU and MFMA order as written; LDS, SALU and memory instructions
+    // may still move across.
+    auto region = [&](auto mh, auto eh, const HalfB& B_, int sb, HalfAcc& mm, const HalfAcc& ep, v4f& P,
+                      auto&& extra) {
+        constexpr int NM = 2 * HB;
+        constexpr int NI = 2 * NX * 5;
+        constexpr int st0 = 2 * decltype(eh)::value;
+        v8h X = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            mm.s[k / HB][k % HB] = score_mma(mh, k / HB, k % HB, B_, sb);
+#pragma unroll
+            for (int e = (k * NI) / NM; e < ((k + 1) * NI) / NM; ++e) {
+                const int qx = e / 5, it = e % 5;
+                const int qq = qx / NX, x = qx % NX;
+                if (it < 4) {
+                    const v2h r = cvt_pair(ep, qq, x, it);
+                    X[2 * it] = r[0];
+                    X[2 * it + 1] = r[1];
+                } else {
+                    P = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wh[st0 + qq][x], X, P, 0, 0, 0);
+                }
+            }
+            extra(k);
+            __builtin_amdgcn_sched_barrier(0x0094);  // SALU, VMEM and LDS may cross
+        }
+    };
+    // Head sums of half EH of A_ added to P, not interleaved (after the last chunk).
+    auto epi_half = [&](auto eh, const HalfAcc& A_, v4f P) {
+        constexpr int st0 = 2 * decltype(eh)::value;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int x = 0; x < NX; ++x) {
+                v8h X;
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const v2h r = cvt_pair(A_, q, x, it);
+                    X[2 * it] = r[0];
+                    X[2 * it + 1] = r[1];
+                }
+                P = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wh[st0 + q][x], X, P, 0, 0, 0);
+            }
+        return P;
+    };
+    // Keeps a half's MFMAs in the region that issues them (they would
+    // otherwise sink to the region that reads their results).
+    auto pin_half = [&](HalfAcc& A_) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) asm volatile("" : "+v"(A_.s[q][hb]));
+    };
+    // Appending the scores of the chunk whose head sums are complete, above
+    // the floor and in lane order, in five pieces spread over the steps of a
+    // region.  Branch free: lanes that do not append write a slot of their
+    // own past CAP.
+    struct FinState { float score; uint32_t key; int s; bool app; uint64_t m; int below; };
+    auto finish_piece = [&](int piece, FinState& f, int chunk, const v4f& P, float ks) {
+        if (piece == 0) f.score = P[0] * (ks * Fscale);
+        if (piece == 1) f.key = score_key(f.score);
+        if (piece == 2) {
+            f.s = chunk * 64 + lane;
+            f.app = active && f.s <= t && f.key > thr;
+        }
+        if (piece == 3) {
+            f.m = wave_ballot(f.app);
+            f.below = lanes_below(f.m);
+            asm volatile("" : "+v"(f.below));  // computed by every lane: keeps the select branch-free
+        }
+        if (piece == 4) {
+            const int o = f.app ? nb + f.below : CAP + lane;
+            rb.key[o] = f.key;
+            rb.pos[o] = (Pos)f.s;
+            nb += __builtin_popcountll(f.m);
+        }
     };
     // The rest of an append step: the optional score-matrix row and the
     // compaction request when the buffer nears capacity.
@@ -922,38 +1029,39 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     for (int pass = 0;; ++pass) {
         HalfAcc hA, hB;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            hB.l[q] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) hB.s[q][hb] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
         HalfB bA, bB;
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        v4f Pacc = v4f{0.f, 0.f, 0.f, 0.f};  // head sums of the chunk in progress
         float ks_prev = 0.f;
         int chunk_prev = 0;  // chunk id of the previous iteration
         if (threadIdx.x < 3) flags[threadIdx.x] = 0u;
         stage_chunk(0);
         stage_chunk(1);
         stage_chunk(2);
-        // chunk 0 landed: at most this wave's copies of chunks 1 and 2 in flight
-        if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F74);                // vmcnt(4)
+        // chunk 0 landed: at most this wave's copies of chunks 1 and 2 in
+        // flight (waves 0 and 1 issue two copies per chunk, the others one)
+        if (wave <= 1) __builtin_amdgcn_s_waitcnt(0x0F74);                // vmcnt(4)
         else __builtin_amdgcn_s_waitcnt(0x0F72);                          // vmcnt(2)
         __syncthreads();
         load_b(0, 0, bA);
+        int sb_next = load_sb(0);
         for (int i = 0; i <= last; ++i) {
+            const int sb_cur = sb_next;
             // Region 1: first half of chunk i on the MFMA (operands read during
-            // the previous region 2), epilogue of the second half of chunk
+            // the previous region 2), head sums of the second half of chunk
             // i-1 (zeros before the first chunk); the second half's operands
             // and the chunk's key scales are read here, before the barrier
             // that releases the chunk's stage slot.
             __builtin_amdgcn_sched_barrier(0);
-            mma_half(bA, hA);
-            epi_half(hB, part[2], part[3]);
             load_b(i, 1, bB);
             const float ks_cur = load_ks(i);
+            region(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, bA, sb_cur, hA, hB, Pacc,
+                   [](int) {});
             // keep this epilogue here (it would otherwise sink into a branch below)
-            asm volatile("" : "+v"(part[2]), "+v"(part[3]));
-            region_pattern(std::true_type{}, std::integral_constant<int, 4>{});
+            asm volatile("" : "+v"(Pacc));
+            pin_half(hA);
             __builtin_amdgcn_sched_barrier(0);
             // This wave's copies of chunk i+1 have landed once at most its
             // copies of chunk i+2 are in flight (loads complete in issue
@@ -962,7 +1070,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             // the score matrix requested, the row's stores share the counter:
             // wait for all.
             if (a.scores) __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
-            else if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F72);       // vmcnt(2)
+            else if (wave <= 1) __builtin_amdgcn_s_waitcnt(0x0F72);       // vmcnt(2)
             else __builtin_amdgcn_s_waitcnt(0x0F71);                      // vmcnt(1)
             __syncthreads();
             // Compaction request of the appends of the (i-2)-th chunk (made
@@ -986,36 +1094,42 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             // Cooperative compaction: a request from any wave makes every
             // wave compact now, so the block pays one stall per event.
             if (want_compact && active && nb > K) nb = wave_compact(rb, nb, (uint32_t)K, &thr, CAP);
-            // Region 2: second half of chunk i on the MFMA, epilogue of its
+            // Region 2: second half of chunk i on the MFMA, head sums of its
             // first half, the appends of chunk i-1 (discarded before the first
             // chunk: nothing is valid yet) and the first-half operands of
             // chunk i+1 (landed, per the barrier above).
-            const float fin_part[4] = {part[0], part[1], part[2], part[3]};
+            const v4f Pfin = Pacc;
             const int chunk_cur = chunk_at(i);
             const bool fin_on = i >= 1;
             const bool was_active = active;
             active = active && fin_on;
-            float fin_score;
+            FinState fs;
             const int nb0 = nb;
             __builtin_amdgcn_sched_barrier(0);
-            mma_half(bB, hB);
-            epi_half(hA, part[0], part[1]);
-            finish(chunk_prev, fin_part, ks_prev, fin_score);
             load_b(i + 1, 0, bA);
-            asm volatile("" : "+v"(part[0]), "+v"(part[1]), "+v"(fin_score));
-            region_pattern(std::true_type{}, std::integral_constant<int, 6>{});
+            sb_next = load_sb(i + 1);
+            Pacc = v4f{0.f, 0.f, 0.f, 0.f};
+            region(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, bB, sb_cur, hB, hA, Pacc,
+                   [&](int k) {
+#pragma unroll
+                       for (int p = 0; p < 5; ++p)
+                           if ((p < 2 * HB - 1 ? p : 2 * HB - 1) == k) finish_piece(p, fs, chunk_prev, Pfin, ks_prev);
+                   });
+            asm volatile("" : "+v"(Pacc), "+v"(fs.score));
+            pin_half(hB);
             __builtin_amdgcn_sched_barrier(0);
             active = was_active;
             if (!fin_on) nb = nb0;
-            if (fin_on) finish_tail(i - 1, chunk_prev, fin_score);
+            if (fin_on) finish_tail(i - 1, chunk_prev, fs.score);
             ks_prev = ks_cur;
             chunk_prev = chunk_cur;
         }
-        epi_half(hB, part[2], part[3]);
+        Pacc = epi_half(std::integral_constant<int, 1>{}, hB, Pacc);
         {
-            float fin_score;
-            finish(chunk_prev, part, ks_prev, fin_score);
-            finish_tail(last, chunk_prev, fin_score);
+            FinState fs;
+#pragma unroll
+            for (int p = 0; p < 5; ++p) finish_piece(p, fs, chunk_prev, Pacc, ks_prev);
+            finish_tail(last, chunk_prev, fs.score);
         }
         __builtin_amdgcn_s_waitcnt(0x0000);  // no stage copy or LDS read may still be in flight
         if (pass == 1) break;
@@ -1041,8 +1155,21 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     wave_emit(rb, nb, K, a.idx_out + row_t * K, a.val_out ? a.val_out + row_t * K : nullptr);
 }
 
+constexpr bool staged_path(int dtype, int L) { return DSAIDX_PREFILL_STAGED && dtype == 2 && L <= 65536; }
+constexpr int pad64(int L) { return (L + 63) / 64 * 64; }
+
 template <int HB>
-hipError_t launch_fp8_staged(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_fp8_staged(const PrefillArgs& a_in, hipStream_t stream) {
+    PrefillArgs a = a_in;
+    a.Lpad = pad64(a.L);
+    a.ks_adj = reinterpret_cast<float*>(a.workspace);
+    a.kexp = reinterpret_cast<uint8_t*>(a.ks_adj + (size_t)a.B * a.Lpad);
+    {
+        const int64_t n = (int64_t)a.B * a.Lpad;
+        hipLaunchKernelGGL(prefill_key_exp_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const size_t smem = kStages * kStageBytes + (size_t)kStagedWaves * kStagedWaveBytes;
     static bool attr = false;
     if (!attr) {
@@ -1059,11 +1186,17 @@ hipError_t launch_fp8_staged(const PrefillArgs& a, hipStream_t stream) {
 
 template <int DT, int HB>
 hipError_t launch_pos(const PrefillArgs& a, hipStream_t stream) {
-    if (DSAIDX_PREFILL_STAGED && DT == 2 && a.L <= 65536) return launch_fp8_staged<HB>(a, stream);
+    if (staged_path(DT, a.L)) return launch_fp8_staged<HB>(a, stream);
     return a.L <= 65536 ? launch_one<DT, HB, true>(a, stream) : launch_one<DT, HB, false>(a, stream);
 }
 
 }  // namespace
+
+size_t prefill_fused_workspace_bytes(int B, int L, int dtype) {
+    if (!staged_path(dtype, L)) return 0;
+    const size_t n = (size_t)B * pad64(L);
+    return (n * 5 + 255) / 256 * 256;  // fp32 adjusted scales, then the E8M0 bytes
+}
 
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream) {
     const int hb = a.H / 16;
