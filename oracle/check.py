@@ -13,6 +13,15 @@ Top-k sets (one row, n_valid valid positions, m = min(k, n_valid)):
   (iv)  each returned score matches the oracle's score of that position
         under the score rule.
 When n_valid <= k the set must be all valid positions.
+
+Signed head weights: every rule above takes, where given, the magnitude sum
+M = sum_h |w_h * q_scale_h| * ReLU(q_h . k / sqrt(D)) of each score into its
+tolerance, max(1e-4, 1e-3 |o|, 1e-3 M), and a swap at the cut is allowed
+when the two scores lie within their summed tolerances of tau.  M is the
+score itself when the weights are non-negative (then nothing changes); with
+mixed signs a score can cancel far below M, and the rounding of the head
+terms of any floating-point evaluation is bounded relative to M, not to the
+cancelled result.
 """
 from __future__ import annotations
 
@@ -22,11 +31,14 @@ ABS_TOL = 1e-4
 REL_TOL = 1e-3
 
 
-def score_tol(o):
-    return np.maximum(ABS_TOL, REL_TOL * np.abs(o))
+def score_tol(o, mag=None):
+    t = np.maximum(ABS_TOL, REL_TOL * np.abs(o))
+    if mag is not None:
+        t = np.maximum(t, REL_TOL * np.abs(np.asarray(mag, np.float64)))
+    return t
 
 
-def check_scores(g: np.ndarray, o: np.ndarray, what: str = "scores") -> None:
+def check_scores(g: np.ndarray, o: np.ndarray, what: str = "scores", mag=None) -> None:
     g = np.asarray(g, np.float64)
     o = np.asarray(o, np.float64)
     mask_o = np.isneginf(o)
@@ -36,15 +48,16 @@ def check_scores(g: np.ndarray, o: np.ndarray, what: str = "scores") -> None:
         raise AssertionError(f"{what}: -inf mismatch at {tuple(i)}: gpu={g[tuple(i)]} oracle={o[tuple(i)]}")
     fin = ~mask_o
     err = np.abs(g[fin] - o[fin])
-    tol = score_tol(o[fin])
+    tol = score_tol(o[fin], None if mag is None else np.asarray(mag, np.float64)[fin])
     if np.any(~(err <= tol)):
         j = np.argmax(err / tol)
         raise AssertionError(f"{what}: {np.sum(~(err <= tol))} of {err.size} outside tolerance; worst gpu="
                              f"{g[fin][j]!r} oracle={o[fin][j]!r} err={err[j]:.3g} tol={tol[j]:.3g}")
 
 
-def check_topk_row(g_idx, g_val, o_row, n_valid: int, K: int, where: str = "") -> dict:
-    """o_row: oracle fp64 scores of positions [0, n_valid).  Returns stats."""
+def check_topk_row(g_idx, g_val, o_row, n_valid: int, K: int, where: str = "", mag_row=None) -> dict:
+    """o_row: oracle fp64 scores of positions [0, n_valid); mag_row: their
+    magnitude sums (signed weights) or None.  Returns stats."""
     g_idx = np.asarray(g_idx, np.int64)
     m = min(K, n_valid)
     head, tail = g_idx[:m], g_idx[m:]
@@ -58,26 +71,32 @@ def check_topk_row(g_idx, g_val, o_row, n_valid: int, K: int, where: str = "") -
         g_val = np.asarray(g_val, np.float64)
         if np.any(~np.isneginf(g_val[m:])):
             raise AssertionError(f"{where}: padding scores must be -inf")
-        check_scores(g_val[:m], o_row[head], what=f"{where} selected scores")
+        check_scores(g_val[:m], o_row[head], what=f"{where} selected scores",
+                     mag=None if mag_row is None else mag_row[head])
     if n_valid <= K:
         return dict(swaps=0)
     s = np.arange(n_valid)
     order = np.lexsort((s, -o_row[:n_valid]))
     O = order[:m]
     tau = o_row[O[-1]]
-    tol = max(ABS_TOL, REL_TOL * abs(tau))
     diff = np.setxor1d(head, O)
-    far = diff[np.abs(o_row[diff] - tau) > tol]
+    if mag_row is None:
+        tol = max(ABS_TOL, REL_TOL * abs(tau))
+        far = diff[np.abs(o_row[diff] - tau) > tol]
+    else:
+        mr = np.asarray(mag_row, np.float64)
+        tol = score_tol(o_row[diff], mr[diff]) + float(score_tol(tau, mr[O[-1]]))
+        far = diff[np.abs(o_row[diff] - tau) > tol]
     if far.size:
         raise AssertionError(f"{where}: {far.size} positions differ from the oracle's set beyond the tie "
                              f"tolerance; e.g. s={far[0]} score={o_row[far[0]]!r} tau={tau!r}")
     return dict(swaps=int(diff.size // 2))
 
 
-def check_topk_rows(g_idx, g_val, o_scores, n_valid, K, where="") -> int:
+def check_topk_rows(g_idx, g_val, o_scores, n_valid, K, where="", mag=None) -> int:
     swaps = 0
     for r in range(g_idx.shape[0]):
         st = check_topk_row(g_idx[r], None if g_val is None else g_val[r], o_scores[r], int(n_valid[r]), K,
-                            where=f"{where} row {r}")
+                            where=f"{where} row {r}", mag_row=None if mag is None else mag[r])
         swaps += st["swaps"]
     return swaps

@@ -74,7 +74,8 @@ def test_prefill_rejects_before_launch(lib, kw, status):
 
 
 def test_prefill_workspace_query(lib):
-    assert lib.indexer_prefill_workspace_bytes(1, 8192, 64, 128, 2048, 2, 0) == 8192 * 5   # fused fp8: key pre-pass
+    # fused fp8: per-key adjusted scale and operand-scale byte (4 + 1 bytes per key)
+    assert lib.indexer_prefill_workspace_bytes(1, 8192, 64, 128, 2048, 2, 0) == 8192 * 5
     assert lib.indexer_prefill_workspace_bytes(2, 256, 4, 32, 16, 0, 0) == 2 * 256 * 256 * 4
     assert lib.indexer_prefill_workspace_bytes(2, 256, 4, 32, 16, 0, 1) == 0
 

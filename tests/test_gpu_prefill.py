@@ -31,11 +31,15 @@ def parity(inp, K, want_scores=False, rows=None, name=""):
     gi, gv, gs = run_prefill(inp, K, want_scores)
     rows = np.arange(L) if rows is None else np.asarray(rows)
     oi, ov, osc = indexer.prefill(inp, K, rows=rows, want_scores=True)
+    mag = None
+    if np.any(np.asarray(inp["w"]) < 0):  # signed weights: tolerances scale with the magnitude sums
+        _, _, mag = indexer.prefill(dict(inp, w=np.abs(inp["w"])), K, rows=rows, want_scores=True)
     swaps = 0
     for b in range(B):
+        mb = None if mag is None else mag[b]
         if want_scores:
-            check_scores(gs[b][rows], osc[b], what=f"{name} scores b={b}")
-        swaps += check_topk_rows(gi[b][rows], gv[b][rows], osc[b], rows + 1, K, where=f"{name} b={b}")
+            check_scores(gs[b][rows], osc[b], what=f"{name} scores b={b}", mag=mb)
+        swaps += check_topk_rows(gi[b][rows], gv[b][rows], osc[b], rows + 1, K, where=f"{name} b={b}", mag=mb)
     say(f"  ok, near-tie swaps={swaps}")
     return gi, gv
 
@@ -177,3 +181,46 @@ def test_fused_long_sequences_sampled(L):
     gi, gv, _ = run_prefill(inp, 2048)
     _, _, osc = indexer.prefill(inp, 2048, rows=rows, want_scores=True)
     check_topk_rows(gi[0][rows], gv[0][rows], osc[0], rows + 1, 2048, where=f"long L={L}")
+
+
+def _e4m3(x):
+    """float32 array -> E4M3FN codes (saturating RNE), no scaling."""
+    t = torch.clamp(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)), -448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("signed", [False, True])
+def test_fused_fp8_codes_far_from_full_range(signed):
+    """fp8 codes that use little of the E4M3 range (magnitudes spread over
+    2^-7 .. 1 per query head and 2^-11 .. 1 per key, arbitrary positive
+    scales) and some all-zero keys: every per-token and per-key operand
+    scale the fused kernel derives is exercised, and the scores and
+    selections match the oracle -- with non-negative head weights under the
+    plain tolerance, with signed ones under the magnitude-sum tolerance."""
+    rng = np.random.default_rng(580)
+    L, H, D, K = 700, 64, 128, 64
+    qv = rng.standard_normal((1, L, H, D)).astype(np.float32) * np.exp2(-rng.integers(0, 8, size=(1, L, H, 1)))
+    kv = rng.standard_normal((1, L, D)).astype(np.float32) * np.exp2(-rng.integers(0, 12, size=(1, L, 1)))
+    kv[:, ::53] = 0.0
+    inp = dict(kind="prefill", B=1, L=L, H=H, D=D, dtype="fp8",
+               q=_e4m3(qv), k=_e4m3(kv),
+               q_scale=rng.uniform(0.5, 2.0, size=(1, L, H)).astype(np.float32),
+               k_scale=rng.uniform(0.5, 2.0, size=(1, L)).astype(np.float32),
+               w=rng.standard_normal((1, L, H)).astype(np.float32))
+    if not signed:
+        inp["w"] = np.abs(inp["w"])
+    parity(inp, K, want_scores=True, name=f"fp8 small codes signed={signed}")
+
+
+def test_fused_fp8_mixed_sign_blocks():
+    """Signed head weights in every third 8-token block, softmax weights in
+    the others: scores and selections match the oracle, the signed rows
+    under the magnitude-sum tolerance."""
+    inp = synth.prefill_inputs(1, 900, 64, 128, "fp8", seed=581)
+    rng = np.random.default_rng(581)
+    w = inp["w"].copy()
+    for blk in range(0, 900 // 8, 3):  # every third block gets signed weights
+        t0 = 8 * blk
+        w[0, t0:t0 + 8] = rng.standard_normal((min(8, 900 - t0), 64)).astype(np.float32)
+    inp["w"] = w
+    parity(inp, 128, want_scores=True, name="fp8 mixed-sign blocks")
