@@ -178,12 +178,12 @@ size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, i
     (void)H; (void)D; (void)topk;
     if (B < 1 || max_context_len < 0) return 0;
     // candidate scores and positions: [B][stride] each; per-query counters
-    // [B][kCtrlStride]; sampled keys [B][decode_sample_words]; page and
-    // sampled-page prefixes [B+1] each.
+    // [B][kCtrlStride]; sampled keys [B][decode_sample_words]; page prefix
+    // over queries [B+1].
     return (size_t)B * decode_score_stride(max_context_len) * 8u +
            (size_t)B * dsaidx::kCtrlStride * sizeof(uint32_t) +
            (size_t)B * decode_sample_words(max_context_len) * sizeof(uint32_t) +
-           (size_t)(B + 1) * 2 * sizeof(int32_t);
+           (size_t)(B + 1) * sizeof(int32_t);
 }
 
 dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
@@ -230,7 +230,6 @@ dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(wp + (size_t)B * stride * 8);  // [B][kCtrlStride]
     uint32_t* sample_key = ctrl + (size_t)B * dsaidx::kCtrlStride;
     int32_t* prefix = reinterpret_cast<int32_t*>(sample_key + (size_t)B * decode_sample_words(max_context_len));
-    int32_t* sprefix = prefix + (B + 1);
     hipError_t e;
     if (max_context_len > 0) {
         dsaidx::DecodeArgs d{};
@@ -247,8 +246,8 @@ dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
         d.inv_sqrt_d = 1.0f / sqrtf((float)D);
         d.ctrl = ctrl;
         d.sample_key = sample_key;
+        d.sample_stride = (int64_t)decode_sample_words(max_context_len);
         d.prefix = prefix;
-        d.sprefix = sprefix;
         d.cand_score = cand_score;
         d.cand_pos = cand_pos;
         d.cand_stride = (int64_t)stride;

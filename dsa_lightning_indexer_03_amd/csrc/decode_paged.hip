@@ -27,15 +27,15 @@
 // per 132 B read, interleaved with the cache reads, costs about a fifth of
 // the scan.  So the scan writes only candidates:
 //
-// 1. A sample pass scores a strided sample of every long query's pages (one
-//    page in kSampleStride, from a per-query offset) and stores the sampled
-//    score keys.
-// 2. A floor kernel takes, per query, the r-th largest sampled key to 22
-//    bits (two radix digits), with r five standard deviations above the
-//    expected number of sampled scores at or above the query's k-th largest.
-// 3. The main pass scores every position and writes only the scores whose
+// 1. A sample kernel scores a strided sample of every long query's pages
+//    (one page in kSampleStride, from a per-query offset) and stores the
+//    score keys; a floor kernel, one workgroup per query, takes the r-th
+//    largest sampled key to 22 bits (two radix digits) as the query's floor,
+//    with r five standard deviations above the expected number of sampled
+//    scores at or above the query's k-th largest.
+// 2. The main scan scores every position and writes only the scores whose
 //    key reaches the query's floor, to the query's candidate list.
-// 4. Verification: if at least min(k, context) scores reached the floor,
+// 3. Verification: if at least min(k, context) scores reached the floor,
 //    the k-th largest score is among them (and so is every score tied with
 //    it, since the floor is a key threshold), so the selection over the
 //    candidates is exact.  Otherwise a repair pass rescores the query in
@@ -101,243 +101,92 @@ __device__ __forceinline__ int sampled_pages(int ctx, int topk) {
     return (np - kSampleStride) / kSampleStride + 1;
 }
 
-// Prologue: per-query page counts and sampled-page counts -> exclusive
-// prefixes over queries (workgroup 0), and clears the per-query counters
-// (all workgroups, 16-byte stores).
+
+// Per-query operands of the scan, lane (n, g): A[hb][j] = the 8 bf16 query
+// values of head 16hb + n, dims [32g + 8j, +8); c[hb][i] = w / sqrt(D) of
+// head 16hb + 4g + i (the lane's accumulator rows).
+template <int HB>
+__device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int n, int g, v8bf (&A)[HB][4],
+                                           float (&c)[HB][4]) {
+    constexpr int H = HB * 16;
+    const uint16_t* qb = a.q + (size_t)b * H * kD;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            A[hb][j] = *reinterpret_cast<const v8bf*>(qb + (16 * hb + n) * kD + 32 * g + 8 * j);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[hb][i] = a.w[(size_t)b * H + 16 * hb + 4 * g + i] * a.inv_sqrt_d;
+}
+
+// Keys of one page into registers: dst[st][0..1] = the lane's 32 bytes of
+// row 16*st + n; ksc = the scale of the lane's key (row lane).
+__device__ __forceinline__ void load_page(const DecodeArgs& a, int page, uint32_t lane_off, int lane,
+                                          v4i (&dst)[4][2], float& ksc) {
+    const uint8_t* pbase = a.k_cache + (size_t)page * kPage * kD;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const uint8_t* rp = pbase + lane_off + st * 16 * kD;
+        dst[st][0] = stream_load(reinterpret_cast<const v4i*>(rp));
+        dst[st][1] = stream_load(reinterpret_cast<const v4i*>(rp + 16));
+    }
+    ksc = stream_load(a.k_scale + (size_t)page * kPage + lane);
+}
+
+// Scores of one page: lane l gets the score of the page's key l.
+template <int HB>
+__device__ __forceinline__ float page_scores(const v8bf (&A)[HB][4], const float (&c)[HB][4],
+                                             const v4i (&cur)[4][2], float ks) {
+    float part[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        v4f acc[HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const v4i& h = cur[st][j >> 1];
+            const v8bf B = widen8(h[(j & 1) * 2], h[(j & 1) * 2 + 1]);
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+                acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[hb][j], B, acc[hb], 0, 0, 0);
+        }
+        float pp = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) pp = fmaf(c[hb][ii], relu(acc[hb][ii]), pp);
+        part[st] = pp;
+    }
+    return reduce_scatter4(part) * ks;
+}
+
+// Prologue (only for batches too large for the scan's LDS prefix): per-query
+// page counts -> exclusive prefix over queries, one workgroup.
 __global__ void __launch_bounds__(1024)
 decode_prologue_kernel(DecodeArgs a) {
-    __shared__ uint32_t wtot[2][16];
-    __shared__ uint32_t carry[2];
+    __shared__ uint32_t wtot[16];
+    __shared__ uint32_t carry;
     const int t = threadIdx.x;
-    const size_t nz4 = (size_t)a.B * kCtrlStride / 4;
-    v4i* z = reinterpret_cast<v4i*>(a.ctrl);
-    for (size_t i = (size_t)blockIdx.x * 1024 + t; i < nz4; i += (size_t)gridDim.x * 1024) z[i] = v4i{0, 0, 0, 0};
-    if (blockIdx.x != 0) return;
-    if (t < 2) carry[t] = 0;
+    if (t == 0) carry = 0;
     __syncthreads();
     for (int b0 = 0; b0 < a.B; b0 += 1024) {
         const int b = b0 + t;
-        uint32_t np = 0, ns = 0;
-        if (b < a.B) {
-            const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
-            np = (uint32_t)((ctx + kPage - 1) / kPage);
-            ns = (uint32_t)sampled_pages(ctx, a.topk);
-        }
-        const uint32_t ip = wave_incl_scan(np), is = wave_incl_scan(ns);
-        if (lane_id() == kWave - 1) { wtot[0][t / kWave] = ip; wtot[1][t / kWave] = is; }
+        uint32_t np = 0;
+        if (b < a.B) np = (uint32_t)((clamp_ctx(a.context_lens[b], a.max_ctx) + kPage - 1) / kPage);
+        const uint32_t ip = wave_incl_scan(np);
+        if (lane_id() == kWave - 1) wtot[t / kWave] = ip;
         __syncthreads();
-        uint32_t rp = carry[0] + ip - np, rs = carry[1] + is - ns;
-        for (int w = 0; w < t / kWave; ++w) { rp += wtot[0][w]; rs += wtot[1][w]; }
-        if (b < a.B) { a.prefix[b] = (int32_t)rp; a.sprefix[b] = (int32_t)rs; }
+        uint32_t rp = carry + ip - np;
+        for (int w = 0; w < t / kWave; ++w) rp += wtot[w];
+        if (b < a.B) a.prefix[b] = (int32_t)rp;
         __syncthreads();
-        if (t == 1023) { carry[0] = rp + np; carry[1] = rs + ns; }
+        if (t == 1023) carry = rp + np;
         __syncthreads();
     }
-    if (t == 0) { a.prefix[a.B] = (int32_t)carry[0]; a.sprefix[a.B] = (int32_t)carry[1]; }
-}
-
-// The scan.  A persistent grid (one resident round of workgroups): the
-// global list of (query, page) pairs -- every page of every query in the
-// main pass, the sampled pages in the sample pass -- query-major, is cut into
-// equal contiguous shares, one per workgroup, so ragged context lengths
-// leave no tail of idle CUs.  Inside a share the 4 waves take interleaved
-// pages (wave w: pages w, w+4, ...).  Each wave keeps two pages of loads in
-// flight while it multiplies the current one; the (query, position, page id)
-// of its next 64 pages sit one per lane, so no load waits on a block-table
-// read.  Query operands are reloaded only when a wave's pages cross into the
-// next query.  Sample pass: every score key is stored, at the page's slot
-// in the sample list.  Main pass: scores whose key reaches the query's floor
-// go to the wave's LDS candidate buffer, flushed to the query's candidate
-// list.
-template <int HB>
-__global__ void __launch_bounds__(kThreadsDec)
-decode_scan_kernel(DecodeArgs a) {
-    __shared__ uint32_t lds_wave[kThreadsDec / kWave][2 * kCandBuf];  // candidate buffer
-    __shared__ int32_t prefix_lds[kPrefixLds];
-    constexpr int NW = kThreadsDec / kWave;
-    const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
-    const int n = lane & 15, g = lane >> 4;
-    constexpr int H = HB * 16;
-    const bool sample = a.sample != 0;
-    float* cbuf_s = reinterpret_cast<float*>(lds_wave[wave]);
-    int32_t* cbuf_p = reinterpret_cast<int32_t*>(lds_wave[wave] + kCandBuf);
-
-    // The page prefix over queries goes to LDS when it fits: the searches
-    // below then cost LDS round trips instead of dependent global loads.
-    const int32_t* prefix = sample ? a.sprefix : a.prefix;
-    const bool pre_in_lds = a.B + 1 <= kPrefixLds;
-    if (pre_in_lds)
-        for (int i = threadIdx.x; i <= a.B; i += kThreadsDec) prefix_lds[i] = prefix[i];
-    __syncthreads();
-    auto prefix_at = [&](int i) -> int { return pre_in_lds ? prefix_lds[i] : prefix[i]; };
-    const int P = prefix_at(a.B);
-    const int64_t G = gridDim.x;
-    const int share_begin = (int)((int64_t)blockIdx.x * P / G);
-    const int share_end = (int)((int64_t)(blockIdx.x + 1) * P / G);
-    // this wave's pages: share_begin + wave + NW*k for k < nk
-    const int nk = share_end - share_begin - wave > 0 ? (share_end - share_begin - wave + NW - 1) / NW : 0;
-    if (nk == 0) return;
-
-    // Query of the share's first page (the last b with prefix[b] <= page).
-    int lo = 0, hi = a.B;
-    {
-        const int p0 = share_begin + wave;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (prefix_at(mid) <= p0) lo = mid; else hi = mid;
-        }
-    }
-    // Per-lane description of pages k0 .. k0+63 of this wave.
-    int walk_b = lo;  // query of page k0 (wave-uniform)
-    auto describe = [&](int k0, int& qb, int& pos0, int& pid) {
-        const int k = k0 + lane;
-        const int gp = share_begin + wave + NW * k;
-        qb = -1; pos0 = 0; pid = 0;
-        if (k < nk) {
-            int bb = walk_b;
-            while (prefix_at(bb + 1) <= gp) ++bb;
-            int j = gp - prefix_at(bb);
-            if (sample) j = sample_offset(bb) + kSampleStride * j;
-            qb = bb;
-            pos0 = j * kPage;
-            pid = a.block_table[(size_t)bb * a.max_pages + j];
-        }
-        const int last = min(63, nk - 1 - k0);
-        if (last >= 0) walk_b = __builtin_amdgcn_readlane(qb, last);
-        // Settle the table loads here (once per 64 pages): left pending, they
-        // would make every later step wait for its own prefetches too.
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    };
-
-    const uint32_t lane_off = (uint32_t)(n * kD + 32 * g);
-    auto load_page = [&](int page, v4i (&dst)[4][2], float& ksc) {
-        const uint8_t* pbase = a.k_cache + (size_t)page * kPage * kD;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const uint8_t* rp = pbase + lane_off + st * 16 * kD;
-            dst[st][0] = stream_load(reinterpret_cast<const v4i*>(rp));
-            dst[st][1] = stream_load(reinterpret_cast<const v4i*>(rp + 16));
-        }
-        ksc = stream_load(a.k_scale + (size_t)page * kPage + lane);
-    };
-
-    v8bf A[HB][4];
-    float c[HB][4];
-    int qcur = -1, ctx_cur = 0;
-    uint32_t floor_key = 0u;  // main pass: candidates have key >= floor_key
-    int nbuf = 0;             // main pass: entries in the wave's candidate buffer
-    uint32_t* cand_n = a.ctrl + 1;  // word 1 of each query's counter block
-    auto flush_cand = [&](int qb) {
-        if (nbuf == 0) return;
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&cand_n[(size_t)qb * kCtrlStride], (uint32_t)nbuf);
-        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-        float* cs = a.cand_score + (size_t)qb * a.cand_stride + base;
-        int32_t* cp = a.cand_pos + (size_t)qb * a.cand_stride + base;
-        for (int j = lane; j < nbuf; j += kWave) {
-            cs[j] = cbuf_s[j];
-            cp[j] = cbuf_p[j];
-        }
-        __builtin_amdgcn_wave_barrier();
-        nbuf = 0;
-    };
-
-    int cq, cpos, cpid;   // lanes: pages k0 .. k0+63
-    int nq, npos, npid;   // lanes: pages k0+64 .. k0+127
-    describe(0, cq, cpos, cpid);
-    describe(64, nq, npos, npid);
-
-    // One pipeline step: prefetch page k+2 into `pre`, multiply page k held
-    // in `cur` (page k+1 is in flight meanwhile).  Called with three buffers
-    // rotating, so no copies.
-    auto step = [&](int k, v4i (&cur)[4][2], float ks_c, v4i (&pre)[4][2], float& ks_p) {
-        const int i = k & 63;
-        const int pb = __builtin_amdgcn_readlane(cq, i);
-        const int ppos = __builtin_amdgcn_readlane(cpos, i);
-        {
-            // Unconditional, so every path issues the same loads and the wait
-            // for `cur` can leave two pages in flight; past the end of the
-            // share the current page is fetched again (unused).
-            const int pid_n = i < 62 ? __builtin_amdgcn_readlane(cpid, i + 2) : __builtin_amdgcn_readlane(npid, i - 62);
-            const int pid = k + 2 < nk ? pid_n : __builtin_amdgcn_readlane(cpid, i);
-            load_page(pid, pre, ks_p);
-        }
-        if (i == 63) {  // roll the page descriptions forward
-            cq = nq; cpos = npos; cpid = npid;
-            describe(k + 65, nq, npos, npid);
-        }
-        if (pb != qcur) {  // entering a new query
-            if (qcur >= 0 && !sample) flush_cand(qcur);
-            qcur = pb;
-            ctx_cur = clamp_ctx(a.context_lens[pb], a.max_ctx);
-            const uint16_t* qb = a.q + (size_t)pb * H * kD;
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    A[hb][j] = *reinterpret_cast<const v8bf*>(qb + (16 * hb + n) * kD + 32 * g + 8 * j);
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii)
-                    c[hb][ii] = a.w[(size_t)pb * H + 16 * hb + 4 * g + ii] * a.inv_sqrt_d;
-            if (!sample) floor_key = a.ctrl[(size_t)pb * kCtrlStride + 2];
-            // Settle the query loads here, on this rare path: otherwise the
-            // common path after it inherits their pending count and waits
-            // for every page load in flight at each step.
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        }
-        float part[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            v4f acc[HB];
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const v4i& h = cur[st][j >> 1];
-                const v8bf B = widen8(h[(j & 1) * 2], h[(j & 1) * 2 + 1]);
-#pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-                    acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[hb][j], B, acc[hb], 0, 0, 0);
-            }
-            float pp = 0.f;
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) pp = fmaf(c[hb][ii], relu(acc[hb][ii]), pp);
-            part[st] = pp;
-        }
-        const float score = reduce_scatter4(part) * ks_c;
-        const int s = ppos + lane;
-        const uint32_t key = score_key(score);
-        if (sample) {
-            a.sample_key[(size_t)(share_begin + wave + NW * k) * kPage + lane] = key;
-        } else {
-            if (nbuf > kCandBuf - kWave) flush_cand(qcur);
-            const bool take = s < ctx_cur && key >= floor_key;
-            const uint64_t m = wave_ballot(take);
-            if (take) {
-                const int o = nbuf + lanes_below(m);
-                cbuf_s[o] = score;
-                cbuf_p[o] = s;
-            }
-            nbuf += __builtin_popcountll(m);
-        }
-    };
-
-    v4i b0[4][2], b1[4][2], b2[4][2];
-    float k0 = 0.f, k1 = 0.f, k2 = 0.f;
-    load_page(__builtin_amdgcn_readlane(cpid, 0), b0, k0);
-    load_page(__builtin_amdgcn_readlane(cpid, nk > 1 ? 1 : 0), b1, k1);
-    for (int k = 0; k < nk; k += 3) {
-        step(k, b0, k0, b2, k2);
-        if (k + 1 < nk) step(k + 1, b1, k1, b0, k0);
-        if (k + 2 < nk) step(k + 2, b2, k2, b1, k1);
-    }
-    if (qcur >= 0 && !sample) flush_cand(qcur);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // the final page prefetches (unused) settle before exit
+    if (t == 0) a.prefix[a.B] = (int32_t)carry;
 }
 
 constexpr int kFloorThreads = 1024;
@@ -386,21 +235,66 @@ __device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint3
     return bin;
 }
 
-// Floor of query b: the r-th largest key of its sample, cut to its top 22
-// bits (first digit by histogram, then the next 11 bits inside that bin).
-// Not sampled, or r beyond the sample: the floor stays 0 and every score of
-// the query is a candidate.  Each thread issues its key loads of a round
-// together, before the histogram updates.
+// Sample pass: workgroup (b, part) of `sample_groups` per query b, 4 waves;
+// wave w of part p scores the sampled pages i = 4p + w + 4 * groups * j of
+// query b (two pages of loads in flight) and stores their score keys.
+template <int HB>
+__global__ void __launch_bounds__(kThreadsDec)
+decode_sample_kernel(DecodeArgs a) {
+    const int groups = a.sample_groups;
+    const int b = blockIdx.x / groups, part = blockIdx.x % groups;
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int n = lane & 15, g = lane >> 4;
+    const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
+    const int ns = sampled_pages(ctx, a.topk);
+    const int first = part * (kThreadsDec / kWave) + wave;
+    const int stride = groups * (kThreadsDec / kWave);
+    if (first >= ns) return;
+    uint32_t* keys = a.sample_key + (size_t)b * a.sample_stride;
+    const int off = sample_offset(b);
+    const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+    const uint32_t lane_off = (uint32_t)(n * kD + 32 * g);
+    v8bf A[HB][4];
+    float c[HB][4];
+    load_query<HB>(a, b, n, g, A, c);
+    v4i p0[4][2], p1[4][2];
+    float k0 = 0.f, k1 = 0.f;
+    load_page(a, bt[off + kSampleStride * first], lane_off, lane, p0, k0);
+    for (int i = first; i < ns; i += 2 * stride) {
+        const int i1 = i + stride;
+        // the next page's loads (again the current one past the end) go out
+        // before this page is scored
+        load_page(a, bt[off + kSampleStride * (i1 < ns ? i1 : i)], lane_off, lane, p1, k1);
+        keys[(size_t)i * kPage + lane] = score_key(page_scores<HB>(A, c, p0, k0));
+        if (i1 >= ns) break;
+        const int i2 = i1 + stride;
+        load_page(a, bt[off + kSampleStride * (i2 < ns ? i2 : i1)], lane_off, lane, p0, k0);
+        keys[(size_t)i1 * kPage + lane] = score_key(page_scores<HB>(A, c, p1, k1));
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the unused prefetches settle before exit
+}
+
+// Floor of query b, one workgroup of kFloorThreads: the r-th largest valid
+// sampled key cut to its top 22 bits (first digit by histogram, then the
+// next 11 bits inside that bin), with r five standard deviations above the
+// expected number of sampled scores at or above the query's k-th largest.
+// Writes the floor (word 2 of the query's counter block; 0 when the query is
+// not sampled or r exceeds its sample, so every score is a candidate) and
+// clears the candidate count (word 1) -- for every query.
 __global__ void __launch_bounds__(kFloorThreads)
 decode_floor_kernel(DecodeArgs a) {
     __shared__ uint32_t h[kHistBins];
     __shared__ uint32_t red[kFloorWaves + 2];
-    constexpr int U = 4;  // keys per thread per round
+    constexpr int U = 4;  // keys per thread per histogram round
     const int b = blockIdx.x, t = threadIdx.x;
+    uint32_t* ctrl = a.ctrl + (size_t)b * kCtrlStride;
     const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
     const int ns = sampled_pages(ctx, a.topk);
-    if (ns == 0) return;
-    const uint32_t* keys = a.sample_key + (size_t)a.sprefix[b] * kPage;
+    if (ns == 0) {
+        if (t == 0) { ctrl[1] = 0u; ctrl[2] = 0u; }
+        return;
+    }
+    const uint32_t* keys = a.sample_key + (size_t)b * a.sample_stride;
     const int off = sample_offset(b);
     const int n_all = ns * kPage;
     auto valid = [&](int e) { return e < n_all && (off + kSampleStride * (e / kPage)) * kPage + e % kPage < ctx; };
@@ -430,13 +324,186 @@ decode_floor_kernel(DecodeArgs a) {
     bin_from_top(h, 0, &m, red);
     const float ex = (float)m * (float)a.topk / (float)ctx;
     const uint32_t r = (uint32_t)ceilf(ex + 5.f * sqrtf(ex) + 8.f);
-    if (r >= m) return;
-    uint32_t above1 = 0;
-    const int bin1 = bin_from_top(h, r, &above1, red);
-    pass(10, bin1);
-    uint32_t above2 = 0;
-    const int bin2 = bin_from_top(h, r - above1, &above2, red);
-    if (t == 0) a.ctrl[(size_t)b * kCtrlStride + 2] = ((uint32_t)bin1 << 21) | ((uint32_t)bin2 << 10);
+    uint32_t fl = 0u;
+    if (r < m) {
+        uint32_t above1 = 0;
+        const int bin1 = bin_from_top(h, r, &above1, red);
+        pass(10, bin1);
+        uint32_t above2 = 0;
+        const int bin2 = bin_from_top(h, r - above1, &above2, red);
+        fl = ((uint32_t)bin1 << 21) | ((uint32_t)bin2 << 10);
+    }
+    if (t == 0) { ctrl[1] = 0u; ctrl[2] = fl; }
+}
+
+// The main scan.  A persistent grid (one resident round of workgroups): the
+// global list of (query, page) pairs, query-major, is cut into equal
+// contiguous shares, one per workgroup, so ragged context lengths leave no
+// tail of idle CUs.  Inside a share the 4 waves take interleaved pages (wave
+// w: pages w, w+4, ...).  Each wave keeps two pages of loads in flight while
+// it multiplies the current one; the (query, position, page id) of its next
+// 64 pages sit one per lane, so no load waits on a block-table read.  Query
+// operands are reloaded only when a wave's pages cross into the next query.
+// Scores whose key reaches the query's floor go to the wave's LDS candidate
+// buffer, flushed to the query's candidate list.  The page prefix over
+// queries is built in LDS from the context lengths (or read from the
+// prologue's output for very large batches).
+template <int HB>
+__global__ void __launch_bounds__(kThreadsDec)
+decode_scan_kernel(DecodeArgs a) {
+    __shared__ uint32_t lds_wave[kThreadsDec / kWave][2 * kCandBuf];  // candidate buffer
+    __shared__ int32_t prefix_lds[kPrefixLds];
+    __shared__ uint32_t wtot[kThreadsDec / kWave];
+    constexpr int NW = kThreadsDec / kWave;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int n = lane & 15, g = lane >> 4;
+    float* cbuf_s = reinterpret_cast<float*>(lds_wave[wave]);
+    int32_t* cbuf_p = reinterpret_cast<int32_t*>(lds_wave[wave] + kCandBuf);
+
+    const bool pre_in_lds = a.B + 1 <= kPrefixLds;
+    if (pre_in_lds) {
+        // exclusive prefix of the per-query page counts, 256 queries a round
+        int carry = 0;
+        for (int b0 = 0; b0 <= a.B; b0 += kThreadsDec) {
+            const int b = b0 + (int)threadIdx.x;
+            const uint32_t np = b < a.B ? (uint32_t)((clamp_ctx(a.context_lens[b], a.max_ctx) + kPage - 1) / kPage)
+                                        : 0u;
+            const uint32_t ip = wave_incl_scan(np);
+            if (lane == kWave - 1) wtot[wave] = ip;
+            __syncthreads();
+            uint32_t rp = (uint32_t)carry + ip - np, tot = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                if (w < wave) rp += wtot[w];
+                tot += wtot[w];
+            }
+            if (b <= a.B) prefix_lds[b] = (int32_t)rp;
+            carry += (int)tot;
+            __syncthreads();
+        }
+    }
+    auto prefix_at = [&](int i) -> int { return pre_in_lds ? prefix_lds[i] : a.prefix[i]; };
+    const int P = prefix_at(a.B);
+    const int64_t G = gridDim.x;
+    const int share_begin = (int)((int64_t)blockIdx.x * P / G);
+    const int share_end = (int)((int64_t)(blockIdx.x + 1) * P / G);
+    // this wave's pages: share_begin + wave + NW*k for k < nk
+    const int nk = share_end - share_begin - wave > 0 ? (share_end - share_begin - wave + NW - 1) / NW : 0;
+    if (nk == 0) return;
+
+    // Query of the share's first page (the last b with prefix[b] <= page).
+    int lo = 0, hi = a.B;
+    {
+        const int p0 = share_begin + wave;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (prefix_at(mid) <= p0) lo = mid; else hi = mid;
+        }
+    }
+    // Per-lane description of pages k0 .. k0+63 of this wave.
+    int walk_b = lo;  // query of page k0 (wave-uniform)
+    auto describe = [&](int k0, int& qb, int& pos0, int& pid) {
+        const int k = k0 + lane;
+        const int gp = share_begin + wave + NW * k;
+        qb = -1; pos0 = 0; pid = 0;
+        if (k < nk) {
+            int bb = walk_b;
+            while (prefix_at(bb + 1) <= gp) ++bb;
+            const int j = gp - prefix_at(bb);
+            qb = bb;
+            pos0 = j * kPage;
+            pid = a.block_table[(size_t)bb * a.max_pages + j];
+        }
+        const int last = min(63, nk - 1 - k0);
+        if (last >= 0) walk_b = __builtin_amdgcn_readlane(qb, last);
+        // Settle the table loads here (once per 64 pages): left pending, they
+        // would make every later step wait for its own prefetches too.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    };
+
+    const uint32_t lane_off = (uint32_t)(n * kD + 32 * g);
+    v8bf A[HB][4];
+    float c[HB][4];
+    int qcur = -1, ctx_cur = 0;
+    uint32_t floor_key = 0u;  // candidates have key >= floor_key
+    int nbuf = 0;             // entries in the wave's candidate buffer
+    uint32_t* cand_n = a.ctrl + 1;  // word 1 of each query's counter block
+    auto flush_cand = [&](int qb) {
+        if (nbuf == 0) return;
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&cand_n[(size_t)qb * kCtrlStride], (uint32_t)nbuf);
+        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+        float* cs = a.cand_score + (size_t)qb * a.cand_stride + base;
+        int32_t* cp = a.cand_pos + (size_t)qb * a.cand_stride + base;
+        for (int j = lane; j < nbuf; j += kWave) {
+            cs[j] = cbuf_s[j];
+            cp[j] = cbuf_p[j];
+        }
+        __builtin_amdgcn_wave_barrier();
+        nbuf = 0;
+    };
+
+    int cq, cpos, cpid;   // lanes: pages k0 .. k0+63
+    int nq, npos, npid;   // lanes: pages k0+64 .. k0+127
+    describe(0, cq, cpos, cpid);
+    describe(64, nq, npos, npid);
+
+    // One pipeline step: prefetch page k+2 into `pre`, multiply page k held
+    // in `cur` (page k+1 is in flight meanwhile).  Called with three buffers
+    // rotating, so no copies.
+    auto step = [&](int k, v4i (&cur)[4][2], float ks_c, v4i (&pre)[4][2], float& ks_p) {
+        const int i = k & 63;
+        const int pb = __builtin_amdgcn_readlane(cq, i);
+        const int ppos = __builtin_amdgcn_readlane(cpos, i);
+        {
+            // Unconditional, so every path issues the same loads and the wait
+            // for `cur` can leave two pages in flight; past the end of the
+            // share the current page is fetched again (unused).
+            const int pid_n = i < 62 ? __builtin_amdgcn_readlane(cpid, i + 2) : __builtin_amdgcn_readlane(npid, i - 62);
+            const int pid = k + 2 < nk ? pid_n : __builtin_amdgcn_readlane(cpid, i);
+            load_page(a, pid, lane_off, lane, pre, ks_p);
+        }
+        if (i == 63) {  // roll the page descriptions forward
+            cq = nq; cpos = npos; cpid = npid;
+            describe(k + 65, nq, npos, npid);
+        }
+        if (pb != qcur) {  // entering a new query
+            if (qcur >= 0) flush_cand(qcur);
+            qcur = pb;
+            ctx_cur = clamp_ctx(a.context_lens[pb], a.max_ctx);
+            load_query<HB>(a, pb, n, g, A, c);
+            floor_key = a.ctrl[(size_t)pb * kCtrlStride + 2];
+            // Settle the query loads here, on this rare path: otherwise the
+            // common path after it inherits their pending count and waits
+            // for every page load in flight at each step.
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
+        const float score = page_scores<HB>(A, c, cur, ks_c);
+        const int s = ppos + lane;
+        const uint32_t key = score_key(score);
+        if (nbuf > kCandBuf - kWave) flush_cand(qcur);
+        const bool take = s < ctx_cur && key >= floor_key;
+        const uint64_t m = wave_ballot(take);
+        if (take) {
+            const int o = nbuf + lanes_below(m);
+            cbuf_s[o] = score;
+            cbuf_p[o] = s;
+        }
+        nbuf += __builtin_popcountll(m);
+    };
+
+    v4i b0[4][2], b1[4][2], b2[4][2];
+    float k0 = 0.f, k1 = 0.f, k2 = 0.f;
+    load_page(a, __builtin_amdgcn_readlane(cpid, 0), lane_off, lane, b0, k0);
+    load_page(a, __builtin_amdgcn_readlane(cpid, nk > 1 ? 1 : 0), lane_off, lane, b1, k1);
+    for (int k = 0; k < nk; k += 3) {
+        step(k, b0, k0, b2, k2);
+        if (k + 1 < nk) step(k + 1, b1, k1, b0, k0);
+        if (k + 2 < nk) step(k + 2, b2, k2, b1, k1);
+    }
+    if (qcur >= 0) flush_cand(qcur);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the final page prefetches (unused) settle before exit
 }
 
 // Repair pass, one workgroup per query: a query whose candidate count fell
@@ -489,11 +556,21 @@ __global__ void zero_u32_kernel(uint32_t* p, size_t n) {
         p[i] = 0u;
 }
 
+
 template <int HB>
-hipError_t launch_scan_pass(const DecodeArgs& a, int64_t max_pages, hipStream_t stream) {
-    // One resident round of workgroups (occupancy queried once per process).
+hipError_t launch_decode_hb(const DecodeArgs& a_in, int64_t max_pages, hipStream_t stream) {
+    DecodeArgs a = a_in;
+    // about a thousand sample workgroups, at least one per query
+    a.sample_groups = a.B >= 1024 ? 1 : (1024 / a.B > 16 ? 16 : 1024 / a.B);
+    hipLaunchKernelGGL(decode_sample_kernel<HB>, dim3((unsigned)(a.B * a.sample_groups)), dim3(kThreadsDec), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_floor_kernel, dim3((unsigned)a.B), dim3(kFloorThreads), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // Main scan: one resident round of workgroups (occupancy queried once
+    // per process), never more workgroups than pages.
     static int resident = 0;
-    hipError_t e;
     if (resident == 0) {
         int dev = 0, per_cu = 0, cus = 0;
         if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
@@ -503,7 +580,6 @@ hipError_t launch_scan_pass(const DecodeArgs& a, int64_t max_pages, hipStream_t 
             return e;
         resident = (per_cu < 1 ? 1 : per_cu) * cus;
     }
-    // Never more workgroups than pages; the kernel tolerates empty shares.
     int64_t grid = resident;
     if (grid > max_pages) grid = max_pages;
     if (grid < 1) grid = 1;
@@ -521,35 +597,23 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_decode_scan(const DecodeArgs& a_in, int H, hipStream_t stream) {
-    {
-        const size_t nz4 = (size_t)a_in.B * kCtrlStride / 4;
-        size_t blocks = (nz4 + 4095) / 4096;
-        blocks = blocks < 1 ? 1 : (blocks > 256 ? 256 : blocks);
-        hipLaunchKernelGGL(decode_prologue_kernel, dim3((unsigned)blocks), dim3(1024), 0, stream, a_in);
+hipError_t launch_decode_scan(const DecodeArgs& a, int H, hipStream_t stream) {
+    hipError_t e;
+    if (a.B + 1 > kPrefixLds) {  // the scan's LDS prefix does not fit: build it in global memory
+        hipLaunchKernelGGL(decode_prologue_kernel, dim3(1), dim3(1024), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int hb = H / 16;
     if (hb < 1 || hb > 4) return hipErrorInvalidValue;
-    const int64_t max_pages = (int64_t)a_in.B * ((a_in.max_ctx + kPage - 1) / kPage);
-    for (int pass = 0; pass < 2; ++pass) {
-        DecodeArgs a = a_in;
-        a.sample = pass == 0 ? 1 : 0;
-        const int64_t pages = pass == 0 ? (max_pages + kSampleStride - 1) / kSampleStride : max_pages;
-        switch (hb) {
-            case 1: e = launch_scan_pass<1>(a, pages, stream); break;
-            case 2: e = launch_scan_pass<2>(a, pages, stream); break;
-            case 3: e = launch_scan_pass<3>(a, pages, stream); break;
-            default: e = launch_scan_pass<4>(a, pages, stream); break;
-        }
-        if (e != hipSuccess) return e;
-        if (pass == 0) {
-            hipLaunchKernelGGL(decode_floor_kernel, dim3((unsigned)a_in.B), dim3(kFloorThreads), 0, stream, a_in);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
+    const int64_t max_pages = (int64_t)a.B * ((a.max_ctx + kPage - 1) / kPage);
+    switch (hb) {
+        case 1: e = launch_decode_hb<1>(a, max_pages, stream); break;
+        case 2: e = launch_decode_hb<2>(a, max_pages, stream); break;
+        case 3: e = launch_decode_hb<3>(a, max_pages, stream); break;
+        default: e = launch_decode_hb<4>(a, max_pages, stream); break;
     }
-    hipLaunchKernelGGL(decode_repair_kernel, dim3((unsigned)a_in.B), dim3(256), 0, stream, a_in, H);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_repair_kernel, dim3((unsigned)a.B), dim3(256), 0, stream, a, H);
     return hipGetLastError();
 }
 

@@ -42,11 +42,11 @@ struct DecodeArgs {
     int B;
     int topk;
     float inv_sqrt_d;
-    int sample;               // set per pass by the launcher: 1 = sample pass, 0 = main pass
     uint32_t* ctrl;           // [B][kCtrlStride] per-query words: 1 = candidate count, 2 = floor key
-    uint32_t* sample_key;     // [sampled pages][64] score keys of the sampled pages
-    int32_t* prefix;          // [B+1] exclusive prefix of per-query page counts
-    int32_t* sprefix;         // [B+1] exclusive prefix of per-query sampled-page counts
+    uint32_t* sample_key;     // [B][sample_stride] score keys of each query's sampled pages
+    int64_t sample_stride;    // >= 64 * (sampled pages of a query at max_ctx)
+    int sample_groups;        // sample workgroups per query (set by the launcher)
+    int32_t* prefix;          // [B+1] exclusive prefix of per-query page counts (large batches only)
     float* cand_score;        // [B][cand_stride] candidate scores
     int32_t* cand_pos;        // [B][cand_stride] candidate positions
     int64_t cand_stride;      // >= max_ctx

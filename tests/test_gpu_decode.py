@@ -203,3 +203,12 @@ def test_constant_scores_long_context():
     for b in range(2):
         assert np.array_equal(np.sort(gi[b]), np.arange(K)), f"q{b}: ties not broken toward low positions"
         assert np.all(gv[b] == 0.0)
+
+
+def test_batch_beyond_lds_prefix():
+    """2100 queries: the scan's page prefix over queries no longer fits its
+    LDS table and comes from global memory instead."""
+    rng = np.random.default_rng(572)
+    ctx = rng.integers(1, 300, size=2100).tolist()
+    d = synth.decode_inputs(2100, ctx, 16, 128, seed=572, permute=True)
+    parity(d, 64, "B=2100", queries=list(range(0, 2100, 97)) + [2099])
