@@ -745,7 +745,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     const int nblk = (L + W - 1) / W;
     const int b = blockIdx.x % a.B;
     const int blk = nblk - 1 - (int)(blockIdx.x / a.B);  // heaviest first
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int t_raw = blk * W + wave;
     const bool live = t_raw < L;        // waves past the end only help stage keys
     const int t = live ? t_raw : L - 1;
@@ -837,12 +837,19 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     // is scanned again without a floor.  Otherwise every dropped key lies
     // below the k-th largest and the selection is exact.
     const int S = last + 1 >= 32 ? (last + 1) / 16 : 0;
-    auto chunk_at = [&](int i) -> int {
-        i = min(i, last);  // the stage copies issued past the end re-read the last chunk
+    // Chunk of order index i from the chunk of index i-1 (scalar, no
+    // division): the sample 16i+15 for i < S, then 0, 1, ... skipping the
+    // sampled chunks; past the last index the last chunk again (the stage
+    // copies issued past the end re-read it).
+    auto chunk_next = [&](int i, int prev) -> int {
+        if (i > last) return prev;
         if (i < S) return 16 * i + 15;
-        const int j = i - S;
-        return j < 15 * S ? j + j / 15 : j + S;
+        if (i == S) return 0;
+        int c = prev + 1;
+        if ((c & 15) == 15 && c < 16 * S) ++c;
+        return c;
     };
+    const int chunk0 = S > 0 ? 15 : 0;
 
     // Stage slot i % 3 receives the i-th chunk of the order: thread x of the
     // block copies 16 key bytes (LDS slot x = row x/8, segment x%8 holds
@@ -852,9 +859,8 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     // clamped to L-1; they only ever feed masked scores.
     const int srow_i = threadIdx.x >> 3;
     const int sseg = (threadIdx.x & 7) ^ ((srow_i >> 1) & 7);
-    auto stage_chunk = [&](int i) {
-        unsigned char* dst = smem_raw + (i % kStages) * kStageBytes;
-        const int chunk = chunk_at(i);
+    auto stage_chunk = [&](int slot, int chunk) {
+        unsigned char* dst = smem_raw + slot * kStageBytes;
         const int r = min(chunk * 64 + srow_i, L - 1);
         const uint8_t* src = kbase + (size_t)r * kD + 16 * sseg;
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 1024 * wave),
@@ -895,8 +901,8 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     // below is branch-free and interleaves its instructions step by step.
     struct HalfAcc { v4f s[2][HB]; };
     struct HalfB { v8i b[2]; };
-    auto load_b = [&](int i, int half, HalfB& B_) {
-        const unsigned char* cur = smem_raw + (i % kStages) * kStageBytes;
+    auto load_b = [&](int slot, int half, HalfB& B_) {
+        const unsigned char* cur = smem_raw + slot * kStageBytes;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int r = 16 * (2 * half + q) + n;
@@ -908,11 +914,11 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     // Adjusted scale of key (i-th chunk)*64 + lane, and the E8M0 bytes of
     // the lane's four subtile keys; read while the chunk's slot is still
     // owned (before the barrier that lets chunk i+3 overwrite it).
-    auto load_ks = [&](int i) {
-        return *reinterpret_cast<const float*>(smem_raw + (i % kStages) * kStageBytes + kStageScaleOff + 4 * lane);
+    auto load_ks = [&](int slot) {
+        return *reinterpret_cast<const float*>(smem_raw + slot * kStageBytes + kStageScaleOff + 4 * lane);
     };
-    auto load_sb = [&](int i) {
-        return *reinterpret_cast<const int*>(smem_raw + (i % kStages) * kStageBytes + kStageExpOff + 4 * n);
+    auto load_sb = [&](int slot) {
+        return *reinterpret_cast<const int*>(smem_raw + slot * kStageBytes + kStageExpOff + 4 * n);
     };
     // Score MFMA of subtile 2*MH + q (q in {0, 1}) and head block hb.
     auto score_mma = [&](auto mh, int q, int hb, const HalfB& B_, int sb) -> v4f {
@@ -1016,13 +1022,13 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         }
     };
     // The rest of an append step: the optional score-matrix row and the
-    // compaction request when the buffer nears capacity.
-    auto finish_tail = [&](int i, int chunk, float score) {
+    // compaction request (flag slot `fslot`) when the buffer nears capacity.
+    auto finish_tail = [&](int fslot, int chunk, float score) {
         if (srow && active) {
             const int s = chunk * 64 + lane;
             if (s < L) srow[s] = s <= t ? score : -INFINITY;
         }
-        if (active && nb > CAP - 2 * kWave && lane == 0) flags[i % 3] = 1u;
+        if (active && nb > CAP - 2 * kWave && lane == 0) flags[fslot] = 1u;
     };
 
     if (threadIdx.x == 0) flags[3] = 0u;
@@ -1037,9 +1043,13 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         float ks_prev = 0.f;
         int chunk_prev = 0;  // chunk id of the previous iteration
         if (threadIdx.x < 3) flags[threadIdx.x] = 0u;
-        stage_chunk(0);
-        stage_chunk(1);
-        stage_chunk(2);
+        // order indices 0..2 into slots 0..2; c_stage tracks index i+3
+        int c_stage = chunk0;
+        stage_chunk(0, c_stage);
+        c_stage = chunk_next(1, c_stage);
+        stage_chunk(1, c_stage);
+        c_stage = chunk_next(2, c_stage);
+        stage_chunk(2, c_stage);
         // chunk 0 landed: at most this wave's copies of chunks 1 and 2 in
         // flight (waves 0 and 1 issue two copies per chunk, the others one)
         if (wave <= 1) __builtin_amdgcn_s_waitcnt(0x0F74);                // vmcnt(4)
@@ -1047,6 +1057,9 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         __syncthreads();
         load_b(0, 0, bA);
         int sb_next = load_sb(0);
+        int chunk_cur = chunk0;  // chunk of order index i
+        // slots of order indices i, i+1, i+2 (mod 3)
+        int s0 = 0, s1 = 1, s2 = 2;
         for (int i = 0; i <= last; ++i) {
             const int sb_cur = sb_next;
             // Region 1: first half of chunk i on the MFMA (operands read during
@@ -1055,8 +1068,8 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             // and the chunk's key scales are read here, before the barrier
             // that releases the chunk's stage slot.
             __builtin_amdgcn_sched_barrier(0);
-            load_b(i, 1, bB);
-            const float ks_cur = load_ks(i);
+            load_b(s0, 1, bB);
+            const float ks_cur = load_ks(s0);
             region(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, bA, sb_cur, hA, hB, Pacc,
                    [](int) {});
             // keep this epilogue here (it would otherwise sink into a branch below)
@@ -1073,41 +1086,31 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             else if (wave <= 1) __builtin_amdgcn_s_waitcnt(0x0F72);       // vmcnt(2)
             else __builtin_amdgcn_s_waitcnt(0x0F71);                      // vmcnt(1)
             __syncthreads();
-            // Compaction request of the appends of the (i-2)-th chunk (made
-            // during iteration i-1).  Slot j % 3 belongs to the appends of the
-            // j-th chunk: set in iteration j+1, read in j+2, cleared in j+3
-            // (each step separated by a barrier).
-            const bool want_compact = i >= 2 && flags[(i - 2) % 3] != 0u;
-            if (threadIdx.x == 0 && i >= 3) flags[(i - 3) % 3] = 0u;
+            // Compaction request of the appends of chunk i-2 (made at the end
+            // of iteration i-1; slot (i-2) % 3 = s1), read now and acted on
+            // after region 2, so the read's latency hides under the MFMAs.
+            // Slot j % 3 belongs to the appends of the j-th chunk: set at the
+            // end of iteration j+1, read in j+2, cleared in j+3 (each step
+            // separated by a barrier).
+            const uint32_t flag_word = flags[s1];
+            if (threadIdx.x == 0 && i >= 3) flags[s0] = 0u;
             // Chunk i+3 goes to chunk i's slot.  Past the last chunk the copy
             // is a clamped dummy, so every chunk issues the same loads.
-            stage_chunk(i + 3);
-            // Buffer maintenance, before the appends of chunk i-1.  The
-            // sample's appends (chunks 0..S-1 of the order) end in iteration
-            // S: set the speculative floor before any other append.
-            if (i == S + 1 && r_spec != 0u && active && (uint32_t)nb > r_spec) {
-                uint32_t fl;
-                nb = wave_floor(rb, nb, r_spec, &fl);
-                thr = fl == 0u ? 0u : fl - 1u;
-                floored = true;
-            }
-            // Cooperative compaction: a request from any wave makes every
-            // wave compact now, so the block pays one stall per event.
-            if (want_compact && active && nb > K) nb = wave_compact(rb, nb, (uint32_t)K, &thr, CAP);
+            c_stage = chunk_next(i + 3, c_stage);
+            stage_chunk(s0, c_stage);
             // Region 2: second half of chunk i on the MFMA, head sums of its
             // first half, the appends of chunk i-1 (discarded before the first
             // chunk: nothing is valid yet) and the first-half operands of
             // chunk i+1 (landed, per the barrier above).
             const v4f Pfin = Pacc;
-            const int chunk_cur = chunk_at(i);
             const bool fin_on = i >= 1;
             const bool was_active = active;
             active = active && fin_on;
             FinState fs;
             const int nb0 = nb;
             __builtin_amdgcn_sched_barrier(0);
-            load_b(i + 1, 0, bA);
-            sb_next = load_sb(i + 1);
+            load_b(s1, 0, bA);
+            sb_next = load_sb(s1);
             Pacc = v4f{0.f, 0.f, 0.f, 0.f};
             region(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, bB, sb_cur, hB, hA, Pacc,
                    [&](int k) {
@@ -1120,16 +1123,31 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             active = was_active;
             if (!fin_on) nb = nb0;
-            if (fin_on) finish_tail(i - 1, chunk_prev, fs.score);
+            // Buffer maintenance after the appends of chunk i-1.  The sample's
+            // appends (chunks 0..S-1 of the order) end in iteration S: the
+            // speculative floor is set before any other append.  Then the
+            // cooperative compaction: a request from any wave makes every
+            // wave compact, so the block pays one stall per event.
+            if (i == S && r_spec != 0u && active && (uint32_t)nb > r_spec) {
+                uint32_t fl;
+                nb = wave_floor(rb, nb, r_spec, &fl);
+                thr = fl == 0u ? 0u : fl - 1u;
+                floored = true;
+            }
+            if (i >= 2 && flag_word != 0u && active && nb > K) nb = wave_compact(rb, nb, (uint32_t)K, &thr, CAP);
+            if (fin_on) finish_tail(s2, chunk_prev, fs.score);
             ks_prev = ks_cur;
             chunk_prev = chunk_cur;
+            chunk_cur = chunk_next(i + 1, chunk_cur);
+            const int sx = s0;
+            s0 = s1; s1 = s2; s2 = sx;
         }
         Pacc = epi_half(std::integral_constant<int, 1>{}, hB, Pacc);
         {
             FinState fs;
 #pragma unroll
             for (int p = 0; p < 5; ++p) finish_piece(p, fs, chunk_prev, Pacc, ks_prev);
-            finish_tail(last, chunk_prev, fs.score);
+            finish_tail(s2, chunk_prev, fs.score);  // no compaction follows: the flag is cleared at the next pass
         }
         __builtin_amdgcn_s_waitcnt(0x0000);  // no stage copy or LDS read may still be in flight
         if (pass == 1) break;
