@@ -1007,7 +1007,10 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         if (piece == 1) f.key = score_key(f.score);
         if (piece == 2) {
             f.s = chunk * 64 + lane;
-            f.app = active && f.s <= t && f.key > thr;
+            // bitwise, not short-circuit: a branch here would split the region
+            int app = (int)(f.s <= t) & (int)(f.key > thr) & (int)active;
+            asm volatile("" : "+v"(app));
+            f.app = app != 0;
         }
         if (piece == 3) {
             f.m = wave_ballot(f.app);
