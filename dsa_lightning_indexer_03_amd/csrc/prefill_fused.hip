@@ -1002,15 +1002,15 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     // region.  Branch free: lanes that do not append write a slot of their
     // own past CAP.
     struct FinState { float score; uint32_t key; int s; bool app; uint64_t m; int below; };
+    uint32_t thr_eff = 0u;  // thr while the wave appends, else 0xFFFFFFFF
     auto finish_piece = [&](int piece, FinState& f, int chunk, const v4f& P, float ks) {
         if (piece == 0) f.score = P[0] * (ks * Fscale);
         if (piece == 1) f.key = score_key(f.score);
         if (piece == 2) {
             f.s = chunk * 64 + lane;
-            // bitwise, not short-circuit: a branch here would split the region
-            int app = (int)(f.s <= t) & (int)(f.key > thr) & (int)active;
-            asm volatile("" : "+v"(app));
-            f.app = app != 0;
+            // bitwise, not short-circuit (a branch here would split the
+            // region); an inactive wave's threshold admits nothing
+            f.app = (f.s <= t) & (f.key > thr_eff);
         }
         if (piece == 3) {
             f.m = wave_ballot(f.app);
@@ -1109,6 +1109,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             const bool fin_on = i >= 1;
             const bool was_active = active;
             active = active && fin_on;
+            thr_eff = active ? thr : 0xFFFFFFFFu;
             FinState fs;
             const int nb0 = nb;
             __builtin_amdgcn_sched_barrier(0);
@@ -1148,6 +1149,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         Pacc = epi_half(std::integral_constant<int, 1>{}, hB, Pacc);
         {
             FinState fs;
+            thr_eff = active ? thr : 0xFFFFFFFFu;
 #pragma unroll
             for (int p = 0; p < 5; ++p) finish_piece(p, fs, chunk_prev, Pacc, ks_prev);
             finish_tail(s2, chunk_prev, fs.score);  // no compaction follows: the flag is cleared at the next pass
