@@ -32,20 +32,20 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # HBM traffic per launch from two rocprofv3 counter passes (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch) over `bench.py --steps 2 --warmup 1
 # --no-cpu-baseline --copy-calibration`.  Each counter is scaled by what it
-# reads for a 1 GiB device-to-device copy (FETCH_SIZE 524315.5 KiB, WRITE_SIZE
+# reads for a 1 GiB device-to-device copy (FETCH_SIZE 524315 KiB, WRITE_SIZE
 # 1048576.0 KiB).  A record applies only while the kernel's sources hash to
 # the value it was taken at; otherwise traffic is reported as null.
-COPY_FETCH_FACTOR = 1048576.0 / 524315.5
+COPY_FETCH_FACTOR = 1048576.0 / 524315.0
 COPY_WRITE_FACTOR = 1048576.0 / 1048576.0
 _DECODE_SRC = ["csrc/decode_paged.hip", "csrc/common.h", "csrc/kernels.h", "build.py"]
-_DECODE_SHA = "cd2fb44ee28417f4cb7678f6528050fb821760a8733ded9120bc0b24454958d5"
+_DECODE_SHA = "35028db8e337541b4e4f8c49ce28f58de1d7802694c6ca0473df069fb8865502"
 COUNTERS = {
     "prefill": {"sources": ["csrc/prefill_fused.hip", "csrc/common.h", "csrc/kernels.h", "build.py"],
-                "sha256": "b1b8eb290a7c10d141fc4c822e5965ed92a5f4d1fff07a7209414cbda94975ce",
-                "fetch_kib": 255343.6, "write_kib": 524303.1},
-    # main scan pass of one decode call (the sample pass reads about 1/20 of it)
-    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 546182.1, "write_kib": 1943.8},
-    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 556954.2, "write_kib": 3878.8},
+                "sha256": "e743839d04e2ecd89759215fbfa43949b823b55c674906d64f7cd19ff235434d",
+                "fetch_kib": 255308.1, "write_kib": 524331.9},
+    # main scan of one decode call (the sample kernel reads about 1/20 of it)
+    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 546155.8, "write_kib": 1940.6},
+    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 556951.6, "write_kib": 3871.8},
 }
 
 
@@ -247,7 +247,7 @@ def main():
                          "128 queries, ctx ~ U[4096,131072], 64-token pages scattered by a seeded permutation"),
                 "kcache_bytes": nbytes, "us_per_call": float(np.mean(dms) * 1e3), "GB/s": gbs,
                 "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "topk": c["topk"],
-                "scan_main_pass_traffic_bytes": measured_traffic(f"decode_scan_w{n}"),
+                "scan_traffic_bytes": measured_traffic(f"decode_scan_w{n}"),
             }
             del args_d, ws
             torch.cuda.empty_cache()
