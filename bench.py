@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 METRIC = "indexer score+top-k pairs/s (prefill L=32K) and decode K-cache GB/s"
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 # HBM traffic per launch from two rocprofv3 counter passes (FETCH_SIZE, then
@@ -144,6 +145,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="skip the prefill headline (profiling aid)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the bf16 L=8192 and tiny prefill timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (for counter calibration)")
     args = ap.parse_args()
@@ -252,6 +254,33 @@ def main():
             del args_d, ws
             torch.cuda.empty_cache()
         result["decode"] = dec
+
+    # ---------------- the other prefill workloads: bf16 L=8192, tiny fp32 ----------------
+    if not args.decode_only and not args.no_extra:
+        extra = {}
+        for n in (2, 1):
+            c = synth.CONFIGS[n]
+            inp_n = synth.config_inputs(n)
+            qn, kn, wn = up(torch, inp_n["q"], dev), up(torch, inp_n["k"], dev), up(torch, inp_n["w"], dev)
+            want = n == 1  # the tiny workload also returns its full score matrix
+
+            def pstep():
+                dsa.indexer_prefill(qn, kn, wn, c["topk"], want_scores=want)
+
+            pms, _ = time_calls(torch, pstep, max(args.steps, 10), args.warmup)
+            pairs_n = c["L"] * (c["L"] + 1) // 2
+            ms_n = float(np.mean(pms))
+            rec = {"what": f"prefill B=1 L={c['L']} H={c['H']} D={c['D']} k={c['topk']} {c['dtype']}"
+                           + (" (full score matrix returned)" if want else ", fused"),
+                   "ms_per_call": ms_n, "ms_min": float(min(pms)), "pairs_per_s": pairs_n / (ms_n * 1e-3)}
+            if n == 2:
+                tf = 2.0 * c["H"] * c["D"] * pairs_n / (ms_n * 1e-3) / 1e12
+                rec.update({"TFLOP/s": tf, "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS})
+            extra[f"workload_{n}"] = rec
+            log(f"prefill workload {n}: {ms_n:.3f} ms/call")
+            del qn, kn, wn
+            torch.cuda.empty_cache()
+        result["prefill_other"] = extra
 
     # ---------------- CPU oracle baseline (rank 0, N=1) ----------------
     if not args.no_cpu_baseline and not args.decode_only:
