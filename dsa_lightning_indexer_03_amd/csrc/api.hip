@@ -34,8 +34,6 @@ bool prefill_is_fused(int dtype, int H, int D) {
 }
 
 size_t decode_score_stride(int max_ctx) { return (size_t)((max_ctx + 63) / 64) * 64; }
-// Bound on one query's sampled keys: at most one page in 32, 64 keys each.
-size_t decode_sample_words(int max_ctx) { return (size_t)(((max_ctx + 63) / 64 + 31) / 32) * 64; }
 
 }  // namespace
 
@@ -178,11 +176,9 @@ size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, i
     (void)H; (void)D; (void)topk;
     if (B < 1 || max_context_len < 0) return 0;
     // candidate scores and positions: [B][stride] each; per-query counters
-    // [B][kCtrlStride]; sampled keys [B][decode_sample_words]; page prefix
-    // over queries [B+1].
+    // [B][kCtrlStride]; page prefix over queries [B+1].
     return (size_t)B * decode_score_stride(max_context_len) * 8u +
            (size_t)B * dsaidx::kCtrlStride * sizeof(uint32_t) +
-           (size_t)B * decode_sample_words(max_context_len) * sizeof(uint32_t) +
            (size_t)(B + 1) * sizeof(int32_t);
 }
 
@@ -228,37 +224,10 @@ dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
     float* cand_score = reinterpret_cast<float*>(wp);
     int32_t* cand_pos = reinterpret_cast<int32_t*>(wp + (size_t)B * stride * 4);
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(wp + (size_t)B * stride * 8);  // [B][kCtrlStride]
-    uint32_t* sample_key = ctrl + (size_t)B * dsaidx::kCtrlStride;
-    int32_t* prefix = reinterpret_cast<int32_t*>(sample_key + (size_t)B * decode_sample_words(max_context_len));
+    int32_t* prefix = reinterpret_cast<int32_t*>(ctrl + (size_t)B * dsaidx::kCtrlStride);
     hipError_t e;
-    if (max_context_len > 0) {
-        dsaidx::DecodeArgs d{};
-        d.q = reinterpret_cast<const uint16_t*>(q);
-        d.w = w;
-        d.k_cache = k_cache;
-        d.k_scale = k_scale;
-        d.block_table = block_table;
-        d.max_pages = max_pages_per_seq;
-        d.context_lens = context_lens;
-        d.max_ctx = max_context_len;
-        d.B = B;
-        d.topk = topk;
-        d.inv_sqrt_d = 1.0f / sqrtf((float)D);
-        d.ctrl = ctrl;
-        d.sample_key = sample_key;
-        d.sample_stride = (int64_t)decode_sample_words(max_context_len);
-        d.prefix = prefix;
-        d.cand_score = cand_score;
-        d.cand_pos = cand_pos;
-        d.cand_stride = (int64_t)stride;
-        e = dsaidx::launch_decode_scan(d, H, st);
-        if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (scan)");
-    } else {
-        e = dsaidx::launch_zero_u32(ctrl, (size_t)B * dsaidx::kCtrlStride, st);
-        if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (clear)");
-    }
     // Exact selection over each query's candidates (every score that can
-    // be selected is among them).
+    // be selected is among them), run by the scan's final kernel.
     dsaidx::SelectArgs s{};
     s.scores = cand_score;
     s.row_stride = (int64_t)stride;
@@ -275,8 +244,32 @@ dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
     s.topk = topk;
     s.idx_out = topk_idx;
     s.val_out = topk_score;
-    e = dsaidx::launch_topk_select(s, B, st);
-    if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (select)");
+    if (max_context_len > 0) {
+        dsaidx::DecodeArgs d{};
+        d.q = reinterpret_cast<const uint16_t*>(q);
+        d.w = w;
+        d.k_cache = k_cache;
+        d.k_scale = k_scale;
+        d.block_table = block_table;
+        d.max_pages = max_pages_per_seq;
+        d.context_lens = context_lens;
+        d.max_ctx = max_context_len;
+        d.B = B;
+        d.topk = topk;
+        d.inv_sqrt_d = 1.0f / sqrtf((float)D);
+        d.ctrl = ctrl;
+        d.prefix = prefix;
+        d.cand_score = cand_score;
+        d.cand_pos = cand_pos;
+        d.cand_stride = (int64_t)stride;
+        e = dsaidx::launch_decode_scan(d, s, H, st);
+        if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (scan)");
+    } else {
+        e = dsaidx::launch_zero_u32(ctrl, (size_t)B * dsaidx::kCtrlStride, st);
+        if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (clear)");
+        e = dsaidx::launch_topk_select(s, B, st);
+        if (e != hipSuccess) return hip_fail(e, "indexer_decode_paged (select)");
+    }
     return DSAIDX_OK;
 }
 

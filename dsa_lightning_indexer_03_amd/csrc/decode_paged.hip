@@ -27,12 +27,13 @@
 // per 132 B read, interleaved with the cache reads, costs about a fifth of
 // the scan.  So the scan writes only candidates:
 //
-// 1. A sample kernel scores a strided sample of every long query's pages
-//    (one page in kSampleStride, from a per-query offset) and stores the
-//    score keys; a floor kernel, one workgroup per query, takes the r-th
-//    largest sampled key to 22 bits (two radix digits) as the query's floor,
-//    with r five standard deviations above the expected number of sampled
-//    scores at or above the query's k-th largest.
+// 1. A sample-and-floor kernel, one workgroup per query, scores a strided
+//    sample of every long query's pages (one page in kSampleStride or
+//    sparser, at most kMaxSamplePages, from a per-query offset), keeps the
+//    score keys in LDS and takes the r-th largest sampled key to 22 bits (two
+//    radix digits) as the query's floor, with r five standard deviations
+//    above the expected number of sampled scores at or above the query's
+//    k-th largest.
 // 2. The main scan scores every position and writes only the scores whose
 //    key reaches the query's floor, to the query's candidate list.
 // 3. Verification: if at least min(k, context) scores reached the floor,
@@ -42,6 +43,7 @@
 //    full.
 #include "common.h"
 #include "kernels.h"
+#include "select_row.h"
 
 namespace dsaidx {
 
@@ -51,7 +53,11 @@ constexpr int kD = 128;
 constexpr int kPage = 64;
 constexpr int kThreadsDec = 256;
 constexpr int kPrefixLds = 2048;   // queries whose page prefix is searched in LDS
-constexpr int kSampleStride = 32;  // one sampled page in this many
+#ifndef DSAIDX_SAMPLE_PAGES
+#define DSAIDX_SAMPLE_PAGES 32
+#endif
+constexpr int kSampleStride = 32;                       // at most one sampled page in this many
+constexpr int kMaxSamplePages = DSAIDX_SAMPLE_PAGES;    // sampled pages of one query, at most
 constexpr int kCandBuf = 1024;     // per-wave LDS candidate buffer (score, position) pairs
 
 #ifndef DSAIDX_DECODE_NT
@@ -88,19 +94,24 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_ctx) {
     return ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
 }
 
-// Sampling of query b: pages sample_offset(b) + kSampleStride * i for
-// i < sampled_pages(ctx).  Only queries with context >= 4k and at least two
-// sampling strides of pages are sampled; the count is the same for every
-// offset (pages o + 32 i < np for all o < 32 when i < (np - 32) / 32 + 1).
-__device__ __forceinline__ int sample_offset(int b) {
-    return (int)(((uint32_t)b * 0x9E3779B1u) >> 27);  // in [0, 32)
-}
-__device__ __forceinline__ int sampled_pages(int ctx, int topk) {
+// Sampling of query b: pages off + stride * i for i < ns, with stride at
+// least kSampleStride and large enough that ns <= kMaxSamplePages, and a
+// hashed per-query offset off in [0, stride).  Only queries with context
+// >= 4k and at least two strides of pages are sampled; the count is the same
+// for every offset (pages o + stride i < np for all o < stride when
+// i < (np - stride) / stride + 1, and that count is <= np / stride).
+struct SamplePlan {
+    int stride, off, ns;
+};
+__device__ __forceinline__ SamplePlan sample_plan(int b, int ctx, int topk) {
     const int np = (ctx + kPage - 1) / kPage;
-    if (ctx < 4 * topk || np < 2 * kSampleStride) return 0;
-    return (np - kSampleStride) / kSampleStride + 1;
+    SamplePlan p;
+    p.stride = (np + kMaxSamplePages - 1) / kMaxSamplePages;
+    if (p.stride < kSampleStride) p.stride = kSampleStride;
+    p.off = (int)(((uint64_t)((uint32_t)b * 0x9E3779B1u) * (uint32_t)p.stride) >> 32);
+    p.ns = (ctx < 4 * topk || np < 2 * p.stride) ? 0 : (np - p.stride) / p.stride + 1;
+    return p;
 }
-
 
 // Per-query operands of the scan, lane (n, g): A[hb][j] = the 8 bf16 query
 // values of head 16hb + n, dims [32g + 8j, +8); c[hb][i] = w / sqrt(D) of
@@ -189,15 +200,15 @@ decode_prologue_kernel(DecodeArgs a) {
     if (t == 0) a.prefix[a.B] = (int32_t)carry;
 }
 
-constexpr int kFloorThreads = 1024;
-constexpr int kFloorWaves = kFloorThreads / kWave;
+constexpr int kSfThreads = 512;  // sample-and-floor workgroup
+constexpr int kSfWaves = kSfThreads / kWave;
 
-// Bin of the 2048-bin LDS histogram h (kFloorThreads threads) where the
-// count from the top reaches r; also the count in the bins above it.  With
-// r == 0 it returns the total count in *above and bin -1.
+// Bin of the 2048-bin LDS histogram h (kSfThreads threads) where the count
+// from the top reaches r; also the count in the bins above it.  With r == 0
+// it returns the total count in *above and bin -1.
 __device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint32_t* above, uint32_t* red) {
     const int t = threadIdx.x;
-    constexpr int kPer = kHistBins / kFloorThreads;
+    constexpr int kPer = kHistBins / kSfThreads;
     const uint32_t* hl = h + kHistBins - kPer * (t + 1);  // thread t: bins from the top, ascending
     uint32_t loc = 0;
 #pragma unroll
@@ -207,7 +218,7 @@ __device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint3
     __syncthreads();
     uint32_t run = incl - loc, total = 0;
 #pragma unroll
-    for (int w = 0; w < kFloorWaves; ++w) {
+    for (int w = 0; w < kSfWaves; ++w) {
         const uint32_t v = red[w];
         total += v;
         if (w < t / kWave) run += v;
@@ -217,105 +228,84 @@ __device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint3
         *above = total;
         return -1;
     }
-    if (t == 0) red[kFloorWaves] = 0xFFFFFFFFu;
+    if (t == 0) red[kSfWaves] = 0xFFFFFFFFu;
     __syncthreads();
 #pragma unroll
     for (int i = kPer - 1; i >= 0; --i) {
         const uint32_t cnt = hl[i];
         if (run < r && r <= run + cnt) {
-            red[kFloorWaves] = (uint32_t)(kHistBins - kPer * (t + 1) + i);
-            red[kFloorWaves + 1] = run;
+            red[kSfWaves] = (uint32_t)(kHistBins - kPer * (t + 1) + i);
+            red[kSfWaves + 1] = run;
         }
         run += cnt;
     }
     __syncthreads();
-    const int bin = (int)red[kFloorWaves];
-    *above = red[kFloorWaves + 1];
+    const int bin = (int)red[kSfWaves];
+    *above = red[kSfWaves + 1];
     __syncthreads();
     return bin;
 }
 
-// Sample pass: workgroup (b, part) of `sample_groups` per query b, 4 waves;
-// wave w of part p scores the sampled pages i = 4p + w + 4 * groups * j of
-// query b (two pages of loads in flight) and stores their score keys.
-template <int HB>
-__global__ void __launch_bounds__(kThreadsDec)
-decode_sample_kernel(DecodeArgs a) {
-    const int groups = a.sample_groups;
-    const int b = blockIdx.x / groups, part = blockIdx.x % groups;
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
-    const int n = lane & 15, g = lane >> 4;
-    const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
-    const int ns = sampled_pages(ctx, a.topk);
-    const int first = part * (kThreadsDec / kWave) + wave;
-    const int stride = groups * (kThreadsDec / kWave);
-    if (first >= ns) return;
-    uint32_t* keys = a.sample_key + (size_t)b * a.sample_stride;
-    const int off = sample_offset(b);
-    const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
-    const uint32_t lane_off = (uint32_t)(n * kD + 32 * g);
-    v8bf A[HB][4];
-    float c[HB][4];
-    load_query<HB>(a, b, n, g, A, c);
-    v4i p0[4][2], p1[4][2];
-    float k0 = 0.f, k1 = 0.f;
-    load_page(a, bt[off + kSampleStride * first], lane_off, lane, p0, k0);
-    for (int i = first; i < ns; i += 2 * stride) {
-        const int i1 = i + stride;
-        // the next page's loads (again the current one past the end) go out
-        // before this page is scored
-        load_page(a, bt[off + kSampleStride * (i1 < ns ? i1 : i)], lane_off, lane, p1, k1);
-        keys[(size_t)i * kPage + lane] = score_key(page_scores<HB>(A, c, p0, k0));
-        if (i1 >= ns) break;
-        const int i2 = i1 + stride;
-        load_page(a, bt[off + kSampleStride * (i2 < ns ? i2 : i1)], lane_off, lane, p0, k0);
-        keys[(size_t)i1 * kPage + lane] = score_key(page_scores<HB>(A, c, p1, k1));
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the unused prefetches settle before exit
-}
-
-// Floor of query b, one workgroup of kFloorThreads: the r-th largest valid
-// sampled key cut to its top 22 bits (first digit by histogram, then the
-// next 11 bits inside that bin), with r five standard deviations above the
-// expected number of sampled scores at or above the query's k-th largest.
+// Sample and floor of query b, one workgroup of kSfThreads per query.
+// 1. Wave w scores the sampled pages w, w + 8, ... (two pages of loads in
+//    flight) and keeps their score keys in LDS.
+// 2. The floor: the r-th largest valid sampled key cut to its top 22 bits
+//    (first digit by histogram, then the next 11 bits inside that bin), with
+//    r five standard deviations above the expected number of sampled scores
+//    at or above the query's k-th largest.
 // Writes the floor (word 2 of the query's counter block; 0 when the query is
 // not sampled or r exceeds its sample, so every score is a candidate) and
 // clears the candidate count (word 1) -- for every query.
-__global__ void __launch_bounds__(kFloorThreads)
-decode_floor_kernel(DecodeArgs a) {
+template <int HB>
+__global__ void __launch_bounds__(kSfThreads)
+decode_sample_floor_kernel(DecodeArgs a) {
+    __shared__ uint32_t skey[kMaxSamplePages * kPage];
     __shared__ uint32_t h[kHistBins];
-    __shared__ uint32_t red[kFloorWaves + 2];
-    constexpr int U = 4;  // keys per thread per histogram round
+    __shared__ uint32_t red[kSfWaves + 2];
     const int b = blockIdx.x, t = threadIdx.x;
+    const int lane = lane_id(), wave = t / kWave;
     uint32_t* ctrl = a.ctrl + (size_t)b * kCtrlStride;
     const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
-    const int ns = sampled_pages(ctx, a.topk);
-    if (ns == 0) {
+    const SamplePlan sp = sample_plan(b, ctx, a.topk);
+    if (sp.ns == 0) {
         if (t == 0) { ctrl[1] = 0u; ctrl[2] = 0u; }
         return;
     }
-    const uint32_t* keys = a.sample_key + (size_t)b * a.sample_stride;
-    const int off = sample_offset(b);
-    const int n_all = ns * kPage;
-    auto valid = [&](int e) { return e < n_all && (off + kSampleStride * (e / kPage)) * kPage + e % kPage < ctx; };
+    if (wave < sp.ns) {
+        const int n = lane & 15, g = lane >> 4;
+        const int32_t* bt = a.block_table + (size_t)b * a.max_pages + sp.off;
+        const uint32_t lane_off = (uint32_t)(n * kD + 32 * g);
+        v8bf A[HB][4];
+        float c[HB][4];
+        load_query<HB>(a, b, n, g, A, c);
+        v4i p0[4][2], p1[4][2];
+        float k0 = 0.f, k1 = 0.f;
+        load_page(a, bt[sp.stride * wave], lane_off, lane, p0, k0);
+        for (int i = wave; i < sp.ns; i += 2 * kSfWaves) {
+            const int i1 = i + kSfWaves;
+            // the next page's loads (again the current one past the end) go
+            // out before this page is scored
+            load_page(a, bt[sp.stride * (i1 < sp.ns ? i1 : i)], lane_off, lane, p1, k1);
+            skey[i * kPage + lane] = score_key(page_scores<HB>(A, c, p0, k0));
+            if (i1 >= sp.ns) break;
+            const int i2 = i1 + kSfWaves;
+            load_page(a, bt[sp.stride * (i2 < sp.ns ? i2 : i1)], lane_off, lane, p0, k0);
+            skey[i1 * kPage + lane] = score_key(page_scores<HB>(A, c, p1, k1));
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the unused prefetches settle
+    }
+    const int n_all = sp.ns * kPage;
+    // sampled entry e is position (off + stride * (e / 64)) * 64 + e % 64;
+    // only the last sampled page can reach past the context
+    auto valid = [&](int e) { return (sp.off + sp.stride * (e / kPage)) * kPage + e % kPage < ctx; };
     // pass over the sample: histogram of digit (key >> shift) & 2047 of the
     // keys whose top bits (key >> 21) equal `sel` (all keys when sel < 0)
     auto pass = [&](int shift, int sel) {
-        for (int i = t; i < kHistBins; i += kFloorThreads) h[i] = 0u;
-        __syncthreads();
-        for (int e0 = 0; e0 < n_all; e0 += U * kFloorThreads) {
-            uint32_t kk[U];
-            bool vv[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int e = e0 + u * kFloorThreads + t;
-                vv[u] = valid(e);
-                kk[u] = vv[u] ? keys[e] : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (vv[u] && (sel < 0 || (int)(kk[u] >> 21) == sel))
-                    atomicAdd(&h[(kk[u] >> shift) & (kHistBins - 1)], 1u);
+        for (int i = t; i < kHistBins; i += kSfThreads) h[i] = 0u;
+        __syncthreads();  // (the first time: also every sampled key is in LDS)
+        for (int e = t; e < n_all; e += kSfThreads) {
+            const uint32_t kk = skey[e];
+            if (valid(e) && (sel < 0 || (int)(kk >> 21) == sel)) atomicAdd(&h[(kk >> shift) & (kHistBins - 1)], 1u);
         }
         __syncthreads();
     };
@@ -506,49 +496,72 @@ decode_scan_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // the final page prefetches (unused) settle before exit
 }
 
-// Repair pass, one workgroup per query: a query whose candidate count fell
-// short of min(k, context) -- its sample floor lay above its k-th largest
-// score -- is rescored in full, every position becoming a candidate.  Plain
-// per-key dot products on the VALU: slow, and reached only by inputs whose
-// sampled pages score unlike the rest of their context.
-__global__ void __launch_bounds__(256)
-decode_repair_kernel(DecodeArgs a, int H) {
-    __shared__ float qs[64 * kD];
-    __shared__ float cs[64];
-    const int b = blockIdx.x;
+// Final kernel, one workgroup per query: verification, repair, selection.
+// A query whose candidate count fell short of min(k, context) -- its sample
+// floor lay above its k-th largest score -- is first rescored in full, every
+// position becoming a candidate (plain per-key dot products on the VALU:
+// slow, and reached only by inputs whose sampled pages score unlike the rest
+// of their context).  Then the exact selection over the candidates.
+template <int HB>
+__global__ void __launch_bounds__(sel::kThreads)
+decode_finish_kernel(DecodeArgs a, SelectArgs sa) {
+    constexpr int H = HB * 16;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    sel::SelShared& sh = *reinterpret_cast<sel::SelShared*>(smem_raw);
+    const int b = blockIdx.x, t = threadIdx.x;
     const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
     uint32_t* cnt = a.ctrl + (size_t)b * kCtrlStride + 1;
     const uint32_t need = (uint32_t)min(a.topk, ctx);
-    if (*cnt >= need) return;
-    const int t = threadIdx.x;
-    for (int i = t; i < H * kD; i += 256)
-        qs[i] = __uint_as_float((uint32_t)a.q[(size_t)b * H * kD + i] << 16);
-    for (int i = t; i < H; i += 256) cs[i] = a.w[(size_t)b * H + i] * a.inv_sqrt_d;
-    __syncthreads();
-    float* out_s = a.cand_score + (size_t)b * a.cand_stride;
-    int32_t* out_p = a.cand_pos + (size_t)b * a.cand_stride;
-    for (int s = t; s < ctx; s += 256) {
-        const int page = a.block_table[(size_t)b * a.max_pages + s / kPage];
-        const uint8_t* row = a.k_cache + ((size_t)page * kPage + (s % kPage)) * kD;
-        float kf[kD];
+    int n_known = (int)*cnt;
+    if ((uint32_t)n_known < need) {
+        // the query and its head coefficients, in the selector's LDS (free until it runs)
+        float* qs = reinterpret_cast<float*>(sh.cand_key);  // [H][kD]
+        float* cs = reinterpret_cast<float*>(sh.cand_pos);  // [H]
+        static_assert(sizeof(sh.cand_key) >= sizeof(float) * H * kD, "query does not fit");
+        for (int i = t; i < H * kD; i += sel::kThreads)
+            qs[i] = __uint_as_float((uint32_t)a.q[(size_t)b * H * kD + i] << 16);
+        for (int i = t; i < H; i += sel::kThreads) cs[i] = a.w[(size_t)b * H + i] * a.inv_sqrt_d;
+        __syncthreads();
+        float* out_s = a.cand_score + (size_t)b * a.cand_stride;
+        int32_t* out_p = a.cand_pos + (size_t)b * a.cand_stride;
+        for (int s = t; s < ctx; s += sel::kThreads) {
+            const int page = a.block_table[(size_t)b * a.max_pages + s / kPage];
+            const uint8_t* row = a.k_cache + ((size_t)page * kPage + (s % kPage)) * kD;
+            uint32_t kw[kD / 4];  // the key row stays packed; each head widens it again
 #pragma unroll
-        for (int d = 0; d < kD; d += 2) {
-            const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)*reinterpret_cast<const uint16_t*>(row + d), false);
-            kf[d] = f[0];
-            kf[d + 1] = f[1];
-        }
-        float acc = 0.f;
-        for (int h = 0; h < H; ++h) {
-            float dot = 0.f;
+            for (int j = 0; j < kD / 16; ++j) {
+                const uint4 v = reinterpret_cast<const uint4*>(row)[j];
+                kw[4 * j] = v.x;
+                kw[4 * j + 1] = v.y;
+                kw[4 * j + 2] = v.z;
+                kw[4 * j + 3] = v.w;
+            }
+            float acc = 0.f;
+#pragma unroll 1
+            for (int h = 0; h < H; ++h) {
+                const float* qh = qs + h * kD;
+                float dot = 0.f;
+#pragma unroll 1
+                for (int j0 = 0; j0 < kD / 4; j0 += 8)  // 32 dimensions per step, to bound the live LDS reads
 #pragma unroll
-            for (int d = 0; d < kD; ++d) dot = fmaf(qs[h * kD + d], kf[d], dot);
-            acc = fmaf(cs[h], fmaxf(dot, 0.f), acc);
+                    for (int j = j0; j < j0 + 8; ++j) {
+                        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)kw[j], false);
+                        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)kw[j], true);
+                        dot = fmaf(qh[4 * j], lo[0], dot);
+                        dot = fmaf(qh[4 * j + 1], lo[1], dot);
+                        dot = fmaf(qh[4 * j + 2], hi[0], dot);
+                        dot = fmaf(qh[4 * j + 3], hi[1], dot);
+                    }
+                acc = fmaf(cs[h], fmaxf(dot, 0.f), acc);
+            }
+            out_s[s] = acc * a.k_scale[(size_t)page * kPage + (s % kPage)];
+            out_p[s] = s;
         }
-        out_s[s] = acc * a.k_scale[(size_t)page * kPage + (s % kPage)];
-        out_p[s] = s;
+        __syncthreads();  // every rescored candidate is written, and the LDS is free again
+        if (t == 0) *cnt = (uint32_t)ctx;
+        n_known = ctx;
     }
-    __syncthreads();
-    if (t == 0) *cnt = (uint32_t)ctx;
+    sel::select_row(sa, b, sh, n_known);
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, size_t n) {
@@ -558,16 +571,11 @@ __global__ void zero_u32_kernel(uint32_t* p, size_t n) {
 
 
 template <int HB>
-hipError_t launch_decode_hb(const DecodeArgs& a_in, int64_t max_pages, hipStream_t stream) {
+hipError_t launch_decode_hb(const DecodeArgs& a_in, const SelectArgs& s, int64_t max_pages, hipStream_t stream) {
     DecodeArgs a = a_in;
-    // about a thousand sample workgroups, at least one per query
-    a.sample_groups = a.B >= 1024 ? 1 : (1024 / a.B > 16 ? 16 : 1024 / a.B);
-    hipLaunchKernelGGL(decode_sample_kernel<HB>, dim3((unsigned)(a.B * a.sample_groups)), dim3(kThreadsDec), 0,
-                       stream, a);
+    hipLaunchKernelGGL(decode_sample_floor_kernel<HB>, dim3((unsigned)a.B), dim3(kSfThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_floor_kernel, dim3((unsigned)a.B), dim3(kFloorThreads), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     // Main scan: one resident round of workgroups (occupancy queried once
     // per process), never more workgroups than pages.
     static int resident = 0;
@@ -584,6 +592,16 @@ hipError_t launch_decode_hb(const DecodeArgs& a_in, int64_t max_pages, hipStream
     if (grid > max_pages) grid = max_pages;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(decode_scan_kernel<HB>, dim3((unsigned)grid), dim3(kThreadsDec), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if ((e = hipFuncSetAttribute((const void*)decode_finish_kernel<HB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)sizeof(sel::SelShared))) != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(decode_finish_kernel<HB>, dim3((unsigned)a.B), dim3(sel::kThreads), sizeof(sel::SelShared),
+                       stream, a, s);
     return hipGetLastError();
 }
 
@@ -597,7 +615,7 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_decode_scan(const DecodeArgs& a, int H, hipStream_t stream) {
+hipError_t launch_decode_scan(const DecodeArgs& a, const SelectArgs& s, int H, hipStream_t stream) {
     hipError_t e;
     if (a.B + 1 > kPrefixLds) {  // the scan's LDS prefix does not fit: build it in global memory
         hipLaunchKernelGGL(decode_prologue_kernel, dim3(1), dim3(1024), 0, stream, a);
@@ -607,14 +625,12 @@ hipError_t launch_decode_scan(const DecodeArgs& a, int H, hipStream_t stream) {
     if (hb < 1 || hb > 4) return hipErrorInvalidValue;
     const int64_t max_pages = (int64_t)a.B * ((a.max_ctx + kPage - 1) / kPage);
     switch (hb) {
-        case 1: e = launch_decode_hb<1>(a, max_pages, stream); break;
-        case 2: e = launch_decode_hb<2>(a, max_pages, stream); break;
-        case 3: e = launch_decode_hb<3>(a, max_pages, stream); break;
-        default: e = launch_decode_hb<4>(a, max_pages, stream); break;
+        case 1: e = launch_decode_hb<1>(a, s, max_pages, stream); break;
+        case 2: e = launch_decode_hb<2>(a, s, max_pages, stream); break;
+        case 3: e = launch_decode_hb<3>(a, s, max_pages, stream); break;
+        default: e = launch_decode_hb<4>(a, s, max_pages, stream); break;
     }
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_repair_kernel, dim3((unsigned)a.B), dim3(256), 0, stream, a, H);
-    return hipGetLastError();
+    return e;
 }
 
 }  // namespace dsaidx

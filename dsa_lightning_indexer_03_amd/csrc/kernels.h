@@ -43,9 +43,6 @@ struct DecodeArgs {
     int topk;
     float inv_sqrt_d;
     uint32_t* ctrl;           // [B][kCtrlStride] per-query words: 1 = candidate count, 2 = floor key
-    uint32_t* sample_key;     // [B][sample_stride] score keys of each query's sampled pages
-    int64_t sample_stride;    // >= 64 * (sampled pages of a query at max_ctx)
-    int sample_groups;        // sample workgroups per query (set by the launcher)
     int32_t* prefix;          // [B+1] exclusive prefix of per-query page counts (large batches only)
     float* cand_score;        // [B][cand_stride] candidate scores
     int32_t* cand_pos;        // [B][cand_stride] candidate positions
@@ -74,7 +71,8 @@ struct PrefillArgs {
 size_t topk_select_smem_bytes();
 hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
-hipError_t launch_decode_scan(const DecodeArgs& a, int H, hipStream_t stream);
+// sample and floor, main scan, then verification + repair + selection (s)
+hipError_t launch_decode_scan(const DecodeArgs& a, const SelectArgs& s, int H, hipStream_t stream);
 hipError_t launch_prefill_scores_generic(const PrefillArgs& a, int dtype, float* out, hipStream_t stream);
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream);
 size_t prefill_fused_workspace_bytes(int B, int L, int dtype);

@@ -102,9 +102,8 @@ def test_decode_rejects_before_launch(lib, kw, status):
 
 def test_decode_workspace_query(lib):
     n = lib.indexer_decode_paged_workspace_bytes(64, 131072, 64, 128, 2048)
-    # candidate scores + positions, per-query counters, sampled keys (one
-    # page in 32 of the 2048 pages), page prefix
-    assert n == 64 * 131072 * 8 + 64 * 64 * 4 + 64 * (2048 // 32) * 64 * 4 + 65 * 4
+    # candidate scores + positions, per-query counters, page prefix
+    assert n == 64 * 131072 * 8 + 64 * 64 * 4 + 65 * 4
 
 
 @pytest.mark.parametrize("args,status", [

@@ -150,15 +150,17 @@ def test_many_queries_short_contexts():
     parity(d, 128, "many", queries=range(0, 300, 7))
 
 
-def sampled_logical_pages(b, ctx, K, page=64, stride=32):
+def sampled_logical_pages(b, ctx, K, page=64, stride=32, max_pages=32):
     """Logical pages the decode scan scores first, to set a query's candidate
-    floor: one page in `stride` from a per-query offset (a multiplicative
-    hash of the query index), for queries with ctx >= 4k spanning at least
-    two strides of pages."""
+    floor: one page in `stride` (sparser when that would exceed `max_pages`
+    pages) from a per-query offset (a multiplicative hash of the query index
+    scaled to the stride), for queries with ctx >= 4k spanning at least two
+    strides of pages."""
     npg = -(-ctx // page)
+    stride = max(stride, -(-npg // max_pages))
     if ctx < 4 * K or npg < 2 * stride:
         return []
-    off = ((b * 0x9E3779B1) & 0xFFFFFFFF) >> 27
+    off = (((b * 0x9E3779B1) & 0xFFFFFFFF) * stride) >> 32
     return [off + stride * i for i in range((npg - stride) // stride + 1)]
 
 
