@@ -248,7 +248,8 @@ __device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint3
 
 // Sample and floor of query b, one workgroup of kSfThreads per query.
 // 1. Wave w scores the sampled pages w, w + 8, ... (two pages of loads in
-//    flight) and keeps their score keys in LDS.
+//    flight, page ids preloaded one per lane) and keeps their score keys in
+//    LDS.
 // 2. The floor: the r-th largest valid sampled key cut to its top 22 bits
 //    (first digit by histogram, then the next 11 bits inside that bin), with
 //    r five standard deviations above the expected number of sampled scores
@@ -266,31 +267,39 @@ decode_sample_floor_kernel(DecodeArgs a) {
     const int lane = lane_id(), wave = t / kWave;
     uint32_t* ctrl = a.ctrl + (size_t)b * kCtrlStride;
     const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
+    // the query operands do not depend on the context: their loads go first
+    const int n = lane & 15, g = lane >> 4;
+    v8bf A[HB][4];
+    float c[HB][4];
+    load_query<HB>(a, b, n, g, A, c);
     const SamplePlan sp = sample_plan(b, ctx, a.topk);
     if (sp.ns == 0) {
         if (t == 0) { ctrl[1] = 0u; ctrl[2] = 0u; }
         return;
     }
     if (wave < sp.ns) {
-        const int n = lane & 15, g = lane >> 4;
-        const int32_t* bt = a.block_table + (size_t)b * a.max_pages + sp.off;
+        // wave w scores the sampled pages w + 8 j, j < npw; their page ids
+        // sit one per lane (lane j), so no page load waits on a table read
+        constexpr int kPerWave = (kMaxSamplePages + kSfWaves - 1) / kSfWaves;
+        static_assert(kPerWave <= kWave, "page ids must fit one per lane");
+        const int npw = (sp.ns - wave + kSfWaves - 1) / kSfWaves;
+        const int mine = wave + kSfWaves * lane;
+        const int pid = (lane < kPerWave && mine < sp.ns)
+                            ? a.block_table[(size_t)b * a.max_pages + sp.off + (size_t)sp.stride * mine] : 0;
         const uint32_t lane_off = (uint32_t)(n * kD + 32 * g);
-        v8bf A[HB][4];
-        float c[HB][4];
-        load_query<HB>(a, b, n, g, A, c);
         v4i p0[4][2], p1[4][2];
         float k0 = 0.f, k1 = 0.f;
-        load_page(a, bt[sp.stride * wave], lane_off, lane, p0, k0);
-        for (int i = wave; i < sp.ns; i += 2 * kSfWaves) {
-            const int i1 = i + kSfWaves;
+        load_page(a, __builtin_amdgcn_readlane(pid, 0), lane_off, lane, p0, k0);
+        for (int j = 0; j < npw; j += 2) {
             // the next page's loads (again the current one past the end) go
             // out before this page is scored
-            load_page(a, bt[sp.stride * (i1 < sp.ns ? i1 : i)], lane_off, lane, p1, k1);
-            skey[i * kPage + lane] = score_key(page_scores<HB>(A, c, p0, k0));
-            if (i1 >= sp.ns) break;
-            const int i2 = i1 + kSfWaves;
-            load_page(a, bt[sp.stride * (i2 < sp.ns ? i2 : i1)], lane_off, lane, p0, k0);
-            skey[i1 * kPage + lane] = score_key(page_scores<HB>(A, c, p1, k1));
+            const int j1 = j + 1 < npw ? j + 1 : j;
+            load_page(a, __builtin_amdgcn_readlane(pid, j1), lane_off, lane, p1, k1);
+            skey[(wave + kSfWaves * j) * kPage + lane] = score_key(page_scores<HB>(A, c, p0, k0));
+            if (j + 1 >= npw) break;
+            const int j2 = j + 2 < npw ? j + 2 : j + 1;
+            load_page(a, __builtin_amdgcn_readlane(pid, j2), lane_off, lane, p0, k0);
+            skey[(wave + kSfWaves * (j + 1)) * kPage + lane] = score_key(page_scores<HB>(A, c, p1, k1));
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the unused prefetches settle
     }
