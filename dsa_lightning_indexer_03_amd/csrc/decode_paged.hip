@@ -247,9 +247,9 @@ __device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint3
 }
 
 // Sample and floor of query b, one workgroup of kSfThreads per query.
-// 1. Wave w scores the sampled pages w, w + 8, ... (two pages of loads in
-//    flight, page ids preloaded one per lane) and keeps their score keys in
-//    LDS.
+// 1. The query is staged in LDS; wave w scores the sampled pages w, w + 8,
+//    ... (two pages of loads in flight, page ids preloaded one per lane) and
+//    keeps their score keys in LDS.
 // 2. The floor: the r-th largest valid sampled key cut to its top 22 bits
 //    (first digit by histogram, then the next 11 bits inside that bin), with
 //    r five standard deviations above the expected number of sampled scores
@@ -262,44 +262,77 @@ __global__ void __launch_bounds__(kSfThreads)
 decode_sample_floor_kernel(DecodeArgs a) {
     __shared__ uint32_t skey[kMaxSamplePages * kPage];
     __shared__ uint32_t h[kHistBins];
+    __shared__ __align__(16) uint16_t qsh[64 * kD];
+    __shared__ float csh[64];
     __shared__ uint32_t red[kSfWaves + 2];
     const int b = blockIdx.x, t = threadIdx.x;
     const int lane = lane_id(), wave = t / kWave;
     uint32_t* ctrl = a.ctrl + (size_t)b * kCtrlStride;
     const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
-    // the query operands do not depend on the context: their loads go first
-    const int n = lane & 15, g = lane >> 4;
-    v8bf A[HB][4];
-    float c[HB][4];
-    load_query<HB>(a, b, n, g, A, c);
+    // The query goes to LDS once per workgroup, with coalesced 16-byte
+    // loads issued before anything that depends on the context.  Row r's
+    // 16-byte pieces are stored XOR-swizzled by r & 15, so the operand reads
+    // below (16 rows, one piece column) touch distinct banks.
+    constexpr int H = 16 * HB;
+    constexpr int kQPieces = H * kD * 2 / 16;
+    constexpr int kQPer = (kQPieces + kSfThreads - 1) / kSfThreads;
+    v4i qv[kQPer];
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i)
+        if (t + i * kSfThreads < kQPieces)
+            qv[i] = reinterpret_cast<const v4i*>(a.q + (size_t)b * H * kD)[t + i * kSfThreads];
+    const float wv = t < H ? a.w[(size_t)b * H + t] * a.inv_sqrt_d : 0.f;
     const SamplePlan sp = sample_plan(b, ctx, a.topk);
     if (sp.ns == 0) {
         if (t == 0) { ctrl[1] = 0u; ctrl[2] = 0u; }
         return;
     }
-    if (wave < sp.ns) {
-        // wave w scores the sampled pages w + 8 j, j < npw; their page ids
-        // sit one per lane (lane j), so no page load waits on a table read
-        constexpr int kPerWave = (kMaxSamplePages + kSfWaves - 1) / kSfWaves;
-        static_assert(kPerWave <= kWave, "page ids must fit one per lane");
-        const int npw = (sp.ns - wave + kSfWaves - 1) / kSfWaves;
-        const int mine = wave + kSfWaves * lane;
-        const int pid = (lane < kPerWave && mine < sp.ns)
-                            ? a.block_table[(size_t)b * a.max_pages + sp.off + (size_t)sp.stride * mine] : 0;
-        const uint32_t lane_off = (uint32_t)(n * kD + 32 * g);
-        v4i p0[4][2], p1[4][2];
-        float k0 = 0.f, k1 = 0.f;
-        load_page(a, __builtin_amdgcn_readlane(pid, 0), lane_off, lane, p0, k0);
-        for (int j = 0; j < npw; j += 2) {
-            // the next page's loads (again the current one past the end) go
-            // out before this page is scored
-            const int j1 = j + 1 < npw ? j + 1 : j;
-            load_page(a, __builtin_amdgcn_readlane(pid, j1), lane_off, lane, p1, k1);
+    // wave w scores the sampled pages w + 8 j, j < npw; their page ids sit
+    // one per lane (lane j), so no page load waits on a table read
+    constexpr int kPerWave = (kMaxSamplePages + kSfWaves - 1) / kSfWaves;
+    static_assert(kPerWave <= kWave, "page ids must fit one per lane");
+    const int npw = wave < sp.ns ? (sp.ns - wave + kSfWaves - 1) / kSfWaves : 0;
+    const int mine = wave + kSfWaves * lane;
+    const int pid = (lane < kPerWave && mine < sp.ns)
+                        ? a.block_table[(size_t)b * a.max_pages + sp.off + (size_t)sp.stride * mine] : 0;
+    const int n = lane & 15, g = lane >> 4;
+    const uint32_t lane_off = (uint32_t)(n * kD + 32 * g);
+    v4i p0[4][2], p1[4][2];
+    float k0 = 0.f, k1 = 0.f;
+    auto page_at = [&](int j) { return __builtin_amdgcn_readlane(pid, j < npw - 1 ? j : npw - 1); };
+    if (npw > 0) {  // the first two pages' loads go out before the barrier
+        load_page(a, page_at(0), lane_off, lane, p0, k0);
+        load_page(a, page_at(1), lane_off, lane, p1, k1);
+    }
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) {
+        const int pc = t + i * kSfThreads;
+        if (pc < kQPieces) reinterpret_cast<v4i*>(qsh)[(pc & ~15) | ((pc ^ (pc >> 4)) & 15)] = qv[i];
+    }
+    if (t < H) csh[t] = wv;
+    // LDS-only fences: the barrier does not wait for the page loads in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (npw > 0) {
+        v8bf A[HB][4];
+        float c[HB][4];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            const int r = 16 * hb + n;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                A[hb][j] = reinterpret_cast<const v8bf*>(qsh)[r * 16 + ((4 * g + j) ^ (r & 15))];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c[hb][i] = csh[16 * hb + 4 * g + i];
+        }
+        for (int j = 0;; j += 2) {
             skey[(wave + kSfWaves * j) * kPage + lane] = score_key(page_scores<HB>(A, c, p0, k0));
             if (j + 1 >= npw) break;
-            const int j2 = j + 2 < npw ? j + 2 : j + 1;
-            load_page(a, __builtin_amdgcn_readlane(pid, j2), lane_off, lane, p0, k0);
+            load_page(a, page_at(j + 2), lane_off, lane, p0, k0);  // (again the last page past the end)
             skey[(wave + kSfWaves * (j + 1)) * kPage + lane] = score_key(page_scores<HB>(A, c, p1, k1));
+            if (j + 2 >= npw) break;
+            load_page(a, page_at(j + 3), lane_off, lane, p1, k1);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the unused prefetches settle
     }
