@@ -38,15 +38,15 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # the value it was taken at; otherwise traffic is reported as null.
 COPY_FETCH_FACTOR = 1048576.0 / 524315.0
 COPY_WRITE_FACTOR = 1048576.0 / 1048576.0
-_DECODE_SRC = ["csrc/decode_paged.hip", "csrc/common.h", "csrc/kernels.h", "build.py"]
-_DECODE_SHA = "35028db8e337541b4e4f8c49ce28f58de1d7802694c6ca0473df069fb8865502"
+_DECODE_SRC = ["csrc/decode_paged.hip", "csrc/select_row.h", "csrc/common.h", "csrc/kernels.h", "build.py"]
+_DECODE_SHA = "807df5c635b8dcecab3b8a255edae03b17ef1091b8617f997bea204f4a794e22"
 COUNTERS = {
     "prefill": {"sources": ["csrc/prefill_fused.hip", "csrc/common.h", "csrc/kernels.h", "build.py"],
-                "sha256": "e743839d04e2ecd89759215fbfa43949b823b55c674906d64f7cd19ff235434d",
-                "fetch_kib": 255308.1, "write_kib": 524331.9},
-    # main scan of one decode call (the sample kernel reads about 1/20 of it)
-    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 546155.8, "write_kib": 1940.6},
-    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 556951.6, "write_kib": 3871.8},
+                "sha256": "22ad21f8ee25b26cbaf594888e7a1c81ac34c83d741171388f713e032d672ffb",
+                "fetch_kib": 255329.7, "write_kib": 524343.1},
+    # main scan of one decode call (the sample kernel reads about 1/60 of it)
+    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 546182.6, "write_kib": 2377.7},
+    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 556966.1, "write_kib": 4106.6},
 }
 
 
@@ -61,22 +61,31 @@ def up(torch, a, dev):
     return torch.from_numpy(a).to(dev)
 
 
-def time_calls(torch, fn, steps, warmup):
-    """Runs fn warmup times, then `steps` times with a HIP event pair around
-    each call on the current stream (the stream the library launches on).
-    Returns per-call milliseconds and the wall time of the timed region."""
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+def time_calls(torch, fn, steps, warmup, warm_seconds=0.2):
+    """Runs fn at least `warmup` times and for at least `warm_seconds` (after
+    the host-side input generation the GPU needs a few hundred calls of a
+    short op to reach its steady clocks), then exactly `steps` times back to
+    back between one pair of HIP events on the current stream (the stream
+    the library launches on), with a device synchronisation on both sides.
+    Returns the mean milliseconds per call and the wall time of the timed
+    region."""
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record()
+    done = 0
+    while done < warmup or time.perf_counter() - t0 < warm_seconds:
         fn()
-        b.record()
+        done += 1
+        if done % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return [a.elapsed_time(b) for a, b in evs], wall
+    return a.elapsed_time(b) / steps, wall
 
 
 def measured_traffic(name):
@@ -180,12 +189,11 @@ def main():
         def step():
             out["r"] = dsa.indexer_prefill(q, k, w, K, q_scale=qs, k_scale=ks)
 
-        ms, wall = time_calls(torch, step, args.steps, args.warmup)
+        ms_avg, wall = time_calls(torch, step, args.steps, args.warmup)
         pairs = L * (L + 1) // 2
-        ms_avg = float(np.mean(ms))
         flops = 2.0 * H * D * pairs
         achieved = flops / (ms_avg * 1e-3) / 1e12
-        log(f"prefill: {ms_avg:.3f} ms/step (min {min(ms):.3f}), {pairs / (ms_avg * 1e-3):.4g} pairs/s, "
+        log(f"prefill: {ms_avg:.3f} ms/step, {pairs / (ms_avg * 1e-3):.4g} pairs/s, "
             f"{achieved:.1f} TFLOP/s")
 
         gpu_idx = out["r"][0].cpu().numpy()[0]
@@ -240,14 +248,14 @@ def main():
             def dstep():
                 dsa.indexer_decode_paged(*args_d, c["topk"], max_context_len=mcl, workspace=ws)
 
-            dms, _ = time_calls(torch, dstep, max(args.steps, 10), args.warmup)
+            dms, _ = time_calls(torch, dstep, max(args.steps, 20), args.warmup)
             nbytes = int(d["context_lens"].astype(np.int64).sum()) * (c["D"] + 4)
-            gbs = nbytes / (np.mean(dms) * 1e-3) / 1e9
-            log(f"decode {n}: {np.mean(dms) * 1e3:.1f} us/call, {gbs:.0f} GB/s")
+            gbs = nbytes / (dms * 1e-3) / 1e9
+            log(f"decode {n}: {dms * 1e3:.1f} us/call, {gbs:.0f} GB/s")
             dec[f"workload_{n}"] = {
                 "what": ("64 queries x 131072-token contiguous fp8 cache" if n == 4 else
                          "128 queries, ctx ~ U[4096,131072], 64-token pages scattered by a seeded permutation"),
-                "kcache_bytes": nbytes, "us_per_call": float(np.mean(dms) * 1e3), "GB/s": gbs,
+                "kcache_bytes": nbytes, "us_per_call": float(dms * 1e3), "GB/s": gbs,
                 "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "topk": c["topk"],
                 "scan_traffic_bytes": measured_traffic(f"decode_scan_w{n}"),
             }
@@ -267,12 +275,11 @@ def main():
             def pstep():
                 dsa.indexer_prefill(qn, kn, wn, c["topk"], want_scores=want)
 
-            pms, _ = time_calls(torch, pstep, max(args.steps, 10), args.warmup)
+            ms_n, _ = time_calls(torch, pstep, max(args.steps, 10), args.warmup)
             pairs_n = c["L"] * (c["L"] + 1) // 2
-            ms_n = float(np.mean(pms))
             rec = {"what": f"prefill B=1 L={c['L']} H={c['H']} D={c['D']} k={c['topk']} {c['dtype']}"
                            + (" (full score matrix returned)" if want else ", fused"),
-                   "ms_per_call": ms_n, "ms_min": float(min(pms)), "pairs_per_s": pairs_n / (ms_n * 1e-3)}
+                   "ms_per_call": ms_n, "pairs_per_s": pairs_n / (ms_n * 1e-3)}
             if n == 2:
                 tf = 2.0 * c["H"] * c["D"] * pairs_n / (ms_n * 1e-3) / 1e12
                 rec.update({"TFLOP/s": tf, "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS})
