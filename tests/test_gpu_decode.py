@@ -164,23 +164,26 @@ def sampled_logical_pages(b, ctx, K, page=64, stride=32, max_pages=32):
     return [off + stride * i for i in range((npg - stride) // stride + 1)]
 
 
-def test_floor_overshoot_is_repaired():
+@pytest.mark.parametrize("ctx,K,seed", [([9000, 5000, 300], 512, 570),
+                                         # strides 35 and 64: contexts beyond 1024 pages sample sparser
+                                         ([70000, 131072, 5000], 2048, 572)])
+def test_floor_overshoot_is_repaired(ctx, K, seed):
     """Key scales of the sampled pages raised 50x: the floor taken from the
     sample lies far above each query's k-th largest score, fewer than k
     scores reach it, and the query is rescored in full.  The result still
     matches the oracle, and the query's candidate count (word 1 of its
     counter block in the workspace) equals its context."""
-    K = 512
-    ctx = [9000, 5000, 300]
-    d = synth.decode_inputs(3, ctx, 64, 128, seed=570, permute=True)
+    B = len(ctx)
+    d = synth.decode_inputs(B, ctx, 64, 128, seed=seed, permute=True)
     hot = 0
-    for b in range(3):
+    for b in range(B):
         for j in sampled_logical_pages(b, ctx[b], K):
             d["k_scale"][d["block_table"][b, j]] *= 50.0
             hot += 1
     assert hot > 0
-    B, mcl = 3, 9000
+    mcl = max(ctx)
     stride = -(-mcl // 64) * 64
+    say(f"decode overshoot: ctx={ctx} K={K} hot pages={hot}")
     ws = torch.zeros(dsa.decode_workspace_bytes(B, mcl, 64, 128, K), dtype=torch.uint8, device="cuda")
     gi, gv = dsa.indexer_decode_paged(dev(d["q"]), dev(d["w"]), dev(d["k_cache"]), dev(d["k_scale"]),
                                       dev(d["block_table"]), dev(d["context_lens"]), K,
@@ -192,7 +195,9 @@ def test_floor_overshoot_is_repaired():
         check_topk_rows(gi[b:b + 1], gv[b:b + 1], o[None], [o.size], K, where=f"overshoot q{b}")
     ctrl = host(ws[B * stride * 8:B * stride * 8 + B * 64 * 4]).view(np.uint32).reshape(B, 64)
     say(f"  candidate counts {ctrl[:, 1].tolist()}")
-    assert ctrl[0, 1] == ctx[0] and ctrl[1, 1] == ctx[1] and ctrl[2, 1] == ctx[2]
+    for b in range(B):
+        if sampled_logical_pages(b, ctx[b], K):
+            assert ctrl[b, 1] == ctx[b]
 
 
 def test_constant_scores_long_context():
