@@ -16,12 +16,15 @@ When n_valid <= k the set must be all valid positions.
 
 Signed head weights: every rule above takes, where given, the magnitude sum
 M = sum_h |w_h * q_scale_h| * ReLU(q_h . k / sqrt(D)) of each score into its
-tolerance, max(1e-4, 1e-3 |o|, 1e-3 M), and a swap at the cut is allowed
-when the two scores lie within their summed tolerances of tau.  M is the
-score itself when the weights are non-negative (then nothing changes); with
-mixed signs a score can cancel far below M, and the rounding of the head
-terms of any floating-point evaluation is bounded relative to M, not to the
-cancelled result.
+tolerance tol = max(1e-4, 1e-3 |o|, 1e-3 M).  M is the score itself when the
+weights are non-negative (then nothing changes); with mixed signs a score
+can cancel far below M, and the rounding of the head terms of any
+floating-point evaluation is bounded relative to M, not to the cancelled
+result.  Tolerances then differ from position to position, so rule (iii)
+reads per position: the returned set must be the top m of some score vector
+within each position's tolerance of the oracle's, i.e. the lowest o + tol
+over the returned positions is at least the highest o - tol over the
+others.
 """
 from __future__ import annotations
 
@@ -84,9 +87,15 @@ def check_topk_row(g_idx, g_val, o_row, n_valid: int, K: int, where: str = "", m
         tol = max(ABS_TOL, REL_TOL * abs(tau))
         far = diff[np.abs(o_row[diff] - tau) > tol]
     else:
-        mr = np.asarray(mag_row, np.float64)
-        tol = score_tol(o_row[diff], mr[diff]) + float(score_tol(tau, mr[O[-1]]))
-        far = diff[np.abs(o_row[diff] - tau) > tol]
+        # per-position tolerances: some scores within them must rank the
+        # returned set first
+        ov = o_row[:n_valid]
+        tv = score_tol(ov, np.asarray(mag_row, np.float64)[:n_valid])
+        sel = np.zeros(n_valid, bool)
+        sel[head] = True
+        lo_in = np.min(ov[sel] + tv[sel])
+        hi_out = np.max(ov[~sel] - tv[~sel])
+        far = diff[(sel[diff] & (ov[diff] + tv[diff] < hi_out)) | (~sel[diff] & (ov[diff] - tv[diff] > lo_in))]
     if far.size:
         raise AssertionError(f"{where}: {far.size} positions differ from the oracle's set beyond the tie "
                              f"tolerance; e.g. s={far[0]} score={o_row[far[0]]!r} tau={tau!r}")

@@ -34,3 +34,19 @@ def test_score_rule():
         check_scores(np.array([1.002]), np.array([1.0]))
     with pytest.raises(AssertionError):
         check_scores(np.array([0.0]), np.array([-np.inf]))
+
+
+def test_signed_weights_swap_uses_each_positions_tolerance():
+    """With magnitude sums given, a position whose tolerance is wide (large
+    M) may fall below a precisely scored one; the returned set is accepted
+    iff some scores within each position's own tolerance rank it first."""
+    o = np.array([1.0, 0.00424, 0.00405, 0.00318, 0.001])
+    wide = np.array([1.0, 14.4, 0.004, 0.0154, 0.001])   # position 1: tol 0.0144
+    check_topk_row([0, 2, 3], None, o, 5, 3, mag_row=wide)
+    narrow = np.array([1.0, 0.004, 0.004, 0.0154, 0.001])  # every tol 1e-4
+    with pytest.raises(AssertionError):
+        check_topk_row([0, 2, 3], None, o, 5, 3, mag_row=narrow)
+    # a wide tolerance elsewhere does not excuse a returned position far
+    # below a precisely scored one that was left out
+    with pytest.raises(AssertionError):
+        check_topk_row([0, 1, 4], None, o, 5, 3, mag_row=wide)
