@@ -57,6 +57,9 @@ constexpr int kD = 128;
 #ifndef DSAIDX_PREFILL_STAGED
 #define DSAIDX_PREFILL_STAGED 1  // fp8 with L <= 65536: stage keys through LDS
 #endif
+#ifndef DSAIDX_PREFILL_STAGED_BF16
+#define DSAIDX_PREFILL_STAGED_BF16 1  // bf16 with L <= 65536: stage keys through LDS
+#endif
 constexpr int kPrefetch = DSAIDX_PREFILL_DEPTH >= 2 ? 2 : 1;
 
 template <bool POS16>
@@ -1178,7 +1181,446 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     wave_emit(rb, nb, K, a.idx_out + row_t * K, a.val_out ? a.val_out + row_t * K : nullptr);
 }
 
+// ---------------------------------------------------------------------------
+// bf16, L <= 65536: keys staged through LDS, head sums on the matrix cores.
+//
+// The scheme of the fp8 kernel above, with what bf16 changes:
+// * A key pre-pass writes every key times 2^-Pk (exact: a power of two) to
+//   the workspace, with 2^Pk as its adjusted scale, and each query head's A
+//   rows are scaled by its own 2^-Pq_h in registers (2^Pq_h goes into the
+//   head's weight).  So again every S_h lies in [-1, 1], the clamped f16
+//   conversion is the ReLU and the head sum is an f16 MFMA.
+// * A 64-key chunk is 16 KB.  Two stages and 2304-entry candidate buffers
+//   fit the LDS beside the eight rows.  One barrier per chunk, at its end: it
+//   certifies that the next chunk has landed and that every wave is done
+//   with this one, whose slot then receives the chunk after next.
+// * A chunk runs as four regions, one 16-key subtile each: its 16 score
+//   MFMAs (4 k-steps of 16x16x32 bf16 per head block), the head sums of the
+//   previous subtile and a share of the previous chunk's appends, while the
+//   next subtile's B operands are read from LDS.
+// * A compaction request made before the barrier is read right after it and
+//   acted on in the same iteration, so the buffer needs one chunk of slack.
+// ---------------------------------------------------------------------------
+constexpr int kBfWaves = 8;
+constexpr int kBfCap = 2304;
+constexpr int kBfStages = 2;
+constexpr size_t kBfWaveBytes = (size_t)(kBfCap + kWave) * 6 + 256 * 4;
+constexpr size_t kBfStageKeyBytes = 64 * kD * 2;
+constexpr size_t kBfStageScaleOff = kBfStageKeyBytes;
+constexpr size_t kBfStageBytes = kBfStageKeyBytes + 64 * 4;
+static_assert(kBfStages * kBfStageBytes + kBfWaves * kBfWaveBytes + 16 <= 160 * 1024, "LDS budget");
+
+// bf16 key pre-pass: for key s of sequence b (positions up to the 64-padded
+// length; rows past the end repeat row L-1): 2^Pk > max_d |k_d| (Pk = 0 for
+// a zero row), the key times 2^-Pk to kscaled and 2^Pk to ks_adj.
+__global__ void __launch_bounds__(256)
+prefill_key_prep_bf16_kernel(PrefillArgs a, uint16_t* kscaled) {
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int Lp = a.Lpad;
+    if (gi >= (int64_t)a.B * Lp) return;
+    const int b = (int)(gi / Lp), s = (int)(gi % Lp);
+    const int sr = s < a.L ? s : a.L - 1;
+    const v4i* row = reinterpret_cast<const v4i*>(reinterpret_cast<const uint16_t*>(a.k) + ((size_t)b * a.L + sr) * kD);
+    v4i v[kD / 8];
+    uint32_t mx = 0;  // largest magnitude bit pattern: bf16 magnitudes order like their bits
+#pragma unroll
+    for (int c = 0; c < kD / 8; ++c) {
+        v[c] = row[c];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t x = (uint32_t)v[c][d] & 0x7FFF7FFFu;
+            mx = max(mx, max(x & 0xFFFFu, x >> 16));
+        }
+    }
+    const float vmax = __uint_as_float(mx << 16);
+    const int pk = vmax > 0.f ? __builtin_amdgcn_frexp_expf(vmax) : 0;  // 2^pk > vmax
+    a.ks_adj[gi] = ldexpf(1.0f, pk);
+    v4i* dst = reinterpret_cast<v4i*>(kscaled + (size_t)gi * kD);
+#pragma unroll
+    for (int c = 0; c < kD / 8; ++c) {
+        v4i o;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t x = (uint32_t)v[c][d];
+            const uint32_t lo = __float_as_uint(ldexpf(__uint_as_float(x << 16), -pk)) >> 16;
+            const uint32_t hi = __float_as_uint(ldexpf(__uint_as_float(x & 0xFFFF0000u), -pk)) >> 16;
+            o[d] = (int)(lo | (hi << 16));
+        }
+        dst[c] = o;
+    }
+}
+
+template <int HB>
+__global__ void __launch_bounds__(kBfWaves * kWave)
+prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    __shared__ uint32_t flags[4];  // [0..2] compaction requests, [3] rescan request
+    using Pos = uint16_t;
+    constexpr int W = kBfWaves;
+    constexpr int CAP = kBfCap;
+    constexpr int H = 16 * HB;
+    constexpr int NX = (HB + 1) / 2;
+    const int L = a.L;
+    const int nblk = (L + W - 1) / W;
+    const int b = blockIdx.x % a.B;
+    const int blk = nblk - 1 - (int)(blockIdx.x / a.B);  // heaviest first
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int t_raw = blk * W + wave;
+    const bool live = t_raw < L;        // waves past the end only help stage keys
+    const int t = live ? t_raw : L - 1;
+    const int lane = lane_id();
+    const int n = lane & 15, g = lane >> 4;
+
+    RowBuf<Pos> rb;
+    unsigned char* wbase = smem_raw + kBfStages * kBfStageBytes + wave * kBfWaveBytes;
+    rb.key = reinterpret_cast<uint32_t*>(wbase);
+    rb.hist = reinterpret_cast<uint32_t*>(wbase + (size_t)(CAP + kWave) * 4);
+    rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)(CAP + kWave) * 4 + 256 * 4);
+
+    const size_t row_t = (size_t)b * L + t;
+    // Query: lane (m, g) holds, for k-step j, q[t][16hb+m][32g+8j .. +8].
+    // Each head h gets its own exponent, 2^Pq_h >= |q_h|_1, its operand rows
+    // are scaled by 2^-Pq_h (exact) and 2^Pq_h moves into its weight: every
+    // S_h then lies in [-1, 1] at its own scale, so the f16 conversion keeps
+    // its relative precision however far the heads' magnitudes spread (the
+    // weights, f16 normals over 29 binades, carry the spread instead).
+    v4i Aw[HB][4];
+    {
+        const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + row_t * H * kD;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Aw[hb][j] = *reinterpret_cast<const v4i*>(qrow + (16 * hb + n) * kD + 32 * g + 8 * j);
+    }
+    v8h Wh[4][NX];
+    float Fscale;  // 2^-E
+    {
+        int Pqh[HB];  // exponent of this lane's head 16hb + n
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            float sabs = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t x = (uint32_t)Aw[hb][j][d] & 0x7FFF7FFFu;
+                    sabs += __uint_as_float(x << 16) + __uint_as_float(x & 0xFFFF0000u);
+                }
+            sabs += __shfl_xor(sabs, 16, kWave);
+            sabs += __shfl_xor(sabs, 32, kWave);
+            Pqh[hb] = sabs > 0.f ? __builtin_amdgcn_frexp_expf(sabs) : 0;  // 2^Pq_h > |q_h|_1
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t x = (uint32_t)Aw[hb][j][d];
+                    const uint32_t lo = __float_as_uint(ldexpf(__uint_as_float(x << 16), -Pqh[hb])) >> 16;
+                    const uint32_t hi = __float_as_uint(ldexpf(__uint_as_float(x & 0xFFFF0000u), -Pqh[hb])) >> 16;
+                    Aw[hb][j][d] = (int)(lo | (hi << 16));
+                }
+        }
+        // head weights c_h 2^Pq_h (no query scales here); lane (m, g) of the
+        // weight operand needs heads 16hb + 4g + i, whose exponents sit in
+        // lane 4g + i
+        float cf[HB][4];
+        float mx = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ph = __shfl(Pqh[hb], 4 * g + i, kWave);
+                cf[hb][i] = ldexpf(a.w[row_t * H + 16 * hb + 4 * g + i] * a.inv_sqrt_d, ph);
+                mx = fmaxf(mx, fabsf(cf[hb][i]));
+            }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
+        int E = mx > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
+        E = E < -100 ? -100 : (E > 100 ? 100 : E);
+        Fscale = ldexpf(1.0f, -E);
+        const int own_st = n >> 2;
+#pragma unroll
+        for (int x = 0; x < NX; ++x) {
+            v8h wv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int hb = 2 * x + (j >> 2);
+                wv[j] = hb < HB ? (_Float16)ldexpf(cf[hb < HB ? hb : 0][j & 3], E) : (_Float16)0.f;
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st) Wh[st][x] = st == own_st ? wv : v8h{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+
+    const uint16_t* kbase = kscaled + (size_t)b * a.Lpad * kD;
+    const float* ksadj = a.ks_adj + (size_t)b * a.Lpad;
+    float* srow = (a.scores && live) ? a.scores + row_t * L : nullptr;
+    const int last = (min(blk * W + W - 1, L - 1)) / 64;   // same for every wave of the block
+
+    // Chunk order, sample and speculative floor: as in the fp8 kernel.
+    const int S = last + 1 >= 32 ? (last + 1) / 16 : 0;
+    auto chunk_next = [&](int i, int prev) -> int {
+        if (i > last) return prev;
+        if (i < S) return 16 * i + 15;
+        if (i == S) return 0;
+        int c = prev + 1;
+        if ((c & 15) == 15 && c < 16 * S) ++c;
+        return c;
+    };
+    const int chunk0 = S > 0 ? 15 : 0;
+
+    // Stage slot i % 2 receives the i-th chunk of the order: thread x of the
+    // block copies two 16-byte pieces (LDS piece p = x + 512c holds, in row
+    // p/16, the global piece (p%16) ^ (row & 15)); wave 0 also copies the
+    // chunk's 64 adjusted key scales.  The padded rows exist in the scaled
+    // copy, so no clamping is needed.
+    auto stage_chunk = [&](int slot, int chunk) {
+        unsigned char* dst = smem_raw + slot * kBfStageBytes;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int p = (int)threadIdx.x + 512 * c;
+            const int r = p >> 4;
+            const uint16_t* src = kbase + (size_t)(chunk * 64 + r) * kD + 8 * ((p & 15) ^ (r & 15));
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 1024 * wave + 8192 * c),
+                                             16, 0, 0);
+        }
+        if (wave == 0)
+            __builtin_amdgcn_global_load_lds(ksadj + chunk * 64 + lane,
+                                             (__attribute__((address_space(3))) void*)(dst + kBfStageScaleOff), 4, 0, 0);
+    };
+    // B operands of subtile st: k-step j = the 8 dims [32g + 8j, +8) of key
+    // row 16st + n, stored at piece (4g + j) ^ n of that row.
+    auto load_bsub = [&](int slot, int st, v8bf (&B_)[4]) {
+        const unsigned char* cur = smem_raw + slot * kBfStageBytes + (16 * st + n) * (kD * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) B_[j] = *reinterpret_cast<const v8bf*>(cur + 16 * ((4 * g + j) ^ n));
+    };
+    auto load_ks = [&](int slot) {
+        return *reinterpret_cast<const float*>(smem_raw + slot * kBfStageBytes + kBfStageScaleOff + 4 * lane);
+    };
+    auto cvt_pair = [&](const v4f (&acc)[HB], int x, int j2) -> v2h {
+        const int hb = 2 * x + (j2 >> 1);
+        if (hb >= HB) return v2h{0, 0};
+        const v2f f = v2f{acc[hb][2 * (j2 & 1)], acc[hb][2 * (j2 & 1) + 1]};
+        const v2h r = __builtin_convertvector(f, v2h);
+        return __builtin_elementwise_min(__builtin_elementwise_max(r, v2h{0, 0}), v2h{1, 1});
+    };
+    // One region: the 4*HB score MFMAs of a subtile (operands B_, results
+    // mm) and the head sums of the previous subtile ep (weights of subtile
+    // EST, added to P), interleaved step by step; extra(k) after step k.
+    auto region = [&](auto est, const v8bf (&B_)[4], v4f (&mm)[HB], const v4f (&ep)[HB], v4f& P, auto&& extra) {
+        constexpr int NM = 4 * HB;
+        constexpr int NI = NX * 5;
+        constexpr int es = decltype(est)::value;
+        v8h X = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            const int j = k / HB, hb = k % HB;
+            mm[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, Aw[hb][j]), B_[j],
+                                                             j == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : mm[hb], 0, 0, 0);
+#pragma unroll
+            for (int e = (k * NI) / NM; e < ((k + 1) * NI) / NM; ++e) {
+                const int x = e / 5, it = e % 5;
+                if (it < 4) {
+                    const v2h r = cvt_pair(ep, x, it);
+                    X[2 * it] = r[0];
+                    X[2 * it + 1] = r[1];
+                } else {
+                    P = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wh[es][x], X, P, 0, 0, 0);
+                }
+            }
+            extra(k);
+            __builtin_amdgcn_sched_barrier(0x0094);  // SALU, VMEM and LDS may cross
+        }
+    };
+    auto pin = [&](v4f (&acc)[HB]) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) asm volatile("" : "+v"(acc[hb]));
+    };
+
+    struct FinState { float score; uint32_t key; int s; bool app; uint64_t m; int below; };
+    const int K = a.topk;
+    int nb = 0;
+    uint32_t thr = 0u;
+    uint32_t thr_eff = 0u;  // thr while the wave appends, else 0xFFFFFFFF
+    bool active = live;
+    bool floored = false;
+    uint32_t r_spec = 0;
+    if (live && S >= 2 && t + 1 > 2 * K) {
+        const float ec = 64.f * (float)S * (float)K / (float)(t + 1);
+        r_spec = (uint32_t)ceilf(ec + 5.f * sqrtf(ec) + 8.f);
+    }
+    auto finish_piece = [&](int piece, FinState& f, int chunk, const v4f& P, float ks) {
+        if (piece == 0) f.score = P[0] * (ks * Fscale);
+        if (piece == 1) f.key = score_key(f.score);
+        if (piece == 2) {
+            f.s = chunk * 64 + lane;
+            f.app = (f.s <= t) & (f.key > thr_eff);
+        }
+        if (piece == 3) {
+            f.m = wave_ballot(f.app);
+            f.below = lanes_below(f.m);
+            asm volatile("" : "+v"(f.below));  // computed by every lane: keeps the select branch-free
+        }
+        if (piece == 4) {
+            const int o = f.app ? nb + f.below : CAP + lane;
+            rb.key[o] = f.key;
+            rb.pos[o] = (Pos)f.s;
+            nb += __builtin_popcountll(f.m);
+        }
+    };
+    auto finish_tail = [&](int fslot, int chunk, float score) {
+        if (srow && active) {
+            const int s = chunk * 64 + lane;
+            if (s < L) srow[s] = s <= t ? score : -INFINITY;
+        }
+        if (active && nb > CAP - kWave && lane == 0) flags[fslot] = 1u;
+    };
+
+    if (threadIdx.x == 0) flags[3] = 0u;
+    for (int pass = 0;; ++pass) {
+        v4f acc0[HB], acc1[HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) acc1[hb] = v4f{0.f, 0.f, 0.f, 0.f};
+        v8bf Bc[4], Bn[4];
+        v4f Pcur = v4f{0.f, 0.f, 0.f, 0.f};  // head sums of the chunk in progress
+        float ks_prev = 0.f;
+        int chunk_prev = 0;
+        if (threadIdx.x < 3) flags[threadIdx.x] = 0u;
+        int c_stage = chunk0;
+        stage_chunk(0, c_stage);
+        c_stage = chunk_next(1, c_stage);
+        stage_chunk(1, c_stage);
+        // chunk 0 landed: at most this wave's copies of chunk 1 in flight
+        if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3)
+        else __builtin_amdgcn_s_waitcnt(0x0F72);            // vmcnt(2)
+        __syncthreads();
+        load_bsub(0, 0, Bc);
+        float ks_cur = load_ks(0);
+        int chunk_cur = chunk0;
+        for (int i = 0; i <= last; ++i) {
+            const int sl = i & 1;
+            const v4f Pprev = Pcur;  // chunk i-1 still lacks its last subtile
+            v4f Pfin = Pprev;
+            // Region 0: subtile 0 of chunk i; head sums of subtile 3 of chunk i-1.
+            __builtin_amdgcn_sched_barrier(0);
+            load_bsub(sl, 1, Bn);
+            region(std::integral_constant<int, 3>{}, Bc, acc0, acc1, Pfin, [](int) {});
+            asm volatile("" : "+v"(Pfin));
+            pin(acc0);
+            __builtin_amdgcn_sched_barrier(0);
+            // Region 1: subtile 1; head sums of subtile 0 (a new chunk sum);
+            // appends of chunk i-1 start (discarded before the first chunk).
+            const bool fin_on = i >= 1;
+            const bool was_active = active;
+            active = active && fin_on;
+            thr_eff = active ? thr : 0xFFFFFFFFu;
+            FinState fs;
+            const int nb0 = nb;
+            Pcur = v4f{0.f, 0.f, 0.f, 0.f};
+            load_bsub(sl, 2, Bc);
+            region(std::integral_constant<int, 0>{}, Bn, acc1, acc0, Pcur, [&](int k) {
+                if (k == 1) finish_piece(0, fs, chunk_prev, Pfin, ks_prev);
+                if (k == 2 * HB + 1) finish_piece(1, fs, chunk_prev, Pfin, ks_prev);
+            });
+            pin(acc1);
+            __builtin_amdgcn_sched_barrier(0);
+            // Region 2: subtile 2; head sums of subtile 1.
+            load_bsub(sl, 3, Bn);
+            region(std::integral_constant<int, 1>{}, Bc, acc0, acc1, Pcur, [&](int k) {
+                if (k == 1) finish_piece(2, fs, chunk_prev, Pfin, ks_prev);
+                if (k == 2 * HB + 1) finish_piece(3, fs, chunk_prev, Pfin, ks_prev);
+            });
+            pin(acc0);
+            __builtin_amdgcn_sched_barrier(0);
+            // Region 3: subtile 3; head sums of subtile 2; the appends end.
+            region(std::integral_constant<int, 2>{}, Bn, acc1, acc0, Pcur, [&](int k) {
+                if (k == 1) finish_piece(4, fs, chunk_prev, Pfin, ks_prev);
+            });
+            asm volatile("" : "+v"(Pcur), "+v"(fs.score));
+            pin(acc1);
+            __builtin_amdgcn_sched_barrier(0);
+            active = was_active;
+            if (!fin_on) nb = nb0;
+            if (fin_on) finish_tail(i % 3, chunk_prev, fs.score);
+            // The next chunk's copies (issued after the previous barrier) and
+            // any score-matrix stores complete; the barrier then makes every
+            // wave's copies visible and certifies that every wave is done
+            // with this chunk's slot.
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __syncthreads();
+            // Compaction requests of this iteration's appends (slot i % 3,
+            // set before the barrier); slot (i-1) % 3 was read by every wave
+            // before it and is cleared for reuse two iterations on.
+            const uint32_t flag_word = flags[i % 3];
+            if (threadIdx.x == 0 && i >= 1) flags[(i + 2) % 3] = 0u;
+            // Chunk i+2 goes to chunk i's slot (a clamped dummy past the end).
+            c_stage = chunk_next(i + 2, c_stage);
+            stage_chunk(sl, c_stage);
+            ks_prev = ks_cur;
+            chunk_prev = chunk_cur;
+            chunk_cur = chunk_next(i + 1, chunk_cur);
+            if (i < last) {
+                load_bsub(sl ^ 1, 0, Bc);
+                ks_cur = load_ks(sl ^ 1);
+            }
+            // The sample's appends (order indices 0..S-1) end in iteration S:
+            // the speculative floor is set before any other append.  Then the
+            // cooperative compaction.
+            if (i == S && r_spec != 0u && active && (uint32_t)nb > r_spec) {
+                uint32_t fl;
+                nb = wave_floor(rb, nb, r_spec, &fl);
+                thr = fl == 0u ? 0u : fl - 1u;
+                floored = true;
+            }
+            if (flag_word != 0u && active && nb > K) nb = wave_compact(rb, nb, (uint32_t)K, &thr, CAP + 128);
+        }
+        // Head sums of the last chunk's subtile 3, then its appends.
+        {
+            v4f Pl = Pcur;
+#pragma unroll
+            for (int x = 0; x < NX; ++x) {
+                v8h X;
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const v2h r = cvt_pair(acc1, x, it);
+                    X[2 * it] = r[0];
+                    X[2 * it + 1] = r[1];
+                }
+                Pl = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wh[3][x], X, Pl, 0, 0, 0);
+            }
+            FinState fs;
+            thr_eff = active ? thr : 0xFFFFFFFFu;
+#pragma unroll
+            for (int p = 0; p < 5; ++p) finish_piece(p, fs, chunk_prev, Pl, ks_prev);
+            // no compaction follows: the slot is not read again in this pass
+            finish_tail((last + 1) % 3, chunk_prev, fs.score);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0000);  // no stage copy or LDS read may still be in flight
+        if (pass == 1) break;
+        // Verification of the floor; any failing row makes the whole block
+        // scan again, with only the failing waves appending.
+        const bool redo = active && floored && nb < K;
+        if (redo && lane == 0) flags[3] = 1u;
+        __syncthreads();
+        if (flags[3] == 0u) break;
+        active = redo;
+        if (redo) {
+            nb = 0;
+            thr = 0u;
+            floored = false;
+        }
+        r_spec = 0u;
+    }
+    if (!live) return;
+    if (srow) {
+        for (int s = (last + 1) * 64 + lane; s < L; s += kWave) srow[s] = -INFINITY;
+    }
+    __builtin_amdgcn_wave_barrier();
+    wave_emit(rb, nb, K, a.idx_out + row_t * K, a.val_out ? a.val_out + row_t * K : nullptr);
+}
+
 constexpr bool staged_path(int dtype, int L) { return DSAIDX_PREFILL_STAGED && dtype == 2 && L <= 65536; }
+constexpr bool staged_bf16_path(int dtype, int L) { return DSAIDX_PREFILL_STAGED_BF16 && dtype == 1 && L <= 65536; }
 constexpr int pad64(int L) { return (L + 63) / 64 * 64; }
 
 template <int HB>
@@ -1207,18 +1649,47 @@ hipError_t launch_fp8_staged(const PrefillArgs& a_in, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int HB>
+hipError_t launch_bf16_staged(const PrefillArgs& a_in, hipStream_t stream) {
+    PrefillArgs a = a_in;
+    a.Lpad = pad64(a.L);
+    a.ks_adj = reinterpret_cast<float*>(a.workspace);
+    uint16_t* kscaled = reinterpret_cast<uint16_t*>(a.ks_adj + (size_t)a.B * a.Lpad);
+    {
+        const int64_t n = (int64_t)a.B * a.Lpad;
+        hipLaunchKernelGGL(prefill_key_prep_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a,
+                           kscaled);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const size_t smem = kBfStages * kBfStageBytes + (size_t)kBfWaves * kBfWaveBytes;
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_fused_bf16_staged_kernel<HB>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const int nblk = (a.L + kBfWaves - 1) / kBfWaves;
+    hipLaunchKernelGGL((prefill_fused_bf16_staged_kernel<HB>), dim3((unsigned)(nblk * a.B)), dim3(kBfWaves * kWave),
+                       smem, stream, a, (const uint16_t*)kscaled);
+    return hipGetLastError();
+}
+
 template <int DT, int HB>
 hipError_t launch_pos(const PrefillArgs& a, hipStream_t stream) {
     if (staged_path(DT, a.L)) return launch_fp8_staged<HB>(a, stream);
+    if (staged_bf16_path(DT, a.L)) return launch_bf16_staged<HB>(a, stream);
     return a.L <= 65536 ? launch_one<DT, HB, true>(a, stream) : launch_one<DT, HB, false>(a, stream);
 }
 
 }  // namespace
 
 size_t prefill_fused_workspace_bytes(int B, int L, int dtype) {
-    if (!staged_path(dtype, L)) return 0;
     const size_t n = (size_t)B * pad64(L);
-    return (n * 5 + 255) / 256 * 256;  // fp32 adjusted scales, then the E8M0 bytes
+    if (staged_path(dtype, L)) return (n * 5 + 255) / 256 * 256;  // fp32 adjusted scales, then the E8M0 bytes
+    if (staged_bf16_path(dtype, L)) return n * (4 + 2 * kD);      // fp32 adjusted scales, then the scaled keys
+    return 0;
 }
 
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream) {

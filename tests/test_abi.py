@@ -76,6 +76,10 @@ def test_prefill_rejects_before_launch(lib, kw, status):
 def test_prefill_workspace_query(lib):
     # fused fp8: per-key adjusted scale and operand-scale byte (4 + 1 bytes per key)
     assert lib.indexer_prefill_workspace_bytes(1, 8192, 64, 128, 2048, 2, 0) == 8192 * 5
+    # bf16 staged: fp32 adjusted scale + the scaled bf16 key, per 64-padded key
+    assert lib.indexer_prefill_workspace_bytes(1, 8192, 64, 128, 2048, 1, 0) == 8192 * 260
+    assert lib.indexer_prefill_workspace_bytes(2, 100, 16, 128, 64, 1, 0) == 2 * 128 * 260
+    assert lib.indexer_prefill_workspace_bytes(1, 70000, 64, 128, 2048, 1, 0) == 0
     assert lib.indexer_prefill_workspace_bytes(2, 256, 4, 32, 16, 0, 0) == 2 * 256 * 256 * 4
     assert lib.indexer_prefill_workspace_bytes(2, 256, 4, 32, 16, 0, 1) == 0
 

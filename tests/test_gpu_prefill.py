@@ -130,20 +130,23 @@ def test_tie_heavy_generic():
     parity(inp, 40, want_scores=True, name="ties generic")
 
 
-def test_fused_small_k_long_rows_sampled():
-    """Long rows with a small k: the fp8 kernel's candidate buffer is cut down
-    many times per row, under a floor set from a strided sample of chunks."""
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_fused_small_k_long_rows_sampled(dtype):
+    """Long rows with a small k: the staged kernels' candidate buffers are cut
+    down many times per row, under a floor set from a strided sample of
+    chunks."""
     L, K = 8192, 64
-    inp = synth.prefill_inputs(1, L, 16, 128, "fp8", seed=5500)
+    inp = synth.prefill_inputs(1, L, 16, 128, dtype, seed=5500)
     rows = np.array([0, 63, 64, 2047, 2048, 4095, 5000, 8190, 8191])
     parity(inp, K, rows=rows, name="small k long rows")
 
 
-def test_fused_floor_rescan_when_sample_holds_the_top():
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_fused_floor_rescan_when_sample_holds_the_top(dtype):
     """Keys at positions 1024 j + [960, 1024) -- the strided chunks a long row
-    of the fp8 kernel scores first -- score far above every other key, so the
-    floor each long row sets from that sample lies above its k-th score: the
-    check at the end of the scan fails and the row is scanned again.  The
+    of the staged kernels scores first -- score far above every other key, so
+    the floor each long row sets from that sample lies above its k-th score:
+    the check at the end of the scan fails and the row is scanned again.  The
     selection must still be exact."""
     L, H, D, K = 4096, 16, 128, 256
     rng = np.random.default_rng(6000)
@@ -153,11 +156,15 @@ def test_fused_floor_rescan_when_sample_holds_the_top():
     hot = (np.arange(L) // 64) % 16 == 15
     k[0, hot] = 2.0 * q0[None, :] + 0.1 * rng.standard_normal((int(hot.sum()), D)).astype(np.float32)
     w = synth.softmax_weights(rng.standard_normal((1, L, H)))
-    qc, qs = synth.quantize_fp8_rows(q)
-    kc, ks = synth.quantize_fp8_rows(k)
-    inp = dict(q=qc, q_scale=qs, k=kc, k_scale=ks, w=w, dtype="fp8")
+    if dtype == "fp8":
+        qc, qs = synth.quantize_fp8_rows(q)
+        kc, ks = synth.quantize_fp8_rows(k)
+        inp = dict(q=qc, q_scale=qs, k=kc, k_scale=ks, w=w, dtype="fp8")
+    else:
+        inp = dict(q=synth.to_bf16_bits(q), q_scale=None, k=synth.to_bf16_bits(k), k_scale=None, w=w,
+                   dtype="bf16")
     rows = np.array([0, 255, 256, 1983, 1984, 2047, 2048, 3000, 4094, 4095])
-    gi, _ = parity(inp, K, rows=rows, name="floor rescan")
+    gi, _ = parity(inp, K, rows=rows, name=f"floor rescan {dtype}")
     hot_pos = np.flatnonzero(hot)
     assert set(gi[0, 4095].tolist()) == set(hot_pos.tolist())
 
@@ -171,16 +178,17 @@ def test_tie_heavy_long_rows_sampled(dtype):
     parity(inp, 512, rows=rows, name="ties long rows")
 
 
-@pytest.mark.parametrize("L", [65536, 66000])
-def test_fused_long_sequences_sampled(L):
-    """Both candidate-buffer layouts (16-bit positions up to L = 65536, 32-bit
-    beyond), checked on sampled rows including the first and last."""
-    inp = synth.prefill_inputs(1, L, 16, 128, "fp8", seed=5000 + L)
+@pytest.mark.parametrize("dtype,L", [("fp8", 65536), ("fp8", 66000), ("bf16", 65536), ("bf16", 66000)])
+def test_fused_long_sequences_sampled(dtype, L):
+    """Both candidate-buffer layouts (16-bit positions up to L = 65536 in the
+    staged kernels, 32-bit beyond), checked on sampled rows including the
+    first and last."""
+    inp = synth.prefill_inputs(1, L, 16, 128, dtype, seed=5000 + L)
     rows = np.array([0, 2046, 2047, 2048, 40000, 65535, L - 1])
-    say(f"prefill long L={L}")
+    say(f"prefill long {dtype} L={L}")
     gi, gv, _ = run_prefill(inp, 2048)
     _, _, osc = indexer.prefill(inp, 2048, rows=rows, want_scores=True)
-    check_topk_rows(gi[0][rows], gv[0][rows], osc[0], rows + 1, 2048, where=f"long L={L}")
+    check_topk_rows(gi[0][rows], gv[0][rows], osc[0], rows + 1, 2048, where=f"long {dtype} L={L}")
 
 
 def _e4m3(x):
@@ -210,6 +218,27 @@ def test_fused_fp8_codes_far_from_full_range(signed):
     if not signed:
         inp["w"] = np.abs(inp["w"])
     parity(inp, K, want_scores=True, name=f"fp8 small codes signed={signed}")
+
+
+@pytest.mark.parametrize("signed", [False, True])
+def test_fused_bf16_values_far_from_unit_range(signed):
+    """bf16 queries and keys whose magnitudes spread over 2^-20 .. 2^10 per
+    query head and per key, with some all-zero keys: the per-token and
+    per-key scales the staged bf16 kernel derives (and the exact rescaling of
+    both operands) are exercised, and scores and selections match the oracle
+    -- with non-negative head weights under the plain tolerance, with signed
+    ones under the magnitude-sum tolerance."""
+    rng = np.random.default_rng(582)
+    L, H, D, K = 700, 64, 128, 64
+    qv = rng.standard_normal((1, L, H, D)).astype(np.float32) * np.exp2(rng.integers(-20, 11, size=(1, L, H, 1)))
+    kv = rng.standard_normal((1, L, D)).astype(np.float32) * np.exp2(rng.integers(-20, 11, size=(1, L, 1)))
+    kv[:, ::53] = 0.0
+    w = rng.standard_normal((1, L, H)).astype(np.float32)
+    if not signed:
+        w = np.abs(w)
+    inp = dict(kind="prefill", B=1, L=L, H=H, D=D, dtype="bf16", q=synth.to_bf16_bits(qv), k=synth.to_bf16_bits(kv),
+               q_scale=None, k_scale=None, w=w)
+    parity(inp, K, want_scores=True, name=f"bf16 wide range signed={signed}")
 
 
 def test_fused_fp8_mixed_sign_blocks():
