@@ -248,7 +248,8 @@ def main():
             def dstep():
                 dsa.indexer_decode_paged(*args_d, c["topk"], max_context_len=mcl, workspace=ws)
 
-            dms, _ = time_calls(torch, dstep, max(args.steps, 20), args.warmup)
+            # a decode call is ~0.2 ms: time at least 200 of them, after 0.5 s of warmup calls
+            dms, _ = time_calls(torch, dstep, max(args.steps, 200), args.warmup, warm_seconds=0.5)
             nbytes = int(d["context_lens"].astype(np.int64).sum()) * (c["D"] + 4)
             gbs = nbytes / (dms * 1e-3) / 1e9
             log(f"decode {n}: {dms * 1e3:.1f} us/call, {gbs:.0f} GB/s")
