@@ -84,7 +84,7 @@ template <typename Pos>
 struct RowBuf {
     uint32_t* key;
     Pos* pos;
-    uint32_t* hist;  // 256 bins
+    uint32_t* hist;  // 256 16-bit bins, two per word (bin b: word b/2, half b%2)
 };
 
 // The buffer routines below walk the buffer 256 entries per step, lane l
@@ -137,7 +137,7 @@ __device__ __forceinline__ void wave_hist(const RowBuf<Pos>& rb, int n, uint32_t
                                           int shift, uint32_t dmask) {
     const int l = lane_id();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rb.hist[l + 64 * i] = 0u;
+    for (int i = 0; i < 2; ++i) rb.hist[l + 64 * i] = 0u;
     __builtin_amdgcn_wave_barrier();
     for (int j0 = 0; j0 < n; j0 += 256) {
         const int j = j0 + 4 * l;
@@ -147,12 +147,18 @@ __device__ __forceinline__ void wave_hist(const RowBuf<Pos>& rb, int n, uint32_t
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t ip = inv_pos(p.v[e]);
-                if (j + e < n && k[e] == kappa && (ip & pm) == pv) atomicAdd(&rb.hist[(ip >> shift) & dmask], 1u);
+                if (j + e < n && k[e] == kappa && (ip & pm) == pv) {
+                    const uint32_t bin = (ip >> shift) & dmask;
+                    atomicAdd(&rb.hist[bin >> 1], 1u << ((bin & 1u) << 4));
+                }
             }
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (j + e < n && (k[e] & pm) == pv) atomicAdd(&rb.hist[(k[e] >> shift) & dmask], 1u);
+                if (j + e < n && (k[e] & pm) == pv) {
+                    const uint32_t bin = (k[e] >> shift) & dmask;
+                    atomicAdd(&rb.hist[bin >> 1], 1u << ((bin & 1u) << 4));
+                }
         }
     }
     __builtin_amdgcn_wave_barrier();
@@ -164,9 +170,9 @@ template <typename Pos>
 __device__ __forceinline__ uint32_t wave_find_bin(const RowBuf<Pos>& rb, uint32_t need, uint32_t* above,
                                                   uint32_t* in_bin) {
     const int l = lane_id();
-    uint32_t c[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = rb.hist[255 - 4 * l - i];
+    // bins 255-4l .. 252-4l: the high and low halves of words 127-2l, 126-2l
+    const uint32_t w_hi = rb.hist[127 - 2 * l], w_lo = rb.hist[126 - 2 * l];
+    const uint32_t c[4] = {w_hi >> 16, w_hi & 0xFFFFu, w_lo >> 16, w_lo & 0xFFFFu};
     const uint32_t loc = c[0] + c[1] + c[2] + c[3];
     const uint32_t incl = wave_incl_scan(loc);
     uint32_t run = incl - loc;
@@ -696,9 +702,9 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
 constexpr int kStagedWaves = 8;
 constexpr int kStagedCap = 2560;   // candidates per row; 8 rows + 3 key chunks fit in 160 KB
 constexpr int kStages = 3;
-// per wave: keys [CAP + 64] u32, histogram [256] u32, positions [CAP + 64] u16; the
+// per wave: keys [CAP + 64] u32, histogram [256] u16, positions [CAP + 64] u16; the
 // 64 slots past CAP take the writes of lanes that do not append
-constexpr size_t kStagedWaveBytes = (size_t)(kStagedCap + kWave) * 6 + 256 * 4;
+constexpr size_t kStagedWaveBytes = (size_t)(kStagedCap + kWave) * 6 + 128 * 4;
 constexpr size_t kStageKeyBytes = 64 * kD;                 // one chunk of fp8 keys,
 constexpr size_t kStageScaleOff = kStageKeyBytes;          // their fp32 scales times 2^Pk,
 constexpr size_t kStageExpOff = kStageKeyBytes + 64 * 4;   // their E8M0 bytes (64 used of 256)
@@ -759,7 +765,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     unsigned char* wbase = smem_raw + kStages * kStageBytes + wave * kStagedWaveBytes;
     rb.key = reinterpret_cast<uint32_t*>(wbase);
     rb.hist = reinterpret_cast<uint32_t*>(wbase + (size_t)(CAP + kWave) * 4);
-    rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)(CAP + kWave) * 4 + 256 * 4);
+    rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)(CAP + kWave) * 4 + 128 * 4);
 
     const size_t row_t = (size_t)b * L + t;
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * L * kD;
@@ -1190,8 +1196,8 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
 //   rows are scaled by its own 2^-Pq_h in registers (2^Pq_h goes into the
 //   head's weight).  So again every S_h lies in [-1, 1], the clamped f16
 //   conversion is the ReLU and the head sum is an f16 MFMA.
-// * A 64-key chunk is 16 KB.  Two stages and 2304-entry candidate buffers
-//   fit the LDS beside the eight rows.  One barrier per chunk, at its end: it
+// * A 64-key chunk is 16 KB.  Two stages fit the LDS beside the eight rows'
+//   2560-entry candidate buffers.  One barrier per chunk, at its end: it
 //   certifies that the next chunk has landed and that every wave is done
 //   with this one, whose slot then receives the chunk after next.
 // * A chunk runs as four regions, one 16-key subtile each: its 16 score
@@ -1202,9 +1208,9 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
 //   acted on in the same iteration, so the buffer needs one chunk of slack.
 // ---------------------------------------------------------------------------
 constexpr int kBfWaves = 8;
-constexpr int kBfCap = 2304;
+constexpr int kBfCap = 2560;
 constexpr int kBfStages = 2;
-constexpr size_t kBfWaveBytes = (size_t)(kBfCap + kWave) * 6 + 256 * 4;
+constexpr size_t kBfWaveBytes = (size_t)(kBfCap + kWave) * 6 + 128 * 4;
 constexpr size_t kBfStageKeyBytes = 64 * kD * 2;
 constexpr size_t kBfStageScaleOff = kBfStageKeyBytes;
 constexpr size_t kBfStageBytes = kBfStageKeyBytes + 64 * 4;
@@ -1275,7 +1281,7 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     unsigned char* wbase = smem_raw + kBfStages * kBfStageBytes + wave * kBfWaveBytes;
     rb.key = reinterpret_cast<uint32_t*>(wbase);
     rb.hist = reinterpret_cast<uint32_t*>(wbase + (size_t)(CAP + kWave) * 4);
-    rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)(CAP + kWave) * 4 + 256 * 4);
+    rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)(CAP + kWave) * 4 + 128 * 4);
 
     const size_t row_t = (size_t)b * L + t;
     // Query: lane (m, g) holds, for k-step j, q[t][16hb+m][32g+8j .. +8].
