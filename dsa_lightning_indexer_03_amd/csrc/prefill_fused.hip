@@ -8,12 +8,17 @@
 // s asc).  As a contraction this is Q[L*H, D] x K[L, D]^T restricted to the
 // causal half; D = 128 and H is a multiple of 16.
 //
-// Layout of the work:
+// Three kernels, by dtype and length:
+// * fp8, L <= 65536 (the headline path) and bf16, L <= 65536: key chunks are
+//   staged through LDS once per workgroup of eight tokens, and the weighted
+//   head sum runs on the matrix cores (sections further down).
+// * bf16 and fp8 beyond L = 65536 (positions need 32 bits, buffers grow): the
+//   unstaged kernel below, whose layout is:
 // * workgroup = W independent waves; wave w owns query token t = W*blk + w and
 //   all 16*HB of its heads.  Blocks are issued heaviest (largest t) first.
-//   For L <= 65536 positions fit 16 bits: W = 8 waves (two per SIMD, so one
-//   wave's MFMAs overlap the other's VALU epilogue) with 3072-entry buffers;
-//   longer sequences use W = 4 with 4096-entry buffers and 32-bit positions.
+//   W = 4 with 4096-entry buffers and 32-bit positions (W = 8 with
+//   3072-entry buffers and 16-bit positions for L <= 65536, reached only
+//   when the staged kernels are switched off at build time).
 // * the token's queries sit in registers as MFMA A operands for the whole
 //   scan (head on M);  keys stream through registers as B operands (key on
 //   N), 16 keys per subtile, 64 keys per step.  No LDS is used for keys and
@@ -23,23 +28,21 @@
 //   16 heads x 16 keys; bf16: four v_mfma_f32_16x16x32_bf16.  The contraction
 //   dimension is split the same way on both operands: lane group g owns the
 //   dims [32g, 32g+32).
-// * epilogue (kernel below; the fp8 kernel with staged keys further down
-//   sums the heads on the matrix cores instead, see there): in registers,
-//   c[t,h] * max(S, 0) summed over the lane's heads,
+// * epilogue in registers: c[t,h] * max(S, 0) summed over the lane's heads,
 //   with c = w * q_scale / sqrt(D) (exact refactoring: ReLU commutes with a
 //   positive scale, and the key's fp8 scale is applied once per key after
 //   the head sum), then a cross-lane reduce-scatter leaves lane l with the
 //   score of key s0 + l.
-// * streaming top-k per wave: a per-row candidate buffer of (key, position)
-//   pairs in LDS, filled in position order.  A score enters the
-//   buffer only if its order-preserving key beats the row threshold.  When
-//   the buffer nears capacity it is compacted: one radix digit below the
-//   buffer's common key prefix locates the bin of the k-th largest key, the
-//   bin's lower edge becomes the new threshold and everything below it is
-//   dropped (stable, so the buffer stays in position order).  The buffer
-//   always holds every entry that can still be in the row's top k.  At the
-//   end an exact radix select over the buffer finds the k-th largest key and
-//   ties at that key go to the lowest positions.
+// All three keep a streaming top-k per wave: a per-row candidate buffer of
+// (key, position) pairs in LDS, filled in position order.  A score enters the
+// buffer only if its order-preserving key beats the row threshold.  When the
+// buffer nears capacity it is compacted: one radix digit below the buffer's
+// common key prefix locates the bin of the k-th largest key, the bin's lower
+// edge becomes the new threshold and everything below it is dropped (stable,
+// so the buffer stays in position order).  The buffer always holds every
+// entry that can still be in the row's top k.  At the end an exact radix
+// select over the buffer finds the k-th largest key and ties at that key go
+// to the lowest positions.
 #include <type_traits>
 
 #include "common.h"
