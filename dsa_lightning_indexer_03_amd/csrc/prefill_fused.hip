@@ -1533,20 +1533,15 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
             });
             pin(acc1);
             __builtin_amdgcn_sched_barrier(0);
-            // Region 2: subtile 2; head sums of subtile 1.
+            // Region 2: subtile 2; head sums of subtile 1; the appends end.
             load_bsub(sl, 3, Bn);
             region(std::integral_constant<int, 1>{}, Bc, acc0, acc1, Pcur, [&](int k) {
-                if (k == 1) finish_piece(2, fs, chunk_prev, Pfin, ks_prev);
-                if (k == 2 * HB + 1) finish_piece(3, fs, chunk_prev, Pfin, ks_prev);
+                if (k == 0) finish_piece(2, fs, chunk_prev, Pfin, ks_prev);
+                if (k == HB) finish_piece(3, fs, chunk_prev, Pfin, ks_prev);
+                if (k == 2 * HB + 1) finish_piece(4, fs, chunk_prev, Pfin, ks_prev);
             });
+            asm volatile("" : "+v"(fs.score));
             pin(acc0);
-            __builtin_amdgcn_sched_barrier(0);
-            // Region 3: subtile 3; head sums of subtile 2; the appends end.
-            region(std::integral_constant<int, 2>{}, Bn, acc1, acc0, Pcur, [&](int k) {
-                if (k == 1) finish_piece(4, fs, chunk_prev, Pfin, ks_prev);
-            });
-            asm volatile("" : "+v"(Pcur), "+v"(fs.score));
-            pin(acc1);
             __builtin_amdgcn_sched_barrier(0);
             active = was_active;
             if (!fin_on) nb = nb0;
@@ -1554,7 +1549,7 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
             // The next chunk's copies (issued after the previous barrier) and
             // any score-matrix stores complete; the barrier then makes every
             // wave's copies visible and certifies that every wave is done
-            // with this chunk's slot.
+            // with this chunk's slot (subtile 3's operands are in registers).
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             __syncthreads();
             // Compaction requests of this iteration's appends (slot i % 3,
@@ -1562,7 +1557,9 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
             // before it and is cleared for reuse two iterations on.
             const uint32_t flag_word = flags[i % 3];
             if (threadIdx.x == 0 && i >= 1) flags[(i + 2) % 3] = 0u;
-            // Chunk i+2 goes to chunk i's slot (a clamped dummy past the end).
+            // Chunk i+2 goes to chunk i's slot (a clamped dummy past the end),
+            // and the next chunk's first operands are read while region 3
+            // multiplies.
             c_stage = chunk_next(i + 2, c_stage);
             stage_chunk(sl, c_stage);
             ks_prev = ks_cur;
@@ -1572,6 +1569,12 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
                 load_bsub(sl ^ 1, 0, Bc);
                 ks_cur = load_ks(sl ^ 1);
             }
+            // Region 3: subtile 3; head sums of subtile 2.
+            __builtin_amdgcn_sched_barrier(0);
+            region(std::integral_constant<int, 2>{}, Bn, acc1, acc0, Pcur, [](int) {});
+            asm volatile("" : "+v"(Pcur));
+            pin(acc1);
+            __builtin_amdgcn_sched_barrier(0);
             // The sample's appends (order indices 0..S-1) end in iteration S:
             // the speculative floor is set before any other append.  Then the
             // cooperative compaction.
