@@ -1421,6 +1421,9 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
         constexpr int NI = NX * 5;
         constexpr int es = decltype(est)::value;
         v8h X = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+        // a wave inside a region issues ahead of its SIMD partner outside one
+        // (measured: 2% faster here; the eight-wave fp8 kernel ran 4% slower)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int k = 0; k < NM; ++k) {
             const int j = k / HB, hb = k % HB;
@@ -1440,6 +1443,7 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
             extra(k);
             __builtin_amdgcn_sched_barrier(0x0094);  // SALU, VMEM and LDS may cross
         }
+        __builtin_amdgcn_s_setprio(0);
     };
     auto pin = [&](v4f (&acc)[HB]) {
 #pragma unroll
