@@ -703,15 +703,29 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
 // key's scale times 2^Pk finish the score.
 // ---------------------------------------------------------------------------
 constexpr int kStagedWaves = 8;
-constexpr int kStagedCap = 2560;   // candidates per row; 8 rows + 3 key chunks fit in 160 KB
+// Candidates per row: the most that fit beside three key chunks.  Every
+// compaction request makes all waves compact, so the buffer's slack above k
+// sets how often the whole block stalls.
+constexpr int kStagedCap = 2712;
 constexpr int kStages = 3;
 // per wave: keys [CAP + 64] u32, histogram [256] u16, positions [CAP + 64] u16; the
 // 64 slots past CAP take the writes of lanes that do not append
 constexpr size_t kStagedWaveBytes = (size_t)(kStagedCap + kWave) * 6 + 128 * 4;
+// Buffer walks read whole 256-entry steps, masking entries past the count,
+// so the last step reads up to entry kWalkEnd - 1.  Its keys stay within the
+// wave's keys and histogram; its positions can run past the wave's region
+// (into the next wave's, or into this padding after the last one).
+constexpr int kWalkEnd = (kStagedCap - 1) / 256 * 256 + 256;
+constexpr size_t kStagedTailPad = 128;
+static_assert((size_t)kWalkEnd * 4 <= (size_t)(kStagedCap + kWave) * 4 + 128 * 4, "key walk stays in the region");
+static_assert((size_t)kWalkEnd * 2 <= (size_t)(kStagedCap + kWave) * 2 + kStagedTailPad, "position walk padding");
+static_assert(kStagedWaveBytes % 16 == 0, "wave regions stay 16-byte aligned");
 constexpr size_t kStageKeyBytes = 64 * kD;                 // one chunk of fp8 keys,
 constexpr size_t kStageScaleOff = kStageKeyBytes;          // their fp32 scales times 2^Pk,
 constexpr size_t kStageExpOff = kStageKeyBytes + 64 * 4;   // their E8M0 bytes (64 used of 256)
 constexpr size_t kStageBytes = kStageExpOff + 256;
+constexpr size_t kStagedLds = kStages * kStageBytes + (size_t)kStagedWaves * kStagedWaveBytes + kStagedTailPad;
+static_assert(kStagedLds + 16 <= 160 * 1024, "LDS budget");
 
 // Key pre-pass: for key s of sequence b (positions up to the 64-padded
 // length; rows past the end repeat row L-1, as the staged copies do):
@@ -1651,7 +1665,7 @@ hipError_t launch_fp8_staged(const PrefillArgs& a_in, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const size_t smem = kStages * kStageBytes + (size_t)kStagedWaves * kStagedWaveBytes;
+    const size_t smem = kStagedLds;
     static bool attr = false;
     if (!attr) {
         hipError_t e = hipFuncSetAttribute((const void*)prefill_fused_fp8_staged_kernel<HB>,
