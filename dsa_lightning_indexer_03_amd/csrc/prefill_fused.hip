@@ -757,6 +757,16 @@ prefill_key_exp_kernel(PrefillArgs a) {
     a.kexp[(size_t)b * Lp + 64 * c + 4 * n + q] = (uint8_t)(127 - pk);
 }
 
+// Rank r of the speculative floor in a row's sample, from the expected
+// number ec of sampled keys at or above the row's k-th largest: 3.5 standard
+// deviations (plus 8) above it.  The floor fails only if the sample holds r
+// keys above the k-th largest (about 1e-5 per row for the sampling model at
+// ec ~ 128), and a failed floor is caught and rescanned.  A wider margin
+// leaves long rows near their buffer's capacity, so they compact more.
+__device__ __forceinline__ uint32_t spec_rank(float ec) {
+    return (uint32_t)ceilf(ec + 3.5f * sqrtf(ec) + 8.f);
+}
+
 template <int HB>
 __global__ void __launch_bounds__(kStagedWaves * kWave)
 prefill_fused_fp8_staged_kernel(PrefillArgs a) {
@@ -856,12 +866,12 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     // (chunks 16i+15, i < S) is scored first; the rest follow in increasing
     // order.  After the sample each long row sets a speculative floor: the
     // lower edge of the radix bin holding the r-th largest sampled key, with
-    // r five standard deviations above the expected number of sampled keys
-    // at or above the row's k-th largest.  Keys below the floor are never
-    // appended.  The floor is verified at the end: if fewer than k keys of
-    // the row cleared it, some of the top k may have been dropped and the row
-    // is scanned again without a floor.  Otherwise every dropped key lies
-    // below the k-th largest and the selection is exact.
+    // r three and a half standard deviations above the expected number of
+    // sampled keys at or above the row's k-th largest.  Keys below the floor
+    // are never appended.  The floor is verified at the end: if fewer than k
+    // keys of the row cleared it, some of the top k may have been dropped and
+    // the row is scanned again without a floor.  Otherwise every dropped key
+    // lies below the k-th largest and the selection is exact.
     const int S = last + 1 >= 32 ? (last + 1) / 16 : 0;
     // Chunk of order index i from the chunk of index i-1 (scalar, no
     // division): the sample 16i+15 for i < S, then 0, 1, ... skipping the
@@ -913,7 +923,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     uint32_t r_spec = 0;  // rank of the floor in the sample (0: no floor)
     if (live && S >= 2 && t + 1 > 2 * K) {
         const float ec = 64.f * (float)S * (float)K / (float)(t + 1);
-        r_spec = (uint32_t)ceilf(ec + 5.f * sqrtf(ec) + 8.f);
+        r_spec = spec_rank(ec);
     }
 
     // Pipeline.  The i-th chunk is copied three chunks ahead into the slot
@@ -1474,7 +1484,7 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     uint32_t r_spec = 0;
     if (live && S >= 2 && t + 1 > 2 * K) {
         const float ec = 64.f * (float)S * (float)K / (float)(t + 1);
-        r_spec = (uint32_t)ceilf(ec + 5.f * sqrtf(ec) + 8.f);
+        r_spec = spec_rank(ec);
     }
     auto finish_piece = [&](int piece, FinState& f, int chunk, const v4f& P, float ks) {
         if (piece == 0) f.score = P[0] * (ks * Fscale);
