@@ -21,7 +21,8 @@ from . import _lib
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
-__all__ = ["indexer_prefill", "indexer_decode_paged", "topk_select", "dtype_code", "F32", "BF16", "FP8_E4M3"]
+__all__ = ["indexer_prefill", "indexer_decode_paged", "topk_select", "kcache_append", "dtype_code", "F32", "BF16",
+           "FP8_E4M3"]
 
 
 def dtype_code(t: torch.Tensor) -> int:
@@ -141,3 +142,28 @@ def topk_select(scores, topk: int, row_len=None, want_values: bool = True):
                          _ptr(ws), nws, _stream(dev))
     _lib.check(st, "topk_select")
     return idx, val
+
+
+def kcache_append(k, seq_ids, positions, block_table, k_cache, k_scale):
+    """Quantise T new keys to FP8 and write them into the paged cache in place.
+
+    k [T,D] bf16 or fp32, seq_ids [T] int32 (outside [0, B): skipped),
+    positions [T] int32, block_table [B,max_pages] int32, k_cache [P,page,D]
+    uint8 E4M3FN codes, k_scale [P,page] fp32.  Returns nothing: k_cache and
+    k_scale are updated on the current stream."""
+    lib = _lib.load()
+    T, D = k.shape
+    P, page, Dk = k_cache.shape
+    if Dk != D or tuple(k_scale.shape) != (P, page):
+        raise ValueError("k_cache / k_scale shape mismatch")
+    if tuple(seq_ids.shape) != (T,) or tuple(positions.shape) != (T,):
+        raise ValueError("seq_ids / positions must have one entry per key")
+    if k_cache.dtype != torch.uint8 or k_scale.dtype != torch.float32:
+        raise ValueError("k_cache must be uint8 codes and k_scale fp32")
+    for name, t in (("k", k), ("seq_ids", seq_ids), ("positions", positions), ("block_table", block_table),
+                    ("k_cache", k_cache), ("k_scale", k_scale)):
+        _dev(t, name)
+    B, mpp = block_table.shape
+    st = lib.indexer_kcache_append(_ptr(k), dtype_code(k), _ptr(seq_ids), _ptr(positions), _ptr(block_table),
+                                   B, mpp, _ptr(k_cache), _ptr(k_scale), P, T, D, page, _stream(k.device))
+    _lib.check(st, "indexer_kcache_append")

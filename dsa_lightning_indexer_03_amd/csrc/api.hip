@@ -56,6 +56,43 @@ const char* dsaidx_status_string(int s) {
 
 const char* dsaidx_last_error(void) { return g_err; }
 
+dsaidx_status indexer_kcache_append(const void* k, int k_dtype, const int32_t* seq_ids,
+                                    const int32_t* positions, const int32_t* block_table, int B,
+                                    int max_pages_per_seq, uint8_t* k_cache, float* k_scale, int num_pages,
+                                    int T, int D, int page_size, void* stream) {
+    g_err[0] = 0;
+    if (T < 0 || B < 1 || max_pages_per_seq < 1 || num_pages < 1 || D < 1 || page_size < 1)
+        return fail(DSAIDX_ERR_SHAPE, "T=%d B=%d max_pages_per_seq=%d num_pages=%d D=%d page_size=%d", T, B,
+                    max_pages_per_seq, num_pages, D, page_size);
+    if (k_dtype != DSAIDX_F32 && k_dtype != DSAIDX_BF16 && k_dtype != DSAIDX_FP8_E4M3)
+        return fail(DSAIDX_ERR_DTYPE, "k_dtype=%d", k_dtype);
+    if (k_dtype == DSAIDX_FP8_E4M3) return fail(DSAIDX_ERR_UNSUPPORTED, "new keys must be bf16 or f32");
+    if (D != 128) return fail(DSAIDX_ERR_UNSUPPORTED, "D=%d (128)", D);
+    if (page_size != 64) return fail(DSAIDX_ERR_UNSUPPORTED, "page_size=%d (64)", page_size);
+    if (T == 0) return DSAIDX_OK;
+    if (!k) return fail(DSAIDX_ERR_NULL, "k is NULL");
+    if (!seq_ids) return fail(DSAIDX_ERR_NULL, "seq_ids is NULL");
+    if (!positions) return fail(DSAIDX_ERR_NULL, "positions is NULL");
+    if (!block_table) return fail(DSAIDX_ERR_NULL, "block_table is NULL");
+    if (!k_cache) return fail(DSAIDX_ERR_NULL, "k_cache is NULL");
+    if (!k_scale) return fail(DSAIDX_ERR_NULL, "k_scale is NULL");
+    if (!aligned16(k) || ((uintptr_t)k_cache & 7u) != 0)
+        return fail(DSAIDX_ERR_UNSUPPORTED, "k must be 16-byte and k_cache 8-byte aligned");
+    dsaidx::KcacheArgs a{};
+    a.k = k;
+    a.seq_ids = seq_ids;
+    a.positions = positions;
+    a.block_table = block_table;
+    a.k_cache = k_cache;
+    a.k_scale = k_scale;
+    a.T = T;
+    a.B = B;
+    a.max_pages = max_pages_per_seq;
+    const hipError_t e = dsaidx::launch_kcache_append(a, k_dtype == DSAIDX_BF16 ? 1 : 0, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "indexer_kcache_append");
+    return DSAIDX_OK;
+}
+
 size_t topk_select_workspace_bytes(int rows, int cols, int topk) {
     (void)rows; (void)cols; (void)topk;
     return 0;

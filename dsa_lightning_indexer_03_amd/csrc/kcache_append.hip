@@ -1,0 +1,126 @@
+// Indexer K-cache write path: per-token FP8 (E4M3FN) quantisation of new
+// keys and their append into the paged cache that the decode scan reads.
+//
+// The pages keep the indexer's keys in an FP8 cache of its own, written once
+// per token and read by every later step ("Lightning Indexer explained",
+// sections 2.1 and 2.4 of the decode walkthrough and section 5; "Study MLA
+// Indexer", data-flow diagram and the notes on its two caches).  This
+// library's reading of what they leave open:
+//   scale  = absmax(key) / 448 in fp32 (1 for an all-zero key);
+//   code_d = the E4M3FN value nearest to key_d / scale (a binary32
+//            quotient), ties to even, magnitudes above 448 saturated;
+//   the key of sequence b at position p goes to page block_table[b][p / 64],
+//   slot p % 64.
+//
+// Layout: 16 lanes per key, so a wave quantises four 128-wide keys at once.
+// Each lane holds 8 elements (16 bytes of bf16 or 32 of f32), the absmax is
+// a 16-lane xor reduction, and each lane stores 8 codes (8 bytes) of the
+// 128-byte row; the first lane of the 16 stores the scale.  Every lane group
+// takes four keys per pass, with all their loads issued before any is used.
+// The hardware conversion rounds to nearest even; values are clamped to
+// +-448 first, so none overflows.  HBM bound: per key 256 bytes (bf16) or
+// 512 (f32) read, 132 written.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsaidx {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kPage = 64;
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // keys per lane group per pass
+
+template <int DT>  // 0 = f32, 1 = bf16
+__device__ __forceinline__ void load_key(const KcacheArgs& a, int64_t i, int l16, float (&x)[8]) {
+    if constexpr (DT == 1) {
+        const v4i u = *reinterpret_cast<const v4i*>(reinterpret_cast<const uint16_t*>(a.k) + i * kD + 8 * l16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __uint_as_float((uint32_t)u[j] << 16);
+            x[2 * j + 1] = __uint_as_float((uint32_t)u[j] & 0xFFFF0000u);
+        }
+    } else {
+        const float* p = reinterpret_cast<const float*>(a.k) + i * kD + 8 * l16;
+        const v4f lo = *reinterpret_cast<const v4f*>(p);
+        const v4f hi = *reinterpret_cast<const v4f*>(p + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = lo[j];
+            x[4 + j] = hi[j];
+        }
+    }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads)
+kcache_append_kernel(KcacheArgs a) {
+    const int l16 = threadIdx.x & 15;
+    const int64_t g0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 4;  // this lane group
+    const int64_t G = ((int64_t)gridDim.x * kThreads) >> 4;                   // lane groups in the grid
+    const int64_t limit = (int64_t)a.max_pages * kPage;
+    for (int64_t i0 = g0; i0 < a.T; i0 += kUnroll * G) {
+        // the keys i0 + u*G: placement words first, then the rows, then the page ids
+        int b[kUnroll], p[kUnroll];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = i0 + u * G;
+            b[u] = i < a.T ? a.seq_ids[i] : -1;
+            p[u] = i < a.T ? a.positions[i] : -1;
+        }
+        float x[kUnroll][8];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = i0 + u * G;
+            if (i < a.T) load_key<DT>(a, i, l16, x[u]);
+            else
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[u][j] = 0.f;
+        }
+        int64_t row[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            ok[u] = b[u] >= 0 && b[u] < a.B && p[u] >= 0 && (int64_t)p[u] < limit;
+            row[u] = ok[u] ? (int64_t)a.block_table[(int64_t)b[u] * a.max_pages + p[u] / kPage] * kPage + p[u] % kPage
+                           : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float m = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[u][j]));
+#pragma unroll
+            for (int d = 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 16));
+            const float scale = m > 0.f ? m / 448.f : 1.f;
+            float q[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = fminf(fmaxf(x[u][j] / scale, -448.f), 448.f);
+            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
+            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], w1, true);
+            if (ok[u]) {
+                *reinterpret_cast<uint2*>(a.k_cache + row[u] * kD + 8 * l16) = uint2{(uint32_t)w0, (uint32_t)w1};
+                if (l16 == 0) a.k_scale[row[u]] = scale;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_kcache_append(const KcacheArgs& a, int dtype, hipStream_t stream) {
+    if (a.T <= 0) return hipSuccess;
+    // 16 lanes per key, four keys per lane group and pass; at most 16
+    // workgroups per compute unit of the 256 are ever needed in flight
+    int64_t blocks = (a.T * 16 + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+    if (blocks > 4096) blocks = 4096;
+    if (dtype == 1)
+        hipLaunchKernelGGL(kcache_append_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(kcache_append_kernel<0>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace dsaidx

@@ -68,6 +68,18 @@ struct PrefillArgs {
     int Lpad;                 // L rounded up to a multiple of 64
 };
 
+// Indexer K-cache write path: T new keys quantised to FP8 and appended.
+struct KcacheArgs {
+    const void* k;               // [T][128] bf16 bit patterns or f32
+    const int32_t* seq_ids;      // [T] sequence of each key (outside [0, B): not written)
+    const int32_t* positions;    // [T] its position (outside [0, max_pages * 64): not written)
+    const int32_t* block_table;  // [B][max_pages] page ids
+    uint8_t* k_cache;            // [num_pages][64][128] E4M3FN codes
+    float* k_scale;              // [num_pages][64] one scale per cached token
+    int64_t T;
+    int B, max_pages;
+};
+
 size_t topk_select_smem_bytes();
 hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
@@ -76,5 +88,6 @@ hipError_t launch_decode_scan(const DecodeArgs& a, const SelectArgs& s, int H, h
 hipError_t launch_prefill_scores_generic(const PrefillArgs& a, int dtype, float* out, hipStream_t stream);
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream);
 size_t prefill_fused_workspace_bytes(int B, int L, int dtype);
+hipError_t launch_kcache_append(const KcacheArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace dsaidx

@@ -155,6 +155,46 @@ dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
 size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, int D, int topk);
 
 /*
+ * indexer_kcache_append -- quantise T new keys to FP8 and write them into the
+ * paged indexer key cache that indexer_decode_paged reads.
+ *
+ * Passage: "Lightning Indexer explained", sections 2.1 and 2.4 of the decode
+ * walkthrough (each token's key is appended to the indexer cache once, when
+ * that token is processed; later steps only read it) and section 5
+ * (Indexer-Cache); "Study MLA Indexer", the data-flow diagram (the key path
+ * ends in an FP8 quantisation) and the notes on its two caches (the cache is
+ * updated before the scoring decision).  The pages fix neither the FP8
+ * flavour nor the scaling; this library stores E4M3FN codes with one fp32
+ * scale per token:
+ *   scale  = max_d |k_d| / 448 (binary32 division; 1 for an all-zero key)
+ *   code_d = the E4M3FN value nearest to k_d / scale (binary32 quotient),
+ *            ties to the even code, magnitudes above 448 saturated, sign kept
+ * so decode(code_d) * scale is within half a code step of k_d.
+ *
+ *   k            [T][D] new keys in k_dtype (DSAIDX_BF16 or DSAIDX_F32),
+ *                16-byte aligned
+ *   seq_ids      [T] int32 sequence (row of block_table) of each key; a key
+ *                whose id lies outside [0, B) is skipped (-1 marks padding)
+ *   positions    [T] int32 position of each key in its sequence; a key whose
+ *                position lies outside [0, max_pages_per_seq * page_size) is
+ *                skipped
+ *   block_table  [B][max_pages_per_seq] int32 page ids (the decode layout:
+ *                position p lives in page block_table[b][p / page_size],
+ *                slot p % page_size)
+ *   k_cache      [num_pages][page_size][D] E4M3FN codes, updated in place
+ *   k_scale      [num_pages][page_size] fp32, updated in place
+ * Slots no key addresses are not touched.  Two keys with the same (sequence,
+ * position) in one call leave one of them, unspecified which.  T = 0 is a
+ * no-op.  No workspace.
+ *
+ * Supported: D = 128, page_size = 64, k_dtype BF16 or F32, 0 <= T.
+ */
+dsaidx_status indexer_kcache_append(const void* k, int k_dtype, const int32_t* seq_ids,
+                                    const int32_t* positions, const int32_t* block_table, int B,
+                                    int max_pages_per_seq, uint8_t* k_cache, float* k_scale, int num_pages,
+                                    int T, int D, int page_size, void* stream);
+
+/*
  * topk_select -- the token selector on its own: top-k of each row of a score
  * matrix.
  *

@@ -30,9 +30,9 @@ def lib():
     return _lib.load(LIB)
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     fns = header_functions()
-    for name in ("indexer_prefill", "indexer_decode_paged", "topk_select"):
+    for name in ("indexer_prefill", "indexer_decode_paged", "topk_select", "indexer_kcache_append"):
         assert name in fns
 
 
@@ -121,3 +121,23 @@ def test_decode_workspace_query(lib):
 ])
 def test_topk_select_rejects_before_launch(lib, args, status):
     assert lib.topk_select(*args, None, 0, None) == status
+
+
+def kcache(lib, k=P, dt=1, seq=P, pos=P, bt=P, B=2, mpp=4, kc=P, ks=P, npg=8, T=16, D=128, ps=64):
+    return lib.indexer_kcache_append(k, dt, seq, pos, bt, B, mpp, kc, ks, npg, T, D, ps, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), NULL), (dict(seq=None), NULL), (dict(pos=None), NULL), (dict(bt=None), NULL),
+    (dict(kc=None), NULL), (dict(ks=None), NULL),
+    (dict(dt=7), DTYPE), (dict(dt=2), UNSUP),
+    (dict(T=-1), SHAPE), (dict(B=0), SHAPE), (dict(mpp=0), SHAPE), (dict(npg=0), SHAPE),
+    (dict(D=64), UNSUP), (dict(ps=32), UNSUP), (dict(k=P + 8), UNSUP), (dict(kc=P + 4), UNSUP),
+])
+def test_kcache_append_rejects_before_launch(lib, kw, status):
+    assert kcache(lib, **kw) == status
+
+
+def test_kcache_append_empty_is_a_no_op(lib):
+    # T = 0 returns before any check of the arrays and before any HIP call
+    assert kcache(lib, T=0, k=None, seq=None, pos=None) == OK
