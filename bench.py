@@ -264,6 +264,46 @@ def main():
             torch.cuda.empty_cache()
         result["decode"] = dec
 
+    # ---------------- K-cache write path: the decode cache written in one bulk append ----------------
+    if not args.no_extra:
+        B4, ctx4 = 64, 131072
+        T = B4 * ctx4
+        g = torch.Generator(device=dev)
+        g.manual_seed(4)
+        kn = torch.randn((T, 128), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        ar = torch.arange(T, device=dev, dtype=torch.int32)
+        seq_ids, positions = ar // ctx4, ar % ctx4
+        table = torch.arange(B4 * (ctx4 // 64), device=dev, dtype=torch.int32).reshape(B4, ctx4 // 64)
+        cache = torch.empty((B4 * ctx4 // 64, 64, 128), dtype=torch.uint8, device=dev)
+        scale = torch.empty((B4 * ctx4 // 64, 64), dtype=torch.float32, device=dev)
+
+        def kstep():
+            dsa.kcache_append(kn, seq_ids, positions, table, cache, scale)
+
+        kms, _ = time_calls(torch, kstep, max(args.steps, 20), args.warmup)
+        nb = T * (256 + 8 + 132)
+        # a decode step's append: one new key per sequence (position 7 of each)
+        k64 = kn[:B4].contiguous()
+        s64 = torch.arange(B4, device=dev, dtype=torch.int32)
+        p64 = torch.full((B4,), 7, device=dev, dtype=torch.int32)
+
+        def kstep1():
+            dsa.kcache_append(k64, s64, p64, table, cache, scale)
+
+        k1ms, _ = time_calls(torch, kstep1, 200, args.warmup, warm_seconds=0.2)
+        log(f"kcache append: {kms:.3f} ms for {T} keys ({nb / (kms * 1e-3) / 1e9:.0f} GB/s); "
+            f"64 keys {k1ms * 1e3:.1f} us")
+        result["kcache_append"] = {
+            "what": "64 sequences x 131072 bf16 keys quantised to fp8 e4m3 (absmax/448 scale) and written "
+                    "through the block table: the decode workload's whole cache in one call",
+            "keys": T, "bytes_per_call": nb, "ms_per_call": kms, "GB/s": nb / (kms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": nb / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "work": "per key 256 B bf16 + 8 B sequence/position read, 128 B codes + 4 B scale written",
+            "us_per_call_64_keys": k1ms * 1e3,
+        }
+        del kn, ar, seq_ids, positions, table, cache, scale, k64, s64, p64
+        torch.cuda.empty_cache()
+
     # ---------------- the other prefill workloads: bf16 L=8192, tiny fp32 ----------------
     if not args.decode_only and not args.no_extra:
         extra = {}

@@ -16,10 +16,15 @@
 // Each lane holds 8 elements (16 bytes of bf16 or 32 of f32), the absmax is
 // a 16-lane xor reduction, and each lane stores 8 codes (8 bytes) of the
 // 128-byte row; the first lane of the 16 stores the scale.  Every lane group
-// takes four keys per pass, with all their loads issued before any is used.
+// takes two keys, with all their loads issued before either is used, and
+// the grid covers all keys in one pass (measured on 8.4M keys: two keys per
+// group beat one, four and eight -- registers against loads in flight --
+// and a grid-stride loop over fewer workgroups was slower).
 // The hardware conversion rounds to nearest even; values are clamped to
-// +-448 first, so none overflows.  HBM bound: per key 256 bytes (bf16) or
-// 512 (f32) read, 132 written.
+// +-448 first, so none overflows.  The quotient is a correctly rounded
+// division: a reciprocal multiply would save ~12% of the time but can land
+// on the other side of a code midpoint.  HBM bound: per key 256 bytes
+// (bf16) or 512 (f32) of key and 8 of placement read, 132 written.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,7 +34,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kPage = 64;
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;  // keys per lane group per pass
+constexpr int kUnroll = 2;  // keys per lane group
 
 template <int DT>  // 0 = f32, 1 = bf16
 __device__ __forceinline__ void load_key(const KcacheArgs& a, int64_t i, int l16, float (&x)[8]) {
@@ -112,10 +117,9 @@ kcache_append_kernel(KcacheArgs a) {
 
 hipError_t launch_kcache_append(const KcacheArgs& a, int dtype, hipStream_t stream) {
     if (a.T <= 0) return hipSuccess;
-    // 16 lanes per key, four keys per lane group and pass; at most 16
-    // workgroups per compute unit of the 256 are ever needed in flight
-    int64_t blocks = (a.T * 16 + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-    if (blocks > 4096) blocks = 4096;
+    // 16 lanes per key, kUnroll keys per lane group: every key in one pass
+    // (at most 2^26 workgroups for T < 2^31)
+    const int64_t blocks = (a.T * 16 + kThreads * kUnroll - 1) / (kThreads * kUnroll);
     if (dtype == 1)
         hipLaunchKernelGGL(kcache_append_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     else

@@ -128,3 +128,33 @@ def test_large_append_then_decode_reads_it():
     gi, gv = run_decode(d, K)
     o = indexer.decode_scores(d, 0)
     check_topk_rows(gi, gv, o[None], [ctx], K, where="decode of the appended cache")
+
+
+def test_full_size_bulk_append_sampled():
+    # the bench's configuration: 64 sequences x 131072 bf16 keys (seeded on the
+    # device), identity block table; sampled keys checked bit for bit
+    dev = torch.device("cuda")
+    B, ctx = 64, 131072
+    T = B * ctx
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    kn = torch.randn((T, 128), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    ar = torch.arange(T, device=dev, dtype=torch.int32)
+    table = torch.arange(B * ctx // 64, device=dev, dtype=torch.int32).reshape(B, ctx // 64)
+    cache = torch.zeros((B * ctx // 64, 64, 128), dtype=torch.uint8, device=dev)
+    scale = torch.zeros((B * ctx // 64, 64), dtype=torch.float32, device=dev)
+    say(f"kcache full size: T={T}")
+    dsa.kcache_append(kn, ar // ctx, ar % ctx, table, cache, scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(44)
+    pick = np.concatenate([[0, T - 1, ctx - 1, ctx], rng.integers(0, T, 4000)])
+    keys = kn[torch.from_numpy(pick).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
+    from oracle.kcache import key_rows_to_f32, quantize_keys
+    codes, sc = quantize_keys(key_rows_to_f32(keys, "bf16"))
+    rows = torch.from_numpy(pick).to(dev)  # identity table: key i sits in row i of the flattened pool
+    g_codes = cache.view(-1, 128)[rows].cpu().numpy()
+    g_sc = scale.view(-1)[rows].cpu().numpy()
+    assert np.array_equal(g_codes, codes)
+    assert np.array_equal(g_sc.view(np.uint32), sc.view(np.uint32))
+    # every slot was written (no zero scale left)
+    assert bool((scale > 0).all())
