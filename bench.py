@@ -304,6 +304,32 @@ def main():
         del kn, ar, seq_ids, positions, table, cache, scale, k64, s64, p64
         torch.cuda.empty_cache()
 
+    # ---------------- the selection's consumer: gather of the selected latent rows ----------------
+    if not args.no_extra:
+        B4, K4, ctx4, row = 64, 2048, 131072, 1024
+        n_pages = B4 * ctx4 // 64
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+        cache = torch.randint(0, 256, (n_pages, 64, row), generator=g, device=dev, dtype=torch.uint8)
+        table = torch.arange(n_pages, device=dev, dtype=torch.int32).reshape(B4, ctx4 // 64)
+        gidx = torch.randint(0, ctx4, (B4, K4), generator=g, device=dev, dtype=torch.int32)
+
+        def gstep():
+            dsa.topk_gather(cache, table, gidx)
+
+        gms, _ = time_calls(torch, gstep, max(args.steps, 200), args.warmup, warm_seconds=0.2)
+        nb = B4 * K4 * (2 * row + 8)
+        log(f"topk gather: {gms * 1e3:.1f} us for {B4}x{K4} rows of {row} B ({nb / (gms * 1e-3) / 1e9:.0f} GB/s)")
+        result["topk_gather"] = {
+            "what": "64 queries x 2048 selected positions gathered from paged 131072-token latent caches "
+                    "(1024-byte rows = 512 bf16), random positions",
+            "rows": B4 * K4, "bytes_per_call": nb, "us_per_call": gms * 1e3, "GB/s": nb / (gms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": nb / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "work": "per row 1024 B read + 1024 B written + 4 B index + 4 B page id",
+        }
+        del cache, table, gidx
+        torch.cuda.empty_cache()
+
     # ---------------- the other prefill workloads: bf16 L=8192, tiny fp32 ----------------
     if not args.decode_only and not args.no_extra:
         extra = {}

@@ -21,8 +21,8 @@ from . import _lib
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
-__all__ = ["indexer_prefill", "indexer_decode_paged", "topk_select", "kcache_append", "dtype_code", "F32", "BF16",
-           "FP8_E4M3"]
+__all__ = ["indexer_prefill", "indexer_decode_paged", "topk_select", "kcache_append", "topk_gather", "dtype_code",
+           "F32", "BF16", "FP8_E4M3"]
 
 
 def dtype_code(t: torch.Tensor) -> int:
@@ -167,3 +167,24 @@ def kcache_append(k, seq_ids, positions, block_table, k_cache, k_scale):
     st = lib.indexer_kcache_append(_ptr(k), dtype_code(k), _ptr(seq_ids), _ptr(positions), _ptr(block_table),
                                    B, mpp, _ptr(k_cache), _ptr(k_scale), P, T, D, page, _stream(k.device))
     _lib.check(st, "indexer_kcache_append")
+
+
+def topk_gather(latent_cache, block_table, topk_idx):
+    """Rows of a paged latent cache at each query's selected positions.
+
+    latent_cache [P,page,E] (any element type; E * element size a multiple of
+    16 bytes), block_table [B,max_pages] int32, topk_idx [B,K] int32 (-1 or
+    outside the table: a zero row).  Returns out [B,K,E] of the cache's dtype."""
+    lib = _lib.load()
+    P, page, E = latent_cache.shape
+    B, K = topk_idx.shape
+    if block_table.shape[0] != B or topk_idx.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise ValueError("block_table [B, max_pages] and topk_idx [B, K] must be int32 with matching B")
+    for name, t in (("latent_cache", latent_cache), ("block_table", block_table), ("topk_idx", topk_idx)):
+        _dev(t, name)
+    out = torch.empty((B, K, E), dtype=latent_cache.dtype, device=latent_cache.device)
+    st = lib.indexer_topk_gather(_ptr(latent_cache), E * latent_cache.element_size(), _ptr(block_table),
+                                 block_table.shape[1], P, page, _ptr(topk_idx), B, K, _ptr(out),
+                                 _stream(latent_cache.device))
+    _lib.check(st, "indexer_topk_gather")
+    return out

@@ -93,6 +93,36 @@ dsaidx_status indexer_kcache_append(const void* k, int k_dtype, const int32_t* s
     return DSAIDX_OK;
 }
 
+dsaidx_status indexer_topk_gather(const void* latent_cache, int row_bytes, const int32_t* block_table,
+                                  int max_pages_per_seq, int num_pages, int page_size,
+                                  const int32_t* topk_idx, int B, int topk, void* out, void* stream) {
+    g_err[0] = 0;
+    if (!latent_cache) return fail(DSAIDX_ERR_NULL, "latent_cache is NULL");
+    if (!block_table) return fail(DSAIDX_ERR_NULL, "block_table is NULL");
+    if (!topk_idx) return fail(DSAIDX_ERR_NULL, "topk_idx is NULL");
+    if (!out) return fail(DSAIDX_ERR_NULL, "out is NULL");
+    if (B < 1 || topk < 1 || max_pages_per_seq < 1 || num_pages < 1 || page_size < 1 || row_bytes < 1)
+        return fail(DSAIDX_ERR_SHAPE, "B=%d topk=%d max_pages_per_seq=%d num_pages=%d page_size=%d row_bytes=%d",
+                    B, topk, max_pages_per_seq, num_pages, page_size, row_bytes);
+    if (page_size != 64) return fail(DSAIDX_ERR_UNSUPPORTED, "page_size=%d (64)", page_size);
+    if (row_bytes % 16 != 0 || row_bytes > 65536)
+        return fail(DSAIDX_ERR_UNSUPPORTED, "row_bytes=%d (a multiple of 16, at most 65536)", row_bytes);
+    if (!aligned16(latent_cache) || !aligned16(out))
+        return fail(DSAIDX_ERR_UNSUPPORTED, "latent_cache and out must be 16-byte aligned");
+    dsaidx::GatherArgs a{};
+    a.cache = reinterpret_cast<const uint8_t*>(latent_cache);
+    a.block_table = block_table;
+    a.idx = topk_idx;
+    a.out = reinterpret_cast<uint8_t*>(out);
+    a.B = B;
+    a.K = topk;
+    a.max_pages = max_pages_per_seq;
+    a.row_bytes = row_bytes;
+    const hipError_t e = dsaidx::launch_topk_gather(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "indexer_topk_gather");
+    return DSAIDX_OK;
+}
+
 size_t topk_select_workspace_bytes(int rows, int cols, int topk) {
     (void)rows; (void)cols; (void)topk;
     return 0;

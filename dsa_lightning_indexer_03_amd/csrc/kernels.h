@@ -80,6 +80,15 @@ struct KcacheArgs {
     int B, max_pages;
 };
 
+// The selection's consumer: rows of a paged latent cache at selected positions.
+struct GatherArgs {
+    const uint8_t* cache;        // [num_pages][64][row_bytes]
+    const int32_t* block_table;  // [B][max_pages] page ids
+    const int32_t* idx;          // [B][K] positions (-1 or outside the table: zero row)
+    uint8_t* out;                // [B][K][row_bytes]
+    int B, K, max_pages, row_bytes;
+};
+
 size_t topk_select_smem_bytes();
 hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
@@ -89,5 +98,6 @@ hipError_t launch_prefill_scores_generic(const PrefillArgs& a, int dtype, float*
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream);
 size_t prefill_fused_workspace_bytes(int B, int L, int dtype);
 hipError_t launch_kcache_append(const KcacheArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_topk_gather(const GatherArgs& a, hipStream_t stream);
 
 }  // namespace dsaidx

@@ -195,6 +195,31 @@ dsaidx_status indexer_kcache_append(const void* k, int k_dtype, const int32_t* s
                                     int T, int D, int page_size, void* stream);
 
 /*
+ * indexer_topk_gather -- the selection's consumer: the rows of a paged latent
+ * cache at each query's selected positions, gathered contiguously.
+ *
+ * Passage: "Study MLA Indexer", the data-flow diagram's last step (the sparse
+ * attention gathers the latent c^KV at the top-k positions) and the first of
+ * its "three whys" (a decode step then moves k * d_c elements, not the whole
+ * context).  The latent cache is taken to share the indexer cache's paging:
+ * position s of query b lives in page block_table[b][s / page_size], slot
+ * s % page_size.  Rows are opaque bytes.
+ *
+ *   latent_cache  [num_pages][page_size][row_bytes], 16-byte aligned
+ *   block_table   [B][max_pages_per_seq] int32 page ids
+ *   topk_idx      [B][topk] int32 positions, e.g. indexer_decode_paged's
+ *                 output; -1, or a position outside
+ *                 [0, max_pages_per_seq * page_size), gives a zero row
+ *   out           out [B][topk][row_bytes], 16-byte aligned
+ * No workspace.
+ *
+ * Supported: page_size = 64, row_bytes a multiple of 16 in [16, 65536].
+ */
+dsaidx_status indexer_topk_gather(const void* latent_cache, int row_bytes, const int32_t* block_table,
+                                  int max_pages_per_seq, int num_pages, int page_size,
+                                  const int32_t* topk_idx, int B, int topk, void* out, void* stream);
+
+/*
  * topk_select -- the token selector on its own: top-k of each row of a score
  * matrix.
  *

@@ -32,7 +32,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     fns = header_functions()
-    for name in ("indexer_prefill", "indexer_decode_paged", "topk_select", "indexer_kcache_append"):
+    for name in ("indexer_prefill", "indexer_decode_paged", "topk_select", "indexer_kcache_append",
+                 "indexer_topk_gather"):
         assert name in fns
 
 
@@ -141,3 +142,17 @@ def test_kcache_append_rejects_before_launch(lib, kw, status):
 def test_kcache_append_empty_is_a_no_op(lib):
     # T = 0 returns before any check of the arrays and before any HIP call
     assert kcache(lib, T=0, k=None, seq=None, pos=None) == OK
+
+
+def gather(lib, lc=P, rb=1024, bt=P, mpp=4, npg=8, ps=64, idx=P, B=2, K=16, out=P):
+    return lib.indexer_topk_gather(lc, rb, bt, mpp, npg, ps, idx, B, K, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lc=None), NULL), (dict(bt=None), NULL), (dict(idx=None), NULL), (dict(out=None), NULL),
+    (dict(B=0), SHAPE), (dict(K=0), SHAPE), (dict(mpp=0), SHAPE), (dict(npg=0), SHAPE), (dict(rb=0), SHAPE),
+    (dict(ps=32), UNSUP), (dict(rb=1000), UNSUP), (dict(rb=65552), UNSUP), (dict(lc=P + 8), UNSUP),
+    (dict(out=P + 4), UNSUP),
+])
+def test_topk_gather_rejects_before_launch(lib, kw, status):
+    assert gather(lib, **kw) == status
