@@ -21,8 +21,8 @@ from . import _lib
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
-__all__ = ["indexer_prefill", "indexer_decode_paged", "topk_select", "kcache_append", "topk_gather", "dtype_code",
-           "F32", "BF16", "FP8_E4M3"]
+__all__ = ["indexer_prefill", "indexer_decode_paged", "topk_select", "kcache_append", "topk_gather",
+           "prefill_chunk_paged", "dtype_code", "F32", "BF16", "FP8_E4M3"]
 
 
 def dtype_code(t: torch.Tensor) -> int:
@@ -188,3 +188,34 @@ def topk_gather(latent_cache, block_table, topk_idx):
                                  _stream(latent_cache.device))
     _lib.check(st, "indexer_topk_gather")
     return out
+
+
+def prefill_chunk_paged(q, q_scale, w, k_cache, k_scale, block_table, q0: int, topk: int,
+                        want_topk_score: bool = True, workspace: torch.Tensor | None = None):
+    """Top-k of a chunk of Lq query tokens per sequence at positions q0 ..
+    q0+Lq-1 against a paged fp8 key cache that holds keys 0 .. q0+Lq-1.
+
+    q [B,Lq,H,D] fp8 codes (uint8), q_scale [B,Lq,H] fp32, w [B,Lq,H] fp32,
+    k_cache [P,page,D] uint8, k_scale [P,page] fp32, block_table [B,max_pages]
+    int32.  Returns (idx int32 [B,Lq,topk] of absolute positions, score fp32
+    or None)."""
+    lib = _lib.load()
+    B, Lq, H, D = q.shape
+    P, page, Dk = k_cache.shape
+    if Dk != D or tuple(k_scale.shape) != (P, page) or tuple(w.shape) != (B, Lq, H):
+        raise ValueError("shape mismatch")
+    if tuple(q_scale.shape) != (B, Lq, H) or block_table.shape[0] != B:
+        raise ValueError("q_scale / block_table shape mismatch")
+    for name, t in (("q", q), ("q_scale", q_scale), ("w", w), ("k_cache", k_cache), ("k_scale", k_scale),
+                    ("block_table", block_table)):
+        _dev(t, name)
+    dev = q.device
+    idx = torch.empty((B, Lq, topk), dtype=torch.int32, device=dev)
+    val = torch.empty((B, Lq, topk), dtype=torch.float32, device=dev) if want_topk_score else None
+    nws = lib.indexer_prefill_chunk_paged_workspace_bytes(B, q0, Lq)
+    ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, dev)
+    st = lib.indexer_prefill_chunk_paged(_ptr(q), _ptr(q_scale), dtype_code(q), _ptr(w), _ptr(k_cache),
+                                         _ptr(k_scale), _ptr(block_table), block_table.shape[1], P, B, q0, Lq, H, D,
+                                         page, topk, _ptr(idx), _ptr(val), _ptr(ws), nws, _stream(dev))
+    _lib.check(st, "indexer_prefill_chunk_paged")
+    return idx, val

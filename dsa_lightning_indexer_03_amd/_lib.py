@@ -28,6 +28,11 @@ SIGNATURES = {
     "topk_select_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "indexer_kcache_append": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                        _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
+    "indexer_prefill_chunk_paged": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p,
+                                             _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                             _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
+                                             _c_void_p]),
+    "indexer_prefill_chunk_paged_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "indexer_topk_gather": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int,
                                      _c_int, _c_void_p, _c_void_p]),
     "dsaidx_status_string": (ctypes.c_char_p, [_c_int]),

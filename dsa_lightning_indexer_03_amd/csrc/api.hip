@@ -239,6 +239,70 @@ dsaidx_status indexer_prefill(const void* q, const float* q_scale, const void* k
     return DSAIDX_OK;
 }
 
+size_t indexer_prefill_chunk_paged_workspace_bytes(int B, int q0, int Lq) {
+    if (B < 1 || q0 < 0 || Lq < 1) return 0;
+    return dsaidx::prefill_fused_workspace_bytes(B, q0 + Lq, DSAIDX_FP8_E4M3);
+}
+
+dsaidx_status indexer_prefill_chunk_paged(const void* q, const float* q_scale, int q_dtype, const float* w,
+                                          const uint8_t* k_cache, const float* k_scale,
+                                          const int32_t* block_table, int max_pages_per_seq, int num_pages,
+                                          int B, int q0, int Lq, int H, int D, int page_size, int topk,
+                                          int32_t* topk_idx, float* topk_score,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!q) return fail(DSAIDX_ERR_NULL, "q is NULL");
+    if (!q_scale) return fail(DSAIDX_ERR_NULL, "q_scale is NULL");
+    if (!w) return fail(DSAIDX_ERR_NULL, "w is NULL");
+    if (!k_cache) return fail(DSAIDX_ERR_NULL, "k_cache is NULL");
+    if (!k_scale) return fail(DSAIDX_ERR_NULL, "k_scale is NULL");
+    if (!block_table) return fail(DSAIDX_ERR_NULL, "block_table is NULL");
+    if (!topk_idx) return fail(DSAIDX_ERR_NULL, "topk_idx is NULL");
+    if (q_dtype != DSAIDX_F32 && q_dtype != DSAIDX_BF16 && q_dtype != DSAIDX_FP8_E4M3)
+        return fail(DSAIDX_ERR_DTYPE, "q_dtype=%d", q_dtype);
+    if (B < 1 || q0 < 0 || Lq < 1 || H < 1 || D < 1 || page_size < 1 || topk < 1 || max_pages_per_seq < 1 ||
+        num_pages < 1)
+        return fail(DSAIDX_ERR_SHAPE, "B=%d q0=%d Lq=%d H=%d D=%d page_size=%d topk=%d max_pages_per_seq=%d "
+                    "num_pages=%d", B, q0, Lq, H, D, page_size, topk, max_pages_per_seq, num_pages);
+    if ((int64_t)q0 + Lq > (int64_t)max_pages_per_seq * page_size)
+        return fail(DSAIDX_ERR_SHAPE, "q0 + Lq = %lld > max_pages_per_seq * page_size = %lld",
+                    (long long)q0 + Lq, (long long)max_pages_per_seq * page_size);
+    if (q_dtype != DSAIDX_FP8_E4M3) return fail(DSAIDX_ERR_UNSUPPORTED, "chunk queries must be fp8 (q_scale given)");
+    if (H % 16 != 0 || H > 64) return fail(DSAIDX_ERR_UNSUPPORTED, "H=%d (16, 32, 48 or 64)", H);
+    if (D != 128) return fail(DSAIDX_ERR_UNSUPPORTED, "D=%d (128)", D);
+    if (page_size != 64) return fail(DSAIDX_ERR_UNSUPPORTED, "page_size=%d (64)", page_size);
+    if (topk > kMaxTopk) return fail(DSAIDX_ERR_UNSUPPORTED, "topk=%d > %d", topk, kMaxTopk);
+    if ((int64_t)q0 + Lq > 65536) return fail(DSAIDX_ERR_UNSUPPORTED, "q0 + Lq = %lld > 65536", (long long)q0 + Lq);
+    if (!aligned16(q) || !aligned16(k_cache)) return fail(DSAIDX_ERR_UNSUPPORTED, "q and k_cache must be 16-byte aligned");
+    if (!aligned16(workspace)) return fail(DSAIDX_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+    const size_t need = indexer_prefill_chunk_paged_workspace_bytes(B, q0, Lq);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSAIDX_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    dsaidx::PrefillArgs a{};
+    a.q = q;
+    a.q_scale = q_scale;
+    a.k = k_cache;
+    a.k_scale = k_scale;
+    a.w = w;
+    a.B = B;
+    a.L = Lq;
+    a.H = H;
+    a.D = D;
+    a.topk = topk;
+    a.inv_sqrt_d = 1.0f / sqrtf((float)D);
+    a.idx_out = topk_idx;
+    a.val_out = topk_score;
+    a.scores = nullptr;
+    a.workspace = workspace;
+    a.q0 = q0;
+    a.Lk = q0 + Lq;
+    a.block_table = block_table;
+    a.max_pages = max_pages_per_seq;
+    const hipError_t e = dsaidx::launch_prefill_chunk_paged(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "indexer_prefill_chunk_paged");
+    return DSAIDX_OK;
+}
+
 size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, int D, int topk) {
     (void)H; (void)D; (void)topk;
     if (B < 1 || max_context_len < 0) return 0;

@@ -65,7 +65,14 @@ struct PrefillArgs {
     // set by the fused launcher from the workspace:
     float* ks_adj;            // [B][Lpad] key scales times 2^Pk
     uint8_t* kexp;            // [B][Lpad] E8M0 bytes 127 - Pk, lane-major within each 64-key chunk
-    int Lpad;                 // L rounded up to a multiple of 64
+    int Lpad;                 // keys rounded up to a multiple of 64
+    // A chunk of L queries at positions q0 .. q0+L-1 against a paged fp8 key
+    // cache (k = the page pool [pages][64][D], k_scale = [pages][64]); key s
+    // of sequence b sits in page block_table[b][s / 64], slot s % 64.
+    int q0;
+    int Lk;                   // keys the chunk sees: q0 + L
+    const int32_t* block_table;
+    int max_pages;
 };
 
 // Indexer K-cache write path: T new keys quantised to FP8 and appended.
@@ -97,6 +104,8 @@ hipError_t launch_decode_scan(const DecodeArgs& a, const SelectArgs& s, int H, h
 hipError_t launch_prefill_scores_generic(const PrefillArgs& a, int dtype, float* out, hipStream_t stream);
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream);
 size_t prefill_fused_workspace_bytes(int B, int L, int dtype);
+// fp8 queries of a chunk against the paged cache (fields q0, Lk, block_table, max_pages)
+hipError_t launch_prefill_chunk_paged(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_kcache_append(const KcacheArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_topk_gather(const GatherArgs& a, hipStream_t stream);
 

@@ -732,14 +732,19 @@ static_assert(kStagedLds + 16 <= 160 * 1024, "LDS budget");
 // 2^Pk >= max_d |k_d| (Pk = 0 for a zero row), ks_adj = k_scale * 2^Pk and
 // the E8M0 byte 127 - Pk, stored at 64*chunk + 4*(s % 16) + (s % 64) / 16 so
 // that lane n of a chunk finds the bytes of its four subtiles in one word.
+template <bool PAGED>
 __global__ void __launch_bounds__(256)
 prefill_key_exp_kernel(PrefillArgs a) {
     const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int Lp = a.Lpad;
     if (gi >= (int64_t)a.B * Lp) return;
     const int b = (int)(gi / Lp), s = (int)(gi % Lp);
-    const int sr = s < a.L ? s : a.L - 1;
-    const uint8_t* row = reinterpret_cast<const uint8_t*>(a.k) + ((size_t)b * a.L + sr) * kD;
+    const int Lk = PAGED ? a.Lk : a.L;
+    const int sr = s < Lk ? s : Lk - 1;
+    // the key's slot: row sr of sequence b, or its page-pool slot
+    const size_t slot = PAGED ? (size_t)a.block_table[(size_t)b * a.max_pages + sr / 64] * 64 + sr % 64
+                              : (size_t)b * a.L + sr;
+    const uint8_t* row = reinterpret_cast<const uint8_t*>(a.k) + slot * kD;
     uint32_t mx = 0;
 #pragma unroll
     for (int c = 0; c < kD / 16; ++c) {
@@ -752,7 +757,7 @@ prefill_key_exp_kernel(PrefillArgs a) {
     }
     const float vmax = __builtin_amdgcn_cvt_f32_fp8((int)mx, 0);
     const int pk = vmax > 0.f ? __builtin_amdgcn_frexp_expf(vmax) : 0;  // 2^pk > vmax
-    a.ks_adj[gi] = ldexpf(a.k_scale[(size_t)b * a.L + sr], pk);
+    a.ks_adj[gi] = ldexpf(a.k_scale[slot], pk);
     const int c = s / 64, n = s % 16, q = (s % 64) / 16;
     a.kexp[(size_t)b * Lp + 64 * c + 4 * n + q] = (uint8_t)(127 - pk);
 }
@@ -767,7 +772,7 @@ __device__ __forceinline__ uint32_t spec_rank(float ec) {
     return (uint32_t)ceilf(ec + 3.5f * sqrtf(ec) + 8.f);
 }
 
-template <int HB>
+template <int HB, bool PAGED>
 __global__ void __launch_bounds__(kStagedWaves * kWave)
 prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -785,6 +790,11 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     const int t_raw = blk * W + wave;
     const bool live = t_raw < L;        // waves past the end only help stage keys
     const int t = live ? t_raw : L - 1;
+    // A chunk of queries against the paged cache starts at position q0 and
+    // sees Lk keys; a whole sequence has q0 = 0 and Lk = L.
+    const int q0 = PAGED ? a.q0 : 0;
+    const int Lk = PAGED ? a.Lk : L;
+    const int tp = q0 + t;              // the token's position: its row sees keys 0 .. tp
     const int lane = lane_id();
     const int n = lane & 15, g = lane >> 4;
 
@@ -860,7 +870,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     const float* ksadj = a.ks_adj + (size_t)b * a.Lpad;
     const uint8_t* kexp = a.kexp + (size_t)b * a.Lpad;
     float* srow = (a.scores && live) ? a.scores + row_t * L : nullptr;
-    const int last = (min(blk * W + W - 1, L - 1)) / 64;   // same for every wave of the block
+    const int last = (q0 + min(blk * W + W - 1, L - 1)) / 64;   // same for every wave of the block
 
     // Chunk order.  When the block spans at least 32 chunks, a strided sample
     // (chunks 16i+15, i < S) is scored first; the rest follow in increasing
@@ -897,8 +907,12 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     const int sseg = (threadIdx.x & 7) ^ ((srow_i >> 1) & 7);
     auto stage_chunk = [&](int slot, int chunk) {
         unsigned char* dst = smem_raw + slot * kStageBytes;
-        const int r = min(chunk * 64 + srow_i, L - 1);
-        const uint8_t* src = kbase + (size_t)r * kD + 16 * sseg;
+        const int r = min(chunk * 64 + srow_i, Lk - 1);
+        // a 64-key chunk is one page of the paged cache
+        const uint8_t* src =
+            PAGED ? reinterpret_cast<const uint8_t*>(a.k) +
+                        ((size_t)a.block_table[(size_t)b * a.max_pages + (r >> 6)] * 64 + (r & 63)) * kD + 16 * sseg
+                  : kbase + (size_t)r * kD + 16 * sseg;
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 1024 * wave),
                                          16, 0, 0);
         if (wave == 0)
@@ -921,8 +935,8 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     bool active = live;   // this wave scores and appends in the current pass
     bool floored = false; // a speculative floor is in force
     uint32_t r_spec = 0;  // rank of the floor in the sample (0: no floor)
-    if (live && S >= 2 && t + 1 > 2 * K) {
-        const float ec = 64.f * (float)S * (float)K / (float)(t + 1);
+    if (live && S >= 2 && tp + 1 > 2 * K) {
+        const float ec = 64.f * (float)S * (float)K / (float)(tp + 1);
         r_spec = spec_rank(ec);
     }
 
@@ -1046,7 +1060,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             f.s = chunk * 64 + lane;
             // bitwise, not short-circuit (a branch here would split the
             // region); an inactive wave's threshold admits nothing
-            f.app = (f.s <= t) & (f.key > thr_eff);
+            f.app = (f.s <= tp) & (f.key > thr_eff);
         }
         if (piece == 3) {
             f.m = wave_ballot(f.app);
@@ -1065,7 +1079,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     auto finish_tail = [&](int fslot, int chunk, float score) {
         if (srow && active) {
             const int s = chunk * 64 + lane;
-            if (s < L) srow[s] = s <= t ? score : -INFINITY;
+            if (s < Lk) srow[s] = s <= tp ? score : -INFINITY;
         }
         if (active && nb > CAP - 2 * kWave && lane == 0) flags[fslot] = 1u;
     };
@@ -1208,7 +1222,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     }
     if (!live) return;
     if (srow) {
-        for (int s = (last + 1) * 64 + lane; s < L; s += kWave) srow[s] = -INFINITY;
+        for (int s = (last + 1) * 64 + lane; s < Lk; s += kWave) srow[s] = -INFINITY;
     }
     __builtin_amdgcn_wave_barrier();
     wave_emit(rb, nb, K, a.idx_out + row_t * K, a.val_out ? a.val_out + row_t * K : nullptr);
@@ -1663,28 +1677,33 @@ constexpr bool staged_path(int dtype, int L) { return DSAIDX_PREFILL_STAGED && d
 constexpr bool staged_bf16_path(int dtype, int L) { return DSAIDX_PREFILL_STAGED_BF16 && dtype == 1 && L <= 65536; }
 constexpr int pad64(int L) { return (L + 63) / 64 * 64; }
 
-template <int HB>
+template <int HB, bool PAGED = false>
 hipError_t launch_fp8_staged(const PrefillArgs& a_in, hipStream_t stream) {
     PrefillArgs a = a_in;
-    a.Lpad = pad64(a.L);
+    if (!PAGED) {
+        a.q0 = 0;
+        a.Lk = a.L;
+    }
+    a.Lpad = pad64(a.Lk);
     a.ks_adj = reinterpret_cast<float*>(a.workspace);
     a.kexp = reinterpret_cast<uint8_t*>(a.ks_adj + (size_t)a.B * a.Lpad);
     {
         const int64_t n = (int64_t)a.B * a.Lpad;
-        hipLaunchKernelGGL(prefill_key_exp_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(prefill_key_exp_kernel<PAGED>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const size_t smem = kStagedLds;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_fused_fp8_staged_kernel<HB>,
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_fused_fp8_staged_kernel<HB, PAGED>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
         attr = true;
     }
     const int nblk = (a.L + kStagedWaves - 1) / kStagedWaves;
-    hipLaunchKernelGGL((prefill_fused_fp8_staged_kernel<HB>), dim3((unsigned)(nblk * a.B)),
+    hipLaunchKernelGGL((prefill_fused_fp8_staged_kernel<HB, PAGED>), dim3((unsigned)(nblk * a.B)),
                        dim3(kStagedWaves * kWave), smem, stream, a);
     return hipGetLastError();
 }
@@ -1730,6 +1749,16 @@ size_t prefill_fused_workspace_bytes(int B, int L, int dtype) {
     if (staged_path(dtype, L)) return (n * 5 + 255) / 256 * 256;  // fp32 adjusted scales, then the E8M0 bytes
     if (staged_bf16_path(dtype, L)) return n * (4 + 2 * kD);      // fp32 adjusted scales, then the scaled keys
     return 0;
+}
+
+hipError_t launch_prefill_chunk_paged(const PrefillArgs& a, hipStream_t stream) {
+    switch (a.H / 16) {
+        case 1: return launch_fp8_staged<1, true>(a, stream);
+        case 2: return launch_fp8_staged<2, true>(a, stream);
+        case 3: return launch_fp8_staged<3, true>(a, stream);
+        case 4: return launch_fp8_staged<4, true>(a, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream) {

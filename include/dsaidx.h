@@ -155,6 +155,46 @@ dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
 size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, int D, int topk);
 
 /*
+ * indexer_prefill_chunk_paged -- a chunk of Lq new query tokens per sequence,
+ * at positions q0 .. q0+Lq-1, scored against the paged FP8 key cache that
+ * already holds keys 0 .. q0+Lq-1 (the chunk's own keys included), with the
+ * top-k of every query.
+ *
+ * Passage: the core formula and causal top-k of indexer_prefill, evaluated
+ * for the rows q0 .. q0+Lq-1 of the sequence; the keys come from the indexer
+ * cache, which each token's key enters before that token is scored
+ * ("Lightning Indexer explained", sections 2.1 and 2.4 of the decode
+ * walkthrough; "Study MLA Indexer", the notes on its two caches).  The
+ * result for query i equals indexer_prefill's row q0+i over the whole
+ * sequence: it sees the q0+i+1 positions 0 .. q0+i.
+ *
+ *   q            [B][Lq][H][D] FP8 E4M3 codes (q_dtype must be
+ *                DSAIDX_FP8_E4M3), q_scale [B][Lq][H] fp32
+ *   w            [B][Lq][H] fp32
+ *   k_cache      [num_pages][page_size][D] E4M3FN codes, k_scale
+ *                [num_pages][page_size] fp32 (as indexer_kcache_append writes)
+ *   block_table  [B][max_pages_per_seq] int32 page ids; position s of
+ *                sequence b is page block_table[b][s / page_size], slot
+ *                s % page_size; q0 + Lq <= max_pages_per_seq * page_size
+ *   topk_idx     out [B][Lq][topk] int32 (absolute positions, -1 padded);
+ *   topk_score   out [B][Lq][topk] fp32 or NULL
+ *   workspace    indexer_prefill_chunk_paged_workspace_bytes(B, q0, Lq)
+ *                bytes of caller-owned device memory, 16-byte aligned
+ *                (5 bytes per visible key, 256-byte rounded)
+ *
+ * Supported: H a multiple of 16 in [16, 64], D = 128, page_size = 64,
+ * 1 <= topk <= 2048, q0 + Lq <= 65536.
+ */
+dsaidx_status indexer_prefill_chunk_paged(const void* q, const float* q_scale, int q_dtype, const float* w,
+                                          const uint8_t* k_cache, const float* k_scale,
+                                          const int32_t* block_table, int max_pages_per_seq, int num_pages,
+                                          int B, int q0, int Lq, int H, int D, int page_size, int topk,
+                                          int32_t* topk_idx, float* topk_score,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+size_t indexer_prefill_chunk_paged_workspace_bytes(int B, int q0, int Lq);
+
+/*
  * indexer_kcache_append -- quantise T new keys to FP8 and write them into the
  * paged indexer key cache that indexer_decode_paged reads.
  *

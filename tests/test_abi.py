@@ -33,7 +33,7 @@ def lib():
 def test_header_declares_the_entry_points():
     fns = header_functions()
     for name in ("indexer_prefill", "indexer_decode_paged", "topk_select", "indexer_kcache_append",
-                 "indexer_topk_gather"):
+                 "indexer_topk_gather", "indexer_prefill_chunk_paged"):
         assert name in fns
 
 
@@ -156,3 +156,26 @@ def gather(lib, lc=P, rb=1024, bt=P, mpp=4, npg=8, ps=64, idx=P, B=2, K=16, out=
 ])
 def test_topk_gather_rejects_before_launch(lib, kw, status):
     assert gather(lib, **kw) == status
+
+
+def chunk(lib, q=P, qs=P, dt=2, w=P, kc=P, ks=P, bt=P, mpp=64, npg=64, B=1, q0=100, Lq=64, H=64, D=128, ps=64,
+          topk=2048, idx=P, val=None, ws=P, nws=1 << 20):
+    return lib.indexer_prefill_chunk_paged(q, qs, dt, w, kc, ks, bt, mpp, npg, B, q0, Lq, H, D, ps, topk, idx, val,
+                                           ws, nws, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(qs=None), NULL), (dict(w=None), NULL), (dict(kc=None), NULL),
+    (dict(ks=None), NULL), (dict(bt=None), NULL), (dict(idx=None), NULL),
+    (dict(dt=9), DTYPE), (dict(dt=1), UNSUP), (dict(B=0), SHAPE), (dict(Lq=0), SHAPE), (dict(q0=-1), SHAPE),
+    (dict(q0=4033), SHAPE), (dict(H=8), UNSUP), (dict(D=64), UNSUP), (dict(ps=32, mpp=128), UNSUP),
+    (dict(topk=4096), UNSUP), (dict(mpp=2048, q0=65500, Lq=64), UNSUP), (dict(ws=None), WS), (dict(nws=100), WS),
+    (dict(kc=P + 8), UNSUP),
+])
+def test_prefill_chunk_rejects_before_launch(lib, kw, status):
+    assert chunk(lib, **kw) == status
+
+
+def test_prefill_chunk_workspace_query(lib):
+    # 5 bytes per visible key (64-padded), rounded to 256: q0 + Lq = 4160 keys
+    assert lib.indexer_prefill_chunk_paged_workspace_bytes(2, 4096, 64) == (2 * 4160 * 5 + 255) // 256 * 256

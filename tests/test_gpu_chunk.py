@@ -1,0 +1,81 @@
+"""GPU parity of indexer_prefill_chunk_paged (a chunk of query tokens at
+positions q0 .. q0+Lq-1 against the paged fp8 key cache) against the fp64
+oracle's prefill rows q0 .. q0+Lq-1 of the whole sequence, and against the
+full fused prefill's rows on the GPU (same per-pair arithmetic: the same
+selected sets and scores)."""
+import numpy as np
+import pytest
+import torch
+
+import dsa_lightning_indexer_03_amd as dsa
+import synth
+from gpu_util import dev, host, run_prefill, say
+from oracle import indexer
+from oracle.check import check_topk_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def paged_sequence(inp, seed, spare=3):
+    """The sequences' fp8 keys placed in a page pool through a permuted table."""
+    B, L = inp["k"].shape[:2]
+    mpp = (L + 63) // 64
+    n_pages = B * mpp + spare
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(n_pages)[: B * mpp].reshape(B, mpp).astype(np.int32)
+    cache = rng.integers(0, 0x7F, size=(n_pages, 64, 128), dtype=np.uint8)   # junk beyond the sequences
+    scales = np.ones((n_pages, 64), np.float32)
+    s = np.arange(L)
+    for b in range(B):
+        cache[table[b, s // 64], s % 64] = inp["k"][b]
+        scales[table[b, s // 64], s % 64] = inp["k_scale"][b]
+    return cache, scales, table
+
+
+def run_chunk(inp, cache, scales, table, q0, Lq, K):
+    q = inp["q"][:, q0:q0 + Lq]
+    idx, val = dsa.prefill_chunk_paged(dev(q), dev(inp["q_scale"][:, q0:q0 + Lq]), dev(inp["w"][:, q0:q0 + Lq]),
+                                       dev(cache), dev(scales), dev(table), q0, K)
+    torch.cuda.synchronize()
+    return host(idx), host(val)
+
+
+@pytest.mark.parametrize("B,q0,Lq,H,K", [
+    (1, 0, 300, 64, 64),        # the chunk is the whole sequence
+    (1, 4000, 100, 64, 2048),   # long rows past 2k: the sampled floor
+    (2, 5000, 37, 32, 64),      # ragged chunk, two sequences
+    (1, 63, 130, 16, 16),       # chunk start and end off the 64-key pages
+])
+def test_chunk_matches_oracle_rows(B, q0, Lq, H, K):
+    L = q0 + Lq
+    inp = synth.prefill_inputs(B, L, H, 128, "fp8", seed=900 + q0 % 97 + Lq)
+    cache, scales, table = paged_sequence(inp, seed=q0 + Lq)
+    say(f"chunk B={B} q0={q0} Lq={Lq} H={H} K={K}")
+    gi, gv = run_chunk(inp, cache, scales, table, q0, Lq, K)
+    rows = np.arange(q0, L)
+    check_rows = rows if Lq <= 40 else np.concatenate([rows[:8], rows[Lq // 2:Lq // 2 + 4], rows[-8:]])
+    _, _, osc = indexer.prefill(inp, K, rows=check_rows, want_scores=True)
+    for b in range(B):
+        check_topk_rows(gi[b][check_rows - q0], gv[b][check_rows - q0], osc[b], check_rows + 1, K,
+                        where=f"chunk b{b}")
+
+
+def test_chunk_equals_full_prefill_rows():
+    q0, Lq, K = 6000, 200, 2048
+    L = q0 + Lq
+    inp = synth.prefill_inputs(1, L, 64, 128, "fp8", seed=931)
+    cache, scales, table = paged_sequence(inp, seed=932)
+    say(f"chunk vs full prefill: q0={q0} Lq={Lq}")
+    gi, gv = run_chunk(inp, cache, scales, table, q0, Lq, K)
+    fi, fv, _ = run_prefill(inp, K)
+    a_i, a_v = gi[0], gv[0]
+    b_i, b_v = fi[0, q0:], fv[0, q0:]
+    oa, ob = np.argsort(a_i, axis=1, kind="stable"), np.argsort(b_i, axis=1, kind="stable")
+    assert np.array_equal(np.take_along_axis(a_i, oa, 1), np.take_along_axis(b_i, ob, 1))
+    assert np.array_equal(np.take_along_axis(a_v, oa, 1), np.take_along_axis(b_v, ob, 1))
