@@ -218,10 +218,39 @@ def main():
             "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": achieved / PEAK_FP8_TFLOPS, "traffic": measured_traffic("prefill"),
                          "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
-                         "kernel": "prefill_fused_fp8_staged_kernel<4>",
+                         "kernel": "prefill_fused_fp8_staged_kernel<4, false>",
                          "work": f"2*H*D flop per causal pair x {pairs} pairs = {flops:.4g} flop per launch"},
             "wall_s_timed": wall,
         }
+        # chunked prefill against the paged cache: the sequence's last 4096 tokens
+        # (positions 28672 .. 32767) over its 32768 keys in a permuted page pool
+        if not args.no_extra:
+            q0c, Lqc = L - 4096, 4096
+            n_pages = L // 64
+            gperm = torch.Generator(device=dev)
+            gperm.manual_seed(6)
+            perm = torch.randperm(n_pages, generator=gperm, device=dev).to(torch.int32)
+            kc = torch.empty((n_pages, 64, D), dtype=torch.uint8, device=dev)
+            ksc = torch.empty((n_pages, 64), dtype=torch.float32, device=dev)
+            kc[perm.long()] = k.view(n_pages, 64, D)
+            ksc[perm.long()] = ks.view(n_pages, 64)
+            tab = perm.view(1, n_pages)
+            qc, qsc, wc = q[:, q0c:].contiguous(), qs[:, q0c:].contiguous(), w[:, q0c:].contiguous()
+
+            def cstep():
+                dsa.prefill_chunk_paged(qc, qsc, wc, kc, ksc, tab, q0c, K)
+
+            cms, _ = time_calls(torch, cstep, max(args.steps, 10), args.warmup)
+            cpairs = Lqc * q0c + Lqc * (Lqc + 1) // 2
+            ctf = 2.0 * H * D * cpairs / (cms * 1e-3) / 1e12
+            log(f"prefill chunk: {cms:.3f} ms for {Lqc} queries at {q0c}.. ({ctf:.0f} TFLOP/s)")
+            result["prefill_chunk_paged"] = {
+                "what": f"B=1 chunk of {Lqc} fp8 queries at positions {q0c}..{L - 1} of the L={L} workload, "
+                        f"scored against its {L} keys in a permuted paged fp8 cache, k={K}",
+                "ms_per_call": cms, "pairs": cpairs, "pairs_per_s": cpairs / (cms * 1e-3), "TFLOP/s": ctf,
+                "frac_of_fp8_peak": ctf / PEAK_FP8_TFLOPS,
+            }
+            del kc, ksc, tab, qc, qsc, wc, perm
         del q, k, w, qs, ks, out
         torch.cuda.empty_cache()
 

@@ -79,3 +79,21 @@ def test_chunk_equals_full_prefill_rows():
     oa, ob = np.argsort(a_i, axis=1, kind="stable"), np.argsort(b_i, axis=1, kind="stable")
     assert np.array_equal(np.take_along_axis(a_i, oa, 1), np.take_along_axis(b_i, ob, 1))
     assert np.array_equal(np.take_along_axis(a_v, oa, 1), np.take_along_axis(b_v, ob, 1))
+
+
+def test_chunk_full_size_sampled():
+    # the bench's configuration: the last 4096 tokens of the L=32768 fp8
+    # workload against its 32768 keys in a permuted page pool, k=2048
+    inp = synth.config_inputs(3)
+    L, K = inp["q"].shape[1], 2048
+    q0, Lq = L - 4096, 4096
+    cache, scales, table = paged_sequence(inp, seed=933, spare=0)
+    say(f"chunk full size: q0={q0} Lq={Lq}")
+    gi, gv = run_chunk(inp, cache, scales, table, q0, Lq, K)
+    rows = np.array([q0, q0 + 1, q0 + 7, q0 + 8, q0 + 2047, q0 + 2048, L - 9, L - 2, L - 1])
+    _, _, osc = indexer.prefill(inp, K, rows=rows, want_scores=True)
+    check_topk_rows(gi[0][rows - q0], gv[0][rows - q0], osc[0], rows + 1, K, where="chunk full size")
+    # every row: k distinct positions inside its history
+    assert np.all(gi[0] >= 0) and np.all(gi[0] <= np.arange(q0, L)[:, None])
+    srt = np.sort(gi[0], axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1])
