@@ -39,14 +39,14 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 COPY_FETCH_FACTOR = 1048576.0 / 524315.0
 COPY_WRITE_FACTOR = 1048576.0 / 1048576.0
 _DECODE_SRC = ["csrc/decode_paged.hip", "csrc/select_row.h", "csrc/common.h", "csrc/kernels.h", "build.py"]
-_DECODE_SHA = "807df5c635b8dcecab3b8a255edae03b17ef1091b8617f997bea204f4a794e22"
+_DECODE_SHA = "b994f09d85857f186da6a3bd56b247d4d0d47b75fa896b0ba2941317424e6e58"
 COUNTERS = {
     "prefill": {"sources": ["csrc/prefill_fused.hip", "csrc/common.h", "csrc/kernels.h", "build.py"],
-                "sha256": "fbd5b6cfbd46370ddd3969a623176c644312efb7842758a913bd7584a074a66b",
-                "fetch_kib": 255171.9, "write_kib": 524355.9},
+                "sha256": "b96b66a8aef677d7524af8effa1ef7fc06bada7b7d8b15d2418854972f186554",
+                "fetch_kib": 255248.7, "write_kib": 524494.9},
     # main scan of one decode call (the sample kernel reads about 1/60 of it)
-    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 546138.3, "write_kib": 2380.2},
-    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 556956.9, "write_kib": 4103.3},
+    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 546155.7, "write_kib": 2382.4},
+    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 556917.6, "write_kib": 4107.1},
 }
 
 
