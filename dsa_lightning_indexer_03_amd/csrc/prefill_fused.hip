@@ -390,6 +390,23 @@ __device__ void wave_emit(const RowBuf<Pos>& rb, int n, int K, int32_t* idx, flo
     wave_keep_pass(rb, n, true, kappa, pos_cut, 0u, idx, val, K);
 }
 
+// Short-row bypass: a row with at most K valid positions selects all of
+// them (positions 0 .. tp, then -1), so when no score is asked for, a block
+// whose rows all qualify writes that directly and scores nothing.  Returns
+// true when the block took the bypass (uniform over the block).
+__device__ __forceinline__ bool short_rows_bypass(const PrefillArgs& a, int b, int blk, int W, int L, int q0,
+                                                  int t_raw, bool live) {
+    if (a.val_out || a.scores) return false;
+    const int last_row = min(blk * W + W - 1, L - 1);
+    if (q0 + last_row + 1 > a.topk) return false;
+    if (live) {
+        const int tp = q0 + t_raw;
+        int32_t* out = a.idx_out + ((size_t)b * L + t_raw) * a.topk;
+        for (int j = lane_id(); j < a.topk; j += kWave) out[j] = j <= tp ? j : -1;
+    }
+    return true;
+}
+
 template <int DT>  // 1 = bf16, 2 = fp8 e4m3
 struct Operands;
 
@@ -795,6 +812,7 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     const int q0 = PAGED ? a.q0 : 0;
     const int Lk = PAGED ? a.Lk : L;
     const int tp = q0 + t;              // the token's position: its row sees keys 0 .. tp
+    if (short_rows_bypass(a, b, blk, W, L, q0, t_raw, live)) return;
     const int lane = lane_id();
     const int n = lane & 15, g = lane >> 4;
 
@@ -1315,6 +1333,7 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     const int t_raw = blk * W + wave;
     const bool live = t_raw < L;        // waves past the end only help stage keys
     const int t = live ? t_raw : L - 1;
+    if (short_rows_bypass(a, b, blk, W, L, 0, t_raw, live)) return;
     const int lane = lane_id();
     const int n = lane & 15, g = lane >> 4;
 
