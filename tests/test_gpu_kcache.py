@@ -158,3 +158,34 @@ def test_full_size_bulk_append_sampled():
     assert np.array_equal(g_sc.view(np.uint32), sc.view(np.uint32))
     # every slot was written (no zero scale left)
     assert bool((scale > 0).all())
+
+
+def test_decode_step_append_score_gather():
+    # one serving step for 3 sequences: append each new token's key at its
+    # position, score the query over its whole context (the new key included),
+    # then gather the selected rows of a latent cache with the same paging
+    from oracle.gather import topk_gather as oracle_gather
+    d = synth.decode_inputs(3, [3000, 700, 4500], 64, 128, seed=71, permute=True)
+    ctx = d["context_lens"].astype(np.int64)
+    rng = np.random.default_rng(72)
+    new = synth.to_bf16_bits(rng.normal(size=(3, 128)).astype(np.float32))
+    pos = (ctx - 1).astype(np.int32)   # each query's own position: its key enters before scoring
+    seq = np.arange(3, dtype=np.int32)
+    kc, ks = dev(d["k_cache"]), dev(d["k_scale"])
+    k_new = torch.from_numpy(new.view(np.int16)).cuda()
+    dsa.kcache_append(k_new, dev(seq), dev(pos), dev(d["block_table"]), kc, ks)
+    torch.cuda.synchronize()
+    o_cache, o_scales = oracle_append(d["k_cache"], d["k_scale"], new, "bf16", seq, pos, d["block_table"])
+    assert np.array_equal(host(kc), o_cache) and np.array_equal(host(ks).view(np.uint32), o_scales.view(np.uint32))
+    d2 = dict(d, k_cache=o_cache, k_scale=o_scales)
+    K = 256
+    gi, gv = dsa.indexer_decode_paged(dev(d["q"]), dev(d["w"]), kc, ks, dev(d["block_table"]),
+                                      dev(d["context_lens"]), K)
+    torch.cuda.synchronize()
+    gi, gv = host(gi), host(gv)
+    for b in range(3):
+        o = indexer.decode_scores(d2, b)
+        check_topk_rows(gi[b:b + 1], gv[b:b + 1], o[None], [o.size], K, where=f"step q{b}")
+    latent = rng.integers(0, 256, size=(d["k_cache"].shape[0], 64, 1024), dtype=np.uint8)
+    rows = host(dsa.topk_gather(dev(latent), dev(d["block_table"]), dev(gi)))
+    assert np.array_equal(rows, oracle_gather(latent, d["block_table"], gi))
