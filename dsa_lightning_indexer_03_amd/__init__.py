@@ -46,6 +46,19 @@ def _dev(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need(t, name: str, *dtypes) -> None:
+    """Index and table tensors must be int32, weights and scales fp32: the
+    library reads them as such, so any other element type would be read as
+    garbage (an int64 block table as pairs of int32 page ids)."""
+    if t is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+
+
+_I32 = torch.int32
+_F32 = torch.float32
+_CODES = (torch.uint8, torch.float8_e4m3fn)
+
+
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -70,6 +83,9 @@ def indexer_prefill(q, k, w, topk: int, q_scale=None, k_scale=None, want_scores:
     dt = dtype_code(q)
     if dtype_code(k) != dt:
         raise ValueError("q and k must share a format")
+    _need(w, "w", _F32)
+    _need(q_scale, "q_scale", _F32)
+    _need(k_scale, "k_scale", _F32)
     for name, t in (("q", q), ("k", k), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale)):
         if t is not None:
             _dev(t, name)
@@ -101,9 +117,16 @@ def indexer_decode_paged(q, w, k_cache, k_scale, block_table, context_lens, topk
         raise ValueError("shape mismatch")
     if block_table.shape[0] != B or tuple(context_lens.shape) != (B,):
         raise ValueError("block_table / context_lens shape mismatch")
+    _need(w, "w", _F32)
+    _need(k_cache, "k_cache", *_CODES)
+    _need(k_scale, "k_scale", _F32)
+    _need(block_table, "block_table", _I32)
+    _need(context_lens, "context_lens", _I32)
     for name, t in (("q", q), ("w", w), ("k_cache", k_cache), ("k_scale", k_scale),
                     ("block_table", block_table), ("context_lens", context_lens)):
         _dev(t, name)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_pages]")
     mpp = block_table.shape[1]
     mcl = mpp * page if max_context_len is None else int(max_context_len)
     dev = q.device
@@ -133,7 +156,10 @@ def topk_select(scores, topk: int, row_len=None, want_values: bool = True):
     rows, cols = scores.shape
     dev = scores.device
     if row_len is not None:
+        _need(row_len, "row_len", _I32)
         _dev(row_len, "row_len")
+        if tuple(row_len.shape) != (rows,):
+            raise ValueError("row_len must hold one length per row")
     idx = torch.empty((rows, topk), dtype=torch.int32, device=dev)
     val = torch.empty((rows, topk), dtype=torch.float32, device=dev) if want_values else None
     nws = lib.topk_select_workspace_bytes(rows, cols, topk)
@@ -160,9 +186,14 @@ def kcache_append(k, seq_ids, positions, block_table, k_cache, k_scale):
         raise ValueError("seq_ids / positions must have one entry per key")
     if k_cache.dtype != torch.uint8 or k_scale.dtype != torch.float32:
         raise ValueError("k_cache must be uint8 codes and k_scale fp32")
+    _need(seq_ids, "seq_ids", _I32)
+    _need(positions, "positions", _I32)
+    _need(block_table, "block_table", _I32)
     for name, t in (("k", k), ("seq_ids", seq_ids), ("positions", positions), ("block_table", block_table),
                     ("k_cache", k_cache), ("k_scale", k_scale)):
         _dev(t, name)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_pages]")
     B, mpp = block_table.shape
     st = lib.indexer_kcache_append(_ptr(k), dtype_code(k), _ptr(seq_ids), _ptr(positions), _ptr(block_table),
                                    B, mpp, _ptr(k_cache), _ptr(k_scale), P, T, D, page, _stream(k.device))
@@ -182,6 +213,8 @@ def topk_gather(latent_cache, block_table, topk_idx):
         raise ValueError("block_table [B, max_pages] and topk_idx [B, K] must be int32 with matching B")
     for name, t in (("latent_cache", latent_cache), ("block_table", block_table), ("topk_idx", topk_idx)):
         _dev(t, name)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_pages]")
     out = torch.empty((B, K, E), dtype=latent_cache.dtype, device=latent_cache.device)
     st = lib.indexer_topk_gather(_ptr(latent_cache), E * latent_cache.element_size(), _ptr(block_table),
                                  block_table.shape[1], P, page, _ptr(topk_idx), B, K, _ptr(out),
@@ -206,6 +239,11 @@ def prefill_chunk_paged(q, q_scale, w, k_cache, k_scale, block_table, q0: int, t
         raise ValueError("shape mismatch")
     if tuple(q_scale.shape) != (B, Lq, H) or block_table.shape[0] != B:
         raise ValueError("q_scale / block_table shape mismatch")
+    _need(q_scale, "q_scale", _F32)
+    _need(w, "w", _F32)
+    _need(k_cache, "k_cache", *_CODES)
+    _need(k_scale, "k_scale", _F32)
+    _need(block_table, "block_table", _I32)
     for name, t in (("q", q), ("q_scale", q_scale), ("w", w), ("k_cache", k_cache), ("k_scale", k_scale),
                     ("block_table", block_table)):
         _dev(t, name)

@@ -2,8 +2,9 @@
 
     python -m dsa_lightning_indexer_03_amd.build
 
-Every HIP source under csrc/ is compiled with hipcc for gfx950 only and
-linked into one shared library next to this file.  Packed-fp32 VALU
+Every HIP source under csrc/ is compiled with hipcc for gfx950 only (one
+object per source under _build/, in parallel) and linked into one shared
+library next to this file.  Packed-fp32 VALU
 instructions are disabled for the device code.
 """
 from __future__ import annotations
@@ -18,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsaidx.so")
+OBJ_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,6 +33,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators in ordinary VGPRs: no accvgpr copies around the epilogues
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # binary32 division and square root correctly rounded: the K-cache write
+    # path's fp8 codes are defined on the correctly rounded quotient key/scale
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wall",
     "-Wno-unused-function",
     f"-I{INCLUDE}",
@@ -42,10 +47,7 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compiles the library and returns its path.  Raises on failure."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + (extra or []) + sources() + ["-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,6 +55,22 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
     if verbose and r.stderr.strip():
         print(r.stderr, file=sys.stderr)
+
+
+def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compiles every source to an object (in parallel), links the library
+    and returns its path.  Raises on failure."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(OBJ_DIR, os.path.basename(f) + ".o") for f in srcs]
+    cflags = [f for f in FLAGS if f != "-shared"] + (extra or [])
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda so: _run([HIPCC] + cflags + ["-c", so[0], "-o", so[1]], verbose), zip(srcs, objs)))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

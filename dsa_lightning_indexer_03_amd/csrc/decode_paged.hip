@@ -42,6 +42,7 @@
 //    candidates is exact.  Otherwise a repair pass rescores the query in
 //    full.
 #include "common.h"
+#include "device_once.h"
 #include "kernels.h"
 #include "select_row.h"
 
@@ -620,28 +621,30 @@ hipError_t launch_decode_hb(const DecodeArgs& a_in, const SelectArgs& s, int64_t
     if (e != hipSuccess) return e;
     // Main scan: one resident round of workgroups (occupancy queried once
     // per process), never more workgroups than pages.
-    static int resident = 0;
-    if (resident == 0) {
-        int dev = 0, per_cu = 0, cus = 0;
-        if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)decode_scan_kernel<HB>,
-                                                               kThreadsDec, 0)) != hipSuccess)
-            return e;
-        resident = (per_cu < 1 ? 1 : per_cu) * cus;
-    }
+    static PerDevice<int> resident_once;
+    int resident = 0;
+    e = resident_once.get(
+        [](int dev, int* v) {
+            int per_cu = 0, cus = 0;
+            hipError_t r = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (r != hipSuccess) return r;
+            r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)decode_scan_kernel<HB>,
+                                                             kThreadsDec, 0);
+            if (r != hipSuccess) return r;
+            *v = (per_cu < 1 ? 1 : per_cu) * cus;
+            return hipSuccess;
+        },
+        &resident);
+    if (e != hipSuccess) return e;
     int64_t grid = resident;
     if (grid > max_pages) grid = max_pages;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(decode_scan_kernel<HB>, dim3((unsigned)grid), dim3(kThreadsDec), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if ((e = hipFuncSetAttribute((const void*)decode_finish_kernel<HB>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)sizeof(sel::SelShared))) != hipSuccess)
-            return e;
-        attr_set = true;
-    }
+    static PerDevice<int> lds_once;
+    if ((e = set_lds_limit(lds_once, (const void*)decode_finish_kernel<HB>, (int)sizeof(sel::SelShared))) !=
+        hipSuccess)
+        return e;
     hipLaunchKernelGGL(decode_finish_kernel<HB>, dim3((unsigned)a.B), dim3(sel::kThreads), sizeof(sel::SelShared),
                        stream, a, s);
     return hipGetLastError();

@@ -46,6 +46,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "device_once.h"
 #include "kernels.h"
 
 namespace dsaidx {
@@ -682,13 +683,9 @@ template <int DT, int HB, bool POS16>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
     using Cfg = BufCfg<POS16>;
     const size_t smem = (size_t)Cfg::kWaves * Cfg::kWaveBytes;
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_fused_kernel<DT, HB, POS16>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static PerDevice<int> lds_once;
+    hipError_t e = set_lds_limit(lds_once, (const void*)prefill_fused_kernel<DT, HB, POS16>, (int)smem);
+    if (e != hipSuccess) return e;
     const int nblk = (a.L + Cfg::kWaves - 1) / Cfg::kWaves;
     hipLaunchKernelGGL((prefill_fused_kernel<DT, HB, POS16>), dim3((unsigned)(nblk * a.B)),
                        dim3(Cfg::kWaves * kWave), smem, stream, a);
@@ -707,17 +704,19 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
 //
 // Epilogue.  The score of key s is sum_h c_h max(S_h, 0) times the key's
 // scale, with c_h = w_h * q_scale_h / sqrt(D) and S_h the dot product of the
-// fp8 values.  |S_h| <= |q_h|_1 * max_d |k_d| <= 2^Pq * 2^Pk, with Pq taken
-// per token and Pk per key (a pre-pass over the keys), so the score MFMAs,
-// run with the E8M0 operand scales 2^-Pq (A) and 2^-Pk (B), leave every
-// value in [-1, 1].  There the conversion to f16 with its [0, 1] clamp is
-// max(S, 0) itself, rounded to nearest (relative error <= 2^-11 down to
-// 2^-14 of the bound), and the weighted sum over heads is one more MFMA
-// (f16, 16x16x32) with the weights c_h * 2^E as its A operand.  Its weights
-// for subtile st sit in the rows 4st..4st+3 only, so the four subtiles of a
-// chunk accumulate into one tile whose element 0 in lane l is the score of
-// key 64*chunk + l: no cross-lane reduction.  The factor 2^(Pq - E) and the
-// key's scale times 2^Pk finish the score.
+// fp8 values.  |S_h| <= |q_h|_1 * max_d |k_d| <= 2^Pq_h * 2^Pk, with Pq_h
+// taken per head of the token and Pk per key (a pre-pass over the keys), so
+// the score MFMAs, run with the E8M0 operand scales 2^-Pq_h (A, one per row,
+// i.e. per head) and 2^-Pk (B, one per key column), leave every value in
+// [-1, 1] at its own head's scale.  There the conversion to f16 with its
+// [0, 1] clamp is max(S, 0) itself, rounded to nearest (relative error
+// <= 2^-11 down to 2^-14 of the head's bound, however far the heads'
+// magnitudes spread), and the weighted sum over heads is one more MFMA
+// (f16, 16x16x32) with the weights c_h * 2^Pq_h * 2^E as its A operand.  Its
+// weights for subtile st sit in the rows 4st..4st+3 only, so the four
+// subtiles of a chunk accumulate into one tile whose element 0 in lane l is
+// the score of key 64*chunk + l: no cross-lane reduction.  The factor 2^-E
+// and the key's scale times 2^Pk finish the score.
 // ---------------------------------------------------------------------------
 constexpr int kStagedWaves = 8;
 // Candidates per row: the most that fit beside three key chunks.  Every
@@ -832,12 +831,13 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
     // 32x + 16 + 4g + (j - 4) for j >= 4; subtile st uses rows 4st..4st+3.
     constexpr int NX = (HB + 1) / 2;
     v8h Wh[4][NX];
-    float Fscale;  // 2^(Pq - E)
-    int sa;        // E8M0 A scale of the score MFMAs: 127 - Pq
+    float Fscale;  // 2^-E
+    int sa[HB];    // E8M0 A scale of the score MFMAs, per lane: 127 - Pq of head 16hb + n (the lane's A row)
     {
-        // 2^Pq >= max_h |q_h|_1 (fp8 values): lane (m, g) sums its 32 bytes of
-        // head 16hb + m, the four lane groups of a row add up, max over rows.
-        float l1 = 0.f;
+        // Each head h gets its own exponent: 2^Pq_h >= |q_h|_1 (fp8 values).
+        // Lane (m, g) sums its 32 bytes of head 16hb + m; the four lane
+        // groups of a row add up, so every lane of row m holds |q_h|_1.
+        int pq[HB];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
             float sabs = 0.f;
@@ -849,12 +849,13 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
             }
             sabs += __shfl_xor(sabs, 16, kWave);
             sabs += __shfl_xor(sabs, 32, kWave);
-            l1 = fmaxf(l1, sabs);
+            pq[hb] = sabs > 0.f ? __builtin_amdgcn_frexp_expf(sabs) : 0;  // 2^Pq > |q_h|_1
+            sa[hb] = 127 - pq[hb];
         }
-#pragma unroll
-        for (int d = 8; d >= 1; d >>= 1) l1 = fmaxf(l1, __shfl_xor(l1, d, kWave));
-        const int Pq = l1 > 0.f ? __builtin_amdgcn_frexp_expf(l1) : 0;  // 2^Pq > l1
-        sa = 127 - Pq;
+        // Head weights c_h = w q_scale / sqrt(D) for the lane's accumulator
+        // rows h = 16hb + 4g + i, times 2^Pq_h (the scale the score MFMA took
+        // out of head h), then all of them by one 2^E that puts the largest
+        // in f16's top binade.
         float cf[HB][4];
         float mx = 0.f;
 #pragma unroll
@@ -862,14 +863,15 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int h = 16 * hb + 4 * g + i;
-                cf[hb][i] = a.w[row_t * H + h] * a.q_scale[row_t * H + h] * a.inv_sqrt_d;
+                const int pqh = __shfl(pq[hb], 4 * g + i, kWave);
+                cf[hb][i] = ldexpf(a.w[row_t * H + h] * a.q_scale[row_t * H + h] * a.inv_sqrt_d, pqh);
                 mx = fmaxf(mx, fabsf(cf[hb][i]));
             }
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
         int E = mx > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
         E = E < -60 ? -60 : (E > 100 ? 100 : E);
-        Fscale = ldexpf(1.0f, Pq - E);
+        Fscale = ldexpf(1.0f, -E);
         // lane (m, g) of the weight operand: row m = n, contraction group g
         const int own_st = n >> 2;
 #pragma unroll
@@ -993,9 +995,9 @@ prefill_fused_fp8_staged_kernel(PrefillArgs a) {
         constexpr int s0 = 2 * decltype(mh)::value;
         if (q == 0)
             return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq.a[hb], B_.b[0], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                      0, 0, 0, sa, s0, sb);
+                                                                      0, 0, 0, sa[hb], s0, sb);
         return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq.a[hb], B_.b[1], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                  0, 0, 0, sa, s0 + 1, sb);
+                                                                  0, 0, 0, sa[hb], s0 + 1, sb);
     };
     // Conversion j2 (of 4) of the B operand of head MFMA x for subtile q of
     // half A_: the pair of heads (hb = 2x + j2/2, i = 2(j2%2), +1) as f16,
@@ -1714,12 +1716,10 @@ hipError_t launch_fp8_staged(const PrefillArgs& a_in, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const size_t smem = kStagedLds;
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_fused_fp8_staged_kernel<HB, PAGED>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    static PerDevice<int> lds_once;
+    {
+        hipError_t e = set_lds_limit(lds_once, (const void*)prefill_fused_fp8_staged_kernel<HB, PAGED>, (int)smem);
         if (e != hipSuccess) return e;
-        attr = true;
     }
     const int nblk = (a.L + kStagedWaves - 1) / kStagedWaves;
     hipLaunchKernelGGL((prefill_fused_fp8_staged_kernel<HB, PAGED>), dim3((unsigned)(nblk * a.B)),
@@ -1741,12 +1741,10 @@ hipError_t launch_bf16_staged(const PrefillArgs& a_in, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const size_t smem = kBfStages * kBfStageBytes + (size_t)kBfWaves * kBfWaveBytes;
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_fused_bf16_staged_kernel<HB>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    static PerDevice<int> lds_once;
+    {
+        hipError_t e = set_lds_limit(lds_once, (const void*)prefill_fused_bf16_staged_kernel<HB>, (int)smem);
         if (e != hipSuccess) return e;
-        attr = true;
     }
     const int nblk = (a.L + kBfWaves - 1) / kBfWaves;
     hipLaunchKernelGGL((prefill_fused_bf16_staged_kernel<HB>), dim3((unsigned)(nblk * a.B)), dim3(kBfWaves * kWave),

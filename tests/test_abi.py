@@ -179,3 +179,65 @@ def test_prefill_chunk_rejects_before_launch(lib, kw, status):
 def test_prefill_chunk_workspace_query(lib):
     # 5 bytes per visible key (64-padded), rounded to 256: q0 + Lq = 4160 keys
     assert lib.indexer_prefill_chunk_paged_workspace_bytes(2, 4096, 64) == (2 * 4160 * 5 + 255) // 256 * 256
+
+
+# ---- the Python binding's own checks (host-side, before any device access) ----
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _wrapper_cases():
+    import torch
+    i32, i64, f32, f64, u8, bf = torch.int32, torch.int64, torch.float32, torch.float64, torch.uint8, torch.bfloat16
+    B, L, H, D, P = 2, 64, 16, 128, 8
+    dec = dict(q=_t((B, H, D), bf), w=_t((B, H), f32), k_cache=_t((P, 64, D), u8), k_scale=_t((P, 64), f32),
+               block_table=_t((B, 4), i32), context_lens=_t((B,), i32), topk=16)
+    pre = dict(q=_t((1, L, H, D), u8), k=_t((1, L, D), u8), w=_t((1, L, H), f32), topk=8,
+               q_scale=_t((1, L, H), f32), k_scale=_t((1, L), f32))
+    kc = dict(k=_t((5, D), bf), seq_ids=_t((5,), i32), positions=_t((5,), i32), block_table=_t((B, 4), i32),
+              k_cache=_t((P, 64, D), u8), k_scale=_t((P, 64), f32))
+    ch = dict(q=_t((B, 32, H, D), u8), q_scale=_t((B, 32, H), f32), w=_t((B, 32, H), f32),
+              k_cache=_t((P, 64, D), u8), k_scale=_t((P, 64), f32), block_table=_t((B, 4), i32), q0=100, topk=16)
+    ga = dict(latent_cache=_t((P, 64, 512), bf), block_table=_t((B, 4), i32), topk_idx=_t((B, 16), i32))
+    cases = []
+    for fn, base, bad in (
+        ("indexer_decode_paged", dec, [("block_table", i64), ("context_lens", i64), ("w", f64), ("k_scale", f64),
+                                       ("k_cache", f32)]),
+        ("indexer_prefill", pre, [("w", f64), ("q_scale", f64), ("k_scale", torch.float16)]),
+        ("kcache_append", kc, [("seq_ids", i64), ("positions", i64), ("block_table", i64)]),
+        ("prefill_chunk_paged", ch, [("block_table", i64), ("q_scale", f64), ("w", f64), ("k_scale", f64),
+                                     ("k_cache", i32)]),
+        ("topk_gather", ga, [("block_table", i64), ("topk_idx", i64)]),
+    ):
+        for name, dt in bad:
+            kw = dict(base)
+            kw[name] = kw[name].to(dt)
+            cases.append((fn, kw, name))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(len(_wrapper_cases())))
+def test_binding_rejects_wrong_element_types(lib, case):
+    """An index or table tensor that is not int32, or a weight / scale tensor
+    that is not fp32, is refused by the binding with a ValueError naming the
+    tensor, before anything reaches the library."""
+    import dsa_lightning_indexer_03_amd as dsa
+    fn, kw, name = _wrapper_cases()[case]
+    with pytest.raises(ValueError, match=name):
+        getattr(dsa, fn)(**kw)
+
+
+def test_binding_rejects_host_tensors(lib):
+    """Well-typed tensors on the host are refused (device pointers only)."""
+    import dsa_lightning_indexer_03_amd as dsa
+    for fn, kw, _ in _wrapper_cases()[:1]:
+        kw = dict(kw)
+        kw["block_table"] = kw["block_table"].to(__import__("torch").int32)
+        kw["context_lens"] = kw["context_lens"].to(__import__("torch").int32)
+        kw["w"] = kw["w"].float()
+        kw["k_scale"] = kw["k_scale"].float()
+        kw["k_cache"] = kw["k_cache"].to(__import__("torch").uint8)
+        with pytest.raises(ValueError, match="device tensor"):
+            getattr(dsa, fn)(**kw)

@@ -9,6 +9,8 @@ import torch
 import dsa_lightning_indexer_03_amd as dsa
 import synth
 from gpu_util import dev, host, say
+from oracle import indexer
+from oracle.check import check_topk_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -27,11 +29,11 @@ def prefill_idx(inp, K, want_topk_score):
     return host(idx)
 
 
-@pytest.mark.parametrize("dtype,L,K", [("fp8", 5000, 2048), ("bf16", 5000, 2048), ("fp8", 300, 512),
-                                       ("bf16", 1000, 64)])
-def test_bypass_equals_scored_path(dtype, L, K):
-    inp = synth.prefill_inputs(1, L, 64, 128, dtype, seed=950 + L + K)
-    say(f"bypass {dtype} L={L} K={K}")
+@pytest.mark.parametrize("dtype,L,K,H", [("fp8", 5000, 2048, 64), ("bf16", 5000, 2048, 64), ("fp8", 300, 512, 64),
+                                         ("bf16", 1000, 64, 64), ("fp8", 3000, 2048, 48), ("bf16", 3000, 2048, 48)])
+def test_bypass_equals_scored_path(dtype, L, K, H):
+    inp = synth.prefill_inputs(1, L, H, 128, dtype, seed=950 + L + K + H)
+    say(f"bypass {dtype} L={L} K={K} H={H}")
     fast = prefill_idx(inp, K, want_topk_score=False)
     full = prefill_idx(inp, K, want_topk_score=True)
     # the order inside a row is unspecified (a block that scores its sampled
@@ -40,6 +42,10 @@ def test_bypass_equals_scored_path(dtype, L, K):
     t = np.arange(min(L, K))          # rows with at most K valid positions: 0 .. t, then -1
     expect = np.where(np.arange(K)[None, :] <= t[:, None], np.arange(K)[None, :], -1)
     assert np.array_equal(fast[0, :min(L, K)], expect)
+    # and the bypassed call's sets against the oracle's, on rows on both sides of k
+    rows = np.array(sorted({0, 1, K // 2, K - 2, K - 1, K, K + 1, L - 2, L - 1} & set(range(L))))
+    _, _, osc = indexer.prefill(inp, K, rows=rows, want_scores=True)
+    check_topk_rows(fast[0][rows], None, osc[0], rows + 1, K, where=f"bypass {dtype} vs oracle")
 
 
 def test_bypass_in_chunks_against_the_cache():

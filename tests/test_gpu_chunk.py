@@ -51,6 +51,7 @@ def run_chunk(inp, cache, scales, table, q0, Lq, K):
     (1, 4000, 100, 64, 2048),   # long rows past 2k: the sampled floor
     (2, 5000, 37, 32, 64),      # ragged chunk, two sequences
     (1, 63, 130, 16, 16),       # chunk start and end off the 64-key pages
+    (1, 3000, 200, 48, 256),    # three head blocks (the odd head-sum operand)
 ])
 def test_chunk_matches_oracle_rows(B, q0, Lq, H, K):
     L = q0 + Lq

@@ -60,7 +60,7 @@ def test_generic_path_edge_lengths(dtype, L):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("L,H,K", [(1, 64, 16), (17, 64, 16), (64, 16, 16), (65, 64, 64), (1000, 64, 64),
-                                   (1000, 32, 7), (5000, 16, 2048)])
+                                   (1000, 32, 7), (5000, 16, 2048), (300, 48, 32), (3000, 48, 256)])
 def test_fused_path(dtype, L, H, K):
     inp = synth.prefill_inputs(1, L, H, 128, dtype, seed=2000 + L + H)
     parity(inp, K, want_scores=(L <= 1000), name=f"fused L={L} H={H}")
@@ -195,6 +195,59 @@ def _e4m3(x):
     """float32 array -> E4M3FN codes (saturating RNE), no scaling."""
     t = torch.clamp(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)), -448.0, 448.0)
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _finite_e4m3_codes():
+    """The 254 E4M3FN codes that are not NaN (0x7F and 0xFF are)."""
+    return np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+
+
+@pytest.mark.parametrize("H", [16, 48])
+def test_fused_fp8_every_code(H):
+    """Every finite E4M3FN code, positive and negative, subnormal and
+    saturated, appears in the keys and in the queries of the fused fp8 path
+    (unit scales): each code is read by the scaled MFMA both as an A and as a
+    B operand, and the scores and selections match the oracle's decoding of
+    the same bytes."""
+    codes = _finite_e4m3_codes()
+    rng = np.random.default_rng(590 + H)
+    L, D, K = 260, 128, 32
+    k = np.empty((1, L, D), np.uint8)
+    q = np.empty((1, L, H, D), np.uint8)
+    # keys 0 and 1 hold all 254 codes (then two zeros); the others a permutation each
+    k[0, :2] = np.concatenate([codes, np.zeros(2, np.uint8)]).reshape(2, D)
+    for s_ in range(2, L):
+        k[0, s_] = rng.permutation(codes)[:D]
+    # every token's first two heads hold all codes too; the other heads a random draw
+    q[0, :, :2] = np.concatenate([codes, np.zeros(2, np.uint8)]).reshape(2, D)[None]
+    q[0, :, 2:] = rng.choice(codes, size=(L, H - 2, D))
+    inp = dict(kind="prefill", B=1, L=L, H=H, D=D, dtype="fp8", q=q, k=k,
+               q_scale=np.ones((1, L, H), np.float32), k_scale=np.ones((1, L), np.float32),
+               w=synth.softmax_weights(rng.standard_normal((1, L, H))))
+    parity(inp, K, want_scores=True, name=f"fp8 every code H={H}")
+
+
+@pytest.mark.parametrize("signed", [False, True])
+def test_fused_fp8_heads_far_apart(signed):
+    """Query heads of one token whose fp8 codes lie 2^0 .. 2^-12 below the
+    token's largest head, with head weights that grow as the head shrinks, so
+    the small heads carry as much of each score as the large ones: each
+    head's ReLU'd dot product must keep its own relative precision (one
+    exponent per head, not per token).  Scores are far above the absolute
+    floor of the tolerance, so the relative bound decides."""
+    rng = np.random.default_rng(583)
+    L, H, D, K = 600, 64, 128, 64
+    j = rng.integers(0, 13, size=(1, L, H, 1))
+    qv = rng.standard_normal((1, L, H, D)).astype(np.float32) * 100.0 * np.exp2(-j)
+    kv = rng.standard_normal((1, L, D)).astype(np.float32) * 100.0
+    kv[:, ::41] = 0.0
+    w = (np.exp2(j[..., 0]) * rng.uniform(0.5, 1.0, size=(1, L, H))).astype(np.float32)
+    if signed:
+        w *= np.where(rng.random((1, L, H)) < 0.5, -1.0, 1.0).astype(np.float32)
+    inp = dict(kind="prefill", B=1, L=L, H=H, D=D, dtype="fp8", q=_e4m3(qv), k=_e4m3(kv),
+               q_scale=rng.uniform(0.5, 2.0, size=(1, L, H)).astype(np.float32),
+               k_scale=rng.uniform(0.5, 2.0, size=(1, L)).astype(np.float32), w=w)
+    parity(inp, K, want_scores=True, name=f"fp8 heads far apart signed={signed}")
 
 
 @pytest.mark.parametrize("signed", [False, True])
