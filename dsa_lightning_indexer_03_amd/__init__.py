@@ -21,7 +21,7 @@ from . import _lib
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
-__all__ = ["indexer_prefill", "indexer_decode_paged", "topk_select", "kcache_append", "topk_gather",
+__all__ = ["indexer_prefill", "indexer_prefill_noalloc", "indexer_decode_paged", "topk_select", "kcache_append", "topk_gather",
            "prefill_chunk_paged", "dtype_code", "F32", "BF16", "FP8_E4M3"]
 
 
@@ -98,6 +98,42 @@ def indexer_prefill(q, k, w, topk: int, q_scale=None, k_scale=None, want_scores:
     st = lib.indexer_prefill(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), dt, _ptr(w), B, L, H, D, topk,
                              _ptr(idx), _ptr(val), _ptr(scores), _ptr(ws), nws, _stream(dev))
     _lib.check(st, "indexer_prefill")
+    return idx, val, scores
+
+
+def indexer_prefill_noalloc(q, k, w, topk: int, q_scale=None, k_scale=None, want_scores: bool = False,
+                            want_topk_score: bool = True, out=None):
+    """indexer_prefill through the library entry point that allocates
+    nothing (its scratch is a fixed device array inside the library).  The
+    outputs are allocated here unless ``out`` = (idx, score or None, scores or
+    None) gives them.  Returns the same triple as indexer_prefill."""
+    lib = _lib.load()
+    B, L, H, D = q.shape
+    if tuple(k.shape) != (B, L, D) or tuple(w.shape) != (B, L, H):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} w{tuple(w.shape)}")
+    dt = dtype_code(q)
+    if dtype_code(k) != dt:
+        raise ValueError("q and k must share a format")
+    _need(w, "w", _F32)
+    _need(q_scale, "q_scale", _F32)
+    _need(k_scale, "k_scale", _F32)
+    for name, t in (("q", q), ("k", k), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale)):
+        if t is not None:
+            _dev(t, name)
+    dev = q.device
+    if out is not None:
+        idx, val, scores = out
+        _need(idx, "idx", _I32)
+        if tuple(idx.shape) != (B, L, topk) or (val is not None and tuple(val.shape) != (B, L, topk)) or \
+                (scores is not None and tuple(scores.shape) != (B, L, L)):
+            raise ValueError("output shapes do not match the call")
+    else:
+        idx = torch.empty((B, L, topk), dtype=torch.int32, device=dev)
+        val = torch.empty((B, L, topk), dtype=torch.float32, device=dev) if want_topk_score else None
+        scores = torch.empty((B, L, L), dtype=torch.float32, device=dev) if want_scores else None
+    st = lib.indexer_prefill_noalloc(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), dt, _ptr(w), B, L, H, D, topk,
+                                     _ptr(idx), _ptr(val), _ptr(scores), _stream(dev))
+    _lib.check(st, "indexer_prefill_noalloc")
     return idx, val, scores
 
 

@@ -19,6 +19,10 @@ SIGNATURES = {
                                  _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "indexer_prefill_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "indexer_prefill_noalloc": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p,
+                                         _c_int, _c_int, _c_int, _c_int, _c_int,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "indexer_prefill_noalloc_scratch_bytes": (_c_size_t, []),
     "indexer_decode_paged": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
                                       _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                       _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),

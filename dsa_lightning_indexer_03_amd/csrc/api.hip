@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include "device_once.h"
 #include "dsaidx.h"
 #include "kernels.h"
 
@@ -162,11 +163,44 @@ size_t indexer_prefill_workspace_bytes(int B, int L, int H, int D, int topk, int
     return (size_t)B * (size_t)L * (size_t)L * sizeof(float);
 }
 
-dsaidx_status indexer_prefill(const void* q, const float* q_scale, const void* k, const float* k_scale,
-                              int qk_dtype, const float* w, int B, int L, int H, int D, int topk,
-                              int32_t* topk_idx, float* topk_score, float* scores,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-    g_err[0] = 0;
+}  // extern "C"
+
+// Scratch of indexer_prefill_noalloc, the entry point that allocates nothing:
+// one copy of this array per device, held until the process ends.  Host code
+// never uses the array's name as a device address (in host code it is only
+// a stand-in); the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current.
+static constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+dsaidx::PerDevice<void*> g_scratch_ptr;
+
+// Workspace of one prefill call: the caller's (checked against `need`), or,
+// for the entry point that allocates nothing, this device's scratch array.
+dsaidx_status prefill_workspace(bool noalloc, void* workspace, size_t workspace_bytes, size_t need, void** out) {
+    if (noalloc) {
+        if (need > kNoAllocScratchBytes)
+            return fail(DSAIDX_ERR_UNSUPPORTED,
+                        "this call needs %zu bytes of scratch; indexer_prefill_noalloc holds %zu (call "
+                        "indexer_prefill with a workspace instead)", need, kNoAllocScratchBytes);
+        const hipError_t e =
+            g_scratch_ptr.get([](int, void** p) { return hipGetSymbolAddress(p, HIP_SYMBOL(scratch)); }, out);
+        if (e != hipSuccess) return hip_fail(e, "indexer_prefill_noalloc (scratch address)");
+        return DSAIDX_OK;
+    }
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(DSAIDX_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if (need > 0 && !aligned16(workspace)) return fail(DSAIDX_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+    *out = workspace;
+    return DSAIDX_OK;
+}
+
+dsaidx_status prefill_run(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                          int qk_dtype, const float* w, int B, int L, int H, int D, int topk,
+                          int32_t* topk_idx, float* topk_score, float* scores,
+                          void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
     if (!q) return fail(DSAIDX_ERR_NULL, "q is NULL");
     if (!k) return fail(DSAIDX_ERR_NULL, "k is NULL");
     if (!w) return fail(DSAIDX_ERR_NULL, "w is NULL");
@@ -205,23 +239,17 @@ dsaidx_status indexer_prefill(const void* q, const float* q_scale, const void* k
     a.scores = scores;
     hipStream_t st = (hipStream_t)stream;
 
+    const size_t need = indexer_prefill_workspace_bytes(B, L, H, D, topk, qk_dtype, scores ? 1 : 0);
+    void* ws = nullptr;
+    const dsaidx_status wst = prefill_workspace(noalloc, workspace, workspace_bytes, need, &ws);
+    if (wst != DSAIDX_OK) return wst;
     if (prefill_is_fused(qk_dtype, H, D)) {
-        const size_t need = dsaidx::prefill_fused_workspace_bytes(B, L, qk_dtype);
-        if (need > 0 && (!workspace || workspace_bytes < need))
-            return fail(DSAIDX_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-        if (need > 0 && !aligned16(workspace)) return fail(DSAIDX_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
-        a.workspace = workspace;
+        a.workspace = ws;
         hipError_t e = dsaidx::launch_prefill_fused(a, qk_dtype, st);
         if (e != hipSuccess) return hip_fail(e, "indexer_prefill (fused)");
         return DSAIDX_OK;
     }
-    float* mat = scores;
-    if (!mat) {
-        const size_t need = indexer_prefill_workspace_bytes(B, L, H, D, topk, qk_dtype, 0);
-        if (!workspace || workspace_bytes < need)
-            return fail(DSAIDX_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-        mat = reinterpret_cast<float*>(workspace);
-    }
+    float* mat = scores ? scores : reinterpret_cast<float*>(ws);
     hipError_t e = dsaidx::launch_prefill_scores_generic(a, qk_dtype, mat, st);
     if (e != hipSuccess) return hip_fail(e, "indexer_prefill (scores)");
     dsaidx::SelectArgs s{};
@@ -237,6 +265,29 @@ dsaidx_status indexer_prefill(const void* q, const float* q_scale, const void* k
     e = dsaidx::launch_topk_select(s, B * L, st);
     if (e != hipSuccess) return hip_fail(e, "indexer_prefill (select)");
     return DSAIDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsaidx_status indexer_prefill(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                              int qk_dtype, const float* w, int B, int L, int H, int D, int topk,
+                              int32_t* topk_idx, float* topk_score, float* scores,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    return prefill_run(q, q_scale, k, k_scale, qk_dtype, w, B, L, H, D, topk, topk_idx, topk_score, scores,
+                       workspace, workspace_bytes, stream, false);
+}
+
+size_t indexer_prefill_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+dsaidx_status indexer_prefill_noalloc(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                      int qk_dtype, const float* w, int B, int L, int H, int D, int topk,
+                                      int32_t* topk_idx, float* topk_score, float* scores, void* stream) {
+    g_err[0] = 0;
+    return prefill_run(q, q_scale, k, k_scale, qk_dtype, w, B, L, H, D, topk, topk_idx, topk_score, scores,
+                       nullptr, 0, stream, true);
 }
 
 size_t indexer_prefill_chunk_paged_workspace_bytes(int B, int q0, int Lq) {

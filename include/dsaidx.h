@@ -18,9 +18,12 @@
  * ---------------------------------------
  * - Every array argument is a DEVICE pointer owned by the caller, row-major
  *   and contiguous unless a stride is given.  The library allocates nothing
- *   and keeps no state between calls; scratch memory is the caller's
- *   `workspace` (size from the matching *_workspace_bytes query; it may be
- *   NULL when that size is 0).
+ *   and keeps no state between calls beyond one-time, per-device set-up
+ *   (kernel attributes, an occupancy query, the address of the no-alloc
+ *   entry point's scratch), made thread-safely on first use; scratch memory
+ *   is the caller's `workspace` (size from the matching *_workspace_bytes
+ *   query; it may be NULL when that size is 0), except for
+ *   indexer_prefill_noalloc below.
  * - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *   enqueue work and return; results are valid after the caller synchronises
  *   the stream.
@@ -117,6 +120,32 @@ dsaidx_status indexer_prefill(const void* q, const float* q_scale,
 
 size_t indexer_prefill_workspace_bytes(int B, int L, int H, int D, int topk, int qk_dtype,
                                        int want_scores);
+
+/*
+ * indexer_prefill_noalloc -- indexer_prefill for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments, outputs and results
+ * as indexer_prefill, without a workspace argument.  Its scratch is a device
+ * array inside the library, one per GPU, of
+ * indexer_prefill_noalloc_scratch_bytes() bytes (32 MiB), held from the
+ * library's first use on that GPU until the process ends.  A call whose
+ * indexer_prefill_workspace_bytes() exceeds it returns
+ * DSAIDX_ERR_UNSUPPORTED before any launch: fp8 inputs up to about 6.7M keys
+ * (B times the 64-padded L), bf16 up to about 129k keys, the other shapes
+ * up to B*L*L*4 bytes unless `scores` is given.  The call makes no hipMalloc,
+ * hipFree or other allocating call.  Every call on one GPU uses the same
+ * scratch: calls that overlap on one GPU (on different streams, or from
+ * different threads) race and give undefined results; calls ordered on one
+ * stream are safe, since each call rewrites what it reads before reading it.
+ */
+dsaidx_status indexer_prefill_noalloc(const void* q, const float* q_scale,
+                                      const void* k, const float* k_scale,
+                                      int qk_dtype, const float* w,
+                                      int B, int L, int H, int D, int topk,
+                                      int32_t* topk_idx, float* topk_score, float* scores,
+                                      void* stream);
+
+size_t indexer_prefill_noalloc_scratch_bytes(void);
 
 /*
  * indexer_decode_paged -- one decode step for B queries, each scoring its

@@ -33,7 +33,7 @@ def lib():
 def test_header_declares_the_entry_points():
     fns = header_functions()
     for name in ("indexer_prefill", "indexer_decode_paged", "topk_select", "indexer_kcache_append",
-                 "indexer_topk_gather", "indexer_prefill_chunk_paged"):
+                 "indexer_topk_gather", "indexer_prefill_chunk_paged", "indexer_prefill_noalloc"):
         assert name in fns
 
 
@@ -72,6 +72,32 @@ def prefill(lib, q=P, qs=None, k=P, ks=None, dt=1, w=P, B=1, L=64, H=16, D=128, 
 def test_prefill_rejects_before_launch(lib, kw, status):
     assert prefill(lib, **kw) == status
     assert lib.dsaidx_last_error()  # a detail message is set
+
+
+def prefill_noalloc(lib, q=P, qs=None, k=P, ks=None, dt=1, w=P, B=1, L=64, H=16, D=128, topk=8,
+                    idx=P, val=None, sc=None):
+    return lib.indexer_prefill_noalloc(q, qs, k, ks, dt, w, B, L, H, D, topk, idx, val, sc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(w=None), NULL), (dict(dt=7), DTYPE), (dict(dt=2), NULL), (dict(B=0), SHAPE),
+    (dict(L=131073), UNSUP), (dict(H=6), UNSUP), (dict(topk=2049), UNSUP), (dict(q=P + 4), UNSUP),
+    # beyond the scratch array: bf16 at 65536 x 2 keys (34 MB), the generic path's L*L matrix
+    (dict(B=2, L=65536), UNSUP), (dict(dt=0, H=4, D=32, L=4096), UNSUP),
+])
+def test_prefill_noalloc_rejects_before_launch(lib, kw, status):
+    """Every check of the entry point that allocates nothing -- including the
+    scratch limit -- runs on the host before any HIP call."""
+    assert prefill_noalloc(lib, **kw) == status
+    assert lib.dsaidx_last_error()
+
+
+def test_prefill_noalloc_scratch_size(lib):
+    n = lib.indexer_prefill_noalloc_scratch_bytes()
+    assert n == 32 << 20
+    # the headline fp8 workload and the bf16 L=8192 workload fit; their workspace sizes are below the array
+    assert lib.indexer_prefill_workspace_bytes(1, 32768, 64, 128, 2048, 2, 0) <= n
+    assert lib.indexer_prefill_workspace_bytes(1, 8192, 64, 128, 2048, 1, 0) <= n
 
 
 def test_prefill_workspace_query(lib):
