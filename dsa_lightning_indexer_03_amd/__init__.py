@@ -22,7 +22,7 @@ from . import _lib
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
 __all__ = ["indexer_prefill", "indexer_prefill_noalloc", "indexer_decode_paged", "topk_select", "kcache_append", "topk_gather",
-           "prefill_chunk_paged", "dtype_code", "F32", "BF16", "FP8_E4M3"]
+           "prefill_chunk_paged", "prefill_chunk_varlen", "dtype_code", "F32", "BF16", "FP8_E4M3"]
 
 
 def dtype_code(t: torch.Tensor) -> int:
@@ -259,37 +259,65 @@ def topk_gather(latent_cache, block_table, topk_idx):
     return out
 
 
-def prefill_chunk_paged(q, q_scale, w, k_cache, k_scale, block_table, q0: int, topk: int,
-                        want_topk_score: bool = True, workspace: torch.Tensor | None = None):
-    """Top-k of a chunk of Lq query tokens per sequence at positions q0 ..
-    q0+Lq-1 against a paged fp8 key cache that holds keys 0 .. q0+Lq-1.
+def prefill_chunk_varlen(q, q_scale, w, cu_seqlens_q, q_start, k_cache, k_scale, block_table, topk: int,
+                         max_kv_len: int, want_topk_score: bool = True, workspace: torch.Tensor | None = None):
+    """Top-k of the query rows of B sequences' chunks (packed one after
+    another) against the paged fp8 key cache: row cu_seqlens_q[b] + i is
+    position q_start[b] + i of sequence b and sees keys 0 .. that position.
 
-    q [B,Lq,H,D] fp8 codes (uint8), q_scale [B,Lq,H] fp32, w [B,Lq,H] fp32,
-    k_cache [P,page,D] uint8, k_scale [P,page] fp32, block_table [B,max_pages]
-    int32.  Returns (idx int32 [B,Lq,topk] of absolute positions, score fp32
-    or None)."""
+    q [T,H,D] fp8 codes (uint8), q_scale [T,H] fp32, w [T,H] fp32,
+    cu_seqlens_q [B+1] int32 (device), q_start [B] int32 (device), k_cache
+    [P,page,D] uint8, k_scale [P,page] fp32, block_table [B,max_pages] int32;
+    ``max_kv_len`` bounds q_start[b] + rows of b (host value).  Returns (idx
+    int32 [T,topk] of absolute positions, score fp32 [T,topk] or None)."""
     lib = _lib.load()
-    B, Lq, H, D = q.shape
+    T, H, D = q.shape
     P, page, Dk = k_cache.shape
-    if Dk != D or tuple(k_scale.shape) != (P, page) or tuple(w.shape) != (B, Lq, H):
+    B = q_start.shape[0]
+    if Dk != D or tuple(k_scale.shape) != (P, page) or tuple(w.shape) != (T, H) or tuple(q_scale.shape) != (T, H):
         raise ValueError("shape mismatch")
-    if tuple(q_scale.shape) != (B, Lq, H) or block_table.shape[0] != B:
-        raise ValueError("q_scale / block_table shape mismatch")
+    if tuple(cu_seqlens_q.shape) != (B + 1,) or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("cu_seqlens_q [B+1], q_start [B] and block_table [B, max_pages] must agree on B")
     _need(q_scale, "q_scale", _F32)
     _need(w, "w", _F32)
     _need(k_cache, "k_cache", *_CODES)
     _need(k_scale, "k_scale", _F32)
     _need(block_table, "block_table", _I32)
-    for name, t in (("q", q), ("q_scale", q_scale), ("w", w), ("k_cache", k_cache), ("k_scale", k_scale),
-                    ("block_table", block_table)):
+    _need(cu_seqlens_q, "cu_seqlens_q", _I32)
+    _need(q_start, "q_start", _I32)
+    for name, t in (("q", q), ("q_scale", q_scale), ("w", w), ("cu_seqlens_q", cu_seqlens_q), ("q_start", q_start),
+                    ("k_cache", k_cache), ("k_scale", k_scale), ("block_table", block_table)):
         _dev(t, name)
     dev = q.device
-    idx = torch.empty((B, Lq, topk), dtype=torch.int32, device=dev)
-    val = torch.empty((B, Lq, topk), dtype=torch.float32, device=dev) if want_topk_score else None
-    nws = lib.indexer_prefill_chunk_paged_workspace_bytes(B, q0, Lq)
+    idx = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    val = torch.empty((T, topk), dtype=torch.float32, device=dev) if want_topk_score else None
+    nws = lib.indexer_prefill_chunk_paged_workspace_bytes(B, T, int(max_kv_len))
     ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, dev)
-    st = lib.indexer_prefill_chunk_paged(_ptr(q), _ptr(q_scale), dtype_code(q), _ptr(w), _ptr(k_cache),
-                                         _ptr(k_scale), _ptr(block_table), block_table.shape[1], P, B, q0, Lq, H, D,
-                                         page, topk, _ptr(idx), _ptr(val), _ptr(ws), nws, _stream(dev))
+    st = lib.indexer_prefill_chunk_paged(_ptr(q), _ptr(q_scale), dtype_code(q), _ptr(w), _ptr(cu_seqlens_q),
+                                         _ptr(q_start), _ptr(k_cache), _ptr(k_scale), _ptr(block_table),
+                                         block_table.shape[1], P, B, T, int(max_kv_len), H, D, page, topk,
+                                         _ptr(idx), _ptr(val), _ptr(ws), nws, _stream(dev))
     _lib.check(st, "indexer_prefill_chunk_paged")
     return idx, val
+
+
+def prefill_chunk_paged(q, q_scale, w, k_cache, k_scale, block_table, q0: int, topk: int,
+                        want_topk_score: bool = True, workspace: torch.Tensor | None = None):
+    """Top-k of a chunk of Lq query tokens per sequence, all at positions q0
+    .. q0+Lq-1, against a paged fp8 key cache that holds keys 0 .. q0+Lq-1
+    (prefill_chunk_varlen with equal chunks).
+
+    q [B,Lq,H,D] fp8 codes (uint8), q_scale [B,Lq,H] fp32, w [B,Lq,H] fp32,
+    k_cache [P,page,D] uint8, k_scale [P,page] fp32, block_table [B,max_pages]
+    int32.  Returns (idx int32 [B,Lq,topk] of absolute positions, score fp32
+    or None)."""
+    B, Lq, H, D = q.shape
+    if tuple(q_scale.shape) != (B, Lq, H) or tuple(w.shape) != (B, Lq, H) or block_table.shape[0] != B:
+        raise ValueError("q_scale / w / block_table shape mismatch")
+    dev = q.device
+    cu = torch.arange(0, (B + 1) * Lq, Lq, dtype=torch.int32, device=dev)
+    qs = torch.full((B,), int(q0), dtype=torch.int32, device=dev)
+    idx, val = prefill_chunk_varlen(q.reshape(B * Lq, H, D), q_scale.reshape(B * Lq, H), w.reshape(B * Lq, H), cu, qs,
+                                    k_cache, k_scale, block_table, topk, int(q0) + Lq,
+                                    want_topk_score=want_topk_score, workspace=workspace)
+    return idx.view(B, Lq, topk), None if val is None else val.view(B, Lq, topk)

@@ -33,9 +33,9 @@ SIGNATURES = {
     "indexer_kcache_append": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                        _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
     "indexer_prefill_chunk_paged": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p,
-                                             _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                             _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
-                                             _c_void_p]),
+                                             _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                             _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "indexer_prefill_chunk_paged_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "indexer_topk_gather": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int,
                                      _c_int, _c_void_p, _c_void_p]),

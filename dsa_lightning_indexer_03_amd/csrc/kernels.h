@@ -73,6 +73,17 @@ struct PrefillArgs {
     int Lk;                   // keys the chunk sees: q0 + L
     const int32_t* block_table;
     int max_pages;
+    // Variable-length chunks against the paged cache: the query rows of
+    // sequence b are cu_q[b] .. cu_q[b+1]-1 (T rows in all), at positions
+    // q_start[b] ..; its cache holds keys 0 .. q_start[b] + (cu_q[b+1] -
+    // cu_q[b]) - 1, at most max_kv keys.  `plan` (set by the launcher, in the
+    // workspace) lists the 8-row blocks, heaviest first.
+    const int32_t* cu_q;
+    const int32_t* q_start;
+    int T;
+    int max_kv;
+    int2* plan;
+    int n_plan;
 };
 
 // Indexer K-cache write path: T new keys quantised to FP8 and appended.
@@ -106,6 +117,11 @@ hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t str
 size_t prefill_fused_workspace_bytes(int B, int L, int dtype);
 // fp8 queries of a chunk against the paged cache (fields q0, Lk, block_table, max_pages)
 hipError_t launch_prefill_chunk_paged(const PrefillArgs& a, hipStream_t stream);
+// Warp-specialised fp8 prefill (csrc/prefill_ws.hip): whole sequences
+// (L <= 131072) and variable-length chunks against the paged cache.
+size_t prefill_ws_workspace_bytes(int B, int max_keys, int n_plan);
+hipError_t launch_prefill_ws(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_ws_varlen(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_kcache_append(const KcacheArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_topk_gather(const GatherArgs& a, hipStream_t stream);
 

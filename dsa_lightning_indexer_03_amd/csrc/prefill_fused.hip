@@ -48,6 +48,7 @@
 #include "common.h"
 #include "device_once.h"
 #include "kernels.h"
+#include "rowbuf.h"
 
 namespace dsaidx {
 
@@ -60,6 +61,9 @@ constexpr int kD = 128;
 #endif
 #ifndef DSAIDX_PREFILL_STAGED
 #define DSAIDX_PREFILL_STAGED 1  // fp8 with L <= 65536: stage keys through LDS
+#endif
+#ifndef DSAIDX_PREFILL_WS
+#define DSAIDX_PREFILL_WS 1  // fp8: the kernel with specialised waves (prefill_ws.hip), all L
 #endif
 #ifndef DSAIDX_PREFILL_STAGED_BF16
 #define DSAIDX_PREFILL_STAGED_BF16 1  // bf16 with L <= 65536: stage keys through LDS
@@ -81,314 +85,6 @@ __device__ __forceinline__ float reduce_scatter4(const float v[4]) {
     const float a1 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
     auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-// Per-wave candidate buffer in LDS.
-template <typename Pos>
-struct RowBuf {
-    uint32_t* key;
-    Pos* pos;
-    uint32_t* hist;  // 256 16-bit bins, two per word (bin b: word b/2, half b%2)
-};
-
-// The buffer routines below walk the buffer 256 entries per step, lane l
-// holding entries 256*step + 4*l .. +3 (one 16-byte key read, one 8- or
-// 16-byte position read), so each step keeps four independent LDS reads in
-// flight instead of one.  Buffer capacities are multiples of 256.
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-typedef float v2f __attribute__((ext_vector_type(2)));
-
-template <typename Pos>
-struct Pos4 { Pos v[4]; };
-
-template <typename Pos>
-__device__ __forceinline__ Pos4<Pos> read_pos4(const Pos* p) {
-    Pos4<Pos> r;
-    if constexpr (sizeof(Pos) == 2) {
-        const uint2 u = *reinterpret_cast<const uint2*>(p);
-        r.v[0] = (Pos)(u.x & 0xFFFF); r.v[1] = (Pos)(u.x >> 16);
-        r.v[2] = (Pos)(u.y & 0xFFFF); r.v[3] = (Pos)(u.y >> 16);
-    } else {
-        const v4u u = *reinterpret_cast<const v4u*>(p);
-        r.v[0] = (Pos)u[0]; r.v[1] = (Pos)u[1]; r.v[2] = (Pos)u[2]; r.v[3] = (Pos)u[3];
-    }
-    return r;
-}
-
-// Exclusive prefix over the wave of a per-lane count (counts < 2^16).
-__device__ __forceinline__ uint32_t wave_excl(uint32_t v, uint32_t* total) {
-    const uint32_t inc = wave_incl_scan(v);
-    *total = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
-    return inc - v;
-}
-
-// Position as an unsigned value of the buffer's position width, inverted so
-// that a lower position compares larger.
-template <typename Pos>
-__device__ __forceinline__ uint32_t inv_pos(Pos p) {
-    return (uint32_t)(Pos)~p;
-}
-
-// Histogram of an 8-bit (or narrower) digit over matching buffer entries.
-// BY_POS = false: digit (key >> shift) & dmask of the entries whose key has
-//   (key & pm) == pv.
-// BY_POS = true: digit of the inverted position of the entries whose key
-//   equals kappa and whose inverted position has (ipos & pm) == pv.
-template <bool BY_POS, typename Pos>
-__device__ __forceinline__ void wave_hist(const RowBuf<Pos>& rb, int n, uint32_t kappa, uint32_t pm, uint32_t pv,
-                                          int shift, uint32_t dmask) {
-    const int l = lane_id();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) rb.hist[l + 64 * i] = 0u;
-    __builtin_amdgcn_wave_barrier();
-    for (int j0 = 0; j0 < n; j0 += 256) {
-        const int j = j0 + 4 * l;
-        const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
-        if constexpr (BY_POS) {
-            const Pos4<Pos> p = read_pos4(rb.pos + j);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t ip = inv_pos(p.v[e]);
-                if (j + e < n && k[e] == kappa && (ip & pm) == pv) {
-                    const uint32_t bin = (ip >> shift) & dmask;
-                    atomicAdd(&rb.hist[bin >> 1], 1u << ((bin & 1u) << 4));
-                }
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (j + e < n && (k[e] & pm) == pv) {
-                    const uint32_t bin = (k[e] >> shift) & dmask;
-                    atomicAdd(&rb.hist[bin >> 1], 1u << ((bin & 1u) << 4));
-                }
-        }
-    }
-    __builtin_amdgcn_wave_barrier();
-}
-
-// Bin (counting down from the top) where the running count reaches `need`.
-// Returns the bin; *above = count in bins above it.
-template <typename Pos>
-__device__ __forceinline__ uint32_t wave_find_bin(const RowBuf<Pos>& rb, uint32_t need, uint32_t* above,
-                                                  uint32_t* in_bin) {
-    const int l = lane_id();
-    // bins 255-4l .. 252-4l: the high and low halves of words 127-2l, 126-2l
-    const uint32_t w_hi = rb.hist[127 - 2 * l], w_lo = rb.hist[126 - 2 * l];
-    const uint32_t c[4] = {w_hi >> 16, w_hi & 0xFFFFu, w_lo >> 16, w_lo & 0xFFFFu};
-    const uint32_t loc = c[0] + c[1] + c[2] + c[3];
-    const uint32_t incl = wave_incl_scan(loc);
-    uint32_t run = incl - loc;
-    int hit = -1;
-    uint32_t ab = 0, cnt = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (hit < 0 && run < need && need <= run + c[i]) { hit = i; ab = run; cnt = c[i]; }
-        run += c[i];
-    }
-    const uint64_t m = wave_ballot(hit >= 0);
-    const int src = __builtin_ctzll(m);
-    const int bin = 255 - 4 * l - (hit < 0 ? 0 : hit);
-    *above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
-    *in_bin = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
-    return (uint32_t)__builtin_amdgcn_readlane(bin, src);
-}
-
-// Common leading bits of all buffer keys: returns their count; *pv = value.
-template <typename Pos>
-__device__ __forceinline__ int wave_common_prefix(const RowBuf<Pos>& rb, int n, uint32_t* pv) {
-    uint32_t o = 0u, a = 0xFFFFFFFFu;
-    const int l = lane_id();
-    for (int j0 = 0; j0 < n; j0 += 256) {
-        const int j = j0 + 4 * l;
-        const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (j + e < n) { o |= k[e]; a &= k[e]; }
-    }
-    o = wave_or(o);
-    a = wave_and(a);
-    const uint32_t diff = o ^ a;
-    const int cp = diff == 0u ? 32 : __clz(diff);
-    *pv = cp == 0 ? 0u : (a & (0xFFFFFFFFu << (32 - cp)));
-    return cp;
-}
-
-// Exact `need`-th largest key of the buffer (1 <= need <= n): returns kappa;
-// *ties = how many entries equal to kappa belong to the top `need` (the rest
-// of the top are strictly greater); *eq = how many entries equal kappa.
-template <typename Pos>
-__device__ uint32_t wave_kth_key(const RowBuf<Pos>& rb, int n, uint32_t need, uint32_t* ties, uint32_t* eq) {
-    uint32_t pv;
-    const int cp = wave_common_prefix(rb, n, &pv);
-    uint32_t pm = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
-    int hi = 32 - cp;
-    uint32_t inb = (uint32_t)n;  // all keys equal when no digit is left
-    while (hi > 0) {
-        const int width = hi < 8 ? hi : 8;
-        const int shift = hi - width;
-        const uint32_t dmask = (1u << width) - 1u;
-        wave_hist<false>(rb, n, 0u, pm, pv, shift, dmask);
-        uint32_t above;
-        const uint32_t b = wave_find_bin(rb, need, &above, &inb);
-        need -= above;
-        pv |= b << shift;
-        pm |= dmask << shift;
-        hi = shift;
-    }
-    *ties = need;
-    *eq = inb;
-    return pv;
-}
-
-// Tie break at the k-th key: among the entries whose key equals kappa, the
-// `ties` lowest positions win (1 <= ties <= count of such entries).  Returns
-// the largest winning position; an entry with key kappa wins iff its
-// position is <= the result.  Radix select on inverted positions.
-template <typename Pos>
-__device__ uint32_t wave_tie_cut(const RowBuf<Pos>& rb, int n, uint32_t kappa, uint32_t ties) {
-    uint32_t pm = 0u, pv = 0u, need = ties;
-    for (int hi = 8 * (int)sizeof(Pos); hi > 0; hi -= 8) {
-        const int shift = hi - 8;
-        wave_hist<true>(rb, n, kappa, pm, pv, shift, 0xFFu);
-        uint32_t above, inb;
-        const uint32_t b = wave_find_bin(rb, need, &above, &inb);
-        need -= above;
-        pv |= b << shift;
-        pm |= 0xFFu << shift;
-    }
-    return inv_pos((Pos)pv);
-}
-
-// One stable pass over the buffer keeping, in buffer order, every entry with
-// key > kappa or (key == kappa and position <= pos_cut) when exact, else
-// every entry with key >= lo_edge.  Kept entries go to the buffer front (in
-// place) or, if idx != nullptr, to the output row.
-template <typename Pos>
-__device__ int wave_keep_pass(const RowBuf<Pos>& rb, int n, bool exact, uint32_t kappa, uint32_t pos_cut,
-                              uint32_t lo_edge, int32_t* idx, float* val, int limit) {
-    const int l = lane_id();
-    int wpos = 0;
-    for (int j0 = 0; j0 < n; j0 += 256) {
-        const int j = j0 + 4 * l;
-        const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
-        const Pos4<Pos> p = read_pos4(rb.pos + j);
-        bool keep[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            keep[e] = j + e < n &&
-                      (exact ? (k[e] > kappa || (k[e] == kappa && (uint32_t)p.v[e] <= pos_cut)) : k[e] >= lo_edge);
-        const uint32_t kc = (uint32_t)keep[0] + keep[1] + keep[2] + keep[3];
-        uint32_t k_tot;
-        int o = wpos + (int)wave_excl(kc, &k_tot);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (keep[e]) {
-                if (idx) {
-                    if (o < limit) {
-                        idx[o] = (int32_t)p.v[e];
-                        if (val) val[o] = key_score(k[e]);
-                    }
-                } else {
-                    rb.key[o] = k[e];
-                    rb.pos[o] = p.v[e];
-                }
-                ++o;
-            }
-        }
-        wpos += (int)k_tot;
-    }
-    __builtin_amdgcn_wave_barrier();
-    return wpos;
-}
-
-// Exact cut of the buffer to its top K by (key desc, position asc): returns
-// kappa and the position cut for wave_keep_pass.
-template <typename Pos>
-__device__ __forceinline__ uint32_t wave_exact_cut(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* pos_cut) {
-    uint32_t ties, eq;
-    const uint32_t kappa = wave_kth_key(rb, n, K, &ties, &eq);
-    *pos_cut = eq > ties ? wave_tie_cut(rb, n, kappa, ties) : 0xFFFFFFFFu;
-    return kappa;
-}
-
-// Drops buffer entries that cannot be in the top K (n > K).  Returns the new
-// count and the new append floor (append iff key > *thr).  Entries equal to
-// the cut key stay admissible: in an out-of-order scan a later one may have
-// a lower position.
-template <typename Pos>
-__device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* thr, int cap) {
-    uint32_t pv;
-    const int cp = wave_common_prefix(rb, n, &pv);
-    uint32_t lo_edge = 0;  // keep keys >= lo_edge
-    bool exact = false;
-    if (cp < 32) {
-        const int hi = 32 - cp;
-        const int width = hi < 8 ? hi : 8;
-        const int shift = hi - width;
-        const uint32_t dmask = (1u << width) - 1u;
-        const uint32_t pm = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
-        wave_hist<false>(rb, n, 0u, pm, pv, shift, dmask);
-        uint32_t above, inb;
-        const uint32_t b = wave_find_bin(rb, K, &above, &inb);
-        lo_edge = pv | (b << shift);
-        // Too many entries would survive (a crowded bin): fall back to exact.
-        if (above + inb > (uint32_t)(cap - 256)) exact = true;
-    } else {
-        exact = true;  // all keys equal
-    }
-    uint32_t kappa = 0, pos_cut = 0;
-    if (exact) kappa = wave_exact_cut(rb, n, K, &pos_cut);
-    const int kept = wave_keep_pass(rb, n, exact, kappa, pos_cut, lo_edge, (int32_t*)nullptr, (float*)nullptr, 0);
-    const uint32_t fl = exact ? kappa : lo_edge;
-    *thr = fl == 0u ? 0u : fl - 1u;
-    return kept;
-}
-
-// Speculative floor: keeps the entries whose key is at least the lower edge
-// of the radix bin (one digit below the common prefix) that holds the r-th
-// largest key, and returns that edge (<= the r-th largest key).  1 <= r <= n.
-template <typename Pos>
-__device__ int wave_floor(const RowBuf<Pos>& rb, int n, uint32_t r, uint32_t* floor_key) {
-    uint32_t pv;
-    const int cp = wave_common_prefix(rb, n, &pv);
-    uint32_t lo_edge = pv;
-    if (cp < 32) {
-        const int hi = 32 - cp;
-        const int width = hi < 8 ? hi : 8;
-        const int shift = hi - width;
-        const uint32_t dmask = (1u << width) - 1u;
-        const uint32_t pm = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
-        wave_hist<false>(rb, n, 0u, pm, pv, shift, dmask);
-        uint32_t above, inb;
-        const uint32_t b = wave_find_bin(rb, r, &above, &inb);
-        lo_edge = pv | (b << shift);
-    }
-    *floor_key = lo_edge;
-    return wave_keep_pass(rb, n, false, 0u, 0u, lo_edge, (int32_t*)nullptr, (float*)nullptr, 0);
-}
-
-// Writes the exact top K of the buffer by (key desc, position asc) -- or all
-// of it when n <= K -- to the output row, then the -1 / -inf padding.
-template <typename Pos>
-__device__ void wave_emit(const RowBuf<Pos>& rb, int n, int K, int32_t* idx, float* val) {
-    const int l = lane_id();
-    if (n <= K) {
-        for (int j = l; j < K; j += kWave) {
-            if (j < n) {
-                idx[j] = (int32_t)rb.pos[j];
-                if (val) val[j] = key_score(rb.key[j]);
-            } else {
-                idx[j] = -1;
-                if (val) val[j] = -INFINITY;
-            }
-        }
-        return;
-    }
-    uint32_t pos_cut;
-    const uint32_t kappa = wave_exact_cut(rb, n, (uint32_t)K, &pos_cut);
-    wave_keep_pass(rb, n, true, kappa, pos_cut, 0u, idx, val, K);
 }
 
 // Short-row bypass: a row with at most K valid positions selects all of
@@ -1763,6 +1459,7 @@ hipError_t launch_pos(const PrefillArgs& a, hipStream_t stream) {
 
 size_t prefill_fused_workspace_bytes(int B, int L, int dtype) {
     const size_t n = (size_t)B * pad64(L);
+    if (DSAIDX_PREFILL_WS && dtype == 2) return prefill_ws_workspace_bytes(B, L, 0);
     if (staged_path(dtype, L)) return (n * 5 + 255) / 256 * 256;  // fp32 adjusted scales, then the E8M0 bytes
     if (staged_bf16_path(dtype, L)) return n * (4 + 2 * kD);      // fp32 adjusted scales, then the scaled keys
     return 0;
@@ -1780,6 +1477,7 @@ hipError_t launch_prefill_chunk_paged(const PrefillArgs& a, hipStream_t stream) 
 
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream) {
     const int hb = a.H / 16;
+    if (DSAIDX_PREFILL_WS && dtype == 2) return launch_prefill_ws(a, stream);
     if (dtype == 2) {
         switch (hb) {
             case 1: return launch_pos<2, 1>(a, stream);

@@ -184,44 +184,56 @@ dsaidx_status indexer_decode_paged(const void* q, int q_dtype, const float* w,
 size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, int D, int topk);
 
 /*
- * indexer_prefill_chunk_paged -- a chunk of Lq new query tokens per sequence,
- * at positions q0 .. q0+Lq-1, scored against the paged FP8 key cache that
- * already holds keys 0 .. q0+Lq-1 (the chunk's own keys included), with the
+ * indexer_prefill_chunk_paged -- chunked prefill of a serving batch: for each
+ * of B sequences, a chunk of new query tokens at its own positions, scored
+ * against that sequence's paged FP8 key cache, which already holds every key
+ * up to the chunk's last position (the chunk's own keys included), with the
  * top-k of every query.
  *
  * Passage: the core formula and causal top-k of indexer_prefill, evaluated
- * for the rows q0 .. q0+Lq-1 of the sequence; the keys come from the indexer
- * cache, which each token's key enters before that token is scored
- * ("Lightning Indexer explained", sections 2.1 and 2.4 of the decode
- * walkthrough; "Study MLA Indexer", the notes on its two caches).  The
- * result for query i equals indexer_prefill's row q0+i over the whole
- * sequence: it sees the q0+i+1 positions 0 .. q0+i.
+ * for a run of rows of each sequence; the keys come from the indexer cache,
+ * which each token's key enters before that token is scored ("Lightning
+ * Indexer explained", sections 2.1 and 2.4 of the decode walkthrough; "Study
+ * MLA Indexer", the notes on its two caches).  Query row cu_seqlens_q[b] + i
+ * is position p = q_start[b] + i of sequence b and sees the p + 1 positions
+ * 0 .. p: its result equals indexer_prefill's row p over the whole sequence.
  *
- *   q            [B][Lq][H][D] FP8 E4M3 codes (q_dtype must be
- *                DSAIDX_FP8_E4M3), q_scale [B][Lq][H] fp32
- *   w            [B][Lq][H] fp32
+ *   q            [T][H][D] FP8 E4M3 codes, the sequences' chunks packed one
+ *                after another (q_dtype must be DSAIDX_FP8_E4M3);
+ *                q_scale [T][H] fp32; w [T][H] fp32
+ *   cu_seqlens_q [B+1] int32 (device): sequence b's rows are
+ *                cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1; cu_seqlens_q[0] = 0,
+ *                nondecreasing, cu_seqlens_q[B] = T (a sequence may have none)
+ *   q_start      [B] int32 (device): position of sequence b's first row
  *   k_cache      [num_pages][page_size][D] E4M3FN codes, k_scale
  *                [num_pages][page_size] fp32 (as indexer_kcache_append writes)
  *   block_table  [B][max_pages_per_seq] int32 page ids; position s of
  *                sequence b is page block_table[b][s / page_size], slot
- *                s % page_size; q0 + Lq <= max_pages_per_seq * page_size
- *   topk_idx     out [B][Lq][topk] int32 (absolute positions, -1 padded);
- *   topk_score   out [B][Lq][topk] fp32 or NULL
- *   workspace    indexer_prefill_chunk_paged_workspace_bytes(B, q0, Lq)
- *                bytes of caller-owned device memory, 16-byte aligned
- *                (5 bytes per visible key, 256-byte rounded)
+ *                s % page_size
+ *   T            number of query rows (host value, = cu_seqlens_q[B])
+ *   max_kv_len   host-side bound: q_start[b] + (its row count) <= max_kv_len
+ *                for every b, and max_kv_len <= max_pages_per_seq * page_size
+ *                (a sequence beyond it sees only its first max_kv_len keys)
+ *   topk_idx     out [T][topk] int32 (absolute positions, -1 padded);
+ *   topk_score   out [T][topk] fp32 or NULL
+ *   workspace    indexer_prefill_chunk_paged_workspace_bytes(B, T,
+ *                max_kv_len) bytes of caller-owned device memory, 16-byte
+ *                aligned: 5 bytes per key up to max_kv_len (64-padded) per
+ *                sequence, 256-byte rounded, then 8 bytes per 8-row block
+ *                (the launch plan)
  *
  * Supported: H a multiple of 16 in [16, 64], D = 128, page_size = 64,
- * 1 <= topk <= 2048, q0 + Lq <= 65536.
+ * 1 <= topk <= 2048, max_kv_len <= 131072.
  */
 dsaidx_status indexer_prefill_chunk_paged(const void* q, const float* q_scale, int q_dtype, const float* w,
+                                          const int32_t* cu_seqlens_q, const int32_t* q_start,
                                           const uint8_t* k_cache, const float* k_scale,
                                           const int32_t* block_table, int max_pages_per_seq, int num_pages,
-                                          int B, int q0, int Lq, int H, int D, int page_size, int topk,
+                                          int B, int T, int max_kv_len, int H, int D, int page_size, int topk,
                                           int32_t* topk_idx, float* topk_score,
                                           void* workspace, size_t workspace_bytes, void* stream);
 
-size_t indexer_prefill_chunk_paged_workspace_bytes(int B, int q0, int Lq);
+size_t indexer_prefill_chunk_paged_workspace_bytes(int B, int T, int max_kv_len);
 
 /*
  * indexer_kcache_append -- quantise T new keys to FP8 and write them into the

@@ -184,18 +184,18 @@ def test_topk_gather_rejects_before_launch(lib, kw, status):
     assert gather(lib, **kw) == status
 
 
-def chunk(lib, q=P, qs=P, dt=2, w=P, kc=P, ks=P, bt=P, mpp=64, npg=64, B=1, q0=100, Lq=64, H=64, D=128, ps=64,
-          topk=2048, idx=P, val=None, ws=P, nws=1 << 20):
-    return lib.indexer_prefill_chunk_paged(q, qs, dt, w, kc, ks, bt, mpp, npg, B, q0, Lq, H, D, ps, topk, idx, val,
-                                           ws, nws, None)
+def chunk(lib, q=P, qs=P, dt=2, w=P, cu=P, q0s=P, kc=P, ks=P, bt=P, mpp=64, npg=64, B=1, T=64, mkv=164, H=64, D=128,
+          ps=64, topk=2048, idx=P, val=None, ws=P, nws=1 << 20):
+    return lib.indexer_prefill_chunk_paged(q, qs, dt, w, cu, q0s, kc, ks, bt, mpp, npg, B, T, mkv, H, D, ps, topk, idx,
+                                           val, ws, nws, None)
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=None), NULL), (dict(qs=None), NULL), (dict(w=None), NULL), (dict(kc=None), NULL),
-    (dict(ks=None), NULL), (dict(bt=None), NULL), (dict(idx=None), NULL),
-    (dict(dt=9), DTYPE), (dict(dt=1), UNSUP), (dict(B=0), SHAPE), (dict(Lq=0), SHAPE), (dict(q0=-1), SHAPE),
-    (dict(q0=4033), SHAPE), (dict(H=8), UNSUP), (dict(D=64), UNSUP), (dict(ps=32, mpp=128), UNSUP),
-    (dict(topk=4096), UNSUP), (dict(mpp=2048, q0=65500, Lq=64), UNSUP), (dict(ws=None), WS), (dict(nws=100), WS),
+    (dict(q=None), NULL), (dict(qs=None), NULL), (dict(w=None), NULL), (dict(cu=None), NULL), (dict(q0s=None), NULL),
+    (dict(kc=None), NULL), (dict(ks=None), NULL), (dict(bt=None), NULL), (dict(idx=None), NULL),
+    (dict(dt=9), DTYPE), (dict(dt=1), UNSUP), (dict(B=0), SHAPE), (dict(T=0), SHAPE), (dict(mkv=0), SHAPE),
+    (dict(mkv=4097), SHAPE), (dict(H=8), UNSUP), (dict(D=64), UNSUP), (dict(ps=32, mpp=128), UNSUP),
+    (dict(topk=4096), UNSUP), (dict(mpp=4096, mkv=131073), UNSUP), (dict(ws=None), WS), (dict(nws=100), WS),
     (dict(kc=P + 8), UNSUP),
 ])
 def test_prefill_chunk_rejects_before_launch(lib, kw, status):
@@ -203,8 +203,12 @@ def test_prefill_chunk_rejects_before_launch(lib, kw, status):
 
 
 def test_prefill_chunk_workspace_query(lib):
-    # 5 bytes per visible key (64-padded), rounded to 256: q0 + Lq = 4160 keys
-    assert lib.indexer_prefill_chunk_paged_workspace_bytes(2, 4096, 64) == (2 * 4160 * 5 + 255) // 256 * 256
+    # 5 bytes per key up to max_kv_len (64-padded) per sequence, rounded to
+    # 256, then one 8-byte plan entry per 8-row block bound (T/8 + B)
+    assert lib.indexer_prefill_chunk_paged_workspace_bytes(2, 128, 4160) == \
+        (2 * 4160 * 5 + 255) // 256 * 256 + (128 // 8 + 2) * 8
+    assert lib.indexer_prefill_chunk_paged_workspace_bytes(64, 64, 131072) == \
+        (64 * 131072 * 5 + 255) // 256 * 256 + (64 // 8 + 64) * 8
 
 
 # ---- the Python binding's own checks (host-side, before any device access) ----
@@ -226,6 +230,9 @@ def _wrapper_cases():
               k_cache=_t((P, 64, D), u8), k_scale=_t((P, 64), f32))
     ch = dict(q=_t((B, 32, H, D), u8), q_scale=_t((B, 32, H), f32), w=_t((B, 32, H), f32),
               k_cache=_t((P, 64, D), u8), k_scale=_t((P, 64), f32), block_table=_t((B, 4), i32), q0=100, topk=16)
+    cv = dict(q=_t((40, H, D), u8), q_scale=_t((40, H), f32), w=_t((40, H), f32), cu_seqlens_q=_t((B + 1,), i32),
+              q_start=_t((B,), i32), k_cache=_t((P, 64, D), u8), k_scale=_t((P, 64), f32),
+              block_table=_t((B, 4), i32), topk=16, max_kv_len=200)
     ga = dict(latent_cache=_t((P, 64, 512), bf), block_table=_t((B, 4), i32), topk_idx=_t((B, 16), i32))
     cases = []
     for fn, base, bad in (
@@ -236,6 +243,8 @@ def _wrapper_cases():
         ("prefill_chunk_paged", ch, [("block_table", i64), ("q_scale", f64), ("w", f64), ("k_scale", f64),
                                      ("k_cache", i32)]),
         ("topk_gather", ga, [("block_table", i64), ("topk_idx", i64)]),
+        ("prefill_chunk_varlen", cv, [("cu_seqlens_q", i64), ("q_start", i64), ("block_table", i64),
+                                      ("q_scale", f64), ("w", f64), ("k_scale", f64), ("k_cache", i32)]),
     ):
         for name, dt in bad:
             kw = dict(base)

@@ -98,3 +98,70 @@ def test_chunk_full_size_sampled():
     assert np.all(gi[0] >= 0) and np.all(gi[0] <= np.arange(q0, L)[:, None])
     srt = np.sort(gi[0], axis=1)
     assert np.all(srt[:, 1:] != srt[:, :-1])
+
+
+def ragged_sequence(Lk, q0, Lq, H, seed):
+    """One sequence of Lk fp8 keys and, for rows q0 .. q0+Lq-1 only, fp8
+    queries and softmax weights.  The other query rows stay zero (np.zeros:
+    never touched, so a 131072-row query array costs no host memory); they
+    are never read.  Draw order: keys, then the chunk's queries, then its
+    weight logits."""
+    rng = np.random.default_rng(seed)
+    kc, ks = synth.quantize_fp8_rows(rng.standard_normal((Lk, 128), dtype=np.float32))
+    q = np.zeros((1, Lk, H, 128), np.uint8)
+    qs = np.ones((1, Lk, H), np.float32)
+    w = np.zeros((1, Lk, H), np.float32)
+    if Lq:
+        qc, qsc = synth.quantize_fp8_rows(rng.standard_normal((Lq, H, 128), dtype=np.float32))
+        q[0, q0:q0 + Lq], qs[0, q0:q0 + Lq] = qc, qsc
+        w[0, q0:q0 + Lq] = synth.softmax_weights(rng.standard_normal((Lq, H)))
+    return dict(kind="prefill", B=1, L=Lk, H=H, D=128, dtype="fp8", q=q, q_scale=qs, k=kc[None], k_scale=ks[None], w=w)
+
+
+@pytest.mark.parametrize("K", [2048, 64])
+def test_varlen_ragged_batch_against_the_cache(K):
+    """A serving batch of chunks of different lengths at different positions
+    in one call: one sequence with no rows, a single-row chunk, chunks off the
+    64-key pages, one straddling position 65536 and one ending exactly at
+    position 131072 (17-bit positions), all in one permuted page pool.  Every
+    row of every chunk against the oracle's row of its own sequence."""
+    H = 32
+    spec = [(0, 300), (5000, 37), (123, 0), (130900, 172), (65500, 100), (2000, 1)]  # (q0, Lq) per sequence
+    seqs = [ragged_sequence(q0 + Lq, q0, Lq, H, seed=970 + i) for i, (q0, Lq) in enumerate(spec)]
+    B = len(spec)
+    pages = [(q0 + Lq + 63) // 64 for q0, Lq in spec]
+    mpp = max(pages)
+    rng = np.random.default_rng(977)
+    pool = rng.permutation(sum(pages) + 5).astype(np.int32)
+    table = np.zeros((B, mpp), np.int32)
+    cache = rng.integers(0, 0x7F, size=(pool.size, 64, 128), dtype=np.uint8)   # junk outside the sequences
+    scales = np.ones((pool.size, 64), np.float32)
+    off = 0
+    for b, sq in enumerate(seqs):
+        table[b, :pages[b]] = pool[off:off + pages[b]]
+        off += pages[b]
+        s = np.arange(sq["L"])
+        cache[table[b, s // 64], s % 64] = sq["k"][0]
+        scales[table[b, s // 64], s % 64] = sq["k_scale"][0]
+    cu = np.concatenate([[0], np.cumsum([Lq for _, Lq in spec])]).astype(np.int32)
+    T = int(cu[-1])
+    qpk = np.concatenate([sq["q"][0, q0:q0 + Lq] for sq, (q0, Lq) in zip(seqs, spec)])
+    qsp = np.concatenate([sq["q_scale"][0, q0:q0 + Lq] for sq, (q0, Lq) in zip(seqs, spec)])
+    wpk = np.concatenate([sq["w"][0, q0:q0 + Lq] for sq, (q0, Lq) in zip(seqs, spec)])
+    q_start = np.array([q0 for q0, _ in spec], np.int32)
+    say(f"varlen chunk batch: B={B} T={T} K={K} max_kv={max(q0 + Lq for q0, Lq in spec)}")
+    gi, gv = dsa.prefill_chunk_varlen(dev(qpk), dev(qsp), dev(wpk), dev(cu), dev(q_start), dev(cache), dev(scales),
+                                      dev(table), K, max(q0 + Lq for q0, Lq in spec))
+    torch.cuda.synchronize()
+    gi, gv = host(gi), host(gv)
+    assert gi.shape == (T, K)
+    for b, (sq, (q0, Lq)) in enumerate(zip(seqs, spec)):
+        if Lq == 0:
+            continue
+        rows = np.arange(q0, q0 + Lq)
+        for a0 in range(0, Lq, 64):
+            rr = rows[a0:a0 + 64]
+            _, _, osc = indexer.prefill(sq, K, rows=rr, want_scores=True)
+            sel = rr - q0 + cu[b]
+            check_topk_rows(gi[sel], gv[sel], osc[0], rr + 1, K, where=f"varlen seq {b} (q0={q0})")
+        say(f"  sequence {b}: rows {q0}..{q0 + Lq - 1} match the oracle")
