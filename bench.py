@@ -41,7 +41,8 @@ COPY_WRITE_FACTOR = 1048576.0 / 1048576.0
 _DECODE_SRC = ["csrc/decode_paged.hip", "csrc/select_row.h", "csrc/common.h", "csrc/kernels.h", "build.py"]
 _DECODE_SHA = "b994f09d85857f186da6a3bd56b247d4d0d47b75fa896b0ba2941317424e6e58"
 COUNTERS = {
-    "prefill": {"sources": ["csrc/prefill_fused.hip", "csrc/common.h", "csrc/kernels.h", "build.py"],
+    "prefill": {"sources": ["csrc/prefill_ws.hip", "csrc/rowbuf.h", "csrc/varlen.h", "csrc/common.h", "csrc/kernels.h",
+                            "build.py"],
                 "sha256": "b707bbef38e6ef71cebf89feeeadd0125e737fd97eb5c1b8f5b2b114bb4971b2",
                 "fetch_kib": 255166.1, "write_kib": 524385.8},
     # main scan of one decode call (the sample kernel reads about 1/60 of it)
@@ -145,6 +146,64 @@ def cpu_baseline_prefill(inp, K, gpu_idx, gpu_val, seconds):
                       f"{threads} {api} threads; every sampled row parity-checked against the GPU output"}
 
 
+# A serving batch of chunked-prefill requests: (position of the chunk's first
+# query, chunk length) per sequence; two chunks end exactly at position 131072.
+VARLEN_SPEC = [(0, 2048), (8192, 1024), (30000, 512), (60000, 2048), (65500, 512), (100000, 1024),
+               (126976, 4096), (129024, 2048)]
+
+
+def bench_varlen(torch, dsa, dev, args):
+    """One call over a ragged batch of chunks (VARLEN_SPEC) against a paged
+    fp8 cache whose 64-token pages are scattered by a seeded permutation;
+    fp8 queries (with per-row scales) and bf16 queries, H=64, D=128, k=2048.
+    Inputs are seeded normals generated on the device."""
+    H, D, K = 64, 128, 2048
+    B = len(VARLEN_SPEC)
+    lens = [q0 + lq for q0, lq in VARLEN_SPEC]
+    pages = [(n + 63) // 64 for n in lens]
+    mpp, n_pages = max(pages), sum(pages)
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    perm = torch.randperm(n_pages, generator=g, device=dev).to(torch.int32)
+    table = torch.zeros((B, mpp), dtype=torch.int32, device=dev)
+    off = 0
+    for b, n in enumerate(pages):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    kf = torch.randn((n_pages * 64, D), generator=g, device=dev)
+    ksc = (kf.abs().amax(dim=1) / 448.0).clamp_min(1e-30)
+    kc = (kf / ksc[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).view(n_pages, 64, D)
+    ksc = ksc.view(n_pages, 64).contiguous()
+    del kf
+    T = sum(lq for _, lq in VARLEN_SPEC)
+    cu = torch.tensor([0] + list(np.cumsum([lq for _, lq in VARLEN_SPEC])), dtype=torch.int32, device=dev)
+    q_start = torch.tensor([q0 for q0, _ in VARLEN_SPEC], dtype=torch.int32, device=dev)
+    qf = torch.randn((T, H, D), generator=g, device=dev)
+    qsc = (qf.abs().amax(dim=2) / 448.0).clamp_min(1e-30)
+    q8 = (qf / qsc[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    qb = qf.to(torch.bfloat16)
+    del qf
+    w = torch.softmax(torch.randn((T, H), generator=g, device=dev), dim=1)
+    pairs = sum(lq * q0 + lq * (lq + 1) // 2 for q0, lq in VARLEN_SPEC)
+    out = {"what": f"one call over {B} sequences' chunks (q_start, rows) = {VARLEN_SPEC}: T={T} query rows, "
+                   f"H={H} D={D} k={K}, against a paged fp8 cache of {sum(lens)} keys in scattered 64-token pages",
+           "pairs": pairs}
+    for name, qq, qs, peak in (("fp8", q8, qsc, PEAK_FP8_TFLOPS), ("bf16", qb, None, PEAK_BF16_TFLOPS)):
+        nws = dsa._lib.load().indexer_prefill_chunk_paged_workspace_bytes(B, T, max(lens), dsa.dtype_code(qq))
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+        def vstep():
+            dsa.prefill_chunk_varlen(qq, qs, w, cu, q_start, kc, ksc, table, K, max(lens), workspace=ws)
+
+        ms, _ = time_calls(torch, vstep, max(args.steps, 10), args.warmup)
+        tf = 2.0 * H * D * pairs / (ms * 1e-3) / 1e12
+        log(f"prefill varlen chunks, {name} queries: {ms:.3f} ms ({pairs / (ms * 1e-3):.4g} pairs/s, {tf:.0f} TFLOP/s)")
+        out[f"{name}_queries"] = {"ms_per_call": ms, "pairs_per_s": pairs / (ms * 1e-3), "TFLOP/s": tf,
+                                  f"frac_of_{name}_peak": tf / peak}
+        del ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,7 +277,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": achieved / PEAK_FP8_TFLOPS, "traffic": measured_traffic("prefill"),
                          "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
-                         "kernel": "prefill_fused_fp8_staged_kernel<4, false>",
+                         "kernel": "prefill_ws_fp8_kernel<4, false, false, false>",
                          "work": f"2*H*D flop per causal pair x {pairs} pairs = {flops:.4g} flop per launch"},
             "wall_s_timed": wall,
         }
@@ -253,6 +312,9 @@ def main():
             del kc, ksc, tab, qc, qsc, wc, perm
         del q, k, w, qs, ks, out
         torch.cuda.empty_cache()
+        if not args.no_extra:
+            result["prefill_chunk_varlen"] = bench_varlen(torch, dsa, dev, args)
+            torch.cuda.empty_cache()
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -22,6 +22,7 @@ from . import _lib
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
 __all__ = ["indexer_prefill", "indexer_prefill_noalloc", "indexer_decode_paged", "topk_select", "kcache_append", "topk_gather",
+           "topk_gather_layers",
            "prefill_chunk_paged", "prefill_chunk_varlen", "dtype_code", "F32", "BF16", "FP8_E4M3"]
 
 
@@ -259,13 +260,57 @@ def topk_gather(latent_cache, block_table, topk_idx):
     return out
 
 
+def topk_gather_layers(latent_caches, block_table, topk_idx, outs=None):
+    """Index Share: one selection gathered from several layers' latent
+    caches in one launch.  latent_caches: a sequence of [P,page,E] tensors of
+    one shape and dtype (at most 64); block_table, topk_idx as topk_gather.
+    Returns a list of [B,K,E] tensors, one per layer (or fills `outs`)."""
+    import ctypes
+
+    lib = _lib.load()
+    caches = list(latent_caches)
+    if not caches:
+        raise ValueError("latent_caches is empty")
+    P, page, E = caches[0].shape
+    for i, c in enumerate(caches):
+        if c.shape != caches[0].shape or c.dtype != caches[0].dtype:
+            raise ValueError(f"latent_caches[{i}] differs in shape or dtype from latent_caches[0]")
+        _dev(c, f"latent_caches[{i}]")
+    B, K = topk_idx.shape
+    _need(block_table, "block_table", _I32)
+    _need(topk_idx, "topk_idx", _I32)
+    for name, t in (("block_table", block_table), ("topk_idx", topk_idx)):
+        _dev(t, name)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages] with the B of topk_idx")
+    if outs is None:
+        outs = [torch.empty((B, K, E), dtype=caches[0].dtype, device=caches[0].device) for _ in caches]
+    else:
+        outs = list(outs)
+        if len(outs) != len(caches):
+            raise ValueError("one output per layer")
+        for i, o in enumerate(outs):
+            if o.shape != (B, K, E) or o.dtype != caches[0].dtype:
+                raise ValueError(f"outs[{i}] must be [B, K, E] of the caches' dtype")
+            _dev(o, f"outs[{i}]")
+    n = len(caches)
+    cp = (ctypes.c_void_p * n)(*[c.data_ptr() for c in caches])
+    op = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    st = lib.indexer_topk_gather_layers(cp, op, n, E * caches[0].element_size(), _ptr(block_table),
+                                        block_table.shape[1], P, page, _ptr(topk_idx), B, K,
+                                        _stream(caches[0].device))
+    _lib.check(st, "indexer_topk_gather_layers")
+    return outs
+
+
 def prefill_chunk_varlen(q, q_scale, w, cu_seqlens_q, q_start, k_cache, k_scale, block_table, topk: int,
                          max_kv_len: int, want_topk_score: bool = True, workspace: torch.Tensor | None = None):
     """Top-k of the query rows of B sequences' chunks (packed one after
     another) against the paged fp8 key cache: row cu_seqlens_q[b] + i is
     position q_start[b] + i of sequence b and sees keys 0 .. that position.
 
-    q [T,H,D] fp8 codes (uint8), q_scale [T,H] fp32, w [T,H] fp32,
+    q [T,H,D] fp8 codes (uint8) with q_scale [T,H] fp32, or bf16 with
+    q_scale None; w [T,H] fp32,
     cu_seqlens_q [B+1] int32 (device), q_start [B] int32 (device), k_cache
     [P,page,D] uint8, k_scale [P,page] fp32, block_table [B,max_pages] int32;
     ``max_kv_len`` bounds q_start[b] + rows of b (host value).  Returns (idx
@@ -274,10 +319,16 @@ def prefill_chunk_varlen(q, q_scale, w, cu_seqlens_q, q_start, k_cache, k_scale,
     T, H, D = q.shape
     P, page, Dk = k_cache.shape
     B = q_start.shape[0]
-    if Dk != D or tuple(k_scale.shape) != (P, page) or tuple(w.shape) != (T, H) or tuple(q_scale.shape) != (T, H):
+    if Dk != D or tuple(k_scale.shape) != (P, page) or tuple(w.shape) != (T, H):
         raise ValueError("shape mismatch")
+    fp8_q = dtype_code(q) == FP8_E4M3
+    if fp8_q != (q_scale is not None):
+        raise ValueError("q_scale [T, H] goes with fp8 queries, None with bf16 queries")
+    if q_scale is not None and tuple(q_scale.shape) != (T, H):
+        raise ValueError("q_scale must be [T, H]")
     if tuple(cu_seqlens_q.shape) != (B + 1,) or block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("cu_seqlens_q [B+1], q_start [B] and block_table [B, max_pages] must agree on B")
+    _need(q, "q", *_CODES, torch.bfloat16, torch.int16, torch.uint16)
     _need(q_scale, "q_scale", _F32)
     _need(w, "w", _F32)
     _need(k_cache, "k_cache", *_CODES)
@@ -287,11 +338,12 @@ def prefill_chunk_varlen(q, q_scale, w, cu_seqlens_q, q_start, k_cache, k_scale,
     _need(q_start, "q_start", _I32)
     for name, t in (("q", q), ("q_scale", q_scale), ("w", w), ("cu_seqlens_q", cu_seqlens_q), ("q_start", q_start),
                     ("k_cache", k_cache), ("k_scale", k_scale), ("block_table", block_table)):
-        _dev(t, name)
+        if t is not None:
+            _dev(t, name)
     dev = q.device
     idx = torch.empty((T, topk), dtype=torch.int32, device=dev)
     val = torch.empty((T, topk), dtype=torch.float32, device=dev) if want_topk_score else None
-    nws = lib.indexer_prefill_chunk_paged_workspace_bytes(B, T, int(max_kv_len))
+    nws = lib.indexer_prefill_chunk_paged_workspace_bytes(B, T, int(max_kv_len), dtype_code(q))
     ws = workspace if workspace is not None and workspace.numel() >= nws else _workspace(nws, dev)
     st = lib.indexer_prefill_chunk_paged(_ptr(q), _ptr(q_scale), dtype_code(q), _ptr(w), _ptr(cu_seqlens_q),
                                          _ptr(q_start), _ptr(k_cache), _ptr(k_scale), _ptr(block_table),
@@ -307,17 +359,20 @@ def prefill_chunk_paged(q, q_scale, w, k_cache, k_scale, block_table, q0: int, t
     .. q0+Lq-1, against a paged fp8 key cache that holds keys 0 .. q0+Lq-1
     (prefill_chunk_varlen with equal chunks).
 
-    q [B,Lq,H,D] fp8 codes (uint8), q_scale [B,Lq,H] fp32, w [B,Lq,H] fp32,
-    k_cache [P,page,D] uint8, k_scale [P,page] fp32, block_table [B,max_pages]
-    int32.  Returns (idx int32 [B,Lq,topk] of absolute positions, score fp32
-    or None)."""
+    q [B,Lq,H,D] fp8 codes (uint8) with q_scale [B,Lq,H] fp32, or bf16 with
+    q_scale None; w [B,Lq,H] fp32, k_cache [P,page,D] uint8, k_scale [P,page]
+    fp32, block_table [B,max_pages] int32.  Returns (idx int32 [B,Lq,topk] of
+    absolute positions, score fp32 or None)."""
     B, Lq, H, D = q.shape
-    if tuple(q_scale.shape) != (B, Lq, H) or tuple(w.shape) != (B, Lq, H) or block_table.shape[0] != B:
-        raise ValueError("q_scale / w / block_table shape mismatch")
+    if tuple(w.shape) != (B, Lq, H) or block_table.shape[0] != B:
+        raise ValueError("w / block_table shape mismatch")
+    if q_scale is not None and tuple(q_scale.shape) != (B, Lq, H):
+        raise ValueError("q_scale must be [B, Lq, H]")
     dev = q.device
     cu = torch.arange(0, (B + 1) * Lq, Lq, dtype=torch.int32, device=dev)
     qs = torch.full((B,), int(q0), dtype=torch.int32, device=dev)
-    idx, val = prefill_chunk_varlen(q.reshape(B * Lq, H, D), q_scale.reshape(B * Lq, H), w.reshape(B * Lq, H), cu, qs,
+    qsc = None if q_scale is None else q_scale.reshape(B * Lq, H)
+    idx, val = prefill_chunk_varlen(q.reshape(B * Lq, H, D), qsc, w.reshape(B * Lq, H), cu, qs,
                                     k_cache, k_scale, block_table, topk, int(q0) + Lq,
                                     want_topk_score=want_topk_score, workspace=workspace)
     return idx.view(B, Lq, topk), None if val is None else val.view(B, Lq, topk)

@@ -36,9 +36,12 @@ SIGNATURES = {
                                              _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                              _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
-    "indexer_prefill_chunk_paged_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
+    "indexer_prefill_chunk_paged_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "indexer_topk_gather": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int,
                                      _c_int, _c_void_p, _c_void_p]),
+    "indexer_topk_gather_layers": (_c_int, [ctypes.POINTER(_c_void_p), ctypes.POINTER(_c_void_p), _c_int, _c_int,
+                                            _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int, _c_int,
+                                            _c_void_p]),
     "dsaidx_status_string": (ctypes.c_char_p, [_c_int]),
     "dsaidx_last_error": (ctypes.c_char_p, []),
     "dsaidx_version": (_c_int, []),

@@ -124,6 +124,47 @@ dsaidx_status indexer_topk_gather(const void* latent_cache, int row_bytes, const
     return DSAIDX_OK;
 }
 
+dsaidx_status indexer_topk_gather_layers(const void* const* latent_caches, void* const* outs, int n_layers,
+                                         int row_bytes, const int32_t* block_table, int max_pages_per_seq,
+                                         int num_pages, int page_size, const int32_t* topk_idx, int B, int topk,
+                                         void* stream) {
+    g_err[0] = 0;
+    if (!latent_caches) return fail(DSAIDX_ERR_NULL, "latent_caches is NULL");
+    if (!outs) return fail(DSAIDX_ERR_NULL, "outs is NULL");
+    if (!block_table) return fail(DSAIDX_ERR_NULL, "block_table is NULL");
+    if (!topk_idx) return fail(DSAIDX_ERR_NULL, "topk_idx is NULL");
+    if (n_layers < 1 || B < 1 || topk < 1 || max_pages_per_seq < 1 || num_pages < 1 || page_size < 1 ||
+        row_bytes < 1)
+        return fail(DSAIDX_ERR_SHAPE,
+                    "n_layers=%d B=%d topk=%d max_pages_per_seq=%d num_pages=%d page_size=%d row_bytes=%d",
+                    n_layers, B, topk, max_pages_per_seq, num_pages, page_size, row_bytes);
+    if (n_layers > dsaidx::kMaxGatherLayers)
+        return fail(DSAIDX_ERR_UNSUPPORTED, "n_layers=%d (at most %d per call)", n_layers,
+                    dsaidx::kMaxGatherLayers);
+    if (page_size != 64) return fail(DSAIDX_ERR_UNSUPPORTED, "page_size=%d (64)", page_size);
+    if (row_bytes % 16 != 0 || row_bytes > 65536)
+        return fail(DSAIDX_ERR_UNSUPPORTED, "row_bytes=%d (a multiple of 16, at most 65536)", row_bytes);
+    dsaidx::GatherLayersArgs a{};
+    for (int l = 0; l < n_layers; ++l) {
+        if (!latent_caches[l]) return fail(DSAIDX_ERR_NULL, "latent_caches[%d] is NULL", l);
+        if (!outs[l]) return fail(DSAIDX_ERR_NULL, "outs[%d] is NULL", l);
+        if (!aligned16(latent_caches[l]) || !aligned16(outs[l]))
+            return fail(DSAIDX_ERR_UNSUPPORTED, "latent_caches[%d] and outs[%d] must be 16-byte aligned", l, l);
+        a.cache[l] = reinterpret_cast<const uint8_t*>(latent_caches[l]);
+        a.out[l] = reinterpret_cast<uint8_t*>(outs[l]);
+    }
+    a.block_table = block_table;
+    a.idx = topk_idx;
+    a.B = B;
+    a.K = topk;
+    a.max_pages = max_pages_per_seq;
+    a.row_bytes = row_bytes;
+    a.n_layers = n_layers;
+    const hipError_t e = dsaidx::launch_topk_gather_layers(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "indexer_topk_gather_layers");
+    return DSAIDX_OK;
+}
+
 size_t topk_select_workspace_bytes(int rows, int cols, int topk) {
     (void)rows; (void)cols; (void)topk;
     return 0;
@@ -290,8 +331,9 @@ dsaidx_status indexer_prefill_noalloc(const void* q, const float* q_scale, const
                        nullptr, 0, stream, true);
 }
 
-size_t indexer_prefill_chunk_paged_workspace_bytes(int B, int T, int max_kv_len) {
+size_t indexer_prefill_chunk_paged_workspace_bytes(int B, int T, int max_kv_len, int q_dtype) {
     if (B < 1 || T < 1 || max_kv_len < 1) return 0;
+    if (q_dtype == DSAIDX_BF16) return dsaidx::prefill_bf16_varlen_workspace_bytes(B, T, max_kv_len);
     return dsaidx::prefill_ws_workspace_bytes(B, max_kv_len, (T + 7) / 8 + B);
 }
 
@@ -304,7 +346,6 @@ dsaidx_status indexer_prefill_chunk_paged(const void* q, const float* q_scale, i
                                           void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     if (!q) return fail(DSAIDX_ERR_NULL, "q is NULL");
-    if (!q_scale) return fail(DSAIDX_ERR_NULL, "q_scale is NULL");
     if (!w) return fail(DSAIDX_ERR_NULL, "w is NULL");
     if (!cu_seqlens_q) return fail(DSAIDX_ERR_NULL, "cu_seqlens_q is NULL");
     if (!q_start) return fail(DSAIDX_ERR_NULL, "q_start is NULL");
@@ -321,7 +362,10 @@ dsaidx_status indexer_prefill_chunk_paged(const void* q, const float* q_scale, i
     if ((int64_t)max_kv_len > (int64_t)max_pages_per_seq * page_size)
         return fail(DSAIDX_ERR_SHAPE, "max_kv_len = %d > max_pages_per_seq * page_size = %lld", max_kv_len,
                     (long long)max_pages_per_seq * page_size);
-    if (q_dtype != DSAIDX_FP8_E4M3) return fail(DSAIDX_ERR_UNSUPPORTED, "chunk queries must be fp8 (q_scale given)");
+    if (q_dtype == DSAIDX_F32) return fail(DSAIDX_ERR_UNSUPPORTED, "chunk queries must be fp8 or bf16");
+    if (q_dtype == DSAIDX_FP8_E4M3 && !q_scale) return fail(DSAIDX_ERR_NULL, "q_scale is NULL (fp8 queries)");
+    if (q_dtype == DSAIDX_BF16 && q_scale)
+        return fail(DSAIDX_ERR_UNSUPPORTED, "q_scale must be NULL for bf16 queries");
     if (H % 16 != 0 || H > 64) return fail(DSAIDX_ERR_UNSUPPORTED, "H=%d (16, 32, 48 or 64)", H);
     if (D != 128) return fail(DSAIDX_ERR_UNSUPPORTED, "D=%d (128)", D);
     if (page_size != 64) return fail(DSAIDX_ERR_UNSUPPORTED, "page_size=%d (64)", page_size);
@@ -330,7 +374,7 @@ dsaidx_status indexer_prefill_chunk_paged(const void* q, const float* q_scale, i
     if ((int64_t)T + 8 * (int64_t)B > (int64_t)0x7FFFFFFF) return fail(DSAIDX_ERR_UNSUPPORTED, "T too large");
     if (!aligned16(q) || !aligned16(k_cache)) return fail(DSAIDX_ERR_UNSUPPORTED, "q and k_cache must be 16-byte aligned");
     if (!aligned16(workspace)) return fail(DSAIDX_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
-    const size_t need = indexer_prefill_chunk_paged_workspace_bytes(B, T, max_kv_len);
+    const size_t need = indexer_prefill_chunk_paged_workspace_bytes(B, T, max_kv_len, q_dtype);
     if (!workspace || workspace_bytes < need)
         return fail(DSAIDX_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
     dsaidx::PrefillArgs a{};
@@ -355,7 +399,8 @@ dsaidx_status indexer_prefill_chunk_paged(const void* q, const float* q_scale, i
     a.q_start = q_start;
     a.T = T;
     a.max_kv = max_kv_len;
-    const hipError_t e = dsaidx::launch_prefill_ws_varlen(a, (hipStream_t)stream);
+    const hipError_t e = q_dtype == DSAIDX_BF16 ? dsaidx::launch_prefill_bf16_varlen(a, (hipStream_t)stream)
+                                                : dsaidx::launch_prefill_ws_varlen(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "indexer_prefill_chunk_paged");
     return DSAIDX_OK;
 }

@@ -107,6 +107,17 @@ struct GatherArgs {
     int B, K, max_pages, row_bytes;
 };
 
+// Index Share: the same selection gathered from several layers' latent caches.
+constexpr int kMaxGatherLayers = 64;
+struct GatherLayersArgs {
+    const uint8_t* cache[kMaxGatherLayers];  // per layer [num_pages][64][row_bytes]
+    uint8_t* out[kMaxGatherLayers];          // per layer [B][K][row_bytes]
+    const int32_t* block_table;              // [B][max_pages] page ids, shared by the layers
+    const int32_t* idx;                      // [B][K] positions, shared by the layers
+    int B, K, max_pages, row_bytes, n_layers;
+    int layers_per_group;                    // set by the launcher
+};
+
 size_t topk_select_smem_bytes();
 hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
@@ -115,8 +126,9 @@ hipError_t launch_decode_scan(const DecodeArgs& a, const SelectArgs& s, int H, h
 hipError_t launch_prefill_scores_generic(const PrefillArgs& a, int dtype, float* out, hipStream_t stream);
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream);
 size_t prefill_fused_workspace_bytes(int B, int L, int dtype);
-// fp8 queries of a chunk against the paged cache (fields q0, Lk, block_table, max_pages)
-hipError_t launch_prefill_chunk_paged(const PrefillArgs& a, hipStream_t stream);
+// bf16 queries of variable-length chunks against the paged fp8 cache.
+size_t prefill_bf16_varlen_workspace_bytes(int B, int T, int max_kv);
+hipError_t launch_prefill_bf16_varlen(const PrefillArgs& a, hipStream_t stream);
 // Warp-specialised fp8 prefill (csrc/prefill_ws.hip): whole sequences
 // (L <= 131072) and variable-length chunks against the paged cache.
 size_t prefill_ws_workspace_bytes(int B, int max_keys, int n_plan);
@@ -124,5 +136,6 @@ hipError_t launch_prefill_ws(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_ws_varlen(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_kcache_append(const KcacheArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_topk_gather(const GatherArgs& a, hipStream_t stream);
+hipError_t launch_topk_gather_layers(const GatherLayersArgs& a, hipStream_t stream);
 
 }  // namespace dsaidx

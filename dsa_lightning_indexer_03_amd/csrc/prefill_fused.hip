@@ -8,12 +8,13 @@
 // s asc).  As a contraction this is Q[L*H, D] x K[L, D]^T restricted to the
 // causal half; D = 128 and H is a multiple of 16.
 //
-// Three kernels, by dtype and length:
-// * fp8, L <= 65536 (the headline path) and bf16, L <= 65536: key chunks are
-//   staged through LDS once per workgroup of eight tokens, and the weighted
-//   head sum runs on the matrix cores (sections further down).
-// * bf16 and fp8 beyond L = 65536 (positions need 32 bits, buffers grow): the
-//   unstaged kernel below, whose layout is:
+// fp8 inputs, at every supported length, run in the kernel with specialised
+// waves (prefill_ws.hip).  This file holds the bf16 kernels:
+// * L <= 65536, and chunks of bf16 queries against the paged fp8 cache: key
+//   chunks are staged through LDS once per workgroup of eight tokens, and the
+//   weighted head sum runs on the matrix cores (sections further down).
+// * beyond L = 65536 (positions need 32 bits, buffers grow): the unstaged
+//   kernel below, whose layout is:
 // * workgroup = W independent waves; wave w owns query token t = W*blk + w and
 //   all 16*HB of its heads.  Blocks are issued heaviest (largest t) first.
 //   W = 4 with 4096-entry buffers and 32-bit positions (W = 8 with
@@ -24,16 +25,13 @@
 //   N), 16 keys per subtile, 64 keys per step.  No LDS is used for keys and
 //   waves never wait for each other; the four waves of a workgroup read the
 //   same key rows close together in time, so the vector L1 serves most of it.
-// * fp8: one v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, scales off) per
-//   16 heads x 16 keys; bf16: four v_mfma_f32_16x16x32_bf16.  The contraction
+// * four v_mfma_f32_16x16x32_bf16 per 16 heads x 16 keys.  The contraction
 //   dimension is split the same way on both operands: lane group g owns the
 //   dims [32g, 32g+32).
 // * epilogue in registers: c[t,h] * max(S, 0) summed over the lane's heads,
-//   with c = w * q_scale / sqrt(D) (exact refactoring: ReLU commutes with a
-//   positive scale, and the key's fp8 scale is applied once per key after
-//   the head sum), then a cross-lane reduce-scatter leaves lane l with the
-//   score of key s0 + l.
-// All three keep a streaming top-k per wave: a per-row candidate buffer of
+//   with c = w / sqrt(D), then a cross-lane reduce-scatter leaves lane l with
+//   the score of key s0 + l.
+// Both keep a streaming top-k per wave: a per-row candidate buffer of
 // (key, position) pairs in LDS, filled in position order.  A score enters the
 // buffer only if its order-preserving key beats the row threshold.  When the
 // buffer nears capacity it is compacted: one radix digit below the buffer's
@@ -49,21 +47,17 @@
 #include "device_once.h"
 #include "kernels.h"
 #include "rowbuf.h"
+#include "varlen.h"
 
 namespace dsaidx {
 
 namespace {
 
 constexpr int kD = 128;
+constexpr int pad64(int n) { return (n + 63) / 64 * 64; }
 
 #ifndef DSAIDX_PREFILL_DEPTH
 #define DSAIDX_PREFILL_DEPTH 1   // key chunks in flight ahead of the one multiplied (1 or 2)
-#endif
-#ifndef DSAIDX_PREFILL_STAGED
-#define DSAIDX_PREFILL_STAGED 1  // fp8 with L <= 65536: stage keys through LDS
-#endif
-#ifndef DSAIDX_PREFILL_WS
-#define DSAIDX_PREFILL_WS 1  // fp8: the kernel with specialised waves (prefill_ws.hip), all L
 #endif
 #ifndef DSAIDX_PREFILL_STAGED_BF16
 #define DSAIDX_PREFILL_STAGED_BF16 1  // bf16 with L <= 65536: stage keys through LDS
@@ -87,57 +81,8 @@ __device__ __forceinline__ float reduce_scatter4(const float v[4]) {
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Short-row bypass: a row with at most K valid positions selects all of
-// them (positions 0 .. tp, then -1), so when no score is asked for, a block
-// whose rows all qualify writes that directly and scores nothing.  Returns
-// true when the block took the bypass (uniform over the block).
-__device__ __forceinline__ bool short_rows_bypass(const PrefillArgs& a, int b, int blk, int W, int L, int q0,
-                                                  int t_raw, bool live) {
-    if (a.val_out || a.scores) return false;
-    const int last_row = min(blk * W + W - 1, L - 1);
-    if (q0 + last_row + 1 > a.topk) return false;
-    if (live) {
-        const int tp = q0 + t_raw;
-        int32_t* out = a.idx_out + ((size_t)b * L + t_raw) * a.topk;
-        for (int j = lane_id(); j < a.topk; j += kWave) out[j] = j <= tp ? j : -1;
-    }
-    return true;
-}
-
 template <int DT>  // 1 = bf16, 2 = fp8 e4m3
 struct Operands;
-
-template <>
-struct Operands<2> {
-    // A: lane (m, g) holds q[t][16hb+m][32g .. 32g+32) as 32 fp8 bytes.
-    template <int HB>
-    struct A { v8i a[HB]; };
-    template <int HB>
-    __device__ static void load_a(A<HB>& A_, const uint8_t* qrow0, int m, int g) {
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            const uint8_t* p = qrow0 + (size_t)(16 * hb + m) * kD + 32 * g;
-            const v4i lo = *reinterpret_cast<const v4i*>(p);
-            const v4i hi = *reinterpret_cast<const v4i*>(p + 16);
-            A_.a[hb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-    }
-    struct Bt { v4i lo, hi; };
-    __device__ static void load_b(Bt& b, const uint8_t* krow, int g) {
-        const uint8_t* p = krow + 32 * g;
-        b.lo = *reinterpret_cast<const v4i*>(p);
-        b.hi = *reinterpret_cast<const v4i*>(p + 16);
-    }
-    template <int HB>
-    __device__ static void mma(v4f (&acc)[HB], const A<HB>& A_, const Bt& b) {
-        const v8i bb = v8i{b.lo[0], b.lo[1], b.lo[2], b.lo[3], b.hi[0], b.hi[1], b.hi[2], b.hi[3]};
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-            acc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A_.a[hb], bb, v4f{0.f, 0.f, 0.f, 0.f},
-                                                                        0, 0, 0, 0, 0, 0);
-    }
-    static constexpr int kRowBytes = kD;
-};
 
 template <>
 struct Operands<1> {
@@ -388,92 +333,6 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// fp8, L <= 65536: keys staged through LDS, head sums on the matrix cores.
-//
-// The 8 waves of a workgroup (8 consecutive tokens, all with the same last
-// 64-key chunk) walk the chunks in lockstep: every 64-key chunk (8 KB of fp8
-// rows) is fetched from L2 once per workgroup with direct global->LDS loads
-// (no VGPRs in flight), triple-buffered, one barrier per chunk.  Rows are
-// stored with their 16-byte segments XOR-swizzled by ((row >> 1) & 7) so the
-// MFMA operand reads (16 rows at a 128-byte stride) spread over the LDS banks.
-//
-// Epilogue.  The score of key s is sum_h c_h max(S_h, 0) times the key's
-// scale, with c_h = w_h * q_scale_h / sqrt(D) and S_h the dot product of the
-// fp8 values.  |S_h| <= |q_h|_1 * max_d |k_d| <= 2^Pq_h * 2^Pk, with Pq_h
-// taken per head of the token and Pk per key (a pre-pass over the keys), so
-// the score MFMAs, run with the E8M0 operand scales 2^-Pq_h (A, one per row,
-// i.e. per head) and 2^-Pk (B, one per key column), leave every value in
-// [-1, 1] at its own head's scale.  There the conversion to f16 with its
-// [0, 1] clamp is max(S, 0) itself, rounded to nearest (relative error
-// <= 2^-11 down to 2^-14 of the head's bound, however far the heads'
-// magnitudes spread), and the weighted sum over heads is one more MFMA
-// (f16, 16x16x32) with the weights c_h * 2^Pq_h * 2^E as its A operand.  Its
-// weights for subtile st sit in the rows 4st..4st+3 only, so the four
-// subtiles of a chunk accumulate into one tile whose element 0 in lane l is
-// the score of key 64*chunk + l: no cross-lane reduction.  The factor 2^-E
-// and the key's scale times 2^Pk finish the score.
-// ---------------------------------------------------------------------------
-constexpr int kStagedWaves = 8;
-// Candidates per row: the most that fit beside three key chunks.  Every
-// compaction request makes all waves compact, so the buffer's slack above k
-// sets how often the whole block stalls.
-constexpr int kStagedCap = 2712;
-constexpr int kStages = 3;
-// per wave: keys [CAP + 64] u32, histogram [256] u16, positions [CAP + 64] u16; the
-// 64 slots past CAP take the writes of lanes that do not append
-constexpr size_t kStagedWaveBytes = (size_t)(kStagedCap + kWave) * 6 + 128 * 4;
-// Buffer walks read whole 256-entry steps, masking entries past the count,
-// so the last step reads up to entry kWalkEnd - 1.  Its keys stay within the
-// wave's keys and histogram; its positions can run past the wave's region
-// (into the next wave's, or into this padding after the last one).
-constexpr int kWalkEnd = (kStagedCap - 1) / 256 * 256 + 256;
-constexpr size_t kStagedTailPad = 128;
-static_assert((size_t)kWalkEnd * 4 <= (size_t)(kStagedCap + kWave) * 4 + 128 * 4, "key walk stays in the region");
-static_assert((size_t)kWalkEnd * 2 <= (size_t)(kStagedCap + kWave) * 2 + kStagedTailPad, "position walk padding");
-static_assert(kStagedWaveBytes % 16 == 0, "wave regions stay 16-byte aligned");
-constexpr size_t kStageKeyBytes = 64 * kD;                 // one chunk of fp8 keys,
-constexpr size_t kStageScaleOff = kStageKeyBytes;          // their fp32 scales times 2^Pk,
-constexpr size_t kStageExpOff = kStageKeyBytes + 64 * 4;   // their E8M0 bytes (64 used of 256)
-constexpr size_t kStageBytes = kStageExpOff + 256;
-constexpr size_t kStagedLds = kStages * kStageBytes + (size_t)kStagedWaves * kStagedWaveBytes + kStagedTailPad;
-static_assert(kStagedLds + 16 <= 160 * 1024, "LDS budget");
-
-// Key pre-pass: for key s of sequence b (positions up to the 64-padded
-// length; rows past the end repeat row L-1, as the staged copies do):
-// 2^Pk >= max_d |k_d| (Pk = 0 for a zero row), ks_adj = k_scale * 2^Pk and
-// the E8M0 byte 127 - Pk, stored at 64*chunk + 4*(s % 16) + (s % 64) / 16 so
-// that lane n of a chunk finds the bytes of its four subtiles in one word.
-template <bool PAGED>
-__global__ void __launch_bounds__(256)
-prefill_key_exp_kernel(PrefillArgs a) {
-    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int Lp = a.Lpad;
-    if (gi >= (int64_t)a.B * Lp) return;
-    const int b = (int)(gi / Lp), s = (int)(gi % Lp);
-    const int Lk = PAGED ? a.Lk : a.L;
-    const int sr = s < Lk ? s : Lk - 1;
-    // the key's slot: row sr of sequence b, or its page-pool slot
-    const size_t slot = PAGED ? (size_t)a.block_table[(size_t)b * a.max_pages + sr / 64] * 64 + sr % 64
-                              : (size_t)b * a.L + sr;
-    const uint8_t* row = reinterpret_cast<const uint8_t*>(a.k) + slot * kD;
-    uint32_t mx = 0;
-#pragma unroll
-    for (int c = 0; c < kD / 16; ++c) {
-        const v4i v = *reinterpret_cast<const v4i*>(row + 16 * c);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t x = (uint32_t)v[d] & 0x7F7F7F7Fu;  // magnitudes: e4m3 orders like its bits
-            mx = max(mx, max(max(x & 0xFFu, (x >> 8) & 0xFFu), max((x >> 16) & 0xFFu, x >> 24)));
-        }
-    }
-    const float vmax = __builtin_amdgcn_cvt_f32_fp8((int)mx, 0);
-    const int pk = vmax > 0.f ? __builtin_amdgcn_frexp_expf(vmax) : 0;  // 2^pk > vmax
-    a.ks_adj[gi] = ldexpf(a.k_scale[slot], pk);
-    const int c = s / 64, n = s % 16, q = (s % 64) / 16;
-    a.kexp[(size_t)b * Lp + 64 * c + 4 * n + q] = (uint8_t)(127 - pk);
-}
-
 // Rank r of the speculative floor in a row's sample, from the expected
 // number ec of sampled keys at or above the row's k-th largest: 3.5 standard
 // deviations (plus 8) above it.  The floor fails only if the sample holds r
@@ -484,475 +343,39 @@ __device__ __forceinline__ uint32_t spec_rank(float ec) {
     return (uint32_t)ceilf(ec + 3.5f * sqrtf(ec) + 8.f);
 }
 
-template <int HB, bool PAGED>
-__global__ void __launch_bounds__(kStagedWaves * kWave)
-prefill_fused_fp8_staged_kernel(PrefillArgs a) {
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    __shared__ uint32_t flags[4];  // [0..2] compaction requests, [3] rescan request
-    using Op = Operands<2>;
-    using Pos = uint16_t;
-    constexpr int W = kStagedWaves;
-    constexpr int CAP = kStagedCap;
-    constexpr int H = 16 * HB;
-    const int L = a.L;
-    const int nblk = (L + W - 1) / W;
-    const int b = blockIdx.x % a.B;
-    const int blk = nblk - 1 - (int)(blockIdx.x / a.B);  // heaviest first
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-    const int t_raw = blk * W + wave;
-    const bool live = t_raw < L;        // waves past the end only help stage keys
-    const int t = live ? t_raw : L - 1;
-    // A chunk of queries against the paged cache starts at position q0 and
-    // sees Lk keys; a whole sequence has q0 = 0 and Lk = L.
-    const int q0 = PAGED ? a.q0 : 0;
-    const int Lk = PAGED ? a.Lk : L;
-    const int tp = q0 + t;              // the token's position: its row sees keys 0 .. tp
-    if (short_rows_bypass(a, b, blk, W, L, q0, t_raw, live)) return;
-    const int lane = lane_id();
-    const int n = lane & 15, g = lane >> 4;
-
-    RowBuf<Pos> rb;
-    unsigned char* wbase = smem_raw + kStages * kStageBytes + wave * kStagedWaveBytes;
-    rb.key = reinterpret_cast<uint32_t*>(wbase);
-    rb.hist = reinterpret_cast<uint32_t*>(wbase + (size_t)(CAP + kWave) * 4);
-    rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)(CAP + kWave) * 4 + 128 * 4);
-
-    const size_t row_t = (size_t)b * L + t;
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * L * kD;
-    typename Op::template A<HB> Aq;
-    Op::template load_a<HB>(Aq, reinterpret_cast<const uint8_t*>(a.q) + row_t * H * kD, n, g);
-
-    // Head weights as the A operand of the f16 head-sum MFMA x (x < NX), in
-    // the contraction order k = 8g + j: head 32x + 4g + j for j < 4, head
-    // 32x + 16 + 4g + (j - 4) for j >= 4; subtile st uses rows 4st..4st+3.
-    constexpr int NX = (HB + 1) / 2;
-    v8h Wh[4][NX];
-    float Fscale;  // 2^-E
-    int sa[HB];    // E8M0 A scale of the score MFMAs, per lane: 127 - Pq of head 16hb + n (the lane's A row)
-    {
-        // Each head h gets its own exponent: 2^Pq_h >= |q_h|_1 (fp8 values).
-        // Lane (m, g) sums its 32 bytes of head 16hb + m; the four lane
-        // groups of a row add up, so every lane of row m holds |q_h|_1.
-        int pq[HB];
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            float sabs = 0.f;
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(Aq.a[hb][d], false);
-                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(Aq.a[hb][d], true);
-                sabs += (fabsf(lo[0]) + fabsf(lo[1])) + (fabsf(hi[0]) + fabsf(hi[1]));
-            }
-            sabs += __shfl_xor(sabs, 16, kWave);
-            sabs += __shfl_xor(sabs, 32, kWave);
-            pq[hb] = sabs > 0.f ? __builtin_amdgcn_frexp_expf(sabs) : 0;  // 2^Pq > |q_h|_1
-            sa[hb] = 127 - pq[hb];
-        }
-        // Head weights c_h = w q_scale / sqrt(D) for the lane's accumulator
-        // rows h = 16hb + 4g + i, times 2^Pq_h (the scale the score MFMA took
-        // out of head h), then all of them by one 2^E that puts the largest
-        // in f16's top binade.
-        float cf[HB][4];
-        float mx = 0.f;
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = 16 * hb + 4 * g + i;
-                const int pqh = __shfl(pq[hb], 4 * g + i, kWave);
-                cf[hb][i] = ldexpf(a.w[row_t * H + h] * a.q_scale[row_t * H + h] * a.inv_sqrt_d, pqh);
-                mx = fmaxf(mx, fabsf(cf[hb][i]));
-            }
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
-        int E = mx > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
-        E = E < -60 ? -60 : (E > 100 ? 100 : E);
-        Fscale = ldexpf(1.0f, -E);
-        // lane (m, g) of the weight operand: row m = n, contraction group g
-        const int own_st = n >> 2;
-#pragma unroll
-        for (int x = 0; x < NX; ++x) {
-            v8h wv;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int hb = 2 * x + (j >> 2);
-                wv[j] = hb < HB ? (_Float16)ldexpf(cf[hb < HB ? hb : 0][j & 3], E) : (_Float16)0.f;
-            }
-#pragma unroll
-            for (int st = 0; st < 4; ++st) Wh[st][x] = st == own_st ? wv : v8h{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-    }
-
-    const float* ksadj = a.ks_adj + (size_t)b * a.Lpad;
-    const uint8_t* kexp = a.kexp + (size_t)b * a.Lpad;
-    float* srow = (a.scores && live) ? a.scores + row_t * L : nullptr;
-    const int last = (q0 + min(blk * W + W - 1, L - 1)) / 64;   // same for every wave of the block
-
-    // Chunk order.  When the block spans at least 32 chunks, a strided sample
-    // (chunks 16i+15, i < S) is scored first; the rest follow in increasing
-    // order.  After the sample each long row sets a speculative floor: the
-    // lower edge of the radix bin holding the r-th largest sampled key, with
-    // r three and a half standard deviations above the expected number of
-    // sampled keys at or above the row's k-th largest.  Keys below the floor
-    // are never appended.  The floor is verified at the end: if fewer than k
-    // keys of the row cleared it, some of the top k may have been dropped and
-    // the row is scanned again without a floor.  Otherwise every dropped key
-    // lies below the k-th largest and the selection is exact.
-    const int S = last + 1 >= 32 ? (last + 1) / 16 : 0;
-    // Chunk of order index i from the chunk of index i-1 (scalar, no
-    // division): the sample 16i+15 for i < S, then 0, 1, ... skipping the
-    // sampled chunks; past the last index the last chunk again (the stage
-    // copies issued past the end re-read it).
-    auto chunk_next = [&](int i, int prev) -> int {
-        if (i > last) return prev;
-        if (i < S) return 16 * i + 15;
-        if (i == S) return 0;
-        int c = prev + 1;
-        if ((c & 15) == 15 && c < 16 * S) ++c;
-        return c;
-    };
-    const int chunk0 = S > 0 ? 15 : 0;
-
-    // Stage slot i % 3 receives the i-th chunk of the order: thread x of the
-    // block copies 16 key bytes (LDS slot x = row x/8, segment x%8 holds
-    // global segment (x%8) ^ ((row >> 1) & 7) of that row), wave 0 also copies
-    // the chunk's 64 adjusted key scales and wave 1 its 64 E8M0 bytes (lanes
-    // 16..63 repeat them into the unused tail).  Rows past the end are
-    // clamped to L-1; they only ever feed masked scores.
-    const int srow_i = threadIdx.x >> 3;
-    const int sseg = (threadIdx.x & 7) ^ ((srow_i >> 1) & 7);
-    auto stage_chunk = [&](int slot, int chunk) {
-        unsigned char* dst = smem_raw + slot * kStageBytes;
-        const int r = min(chunk * 64 + srow_i, Lk - 1);
-        // a 64-key chunk is one page of the paged cache
-        const uint8_t* src =
-            PAGED ? reinterpret_cast<const uint8_t*>(a.k) +
-                        ((size_t)a.block_table[(size_t)b * a.max_pages + (r >> 6)] * 64 + (r & 63)) * kD + 16 * sseg
-                  : kbase + (size_t)r * kD + 16 * sseg;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 1024 * wave),
-                                         16, 0, 0);
-        if (wave == 0)
-            __builtin_amdgcn_global_load_lds(ksadj + chunk * 64 + lane,
-                                             (__attribute__((address_space(3))) void*)(dst + kStageScaleOff),
-                                             4, 0, 0);
-        if (wave == 1)
-            __builtin_amdgcn_global_load_lds(kexp + chunk * 64 + 4 * (lane & 15),
-                                             (__attribute__((address_space(3))) void*)(dst + kStageExpOff),
-                                             4, 0, 0);
-    };
-    // Swizzled byte offset of (row r, 16-byte segment j) inside a stage.
-    // Rows r and r+1 share a swizzle value and lie in opposite bank halves,
-    // so the 16 rows one operand read touches use all 64 banks once.
-    auto soff = [](int r, int j) { return r * kD + 16 * (j ^ ((r >> 1) & 7)); };
-
-    const int K = a.topk;
-    int nb = 0;
-    uint32_t thr = 0u;
-    bool active = live;   // this wave scores and appends in the current pass
-    bool floored = false; // a speculative floor is in force
-    uint32_t r_spec = 0;  // rank of the floor in the sample (0: no floor)
-    if (live && S >= 2 && tp + 1 > 2 * K) {
-        const float ec = 64.f * (float)S * (float)K / (float)(tp + 1);
-        r_spec = spec_rank(ec);
-    }
-
-    // Pipeline.  The i-th chunk is copied three chunks ahead into the slot
-    // of chunk i-3 (free once every wave has read that chunk into registers)
-    // and waited for at the barrier in the middle of iteration i-1, so a copy
-    // has about two chunk-times to arrive.  Within a chunk the work runs at
-    // half-chunk (32-key) granularity: while the matrix cores multiply one
-    // half, the head sums of the previous one are formed.  Issue is in order
-    // within a wave and the waves of a SIMD run in step (one barrier per
-    // chunk), so the overlap has to come from within each wave: each region
-    // below is branch-free and interleaves its instructions step by step.
-    struct HalfAcc { v4f s[2][HB]; };
-    struct HalfB { v8i b[2]; };
-    auto load_b = [&](int slot, int half, HalfB& B_) {
-        const unsigned char* cur = smem_raw + slot * kStageBytes;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int r = 16 * (2 * half + q) + n;
-            const v4i lo = *reinterpret_cast<const v4i*>(cur + soff(r, 2 * g));
-            const v4i hi = *reinterpret_cast<const v4i*>(cur + soff(r, 2 * g + 1));
-            B_.b[q] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-    };
-    // Adjusted scale of key (i-th chunk)*64 + lane, and the E8M0 bytes of
-    // the lane's four subtile keys; read while the chunk's slot is still
-    // owned (before the barrier that lets chunk i+3 overwrite it).
-    auto load_ks = [&](int slot) {
-        return *reinterpret_cast<const float*>(smem_raw + slot * kStageBytes + kStageScaleOff + 4 * lane);
-    };
-    auto load_sb = [&](int slot) {
-        return *reinterpret_cast<const int*>(smem_raw + slot * kStageBytes + kStageExpOff + 4 * n);
-    };
-    // Score MFMA of subtile 2*MH + q (q in {0, 1}) and head block hb.
-    auto score_mma = [&](auto mh, int q, int hb, const HalfB& B_, int sb) -> v4f {
-        constexpr int s0 = 2 * decltype(mh)::value;
-        if (q == 0)
-            return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq.a[hb], B_.b[0], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                      0, 0, 0, sa[hb], s0, sb);
-        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq.a[hb], B_.b[1], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                  0, 0, 0, sa[hb], s0 + 1, sb);
-    };
-    // Conversion j2 (of 4) of the B operand of head MFMA x for subtile q of
-    // half A_: the pair of heads (hb = 2x + j2/2, i = 2(j2%2), +1) as f16,
-    // clamped to [0, 1].
-    auto cvt_pair = [&](const HalfAcc& A_, int q, int x, int j2) -> v2h {
-        const int hb = 2 * x + (j2 >> 1);
-        if (hb >= HB) return v2h{0, 0};
-        const v2f f = v2f{A_.s[q][hb][2 * (j2 & 1)], A_.s[q][hb][2 * (j2 & 1) + 1]};
-        const v2h r = __builtin_convertvector(f, v2h);
-        return __builtin_elementwise_min(__builtin_elementwise_max(r, v2h{0, 0}), v2h{1, 1});
-    };
-    // One region: the 2*HB score MFMAs of half MH (operands B_, results mm)
-    // and the head sums of half EH of the previous results ep (added to P),
-    // interleaved step by step.  Step k issues score MFMA k, then its share
-    // of the head-sum work (items: four conversions, then the head MFMA they
-    // feed), then extra(k).  The scheduling barrier after each step keeps
-    // the VALU and MFMA order as written; LDS, SALU and memory instructions
-    // may still move across.
-    auto region = [&](auto mh, auto eh, const HalfB& B_, int sb, HalfAcc& mm, const HalfAcc& ep, v4f& P,
-                      auto&& extra) {
-        constexpr int NM = 2 * HB;
-        constexpr int NI = 2 * NX * 5;
-        constexpr int st0 = 2 * decltype(eh)::value;
-        v8h X = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int k = 0; k < NM; ++k) {
-            mm.s[k / HB][k % HB] = score_mma(mh, k / HB, k % HB, B_, sb);
-#pragma unroll
-            for (int e = (k * NI) / NM; e < ((k + 1) * NI) / NM; ++e) {
-                const int qx = e / 5, it = e % 5;
-                const int qq = qx / NX, x = qx % NX;
-                if (it < 4) {
-                    const v2h r = cvt_pair(ep, qq, x, it);
-                    X[2 * it] = r[0];
-                    X[2 * it + 1] = r[1];
-                } else {
-                    P = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wh[st0 + qq][x], X, P, 0, 0, 0);
-                }
-            }
-            extra(k);
-            __builtin_amdgcn_sched_barrier(0x0094);  // SALU, VMEM and LDS may cross
-        }
-    };
-    // Head sums of half EH of A_ added to P, not interleaved (after the last chunk).
-    auto epi_half = [&](auto eh, const HalfAcc& A_, v4f P) {
-        constexpr int st0 = 2 * decltype(eh)::value;
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int x = 0; x < NX; ++x) {
-                v8h X;
-#pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const v2h r = cvt_pair(A_, q, x, it);
-                    X[2 * it] = r[0];
-                    X[2 * it + 1] = r[1];
-                }
-                P = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wh[st0 + q][x], X, P, 0, 0, 0);
-            }
-        return P;
-    };
-    // Keeps a half's MFMAs in the region that issues them (they would
-    // otherwise sink to the region that reads their results).
-    auto pin_half = [&](HalfAcc& A_) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) asm volatile("" : "+v"(A_.s[q][hb]));
-    };
-    // Appending the scores of the chunk whose head sums are complete, above
-    // the floor and in lane order, in five pieces spread over the steps of a
-    // region.  Branch free: lanes that do not append write a slot of their
-    // own past CAP.
-    struct FinState { float score; uint32_t key; int s; bool app; uint64_t m; int below; };
-    uint32_t thr_eff = 0u;  // thr while the wave appends, else 0xFFFFFFFF
-    auto finish_piece = [&](int piece, FinState& f, int chunk, const v4f& P, float ks) {
-        if (piece == 0) f.score = P[0] * (ks * Fscale);
-        if (piece == 1) f.key = score_key(f.score);
-        if (piece == 2) {
-            f.s = chunk * 64 + lane;
-            // bitwise, not short-circuit (a branch here would split the
-            // region); an inactive wave's threshold admits nothing
-            f.app = (f.s <= tp) & (f.key > thr_eff);
-        }
-        if (piece == 3) {
-            f.m = wave_ballot(f.app);
-            f.below = lanes_below(f.m);
-            asm volatile("" : "+v"(f.below));  // computed by every lane: keeps the select branch-free
-        }
-        if (piece == 4) {
-            const int o = f.app ? nb + f.below : CAP + lane;
-            rb.key[o] = f.key;
-            rb.pos[o] = (Pos)f.s;
-            nb += __builtin_popcountll(f.m);
-        }
-    };
-    // The rest of an append step: the optional score-matrix row and the
-    // compaction request (flag slot `fslot`) when the buffer nears capacity.
-    auto finish_tail = [&](int fslot, int chunk, float score) {
-        if (srow && active) {
-            const int s = chunk * 64 + lane;
-            if (s < Lk) srow[s] = s <= tp ? score : -INFINITY;
-        }
-        if (active && nb > CAP - 2 * kWave && lane == 0) flags[fslot] = 1u;
-    };
-
-    if (threadIdx.x == 0) flags[3] = 0u;
-    for (int pass = 0;; ++pass) {
-        HalfAcc hA, hB;
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) hB.s[q][hb] = v4f{0.f, 0.f, 0.f, 0.f};
-        HalfB bA, bB;
-        v4f Pacc = v4f{0.f, 0.f, 0.f, 0.f};  // head sums of the chunk in progress
-        float ks_prev = 0.f;
-        int chunk_prev = 0;  // chunk id of the previous iteration
-        if (threadIdx.x < 3) flags[threadIdx.x] = 0u;
-        // order indices 0..2 into slots 0..2; c_stage tracks index i+3
-        int c_stage = chunk0;
-        stage_chunk(0, c_stage);
-        c_stage = chunk_next(1, c_stage);
-        stage_chunk(1, c_stage);
-        c_stage = chunk_next(2, c_stage);
-        stage_chunk(2, c_stage);
-        // chunk 0 landed: at most this wave's copies of chunks 1 and 2 in
-        // flight (waves 0 and 1 issue two copies per chunk, the others one)
-        if (wave <= 1) __builtin_amdgcn_s_waitcnt(0x0F74);                // vmcnt(4)
-        else __builtin_amdgcn_s_waitcnt(0x0F72);                          // vmcnt(2)
-        __syncthreads();
-        load_b(0, 0, bA);
-        int sb_next = load_sb(0);
-        int chunk_cur = chunk0;  // chunk of order index i
-        // slots of order indices i, i+1, i+2 (mod 3)
-        int s0 = 0, s1 = 1, s2 = 2;
-        for (int i = 0; i <= last; ++i) {
-            const int sb_cur = sb_next;
-            // Region 1: first half of chunk i on the MFMA (operands read during
-            // the previous region 2), head sums of the second half of chunk
-            // i-1 (zeros before the first chunk); the second half's operands
-            // and the chunk's key scales are read here, before the barrier
-            // that releases the chunk's stage slot.
-            __builtin_amdgcn_sched_barrier(0);
-            load_b(s0, 1, bB);
-            const float ks_cur = load_ks(s0);
-            region(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, bA, sb_cur, hA, hB, Pacc,
-                   [](int) {});
-            // keep this epilogue here (it would otherwise sink into a branch below)
-            asm volatile("" : "+v"(Pacc));
-            pin_half(hA);
-            __builtin_amdgcn_sched_barrier(0);
-            // This wave's copies of chunk i+1 have landed once at most its
-            // copies of chunk i+2 are in flight (loads complete in issue
-            // order); the barrier then makes every wave's copies visible and
-            // certifies that every wave is done reading chunk i's slot.  With
-            // the score matrix requested, the row's stores share the counter:
-            // wait for all.
-            if (a.scores) __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
-            else if (wave <= 1) __builtin_amdgcn_s_waitcnt(0x0F72);       // vmcnt(2)
-            else __builtin_amdgcn_s_waitcnt(0x0F71);                      // vmcnt(1)
-            __syncthreads();
-            // Compaction request of the appends of chunk i-2 (made at the end
-            // of iteration i-1; slot (i-2) % 3 = s1), read now and acted on
-            // after region 2, so the read's latency hides under the MFMAs.
-            // Slot j % 3 belongs to the appends of the j-th chunk: set at the
-            // end of iteration j+1, read in j+2, cleared in j+3 (each step
-            // separated by a barrier).
-            const uint32_t flag_word = flags[s1];
-            if (threadIdx.x == 0 && i >= 3) flags[s0] = 0u;
-            // Chunk i+3 goes to chunk i's slot.  Past the last chunk the copy
-            // is a clamped dummy, so every chunk issues the same loads.
-            c_stage = chunk_next(i + 3, c_stage);
-            stage_chunk(s0, c_stage);
-            // Region 2: second half of chunk i on the MFMA, head sums of its
-            // first half, the appends of chunk i-1 (discarded before the first
-            // chunk: nothing is valid yet) and the first-half operands of
-            // chunk i+1 (landed, per the barrier above).
-            const v4f Pfin = Pacc;
-            const bool fin_on = i >= 1;
-            const bool was_active = active;
-            active = active && fin_on;
-            thr_eff = active ? thr : 0xFFFFFFFFu;
-            FinState fs;
-            const int nb0 = nb;
-            __builtin_amdgcn_sched_barrier(0);
-            load_b(s1, 0, bA);
-            sb_next = load_sb(s1);
-            Pacc = v4f{0.f, 0.f, 0.f, 0.f};
-            region(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, bB, sb_cur, hB, hA, Pacc,
-                   [&](int k) {
-#pragma unroll
-                       for (int p = 0; p < 5; ++p)
-                           if ((p < 2 * HB - 1 ? p : 2 * HB - 1) == k) finish_piece(p, fs, chunk_prev, Pfin, ks_prev);
-                   });
-            asm volatile("" : "+v"(Pacc), "+v"(fs.score));
-            pin_half(hB);
-            __builtin_amdgcn_sched_barrier(0);
-            active = was_active;
-            if (!fin_on) nb = nb0;
-            // Buffer maintenance after the appends of chunk i-1.  The sample's
-            // appends (chunks 0..S-1 of the order) end in iteration S: the
-            // speculative floor is set before any other append.  Then the
-            // cooperative compaction: a request from any wave makes every
-            // wave compact, so the block pays one stall per event.
-            if (i == S && r_spec != 0u && active && (uint32_t)nb > r_spec) {
-                uint32_t fl;
-                nb = wave_floor(rb, nb, r_spec, &fl);
-                thr = fl == 0u ? 0u : fl - 1u;
-                floored = true;
-            }
-            if (i >= 2 && flag_word != 0u && active && nb > K) nb = wave_compact(rb, nb, (uint32_t)K, &thr, CAP);
-            if (fin_on) finish_tail(s2, chunk_prev, fs.score);
-            ks_prev = ks_cur;
-            chunk_prev = chunk_cur;
-            chunk_cur = chunk_next(i + 1, chunk_cur);
-            const int sx = s0;
-            s0 = s1; s1 = s2; s2 = sx;
-        }
-        Pacc = epi_half(std::integral_constant<int, 1>{}, hB, Pacc);
-        {
-            FinState fs;
-            thr_eff = active ? thr : 0xFFFFFFFFu;
-#pragma unroll
-            for (int p = 0; p < 5; ++p) finish_piece(p, fs, chunk_prev, Pacc, ks_prev);
-            finish_tail(s2, chunk_prev, fs.score);  // no compaction follows: the flag is cleared at the next pass
-        }
-        __builtin_amdgcn_s_waitcnt(0x0000);  // no stage copy or LDS read may still be in flight
-        if (pass == 1) break;
-        // Verification of the floor (see above); any failing row makes the
-        // whole block scan again, with only the failing waves appending.
-        const bool redo = active && floored && nb < K;
-        if (redo && lane == 0) flags[3] = 1u;
-        __syncthreads();
-        if (flags[3] == 0u) break;
-        active = redo;
-        if (redo) {
-            nb = 0;
-            thr = 0u;
-            floored = false;
-        }
-        r_spec = 0u;
-    }
-    if (!live) return;
-    if (srow) {
-        for (int s = (last + 1) * 64 + lane; s < Lk; s += kWave) srow[s] = -INFINITY;
-    }
-    __builtin_amdgcn_wave_barrier();
-    wave_emit(rb, nb, K, a.idx_out + row_t * K, a.val_out ? a.val_out + row_t * K : nullptr);
-}
 
 // ---------------------------------------------------------------------------
-// bf16, L <= 65536: keys staged through LDS, head sums on the matrix cores.
+// bf16 queries, keys staged through LDS, head sums on the matrix cores: whole
+// sequences of bf16 keys (L <= 65536), and chunks of bf16 queries against
+// the paged fp8 key cache (variable length, positions up to 131072).
 //
-// The scheme of the fp8 kernel above, with what bf16 changes:
-// * A key pre-pass writes every key times 2^-Pk (exact: a power of two) to
-//   the workspace, with 2^Pk as its adjusted scale, and each query head's A
-//   rows are scaled by its own 2^-Pq_h in registers (2^Pq_h goes into the
-//   head's weight).  So again every S_h lies in [-1, 1], the clamped f16
-//   conversion is the ReLU and the head sum is an f16 MFMA.
+// The 8 waves of a workgroup (8 consecutive query rows of one sequence, all
+// with the same last 64-key chunk) walk the key chunks in lockstep: every
+// chunk is fetched from L2 once per workgroup with direct global->LDS loads
+// (no VGPRs in flight), rows stored with their 16-byte pieces XOR-swizzled
+// so the MFMA operand reads spread over the LDS banks.
+//
+// Epilogue.  The score of key s is sum_h c_h max(S_h, 0) times the key's
+// scale (1 for bf16 keys), with c_h = w_h / sqrt(D) and S_h the dot product
+// of the stored values.  |S_h| <= |q_h|_1 * max_d |k_d| <= 2^Pq_h * 2^Pk,
+// with Pq_h taken per head of the token and Pk per key.  A key pre-pass
+// writes every key times 2^-Pk to the workspace as bf16 (exact: a power of
+// two), with the key's scale times 2^Pk as its adjusted scale; fp8 keys of
+// the paged cache are widened to bf16 there (exact: every E4M3 value is a
+// bf16 value).  Each query head's A rows are scaled by its own 2^-Pq_h in
+// registers.  So the score MFMAs (bf16 x bf16 16x16x32 into fp32, four
+// k-steps per 16 heads x 16 keys) leave every value in [-1, 1] at its own
+// head's scale.  There the conversion to f16 with its [0, 1] clamp is
+// max(S, 0) itself, rounded to nearest (relative error <= 2^-11 down to
+// 2^-14 of the head's bound, however far the heads' magnitudes spread), and
+// the weighted sum over heads is one more MFMA (f16, 16x16x32) with the
+// weights c_h * 2^Pq_h * 2^E as its A operand.  Its weights for subtile st
+// sit in the rows 4st..4st+3 only, so the four subtiles of a chunk
+// accumulate into one tile whose element 0 in lane l is the score of key
+// 64*chunk + l: no cross-lane reduction.  The factor 2^-E and the adjusted
+// key scale finish the score.
+//
+// Pipeline:
 // * A 64-key chunk is 16 KB.  Two stages fit the LDS beside the eight rows'
 //   2560-entry candidate buffers.  One barrier per chunk, at its end: it
 //   certifies that the next chunk has landed and that every wave is done
@@ -978,6 +401,7 @@ static_assert(kBfStages * kBfStageBytes + kBfWaves * kBfWaveBytes + 16 <= 160 * 
 // a zero row), the key times 2^-Pk to kscaled and 2^Pk to ks_adj.
 __global__ void __launch_bounds__(256)
 prefill_key_prep_bf16_kernel(PrefillArgs a, uint16_t* kscaled) {
+    static_assert(kBfWaves == kBlockRows, "one query row per wave");
     const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int Lp = a.Lpad;
     if (gi >= (int64_t)a.B * Lp) return;
@@ -1013,7 +437,58 @@ prefill_key_prep_bf16_kernel(PrefillArgs a, uint16_t* kscaled) {
     }
 }
 
-template <int HB>
+// The same pre-pass for chunks against the paged fp8 cache: key s < pad64(Lk)
+// of sequence b (rows past the end repeat key Lk-1) is read from its cache
+// slot, widened to bf16 and scaled by 2^-Pk (both exact), and its adjusted
+// scale is k_scale * 2^Pk.
+__global__ void __launch_bounds__(256)
+prefill_key_prep_paged_fp8_kernel(PrefillArgs a, uint16_t* kscaled) {
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int Lp = a.Lpad;
+    if (gi >= (int64_t)a.B * Lp) return;
+    const int b = (int)(gi / Lp), s = (int)(gi % Lp);
+    const int Lq = a.cu_q[b + 1] - a.cu_q[b];
+    const int Lk = min(max(a.q_start[b], 0) + Lq, a.max_kv);
+    if (Lq <= 0 || Lk <= 0 || s >= pad64(Lk)) return;
+    const size_t slot = key_slot<true>(a, b, s < Lk ? s : Lk - 1);
+    const v4i* row = reinterpret_cast<const v4i*>(reinterpret_cast<const uint8_t*>(a.k) + slot * kD);
+    v4i v[kD / 16];
+    uint32_t mx = 0;
+#pragma unroll
+    for (int c = 0; c < kD / 16; ++c) {
+        v[c] = row[c];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t x = (uint32_t)v[c][d] & 0x7F7F7F7Fu;  // magnitudes: e4m3 orders like its bits
+            mx = max(mx, max(max(x & 0xFFu, (x >> 8) & 0xFFu), max((x >> 16) & 0xFFu, x >> 24)));
+        }
+    }
+    const float vmax = __builtin_amdgcn_cvt_f32_fp8((int)mx, 0);
+    const int pk = vmax > 0.f ? __builtin_amdgcn_frexp_expf(vmax) : 0;  // 2^pk > vmax
+    a.ks_adj[gi] = ldexpf(a.k_scale[slot], pk);
+    v4i* dst = reinterpret_cast<v4i*>(kscaled + (size_t)gi * kD);
+#pragma unroll
+    for (int c = 0; c < kD / 16; ++c) {
+        v4i o[2];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(v[c][d], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(v[c][d], true);
+            // at most 4 significant bits, scaled by a power of two: the top
+            // 16 bits of the fp32 pattern are the exact bf16 value
+            const uint32_t b0 = __float_as_uint(ldexpf(lo[0], -pk)) >> 16;
+            const uint32_t b1 = __float_as_uint(ldexpf(lo[1], -pk)) >> 16;
+            const uint32_t b2 = __float_as_uint(ldexpf(hi[0], -pk)) >> 16;
+            const uint32_t b3 = __float_as_uint(ldexpf(hi[1], -pk)) >> 16;
+            o[d >> 1][2 * (d & 1)] = (int)(b0 | (b1 << 16));
+            o[d >> 1][2 * (d & 1) + 1] = (int)(b2 | (b3 << 16));
+        }
+        dst[2 * c] = o[0];
+        dst[2 * c + 1] = o[1];
+    }
+}
+
+template <int HB, bool VARLEN, bool P17>
 __global__ void __launch_bounds__(kBfWaves * kWave)
 prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -1023,15 +498,26 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     constexpr int CAP = kBfCap;
     constexpr int H = 16 * HB;
     constexpr int NX = (HB + 1) / 2;
-    const int L = a.L;
-    const int nblk = (L + W - 1) / W;
-    const int b = blockIdx.x % a.B;
-    const int blk = nblk - 1 - (int)(blockIdx.x / a.B);  // heaviest first
+    Seg sg;
+    if (!block_seg<VARLEN>(a, sg)) return;
+    const int b = sg.b, blk = sg.blk;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-    const int t_raw = blk * W + wave;
-    const bool live = t_raw < L;        // waves past the end only help stage keys
-    const int t = live ? t_raw : L - 1;
-    if (short_rows_bypass(a, b, blk, W, L, 0, t_raw, live)) return;
+    const int tl_raw = blk * W + wave;  // the wave's row within the sequence's rows
+    const bool live = tl_raw < sg.Lq;   // waves past the end only help stage keys
+    const int tl = live ? tl_raw : sg.Lq - 1;
+    const int t = sg.q0 + tl;           // its position
+    const int tv = min(t, sg.Lk - 1);   // its last valid key
+    const int last_row = min(blk * W + W - 1, sg.Lq - 1);
+    // Short rows, no scores asked for: a row with at most k valid positions
+    // selects all of them, so a block whose rows all qualify writes
+    // positions 0 .. t, then -1, without scoring.
+    if (!a.val_out && !a.scores && sg.q0 + last_row + 1 <= a.topk) {
+        if (live) {
+            int32_t* out = a.idx_out + (size_t)(sg.row0 + tl_raw) * a.topk;
+            for (int j = lane_id(); j < a.topk; j += kWave) out[j] = j <= tv ? j : -1;
+        }
+        return;
+    }
     const int lane = lane_id();
     const int n = lane & 15, g = lane >> 4;
 
@@ -1041,7 +527,7 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     rb.hist = reinterpret_cast<uint32_t*>(wbase + (size_t)(CAP + kWave) * 4);
     rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)(CAP + kWave) * 4 + 128 * 4);
 
-    const size_t row_t = (size_t)b * L + t;
+    const size_t row_t = (size_t)sg.row0 + tl;
     // Query: lane (m, g) holds, for k-step j, q[t][16hb+m][32g+8j .. +8].
     // Each head h gets its own exponent, 2^Pq_h >= |q_h|_1, its operand rows
     // are scaled by 2^-Pq_h (exact) and 2^Pq_h moves into its weight: every
@@ -1117,8 +603,10 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
 
     const uint16_t* kbase = kscaled + (size_t)b * a.Lpad * kD;
     const float* ksadj = a.ks_adj + (size_t)b * a.Lpad;
-    float* srow = (a.scores && live) ? a.scores + row_t * L : nullptr;
-    const int last = (min(blk * W + W - 1, L - 1)) / 64;   // same for every wave of the block
+    const int Lk = sg.Lk;
+    float* srow = (!VARLEN && a.scores && live) ? a.scores + row_t * Lk : nullptr;
+    // the block's last chunk, the same for every wave of it
+    const int last = min((sg.q0 + last_row) / 64, (Lk - 1) / 64);
 
     // Chunk order, sample and speculative floor: as in the fp8 kernel.
     const int S = last + 1 >= 32 ? (last + 1) / 16 : 0;
@@ -1213,17 +701,17 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     bool active = live;
     bool floored = false;
     uint32_t r_spec = 0;
-    if (live && S >= 2 && t + 1 > 2 * K) {
-        const float ec = 64.f * (float)S * (float)K / (float)(t + 1);
+    if (live && S >= 2 && tv + 1 > 2 * K) {
+        const float ec = 64.f * (float)S * (float)K / (float)(tv + 1);
         r_spec = spec_rank(ec);
     }
     auto finish_piece = [&](int piece, FinState& f, int chunk, const v4f& P, float ks) {
         if (piece == 0) f.score = P[0] * (ks * Fscale);
-        if (piece == 1) f.key = score_key(f.score);
-        if (piece == 2) {
+        if (piece == 1) {
             f.s = chunk * 64 + lane;
-            f.app = (f.s <= t) & (f.key > thr_eff);
+            f.key = entry_word<P17>(f.score, (uint32_t)f.s);
         }
+        if (piece == 2) f.app = (f.s <= tv) & (f.key > thr_eff);
         if (piece == 3) {
             f.m = wave_ballot(f.app);
             f.below = lanes_below(f.m);
@@ -1239,7 +727,7 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     auto finish_tail = [&](int fslot, int chunk, float score) {
         if (srow && active) {
             const int s = chunk * 64 + lane;
-            if (s < L) srow[s] = s <= t ? score : -INFINITY;
+            if (s < Lk) srow[s] = s <= t ? score : -INFINITY;
         }
         if (active && nb > CAP - kWave && lane == 0) flags[fslot] = 1u;
     };
@@ -1384,44 +872,13 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     }
     if (!live) return;
     if (srow) {
-        for (int s = (last + 1) * 64 + lane; s < L; s += kWave) srow[s] = -INFINITY;
+        for (int s = (last + 1) * 64 + lane; s < Lk; s += kWave) srow[s] = -INFINITY;
     }
     __builtin_amdgcn_wave_barrier();
-    wave_emit(rb, nb, K, a.idx_out + row_t * K, a.val_out ? a.val_out + row_t * K : nullptr);
+    wave_emit<Pos, P17>(rb, nb, K, a.idx_out + row_t * K, a.val_out ? a.val_out + row_t * K : nullptr);
 }
 
-constexpr bool staged_path(int dtype, int L) { return DSAIDX_PREFILL_STAGED && dtype == 2 && L <= 65536; }
 constexpr bool staged_bf16_path(int dtype, int L) { return DSAIDX_PREFILL_STAGED_BF16 && dtype == 1 && L <= 65536; }
-constexpr int pad64(int L) { return (L + 63) / 64 * 64; }
-
-template <int HB, bool PAGED = false>
-hipError_t launch_fp8_staged(const PrefillArgs& a_in, hipStream_t stream) {
-    PrefillArgs a = a_in;
-    if (!PAGED) {
-        a.q0 = 0;
-        a.Lk = a.L;
-    }
-    a.Lpad = pad64(a.Lk);
-    a.ks_adj = reinterpret_cast<float*>(a.workspace);
-    a.kexp = reinterpret_cast<uint8_t*>(a.ks_adj + (size_t)a.B * a.Lpad);
-    {
-        const int64_t n = (int64_t)a.B * a.Lpad;
-        hipLaunchKernelGGL(prefill_key_exp_kernel<PAGED>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                           a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    const size_t smem = kStagedLds;
-    static PerDevice<int> lds_once;
-    {
-        hipError_t e = set_lds_limit(lds_once, (const void*)prefill_fused_fp8_staged_kernel<HB, PAGED>, (int)smem);
-        if (e != hipSuccess) return e;
-    }
-    const int nblk = (a.L + kStagedWaves - 1) / kStagedWaves;
-    hipLaunchKernelGGL((prefill_fused_fp8_staged_kernel<HB, PAGED>), dim3((unsigned)(nblk * a.B)),
-                       dim3(kStagedWaves * kWave), smem, stream, a);
-    return hipGetLastError();
-}
 
 template <int HB>
 hipError_t launch_bf16_staged(const PrefillArgs& a_in, hipStream_t stream) {
@@ -1439,58 +896,86 @@ hipError_t launch_bf16_staged(const PrefillArgs& a_in, hipStream_t stream) {
     const size_t smem = kBfStages * kBfStageBytes + (size_t)kBfWaves * kBfWaveBytes;
     static PerDevice<int> lds_once;
     {
-        hipError_t e = set_lds_limit(lds_once, (const void*)prefill_fused_bf16_staged_kernel<HB>, (int)smem);
+        hipError_t e = set_lds_limit(lds_once, (const void*)prefill_fused_bf16_staged_kernel<HB, false, false>,
+                                     (int)smem);
         if (e != hipSuccess) return e;
     }
     const int nblk = (a.L + kBfWaves - 1) / kBfWaves;
-    hipLaunchKernelGGL((prefill_fused_bf16_staged_kernel<HB>), dim3((unsigned)(nblk * a.B)), dim3(kBfWaves * kWave),
-                       smem, stream, a, (const uint16_t*)kscaled);
+    hipLaunchKernelGGL((prefill_fused_bf16_staged_kernel<HB, false, false>), dim3((unsigned)(nblk * a.B)),
+                       dim3(kBfWaves * kWave), smem, stream, a, (const uint16_t*)kscaled);
     return hipGetLastError();
 }
 
-template <int DT, int HB>
-hipError_t launch_pos(const PrefillArgs& a, hipStream_t stream) {
-    if (staged_path(DT, a.L)) return launch_fp8_staged<HB>(a, stream);
-    if (staged_bf16_path(DT, a.L)) return launch_bf16_staged<HB>(a, stream);
-    return a.L <= 65536 ? launch_one<DT, HB, true>(a, stream) : launch_one<DT, HB, false>(a, stream);
+// Workspace of a bf16 chunk call: adjusted scales [B][pad64(max_kv)] fp32,
+// scaled bf16 keys [B][pad64(max_kv)][128], the block plan.
+size_t bf16_varlen_scaled_off(int B, int max_kv) { return (size_t)B * pad64(max_kv) * 4; }
+size_t bf16_varlen_plan_off(int B, int max_kv) { return (size_t)B * pad64(max_kv) * (4 + 2 * kD); }
+
+template <int HB, bool P17>
+hipError_t launch_bf16_varlen(const PrefillArgs& a_in, hipStream_t stream) {
+    PrefillArgs a = a_in;
+    a.Lpad = pad64(a.max_kv);
+    a.ks_adj = reinterpret_cast<float*>(a.workspace);
+    uint16_t* kscaled = reinterpret_cast<uint16_t*>(static_cast<char*>(a.workspace) +
+                                                    bf16_varlen_scaled_off(a.B, a.max_kv));
+    a.n_plan = (a.T + kBlockRows - 1) / kBlockRows + a.B;
+    a.plan = reinterpret_cast<int2*>(static_cast<char*>(a.workspace) + bf16_varlen_plan_off(a.B, a.max_kv));
+    hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)a.B * a.Lpad;
+    hipLaunchKernelGGL(prefill_key_prep_paged_fp8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a,
+                       kscaled);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t smem = kBfStages * kBfStageBytes + (size_t)kBfWaves * kBfWaveBytes;
+    static PerDevice<int> lds_once;
+    if ((e = set_lds_limit(lds_once, (const void*)prefill_fused_bf16_staged_kernel<HB, true, P17>, (int)smem)) !=
+        hipSuccess)
+        return e;
+    hipLaunchKernelGGL((prefill_fused_bf16_staged_kernel<HB, true, P17>), dim3((unsigned)a.n_plan),
+                       dim3(kBfWaves * kWave), smem, stream, a, (const uint16_t*)kscaled);
+    return hipGetLastError();
+}
+
+template <int HB>
+hipError_t launch_bf16(const PrefillArgs& a, hipStream_t stream) {
+    if (staged_bf16_path(1, a.L)) return launch_bf16_staged<HB>(a, stream);
+    return a.L <= 65536 ? launch_one<1, HB, true>(a, stream) : launch_one<1, HB, false>(a, stream);
 }
 
 }  // namespace
 
 size_t prefill_fused_workspace_bytes(int B, int L, int dtype) {
     const size_t n = (size_t)B * pad64(L);
-    if (DSAIDX_PREFILL_WS && dtype == 2) return prefill_ws_workspace_bytes(B, L, 0);
-    if (staged_path(dtype, L)) return (n * 5 + 255) / 256 * 256;  // fp32 adjusted scales, then the E8M0 bytes
+    if (dtype == 2) return prefill_ws_workspace_bytes(B, L, 0);
     if (staged_bf16_path(dtype, L)) return n * (4 + 2 * kD);      // fp32 adjusted scales, then the scaled keys
     return 0;
 }
 
-hipError_t launch_prefill_chunk_paged(const PrefillArgs& a, hipStream_t stream) {
+size_t prefill_bf16_varlen_workspace_bytes(int B, int T, int max_kv) {
+    const size_t n_plan = (size_t)(T + kBlockRows - 1) / kBlockRows + B;
+    return bf16_varlen_plan_off(B, max_kv) + n_plan * sizeof(int2);
+}
+
+hipError_t launch_prefill_bf16_varlen(const PrefillArgs& a, hipStream_t stream) {
+    const bool p17 = a.max_kv > 65536;
     switch (a.H / 16) {
-        case 1: return launch_fp8_staged<1, true>(a, stream);
-        case 2: return launch_fp8_staged<2, true>(a, stream);
-        case 3: return launch_fp8_staged<3, true>(a, stream);
-        case 4: return launch_fp8_staged<4, true>(a, stream);
+        case 1: return p17 ? launch_bf16_varlen<1, true>(a, stream) : launch_bf16_varlen<1, false>(a, stream);
+        case 2: return p17 ? launch_bf16_varlen<2, true>(a, stream) : launch_bf16_varlen<2, false>(a, stream);
+        case 3: return p17 ? launch_bf16_varlen<3, true>(a, stream) : launch_bf16_varlen<3, false>(a, stream);
+        case 4: return p17 ? launch_bf16_varlen<4, true>(a, stream) : launch_bf16_varlen<4, false>(a, stream);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_fused(const PrefillArgs& a, int dtype, hipStream_t stream) {
-    const int hb = a.H / 16;
-    if (DSAIDX_PREFILL_WS && dtype == 2) return launch_prefill_ws(a, stream);
-    if (dtype == 2) {
-        switch (hb) {
-            case 1: return launch_pos<2, 1>(a, stream);
-            case 2: return launch_pos<2, 2>(a, stream);
-            case 3: return launch_pos<2, 3>(a, stream);
-            case 4: return launch_pos<2, 4>(a, stream);
-        }
-    } else if (dtype == 1) {
-        switch (hb) {
-            case 1: return launch_pos<1, 1>(a, stream);
-            case 2: return launch_pos<1, 2>(a, stream);
-            case 3: return launch_pos<1, 3>(a, stream);
-            case 4: return launch_pos<1, 4>(a, stream);
+    if (dtype == 2) return launch_prefill_ws(a, stream);  // fp8: the kernel with specialised waves
+    if (dtype == 1) {
+        switch (a.H / 16) {
+            case 1: return launch_bf16<1>(a, stream);
+            case 2: return launch_bf16<2>(a, stream);
+            case 3: return launch_bf16<3>(a, stream);
+            case 4: return launch_bf16<4>(a, stream);
         }
     }
     return hipErrorInvalidValue;

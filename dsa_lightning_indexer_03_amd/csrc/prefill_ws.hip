@@ -52,6 +52,7 @@
 #include "device_once.h"
 #include "kernels.h"
 #include "rowbuf.h"
+#include "varlen.h"
 
 namespace dsaidx {
 
@@ -59,7 +60,7 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kWsWaves = 8;    // 4 matrix waves + 4 selection waves
-constexpr int kWsRows = 8;     // query rows per workgroup
+constexpr int kWsRows = kBlockRows;  // query rows per workgroup
 // Candidates per row: the most that fit beside three key stages and the
 // score ring.
 constexpr int kWsCap = 2624;
@@ -106,49 +107,6 @@ __device__ __forceinline__ uint32_t spec_rank(float ec) {
     return (uint32_t)ceilf(ec + 3.5f * sqrtf(ec) + 8.f);
 }
 
-// The rows a workgroup owns.
-struct Seg {
-    int b;     // sequence
-    int blk;   // 8-row block within the sequence
-    int row0;  // global row of the sequence's first query
-    int Lq;    // query rows of the sequence
-    int q0;    // position of its first query
-    int Lk;    // keys it sees (its last query's position + 1)
-};
-
-template <bool VARLEN>
-__device__ __forceinline__ bool block_seg(const PrefillArgs& a, Seg& s) {
-    if constexpr (VARLEN) {
-        const int2 e = a.plan[blockIdx.x];
-        s.b = uniform(e.x);
-        if (s.b < 0) return false;
-        s.blk = uniform(e.y);
-        s.row0 = uniform(a.cu_q[s.b]);
-        s.Lq = uniform(a.cu_q[s.b + 1]) - s.row0;
-        s.q0 = max(uniform(a.q_start[s.b]), 0);
-        s.Lk = min(s.q0 + s.Lq, a.max_kv);
-        return s.Lq > 0 && s.Lk > 0;
-    } else {
-        const int nblk = (a.L + kWsRows - 1) / kWsRows;
-        s.b = (int)(blockIdx.x % (unsigned)a.B);
-        s.blk = nblk - 1 - (int)(blockIdx.x / (unsigned)a.B);  // heaviest first
-        s.row0 = s.b * a.L;
-        s.Lq = a.L;
-        s.q0 = 0;
-        s.Lk = a.L;
-        return true;
-    }
-}
-
-// Storage slot (row of k / k_cache) of key r < Lk of sequence b.
-template <bool VARLEN>
-__device__ __forceinline__ size_t key_slot(const PrefillArgs& a, int b, int r) {
-    if constexpr (VARLEN)
-        return (size_t)a.block_table[(size_t)b * a.max_pages + (r >> 6)] * 64 + (r & 63);
-    else
-        return (size_t)b * a.L + r;
-}
-
 // Key pre-pass, one thread per key s < pad64(Lk) of sequence b (rows past
 // the end repeat key Lk-1, as the stage copies do): 2^Pk > max_d |k_d| (Pk = 0
 // for a zero row), ks_adj = k_scale * 2^Pk and the E8M0 byte 127 - Pk at
@@ -187,56 +145,6 @@ ws_key_prep_kernel(PrefillArgs a) {
     a.ks_adj[gi] = ldexpf(a.k_scale[slot], pk);
     const int c = s / 64, n = s % 16, q = (s % 64) / 16;
     a.kexp[(size_t)b * Lp + 64 * c + 4 * n + q] = (uint8_t)(127 - pk);
-}
-
-// Block plan of a variable-length call: every 8-row block (sequence b, block
-// j) of every sequence, ordered by the number of key chunks it scans,
-// largest first (a counting sort over the 2048 possible chunk counts), then
-// (-1, 0) up to n_plan.  One workgroup.
-__global__ void __launch_bounds__(1024)
-ws_plan_kernel(PrefillArgs a) {
-    __shared__ uint32_t cnt[2048];
-    __shared__ uint32_t wtot[16];
-    __shared__ uint32_t total;
-    const int t = threadIdx.x;
-    for (int i = t; i < 2048; i += 1024) cnt[i] = 0u;
-    __syncthreads();
-    // bucket = the block's last chunk (its last row's position, clamped to the keys)
-    auto for_each_block = [&](auto&& f) {
-        for (int b = 0; b < a.B; ++b) {
-            const int r0 = a.cu_q[b];
-            const int Lq = a.cu_q[b + 1] - r0;
-            if (Lq <= 0) continue;
-            const int q0 = max(a.q_start[b], 0);
-            const int Lk = min(q0 + Lq, a.max_kv);
-            if (Lk <= 0) continue;
-            const int nbk = (Lq + kWsRows - 1) / kWsRows;
-            for (int j = t; j < nbk; j += 1024) {
-                const int lr = min(kWsRows * j + kWsRows - 1, Lq - 1);
-                const int w = min(min(q0 + lr, Lk - 1) >> 6, 2047);
-                f(b, j, w);
-            }
-        }
-    };
-    for_each_block([&](int, int, int w) { atomicAdd(&cnt[w], 1u); });
-    __syncthreads();
-    // thread t owns buckets 2047 - 2t and 2046 - 2t: start offsets from the top
-    const uint32_t c0 = cnt[2047 - 2 * t], c1 = cnt[2046 - 2 * t];
-    const uint32_t incl = wave_incl_scan(c0 + c1);
-    if (lane_id() == kWave - 1) wtot[t / kWave] = incl;
-    __syncthreads();
-    uint32_t base = incl - (c0 + c1);
-    for (int w = 0; w < t / kWave; ++w) base += wtot[w];
-    if (t == 1023) total = base + c0 + c1;
-    __syncthreads();
-    cnt[2047 - 2 * t] = base;
-    cnt[2046 - 2 * t] = base + c0;
-    __syncthreads();
-    for_each_block([&](int b, int j, int w) {
-        const uint32_t p = atomicAdd(&cnt[w], 1u);
-        if (p < (uint32_t)a.n_plan) a.plan[p] = make_int2(b, j);
-    });
-    for (uint32_t p = total + (uint32_t)t; p < (uint32_t)a.n_plan; p += 1024u) a.plan[p] = make_int2(-1, 0);
 }
 
 template <int HB, bool VARLEN, bool P17, bool ROWS>
@@ -840,7 +748,7 @@ hipError_t launch_prefill_ws_varlen(const PrefillArgs& a_in, hipStream_t stream)
     a.kexp = reinterpret_cast<uint8_t*>(a.ks_adj + (size_t)a.B * a.Lpad);
     a.n_plan = (a.T + kWsRows - 1) / kWsRows + a.B;
     a.plan = reinterpret_cast<int2*>(reinterpret_cast<char*>(a.workspace) + scales_bytes(a.B, a.max_kv));
-    hipLaunchKernelGGL(ws_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nk = (int64_t)a.B * a.Lpad;

@@ -198,9 +198,11 @@ size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, i
  * is position p = q_start[b] + i of sequence b and sees the p + 1 positions
  * 0 .. p: its result equals indexer_prefill's row p over the whole sequence.
  *
- *   q            [T][H][D] FP8 E4M3 codes, the sequences' chunks packed one
- *                after another (q_dtype must be DSAIDX_FP8_E4M3);
- *                q_scale [T][H] fp32; w [T][H] fp32
+ *   q            [T][H][D], the sequences' chunks packed one after another:
+ *                FP8 E4M3 codes with q_scale [T][H] fp32 (q_dtype
+ *                DSAIDX_FP8_E4M3), or bf16 with q_scale NULL (q_dtype
+ *                DSAIDX_BF16; scored against the cache's fp8 keys widened
+ *                exactly to bf16);  w [T][H] fp32
  *   cu_seqlens_q [B+1] int32 (device): sequence b's rows are
  *                cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1; cu_seqlens_q[0] = 0,
  *                nondecreasing, cu_seqlens_q[B] = T (a sequence may have none)
@@ -217,10 +219,11 @@ size_t indexer_decode_paged_workspace_bytes(int B, int max_context_len, int H, i
  *   topk_idx     out [T][topk] int32 (absolute positions, -1 padded);
  *   topk_score   out [T][topk] fp32 or NULL
  *   workspace    indexer_prefill_chunk_paged_workspace_bytes(B, T,
- *                max_kv_len) bytes of caller-owned device memory, 16-byte
- *                aligned: 5 bytes per key up to max_kv_len (64-padded) per
- *                sequence, 256-byte rounded, then 8 bytes per 8-row block
- *                (the launch plan)
+ *                max_kv_len, q_dtype) bytes of caller-owned device memory,
+ *                16-byte aligned: per key up to max_kv_len (64-padded) per
+ *                sequence 5 bytes for fp8 queries (256-byte rounded) or 260
+ *                bytes for bf16 queries (the keys widened to bf16), then 8
+ *                bytes per 8-row block (the launch plan)
  *
  * Supported: H a multiple of 16 in [16, 64], D = 128, page_size = 64,
  * 1 <= topk <= 2048, max_kv_len <= 131072.
@@ -233,7 +236,7 @@ dsaidx_status indexer_prefill_chunk_paged(const void* q, const float* q_scale, i
                                           int32_t* topk_idx, float* topk_score,
                                           void* workspace, size_t workspace_bytes, void* stream);
 
-size_t indexer_prefill_chunk_paged_workspace_bytes(int B, int T, int max_kv_len);
+size_t indexer_prefill_chunk_paged_workspace_bytes(int B, int T, int max_kv_len, int q_dtype);
 
 /*
  * indexer_kcache_append -- quantise T new keys to FP8 and write them into the
@@ -299,6 +302,34 @@ dsaidx_status indexer_kcache_append(const void* k, int k_dtype, const int32_t* s
 dsaidx_status indexer_topk_gather(const void* latent_cache, int row_bytes, const int32_t* block_table,
                                   int max_pages_per_seq, int num_pages, int page_size,
                                   const int32_t* topk_idx, int B, int topk, void* out, void* stream);
+
+/*
+ * indexer_topk_gather_layers -- Index Share: one selection, gathered from
+ * the latent caches of several layers in one launch.
+ *
+ * Passage: "Lightning Indexer explained", section 1, question 4 of the Q&A
+ * (Index Share: the top-k is computed at F layers and reused by S layers,
+ * which skip their own indexer) and section 3 (the selection I is reused
+ * across layers).  The reusing layers read their own latent caches at the
+ * shared positions; every layer's cache shares the block table and row
+ * size.  Layer l's output equals indexer_topk_gather of latent_caches[l]
+ * with the same table and indices; the indices and page ids are read once
+ * for all layers.
+ *
+ *   latent_caches  HOST array [n_layers] of device pointers, each
+ *                  [num_pages][page_size][row_bytes], 16-byte aligned
+ *   outs           HOST array [n_layers] of device pointers, each out
+ *                  [B][topk][row_bytes], 16-byte aligned
+ *   block_table, topk_idx, B, topk, row_bytes: as indexer_topk_gather
+ * The pointer arrays are read during the call only.  No workspace.
+ *
+ * Supported: 1 <= n_layers <= 64, page_size = 64, row_bytes a multiple of
+ * 16 in [16, 65536].
+ */
+dsaidx_status indexer_topk_gather_layers(const void* const* latent_caches, void* const* outs, int n_layers,
+                                         int row_bytes, const int32_t* block_table, int max_pages_per_seq,
+                                         int num_pages, int page_size, const int32_t* topk_idx, int B, int topk,
+                                         void* stream);
 
 /*
  * topk_select -- the token selector on its own: top-k of each row of a score

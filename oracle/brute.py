@@ -39,15 +39,16 @@ def _val(x, dtype: str, scale=None) -> float:
     return fp8_value(int(x)) * float(scale)
 
 
-def score(q_t, k_s, w_t, dtype, qs_t=None, ks_s=None) -> float:
-    """One I[t,s]: q_t [H][D], k_s [D], w_t [H] as stored."""
+def score(q_t, k_s, w_t, dtype, qs_t=None, ks_s=None, q_dtype=None) -> float:
+    """One I[t,s]: q_t [H][D], k_s [D], w_t [H] as stored (queries in
+    q_dtype when it is given, else in the keys' dtype)."""
     H, D = len(q_t), len(k_s)
     kv = [_val(k_s[c], dtype, ks_s) for c in range(D)]
     total = 0.0
     for i in range(H):
         dot = 0.0
         for c in range(D):
-            dot += _val(q_t[i][c], dtype, None if qs_t is None else qs_t[i]) * kv[c]
+            dot += _val(q_t[i][c], q_dtype or dtype, None if qs_t is None else qs_t[i]) * kv[c]
         total += float(w_t[i]) * max(dot / math.sqrt(D), 0.0)
     return total
 
@@ -60,7 +61,7 @@ def topk(values: list, K: int) -> tuple[list, list]:
     return idx, val
 
 
-def prefill_one(q, k, w, dtype, K, q_scale=None, k_scale=None):
+def prefill_one(q, k, w, dtype, K, q_scale=None, k_scale=None, q_dtype=None):
     """One sequence: q [L][H][D], k [L][D], w [L][H].  Returns
     (I as list of rows with -inf at s > t, idx rows, val rows)."""
     L = len(q)
@@ -71,7 +72,7 @@ def prefill_one(q, k, w, dtype, K, q_scale=None, k_scale=None):
             if s <= t:
                 row.append(score(q[t], k[s], w[t], dtype,
                                  None if q_scale is None else q_scale[t],
-                                 None if k_scale is None else k_scale[s]))
+                                 None if k_scale is None else k_scale[s], q_dtype))
             else:
                 row.append(-math.inf)
         I.append(row)

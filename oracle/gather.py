@@ -15,6 +15,12 @@ they leave open, and the readings taken here:
 * A row is opaque bytes (the element type does not matter to a gather).
 * A padding index (-1), or any index outside [0, max_pages * page_size),
   yields a zero row.
+
+Index Share (Lightning Indexer explained, section 1, question 4 of the Q&A,
+and section 3): the top-k computed at one layer is reused by the layers that
+follow it.  Each reusing layer then reads its own latent cache at the shared
+positions, so the multi-layer gather is the single-layer gather applied to
+each layer's cache with one index set.
 """
 from __future__ import annotations
 
@@ -35,3 +41,10 @@ def topk_gather(latent_cache: np.ndarray, block_table: np.ndarray, topk_idx: np.
             if 0 <= s < limit:
                 out[b, j] = latent_cache[int(block_table[b, s // page_size]), s % page_size]
     return out
+
+
+def topk_gather_layers(latent_caches, block_table: np.ndarray, topk_idx: np.ndarray,
+                       page_size: int = 64) -> list:
+    """One selection served to several layers: layer l's rows are gathered
+    from latent_caches[l] at the same positions (and with the same table)."""
+    return [topk_gather(c, block_table, topk_idx, page_size) for c in latent_caches]

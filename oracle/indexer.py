@@ -49,12 +49,14 @@ def _scores_block(qd_rows: np.ndarray, kd: np.ndarray, w_rows: np.ndarray) -> np
     return np.einsum("rh,rhn->rn", w_rows, r)                                   # step 4
 
 
-def prefill_scores(q, k, w, dtype: str, q_scale=None, k_scale=None, rows=None) -> np.ndarray:
+def prefill_scores(q, k, w, dtype: str, q_scale=None, k_scale=None, rows=None, q_dtype=None) -> np.ndarray:
     """Score rows of ONE sequence.
 
     q [L,H,D], k [L,D], w [L,H] as stored (see ``formats.decode``); q_scale
-    [L,H] and k_scale [L] for fp8.  Returns fp64 [len(rows), L] with -inf at
-    s > t (all rows when ``rows`` is None).
+    [L,H] and k_scale [L] for fp8.  ``q_dtype`` is the queries' format when
+    it differs from the keys' (bf16 queries of a chunk scored against an fp8
+    key cache: each side decoded on its own, step 1).  Returns fp64
+    [len(rows), L] with -inf at s > t (all rows when ``rows`` is None).
     """
     L, H, D = q.shape
     rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -66,7 +68,7 @@ def prefill_scores(q, k, w, dtype: str, q_scale=None, k_scale=None, rows=None) -
     for a in range(0, rows.size, blk):
         rr = rows[a:a + blk]
         n = int(rr.max()) + 1
-        qd = decode(q[rr], dtype, None if q_scale is None else q_scale[rr])
+        qd = decode(q[rr], q_dtype or dtype, None if q_scale is None else q_scale[rr])
         I = _scores_block(qd, kd[:n], wd[rr])
         s = np.arange(n)
         I = np.where(s[None, :] <= rr[:, None], I, -np.inf)                    # step 5
@@ -92,7 +94,8 @@ def prefill(inp: dict, K: int, rows=None, want_scores: bool = False):
     """Oracle of one prefill call over every batch element.
 
     ``inp`` holds q [B,L,H,D], k [B,L,D], w [B,L,H] (+ q_scale [B,L,H],
-    k_scale [B,L] for fp8) and "dtype".  Returns (idx [B,R,K] int32,
+    k_scale [B,L] for fp8) and "dtype" (+ "q_dtype" when the queries' format
+    differs from the keys').  Returns (idx [B,R,K] int32,
     val [B,R,K] fp64, scores [B,R,L] fp64 or None) for the R requested rows.
     """
     q, k, w, dt = inp["q"], inp["k"], inp["w"], inp["dtype"]
@@ -104,7 +107,8 @@ def prefill(inp: dict, K: int, rows=None, want_scores: bool = False):
     qs, ks = inp.get("q_scale"), inp.get("k_scale")
     for b in range(B):
         I = prefill_scores(q[b], k[b], w[b], dt,
-                           None if qs is None else qs[b], None if ks is None else ks[b], rows)
+                           None if qs is None else qs[b], None if ks is None else ks[b], rows,
+                           q_dtype=inp.get("q_dtype"))
         for j, t in enumerate(rows):
             idx[b, j], val[b, j] = select_topk(I[j], int(t) + 1, K)
         if want_scores:

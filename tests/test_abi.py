@@ -33,7 +33,8 @@ def lib():
 def test_header_declares_the_entry_points():
     fns = header_functions()
     for name in ("indexer_prefill", "indexer_decode_paged", "topk_select", "indexer_kcache_append",
-                 "indexer_topk_gather", "indexer_prefill_chunk_paged", "indexer_prefill_noalloc"):
+                 "indexer_topk_gather", "indexer_prefill_chunk_paged", "indexer_prefill_noalloc",
+                 "indexer_topk_gather_layers"):
         assert name in fns
 
 
@@ -184,6 +185,28 @@ def test_topk_gather_rejects_before_launch(lib, kw, status):
     assert gather(lib, **kw) == status
 
 
+def gather_layers(lib, n=3, lc=P, out=P, rb=1024, bt=P, mpp=8, npg=8, ps=64, idx=P, B=2, K=16, caches=None,
+                  outs=None):
+    cp = (ctypes.c_void_p * max(n, 1))(*([lc] * max(n, 1) if caches is None else caches))
+    op = (ctypes.c_void_p * max(n, 1))(*([out] * max(n, 1) if outs is None else outs))
+    return lib.indexer_topk_gather_layers(cp, op, n, rb, bt, mpp, npg, ps, idx, B, K, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), NULL), (dict(idx=None), NULL), (dict(caches=[P, None, P]), NULL), (dict(outs=[P, P, None]), NULL),
+    (dict(n=0), SHAPE), (dict(B=0), SHAPE), (dict(K=0), SHAPE), (dict(rb=0), SHAPE), (dict(mpp=0), SHAPE),
+    (dict(n=65), UNSUP), (dict(ps=32), UNSUP), (dict(rb=1000), UNSUP), (dict(caches=[P, P + 8, P]), UNSUP),
+    (dict(outs=[P + 4, P, P]), UNSUP),
+])
+def test_topk_gather_layers_rejects_before_launch(lib, kw, status):
+    assert gather_layers(lib, **kw) == status
+
+
+def test_topk_gather_layers_null_arrays(lib):
+    assert lib.indexer_topk_gather_layers(None, (ctypes.c_void_p * 1)(P), 1, 1024, P, 8, 8, 64, P, 2, 16, None) == NULL
+    assert lib.indexer_topk_gather_layers((ctypes.c_void_p * 1)(P), None, 1, 1024, P, 8, 8, 64, P, 2, 16, None) == NULL
+
+
 def chunk(lib, q=P, qs=P, dt=2, w=P, cu=P, q0s=P, kc=P, ks=P, bt=P, mpp=64, npg=64, B=1, T=64, mkv=164, H=64, D=128,
           ps=64, topk=2048, idx=P, val=None, ws=P, nws=1 << 20):
     return lib.indexer_prefill_chunk_paged(q, qs, dt, w, cu, q0s, kc, ks, bt, mpp, npg, B, T, mkv, H, D, ps, topk, idx,
@@ -193,7 +216,8 @@ def chunk(lib, q=P, qs=P, dt=2, w=P, cu=P, q0s=P, kc=P, ks=P, bt=P, mpp=64, npg=
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), NULL), (dict(qs=None), NULL), (dict(w=None), NULL), (dict(cu=None), NULL), (dict(q0s=None), NULL),
     (dict(kc=None), NULL), (dict(ks=None), NULL), (dict(bt=None), NULL), (dict(idx=None), NULL),
-    (dict(dt=9), DTYPE), (dict(dt=1), UNSUP), (dict(B=0), SHAPE), (dict(T=0), SHAPE), (dict(mkv=0), SHAPE),
+    (dict(dt=9), DTYPE), (dict(dt=0), UNSUP), (dict(dt=1, qs=P), UNSUP), (dict(B=0), SHAPE), (dict(T=0), SHAPE),
+    (dict(mkv=0), SHAPE),
     (dict(mkv=4097), SHAPE), (dict(H=8), UNSUP), (dict(D=64), UNSUP), (dict(ps=32, mpp=128), UNSUP),
     (dict(topk=4096), UNSUP), (dict(mpp=4096, mkv=131073), UNSUP), (dict(ws=None), WS), (dict(nws=100), WS),
     (dict(kc=P + 8), UNSUP),
@@ -203,12 +227,17 @@ def test_prefill_chunk_rejects_before_launch(lib, kw, status):
 
 
 def test_prefill_chunk_workspace_query(lib):
-    # 5 bytes per key up to max_kv_len (64-padded) per sequence, rounded to
-    # 256, then one 8-byte plan entry per 8-row block bound (T/8 + B)
-    assert lib.indexer_prefill_chunk_paged_workspace_bytes(2, 128, 4160) == \
+    # fp8 queries: 5 bytes per key up to max_kv_len (64-padded) per sequence,
+    # rounded to 256, then one 8-byte plan entry per 8-row block bound (T/8 + B)
+    assert lib.indexer_prefill_chunk_paged_workspace_bytes(2, 128, 4160, 2) == \
         (2 * 4160 * 5 + 255) // 256 * 256 + (128 // 8 + 2) * 8
-    assert lib.indexer_prefill_chunk_paged_workspace_bytes(64, 64, 131072) == \
+    assert lib.indexer_prefill_chunk_paged_workspace_bytes(64, 64, 131072, 2) == \
         (64 * 131072 * 5 + 255) // 256 * 256 + (64 // 8 + 64) * 8
+    # bf16 queries: 4 + 256 bytes per key (adjusted scale, key widened to
+    # bf16), then the plan
+    assert lib.indexer_prefill_chunk_paged_workspace_bytes(2, 128, 4100, 1) == \
+        2 * 4160 * 260 + (128 // 8 + 2) * 8
+    assert lib.indexer_prefill_chunk_paged_workspace_bytes(3, 0, 4100, 1) == 0
 
 
 # ---- the Python binding's own checks (host-side, before any device access) ----

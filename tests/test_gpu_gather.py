@@ -2,7 +2,9 @@
 selected positions) against the oracle (oracle/gather.py): exact bytes, with
 padding and out-of-table indices, several row sizes and ragged B * K, the
 paged decode's own output as the indices, and the full-size configuration
-the bench times (sampled rows)."""
+the bench times (sampled rows).  Also Index Share's multi-layer gather
+(indexer_topk_gather_layers): every layer's output against the oracle's
+gather of that layer, with one and with several layer groups per launch."""
 import numpy as np
 import pytest
 import torch
@@ -11,6 +13,7 @@ import dsa_lightning_indexer_03_amd as dsa
 import synth
 from gpu_util import dev, host, run_decode, say
 from oracle.gather import topk_gather as oracle_gather
+from oracle.gather import topk_gather_layers as oracle_gather_layers
 
 pytestmark = pytest.mark.gpu
 
@@ -74,3 +77,37 @@ def test_full_size_sampled():
     expect = host(flat[rows]) * (s >= 0)[:, None].astype(np.uint8)
     got = host(out[torch.from_numpy(bs).cuda(), torch.from_numpy(js).cuda()])
     assert np.array_equal(got, expect)
+
+
+@pytest.mark.parametrize("S,B,K,row", [(3, 5, 300, 656), (61, 1, 64, 1152), (64, 2, 33, 48), (2, 16, 2048, 1024)])
+def test_layers_share_one_selection(S, B, K, row):
+    """Index Share: S layers gather the same selection from their own caches
+    (S=61 with 16 waves of rows splits the layers into groups; S=2 with
+    8192 waves runs all layers in one group)."""
+    rng = np.random.default_rng(S * 7919 + B * 131 + K + row)
+    mpp, n_pages = 5, B * 5 + 2
+    say(f"gather layers S={S} B={B} K={K} row={row}")
+    caches = [rng.integers(0, 256, size=(n_pages, 64, row), dtype=np.uint8) for _ in range(S)]
+    table = rng.permutation(n_pages)[: B * mpp].reshape(B, mpp).astype(np.int32)
+    idx = rng.integers(0, mpp * 64, size=(B, K)).astype(np.int32)
+    idx[rng.random((B, K)) < 0.1] = -1
+    idx[0, 0] = mpp * 64
+    outs = dsa.topk_gather_layers([dev(c) for c in caches], dev(table), dev(idx))
+    torch.cuda.synchronize()
+    want = oracle_gather_layers(caches, table, idx)
+    for l in range(S):
+        assert np.array_equal(host(outs[l]), want[l]), f"layer {l}"
+
+
+def test_layers_match_the_single_layer_gather():
+    """The multi-layer launch writes, per layer, exactly what a single-layer
+    gather writes (decode output as indices, bf16 latent rows)."""
+    d = synth.decode_inputs(2, [3000, 200], 64, 128, seed=63, permute=True)
+    gi, _ = run_decode(d, 256)
+    rng = np.random.default_rng(64)
+    n_pages = d["k_cache"].shape[0]
+    lat = [dev(synth.to_bf16_bits(rng.normal(size=(n_pages, 64, 512)).astype(np.float32))) for _ in range(4)]
+    bt, ix = dev(d["block_table"]), dev(gi)
+    outs = dsa.topk_gather_layers(lat, bt, ix)
+    for l in range(4):
+        assert torch.equal(outs[l], dsa.topk_gather(lat[l], bt, ix)), f"layer {l}"

@@ -2,7 +2,7 @@
 the padding rule, and agreement with a vectorised re-indexing."""
 import numpy as np
 
-from oracle.gather import topk_gather
+from oracle.gather import topk_gather, topk_gather_layers
 
 
 def test_hand_worked_gather():
@@ -28,3 +28,17 @@ def test_matches_vectorised_indexing():
     pages = table[b, np.where(valid, idx, 0) // 64]
     ref = cache[pages, np.where(valid, idx, 0) % 64] * valid[..., None]
     assert np.array_equal(out, ref)
+
+
+def test_layers_share_one_selection():
+    # three layers whose rows encode (layer, page, slot): each output row
+    # names the layer it came from and the page/slot the shared index maps to
+    cache = np.array([[[[40 * l + 10 * p + s] * 4 for s in range(2)] for p in range(3)] for l in range(3)],
+                     np.uint8)
+    table = np.array([[2, 0], [1, 2]], np.int32)
+    idx = np.array([[3, 0, -1], [1, 2, 4]], np.int32)
+    outs = topk_gather_layers(list(cache), table, idx, page_size=2)
+    assert len(outs) == 3
+    for l, o in enumerate(outs):
+        # the rows of the single-layer hand case, offset by 40 * layer; padding rows stay zero
+        assert o[:, :, 0].tolist() == [[1 + 40 * l, 20 + 40 * l, 0], [11 + 40 * l, 20 + 40 * l, 0]]

@@ -101,6 +101,28 @@ def test_brute_force_agrees():
     assert check_brute()
 
 
+def test_brute_force_agrees_bf16_queries_fp8_keys():
+    """Chunks of bf16 queries against the fp8 cache: the queries and the keys
+    are decoded each in its own format (scalar decoders in the brute force)."""
+    L, H, D, K = 11, 3, 6, 4
+    kin = random_small("fp8", L, H, D, 31)
+    qin = random_small("bf16", L, H, D, 32)
+    inp = dict(kin, q=qin["q"], q_scale=None, q_dtype="bf16")
+    idx, _, I = indexer.prefill(inp, K, want_scores=True)
+    bI, bidx, _ = brute.prefill_one(inp["q"][0].tolist(), inp["k"][0].tolist(), inp["w"][0].tolist(), "fp8", K,
+                                    None, inp["k_scale"][0].tolist(), q_dtype="bf16")
+    bI = np.array(bI)
+    fin = np.isfinite(bI)
+    assert np.array_equal(fin, np.isfinite(I[0]))
+    assert np.allclose(I[0][fin], bI[fin], rtol=1e-12, atol=1e-14)
+    assert np.array_equal(idx[0], np.array(bidx))
+    # decoding the bf16 queries as fp8 codes would change every score
+    wrong = dict(inp, q=(qin["q"] & 0xFF).astype(np.uint8), q_scale=np.ones((1, L, H), np.float32))
+    wrong.pop("q_dtype")
+    _, _, Iw = indexer.prefill(wrong, K, want_scores=True)
+    assert not np.allclose(Iw[0][fin], I[0][fin])
+
+
 def test_brute_force_tie_heavy():
     inp = synth.tie_heavy_prefill(1, 16, 2, 4, "f32", 7, n_proto=2)
     idx, _, I = indexer.prefill(inp, 5, want_scores=True)
