@@ -303,6 +303,32 @@ def topk_gather_layers(latent_caches, block_table, topk_idx, outs=None):
     return outs
 
 
+def probe_mfma(kind: int, blocks: int, iters: int, device="cuda"):
+    """Measurement probe: blocks x 4 waves x iters x 8 MFMAs of one shape
+    (0: fp8 16x16x128 scaled, 1: bf16 16x16x32, 2: f16 16x16x32).  Returns
+    the (meaningless) output tensor; time the call with events."""
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    _lib.check(_lib.load().dsaidx_probe_mfma(kind, blocks, iters, _ptr(out), _stream(out.device)),
+               "dsaidx_probe_mfma")
+    return out
+
+
+def probe_page_read(k_cache, k_scale, page_ids, blocks: int, out=None):
+    """Measurement probe: reads the pages page_ids of a paged fp8 key cache
+    (8448 bytes each) with the decode scan's load layout."""
+    _need(k_cache, "k_cache", *_CODES)
+    _need(k_scale, "k_scale", _F32)
+    _need(page_ids, "page_ids", _I32)
+    for name, t in (("k_cache", k_cache), ("k_scale", k_scale), ("page_ids", page_ids)):
+        _dev(t, name)
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=k_cache.device)
+    _lib.check(_lib.load().dsaidx_probe_page_read(_ptr(k_cache), _ptr(k_scale), _ptr(page_ids), page_ids.numel(),
+                                                  blocks, _ptr(out), _stream(k_cache.device)),
+               "dsaidx_probe_page_read")
+    return out
+
+
 def prefill_chunk_varlen(q, q_scale, w, cu_seqlens_q, q_start, k_cache, k_scale, block_table, topk: int,
                          max_kv_len: int, want_topk_score: bool = True, workspace: torch.Tensor | None = None):
     """Top-k of the query rows of B sequences' chunks (packed one after

@@ -42,6 +42,8 @@ SIGNATURES = {
     "indexer_topk_gather_layers": (_c_int, [ctypes.POINTER(_c_void_p), ctypes.POINTER(_c_void_p), _c_int, _c_int,
                                             _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int, _c_int,
                                             _c_void_p]),
+    "dsaidx_probe_mfma": (_c_int, [_c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
+    "dsaidx_probe_page_read": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_void_p, _c_void_p]),
     "dsaidx_status_string": (ctypes.c_char_p, [_c_int]),
     "dsaidx_last_error": (ctypes.c_char_p, []),
     "dsaidx_version": (_c_int, []),

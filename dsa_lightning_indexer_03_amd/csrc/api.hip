@@ -165,6 +165,29 @@ dsaidx_status indexer_topk_gather_layers(const void* const* latent_caches, void*
     return DSAIDX_OK;
 }
 
+dsaidx_status dsaidx_probe_mfma(int kind, int blocks, int iters, float* out, void* stream) {
+    g_err[0] = 0;
+    if (!out) return fail(DSAIDX_ERR_NULL, "out is NULL");
+    if (kind < 0 || kind > 2) return fail(DSAIDX_ERR_UNSUPPORTED, "kind=%d (0, 1 or 2)", kind);
+    if (blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 20))
+        return fail(DSAIDX_ERR_SHAPE, "blocks=%d iters=%d", blocks, iters);
+    const hipError_t e = dsaidx::launch_probe_mfma(kind, blocks, iters, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "dsaidx_probe_mfma");
+    return DSAIDX_OK;
+}
+
+dsaidx_status dsaidx_probe_page_read(const uint8_t* k_cache, const float* k_scale, const int32_t* page_ids, int n,
+                                     int blocks, float* out, void* stream) {
+    g_err[0] = 0;
+    if (!k_cache || !k_scale || !page_ids || !out) return fail(DSAIDX_ERR_NULL, "a required pointer is NULL");
+    if (n < 1 || blocks < 1 || blocks > 65536) return fail(DSAIDX_ERR_SHAPE, "n=%d blocks=%d", n, blocks);
+    if (!aligned16(k_cache)) return fail(DSAIDX_ERR_UNSUPPORTED, "k_cache must be 16-byte aligned");
+    const hipError_t e =
+        dsaidx::launch_probe_page_read(k_cache, k_scale, page_ids, n, blocks, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "dsaidx_probe_page_read");
+    return DSAIDX_OK;
+}
+
 size_t topk_select_workspace_bytes(int rows, int cols, int topk) {
     (void)rows; (void)cols; (void)topk;
     return 0;

@@ -137,5 +137,9 @@ hipError_t launch_prefill_ws_varlen(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_kcache_append(const KcacheArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_topk_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_topk_gather_layers(const GatherLayersArgs& a, hipStream_t stream);
+// Measurement probes (csrc/probes.hip).
+hipError_t launch_probe_mfma(int kind, int blocks, int iters, float* out, hipStream_t stream);
+hipError_t launch_probe_page_read(const uint8_t* k_cache, const float* k_scale, const int32_t* page_ids, int n,
+                                  int blocks, float* out, hipStream_t stream);
 
 }  // namespace dsaidx

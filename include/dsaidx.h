@@ -354,6 +354,32 @@ dsaidx_status topk_select(const float* scores, int rows, int cols, int64_t row_s
 
 size_t topk_select_workspace_bytes(int rows, int cols, int topk);
 
+/*
+ * dsaidx_probe_mfma, dsaidx_probe_page_read -- measurement probes.  They
+ * compute nothing of the method: they measure what this GPU delivers for
+ * the two resources the indexer's kernels are bound by, so a kernel can be
+ * reported against a measured peak beside the published one.
+ *
+ * dsaidx_probe_mfma: `blocks` workgroups of 256 threads; each wave runs
+ * `iters` rounds of 8 independent MFMAs of one shape:
+ *   kind 0  v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 x E4M3 (65536 flop each)
+ *   kind 1  v_mfma_f32_16x16x32_bf16 (16384 flop each)
+ *   kind 2  v_mfma_f32_16x16x32_f16 (16384 flop each)
+ * so one call performs blocks * 4 * iters * 8 MFMAs.
+ *
+ * dsaidx_probe_page_read: reads pages page_ids[0..n) of a paged fp8 key
+ * cache laid out as indexer_decode_paged reads it (page = 64 rows of 128
+ * code bytes, 8192 B, plus its 64 fp32 scales, 256 B) with the decode
+ * scan's load layout, `blocks` workgroups of 256 threads: 8448 * n bytes
+ * per call.
+ *
+ *   out  [blocks * 256] fp32 device array (values carry no meaning)
+ * Supported: 1 <= blocks <= 65536, 1 <= iters <= 1 << 20, 1 <= n.
+ */
+dsaidx_status dsaidx_probe_mfma(int kind, int blocks, int iters, float* out, void* stream);
+dsaidx_status dsaidx_probe_page_read(const uint8_t* k_cache, const float* k_scale, const int32_t* page_ids, int n,
+                                     int blocks, float* out, void* stream);
+
 /* Static text for a status code. */
 const char* dsaidx_status_string(int status);
 

@@ -207,6 +207,23 @@ def test_topk_gather_layers_null_arrays(lib):
     assert lib.indexer_topk_gather_layers((ctypes.c_void_p * 1)(P), None, 1, 1024, P, 8, 8, 64, P, 2, 16, None) == NULL
 
 
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 8, None), NULL), ((3, 4, 8, P), UNSUP), ((-1, 4, 8, P), UNSUP), ((0, 0, 8, P), SHAPE),
+    ((1, 65537, 8, P), SHAPE), ((2, 4, 0, P), SHAPE), ((2, 4, (1 << 20) + 1, P), SHAPE),
+])
+def test_probe_mfma_rejects_before_launch(lib, args, status):
+    assert lib.dsaidx_probe_mfma(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, P, P, 8, 4, P), NULL), ((P, None, P, 8, 4, P), NULL), ((P, P, None, 8, 4, P), NULL),
+    ((P, P, P, 8, 4, None), NULL), ((P, P, P, 0, 4, P), SHAPE), ((P, P, P, 8, 0, P), SHAPE),
+    ((P + 8, P, P, 8, 4, P), UNSUP),
+])
+def test_probe_page_read_rejects_before_launch(lib, args, status):
+    assert lib.dsaidx_probe_page_read(*args, None) == status
+
+
 def chunk(lib, q=P, qs=P, dt=2, w=P, cu=P, q0s=P, kc=P, ks=P, bt=P, mpp=64, npg=64, B=1, T=64, mkv=164, H=64, D=128,
           ps=64, topk=2048, idx=P, val=None, ws=P, nws=1 << 20):
     return lib.indexer_prefill_chunk_paged(q, qs, dt, w, cu, q0s, kc, ks, bt, mpp, npg, B, T, mkv, H, D, ps, topk, idx,
