@@ -566,6 +566,10 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
     }
 
     // ---------------- selection waves ----------------
+    // They are the longer side of the pipeline: where both waves of a SIMD
+    // can issue, this one goes first (the matrix wave's MFMAs still fill the
+    // matrix core between its own instructions).
+    __builtin_amdgcn_s_setprio(1);
     if (m == 0 && lane == 3) flags[3] = 0u;
     for (int pass = 0;; ++pass) {
         if (m == 0 && lane < 3) flags[lane] = 0u;

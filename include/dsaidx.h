@@ -159,7 +159,12 @@ size_t indexer_prefill_noalloc_scratch_bytes(void);
  * b lives in page block_table[b][s / page_size], slot s % page_size of the
  * shared page pool (paging is this library's layout of that cache).
  *
- *   q            [B][H][D] bf16 (q_dtype must be DSAIDX_BF16)
+ *   q            [B][H][D] bf16 (q_dtype must be DSAIDX_BF16).  The scan
+ *                multiplies the query as a bf16 MFMA operand; an fp32 query
+ *                would have to be rounded to bf16 first, which changes its
+ *                scores, so DSAIDX_F32 returns DSAIDX_ERR_UNSUPPORTED rather
+ *                than rounding silently (a caller who wants that rounding
+ *                converts explicitly, and gets the rounded query's scores)
  *   w            [B][H] fp32
  *   k_cache      [num_pages][page_size][D] FP8 E4M3 codes
  *   k_scale      [num_pages][page_size] fp32, one scale per cached token
