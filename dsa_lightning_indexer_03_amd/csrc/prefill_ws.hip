@@ -595,8 +595,9 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
             }
             const int s_prev = s_cur == 0 ? 2 : s_cur - 1;   // (i - 1) % 3
             const int s_next = s_cur == 2 ? 0 : s_cur + 1;   // (i + 1) % 3
-            // compaction request of iteration i-1, read beside the ring
-            const uint32_t fw = i >= 1 ? flags[s_prev] : 0u;
+            // The compaction request of iteration i-1 is read right behind the
+            // ring, so that one LDS wait covers both reads.
+            uint32_t fw_raw;
             if (i >= 2) {
                 // Appends of chunk i-2 (ring slot i % 2).  Branch free: lanes
                 // that do not append write a slot of their own past CAP.
@@ -605,6 +606,7 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
                 float sc[2];
 #pragma unroll
                 for (int j = 0; j < 2; ++j) sc[j] = slot[64 * j];
+                fw_raw = flags[s_prev];
                 const int s = c * 64 + lane;
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
@@ -619,7 +621,10 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
                     if (ROWS && act[j] && s < sg.Lk) srow[j][s] = valid ? sc[j] : -INFINITY;
                 }
                 c_sel = chunk_next(i - 1, c_sel);
+            } else {
+                fw_raw = flags[s_prev];
             }
+            const uint32_t fw = i >= 1 ? fw_raw : 0u;
             // Compaction requested after the appends of iteration i-1 (read
             // only now, behind this iteration's appends): every row of the
             // block well above k compacts at once, so the block stalls once
