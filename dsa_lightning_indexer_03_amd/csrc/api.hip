@@ -26,7 +26,7 @@ dsaidx_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-constexpr int kMaxTopk = 2048;
+using dsaidx::kMaxTopk;
 constexpr int kMaxL = 131072;
 constexpr int kMaxSelectCols = 4194304;
 

@@ -9,6 +9,7 @@ namespace dsaidx {
 
 constexpr int kHistBins = 2048;        // first radix digit: score key bits [31:21]
 constexpr int kCtrlStride = 64;        // u32 words between per-query counters (own cache lines)
+constexpr int kMaxTopk = 2048;          // largest k any entry point accepts
 
 struct SelectArgs {
     const float* scores;

@@ -64,6 +64,8 @@ constexpr int kWsRows = kBlockRows;  // query rows per workgroup
 // Candidates per row: the most that fit beside three key stages and the
 // score ring.
 constexpr int kWsCap = 2624;
+// a row asking for compaction (count above kWsCap - 128) always takes part (count above its cut rank + 128)
+static_assert(kMaxTopk + 128 < kWsCap - 2 * kWave, "the requesting row joins its compaction");
 constexpr int kWsStages = 3;
 constexpr size_t kWsStageKeyBytes = 64 * kD;               // one chunk of fp8 keys,
 constexpr size_t kWsStageScaleOff = kWsStageKeyBytes;      // their fp32 scales times 2^Pk,
@@ -272,7 +274,7 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
     RowBuf<Pos> rb[2];
     int nb[2];
     uint32_t thr[2], rspec[2];
-    bool live[2], act[2], floored[2];
+    bool live[2], act[2], floored[2], spec_ok[2];
     int tp[2];
     // score-matrix rows as global (not generic) pointers: a generic store
     // could address LDS, and the barrier's release would then have to wait
@@ -294,6 +296,7 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
             thr[j] = 0u;
             floored[j] = false;
             rspec[j] = 0u;
+            spec_ok[j] = live[j] && tp[j] + 1 > 2 * K;
             if (live[j] && S >= 2 && tp[j] + 1 > 2 * K)
                 rspec[j] = spec_rank(64.f * (float)S * (float)K / (float)(tp[j] + 1));
             srow[j] = (ROWS && live[j]) ? (gfloat*)(a.scores + (size_t)(sg.row0 + t) * a.L) : nullptr;
@@ -627,14 +630,29 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
             const uint32_t fw = i >= 1 ? fw_raw : 0u;
             // Compaction requested after the appends of iteration i-1 (read
             // only now, behind this iteration's appends): every row of the
-            // block well above k compacts at once, so the block stalls once
-            // per event.  A request leaves two chunks of slack.
+            // block well above its cut rank compacts at once, so the block
+            // stalls once per event.  A request leaves two chunks of slack.
+            // A long row cuts speculatively: of the n_seen keys scanned so
+            // far, about k n_seen / (t+1) belong to its final top k, so the
+            // cut rank is that count plus three and a half standard
+            // deviations and 8 (capped at k), verified with the floors.
             if (i >= 1) {
                 if (m == 0 && lane == 0) flags[s_next] = 0u;
                 if (fw != 0u) {
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        if (act[j] && nb[j] > K + 256) nb[j] = wave_compact(rb[j], nb[j], (uint32_t)K, &thr[j], CAP);
+                    for (int j = 0; j < 2; ++j) {
+                        uint32_t r = (uint32_t)K;
+                        if (spec_ok[j]) {
+                            const float rows_keys = (float)(tp[j] + 1);
+                            const float seen = fminf(64.f * (float)(i - 1), rows_keys);
+                            r = min(r, spec_rank((float)K * seen / rows_keys));
+                        }
+                        if (act[j] && nb[j] > (int)r + 128) {
+                            bool sp;
+                            nb[j] = wave_compact(rb[j], nb[j], (uint32_t)K, &thr[j], CAP, r, &sp);
+                            floored[j] |= sp;
+                        }
+                    }
                 }
             }
             if (i >= 2 && i - 2 == S - 1) {
@@ -670,6 +688,7 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
         for (int j = 0; j < 2; ++j) {
             act[j] = redo[j];
             rspec[j] = 0u;
+            spec_ok[j] = false;
             if (redo[j]) {
                 nb[j] = 0;
                 thr[j] = 0u;

@@ -272,8 +272,18 @@ __device__ __forceinline__ uint32_t wave_exact_cut(const RowBuf<Pos>& rb, int n,
 // count and the new append floor (append iff key > *thr).  Entries equal to
 // the cut key stay admissible: in an out-of-order scan a later one may have
 // a lower position.
+//
+// Speculative cut (1 <= r < K): the cut is the lower edge of the radix bin
+// that holds the r-th largest key instead of the K-th, so fewer entries
+// survive and the buffer refills later.  Every entry at or above the edge
+// stays, so the buffer still holds every scanned key above the new floor;
+// *spec reports whether this cut was taken (the caller must then verify at
+// the end that at least K keys lie above its floor).  A crowded bin falls
+// back to the exact cut at K, which is never speculative.
 template <typename Pos>
-__device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* thr, int cap) {
+__device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* thr, int cap, uint32_t r = 0u,
+                            bool* spec = nullptr) {
+    const uint32_t want = (r != 0u && r < K) ? r : K;
     uint32_t pv;
     const int cp = wave_common_prefix(rb, n, &pv);
     uint32_t lo_edge = 0;  // keep keys >= lo_edge
@@ -286,7 +296,7 @@ __device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* 
         const uint32_t pm = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
         wave_hist<false>(rb, n, 0u, pm, pv, shift, dmask);
         uint32_t above, inb;
-        const uint32_t b = wave_find_bin(rb, K, &above, &inb);
+        const uint32_t b = wave_find_bin(rb, want, &above, &inb);
         lo_edge = pv | (b << shift);
         // Too many entries would survive (a crowded bin): fall back to exact.
         if (above + inb > (uint32_t)(cap - 256)) exact = true;
@@ -298,6 +308,7 @@ __device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* 
     const int kept = wave_keep_pass(rb, n, exact, kappa, pos_cut, lo_edge, (int32_t*)nullptr, (float*)nullptr, 0);
     const uint32_t fl = exact ? kappa : lo_edge;
     *thr = fl == 0u ? 0u : fl - 1u;
+    if (spec) *spec = !exact && want < K;
     return kept;
 }
 
