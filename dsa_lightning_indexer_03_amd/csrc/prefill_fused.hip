@@ -389,6 +389,8 @@ __device__ __forceinline__ uint32_t spec_rank(float ec) {
 // ---------------------------------------------------------------------------
 constexpr int kBfWaves = 8;
 constexpr int kBfCap = 2560;
+// a row asking for compaction (count above kBfCap - 64) always takes part (count above its cut rank + 128)
+static_assert(kMaxTopk + 128 < kBfCap - kWave, "the requesting row joins its compaction");
 constexpr int kBfStages = 2;
 constexpr size_t kBfWaveBytes = (size_t)(kBfCap + kWave) * 6 + 128 * 4;
 constexpr size_t kBfStageKeyBytes = 64 * kD * 2;
@@ -701,6 +703,7 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     bool active = live;
     bool floored = false;
     uint32_t r_spec = 0;
+    bool spec_ok = live && tv + 1 > 2 * K;  // speculative compaction cuts (first pass only)
     if (live && S >= 2 && tv + 1 > 2 * K) {
         const float ec = 64.f * (float)S * (float)K / (float)(tv + 1);
         r_spec = spec_rank(ec);
@@ -831,7 +834,22 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
                 thr = fl == 0u ? 0u : fl - 1u;
                 floored = true;
             }
-            if (flag_word != 0u && active && nb > K) nb = wave_compact(rb, nb, (uint32_t)K, &thr, CAP + 128);
+            // A long row cuts speculatively: of the 64 i keys scanned so far
+            // (order indices 0 .. i-1), about k 64 i / (t+1) belong to its
+            // final top k; the cut rank is that count plus three and a half
+            // standard deviations and 8 (capped at k), verified with the floor.
+            if (flag_word != 0u && active) {
+                uint32_t r = (uint32_t)K;
+                if (spec_ok) {
+                    const float row_keys = (float)(tv + 1);
+                    r = min(r, spec_rank((float)K * fminf(64.f * (float)i, row_keys) / row_keys));
+                }
+                if (nb > (int)r + 128) {
+                    bool sp;
+                    nb = wave_compact(rb, nb, (uint32_t)K, &thr, CAP + 128, r, &sp);
+                    floored |= sp;
+                }
+            }
         }
         // Head sums of the last chunk's subtile 3, then its appends.
         {
@@ -869,6 +887,7 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
             floored = false;
         }
         r_spec = 0u;
+        spec_ok = false;
     }
     if (!live) return;
     if (srow) {
