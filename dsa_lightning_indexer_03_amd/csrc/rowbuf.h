@@ -72,13 +72,6 @@ __device__ __forceinline__ Pos4<Pos> read_pos4(const Pos* p) {
     return r;
 }
 
-// Exclusive prefix over the wave of a per-lane count (counts < 2^16).
-__device__ __forceinline__ uint32_t wave_excl(uint32_t v, uint32_t* total) {
-    const uint32_t inc = wave_incl_scan(v);
-    *total = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
-    return inc - v;
-}
-
 // Position as an unsigned value of the buffer's position width, inverted so
 // that a lower position compares larger.
 template <typename Pos>
@@ -118,6 +111,31 @@ __device__ __forceinline__ void wave_hist(const RowBuf<Pos>& rb, int n, uint32_t
                     const uint32_t bin = (k[e] >> shift) & dmask;
                     atomicAdd(&rb.hist[bin >> 1], 1u << ((bin & 1u) << 4));
                 }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Histogram of digit (key >> shift) & (2^width - 1) over all n entries,
+// for a digit right below the keys' common prefix (every entry takes part).
+// Branch free: a lane past the end adds zero.
+template <typename Pos>
+__device__ __forceinline__ void wave_hist_top(const RowBuf<Pos>& rb, int n, int shift, int width) {
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) rb.hist[l + 64 * i] = 0u;
+    __builtin_amdgcn_wave_barrier();
+    for (int j0 = 0; j0 < n; j0 += 256) {
+        const int j = j0 + 4 * l;
+        const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
+        const bool full = j0 + 256 <= n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // bin b: word b / 2, half b % 2
+            const uint32_t word = __builtin_amdgcn_ubfe(k[e], (uint32_t)shift + 1u, (uint32_t)width - 1u);
+            const uint32_t half = __builtin_amdgcn_ubfe(k[e], (uint32_t)shift, 1u);
+            const uint32_t inc = (full | (j + e < n)) ? 1u << (half << 4) : 0u;
+            atomicAdd(&rb.hist[word], inc);
         }
     }
     __builtin_amdgcn_wave_barrier();
@@ -180,11 +198,14 @@ __device__ uint32_t wave_kth_key(const RowBuf<Pos>& rb, int n, uint32_t need, ui
     uint32_t pm = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
     int hi = 32 - cp;
     uint32_t inb = (uint32_t)n;  // all keys equal when no digit is left
+    bool first = true;
     while (hi > 0) {
         const int width = hi < 8 ? hi : 8;
         const int shift = hi - width;
         const uint32_t dmask = (1u << width) - 1u;
-        wave_hist<false>(rb, n, 0u, pm, pv, shift, dmask);
+        if (first) wave_hist_top(rb, n, shift, width);  // every entry shares the prefix
+        else wave_hist<false>(rb, n, 0u, pm, pv, shift, dmask);
+        first = false;
         uint32_t above;
         const uint32_t b = wave_find_bin(rb, need, &above, &inb);
         need -= above;
@@ -216,50 +237,70 @@ __device__ uint32_t wave_tie_cut(const RowBuf<Pos>& rb, int n, uint32_t kappa, u
     return inv_pos((Pos)pv);
 }
 
-// One stable pass over the buffer keeping, in buffer order, every entry with
-// key > kappa or (key == kappa and position <= pos_cut) when exact, else
-// every entry with key >= lo_edge.  Kept entries go to the buffer front (in
-// place) or, if idx != nullptr, to the output row.
+// One pass over the buffer keeping every entry with key > kappa or (key ==
+// kappa and position <= pos_cut) when EXACT, else every entry with key >=
+// lo_edge, to the buffer front, in place.  Within a step the kept entries
+// are written slot by slot (slot e of every lane, then slot e+1), so the
+// lanes of one store write consecutive words; this stays below the step's
+// own entries (at most 256 kept, starting at or below the step's first
+// index), which are already in registers.  Branch free: a lane that drops
+// its entry writes it to a slot of its own in the histogram words (not
+// needed once the cut is known).
+template <bool EXACT, typename Pos>
+__device__ int wave_keep_inplace(const RowBuf<Pos>& rb, int n, uint32_t kappa, uint32_t pos_cut, uint32_t lo_edge) {
+    const int l = lane_id();
+    uint32_t* const dk = rb.hist + l;
+    Pos* const dp = reinterpret_cast<Pos*>(rb.hist + kWave) + l;
+    int wpos = 0;
+    for (int j0 = 0; j0 < n; j0 += 256) {
+        const int j = j0 + 4 * l;
+        const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
+        const Pos4<Pos> p = read_pos4(rb.pos + j);
+        const bool full = j0 + 256 <= n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // bitwise, not short-circuit, operators: no branches
+            bool keep = EXACT ? ((k[e] > kappa) | ((k[e] == kappa) & ((uint32_t)p.v[e] <= pos_cut))) : k[e] >= lo_edge;
+            keep &= full | (j + e < n);
+            const uint64_t m = wave_ballot(keep);
+            const int o = wpos + lanes_below(m);
+            *(keep ? rb.key + o : dk) = k[e];
+            *(keep ? rb.pos + o : dp) = p.v[e];
+            wpos += __builtin_popcountll(m);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    return wpos;
+}
+
+// The exact top K (key > kappa, or key == kappa and position <= pos_cut) of
+// the buffer to the output row, in buffer order of a step's slots.
 template <typename Pos, bool P17 = false>
-__device__ int wave_keep_pass(const RowBuf<Pos>& rb, int n, bool exact, uint32_t kappa, uint32_t pos_cut,
-                              uint32_t lo_edge, int32_t* idx, float* val, int limit) {
+__device__ int wave_keep_out(const RowBuf<Pos>& rb, int n, uint32_t kappa, uint32_t pos_cut, int32_t* idx,
+                             float* val, int limit) {
     const int l = lane_id();
     int wpos = 0;
     for (int j0 = 0; j0 < n; j0 += 256) {
         const int j = j0 + 4 * l;
         const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
         const Pos4<Pos> p = read_pos4(rb.pos + j);
-        bool keep[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            keep[e] = j + e < n &&
-                      (exact ? (k[e] > kappa || (k[e] == kappa && (uint32_t)p.v[e] <= pos_cut)) : k[e] >= lo_edge);
-        const uint32_t kc = (uint32_t)keep[0] + keep[1] + keep[2] + keep[3];
-        uint32_t k_tot;
-        int o = wpos + (int)wave_excl(kc, &k_tot);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if (keep[e]) {
-                if (idx) {
-                    if (o < limit) {
-                        idx[o] = entry_pos<P17>(k[e], (uint32_t)p.v[e]);
-                        if (val) val[o] = entry_score<P17>(k[e]);
-                    }
-                } else {
-                    rb.key[o] = k[e];
-                    rb.pos[o] = p.v[e];
-                }
-                ++o;
+            const bool keep = j + e < n && (k[e] > kappa || (k[e] == kappa && (uint32_t)p.v[e] <= pos_cut));
+            const uint64_t m = wave_ballot(keep);
+            const int o = wpos + lanes_below(m);
+            if (keep && o < limit) {
+                idx[o] = entry_pos<P17>(k[e], (uint32_t)p.v[e]);
+                if (val) val[o] = entry_score<P17>(k[e]);
             }
+            wpos += __builtin_popcountll(m);
         }
-        wpos += (int)k_tot;
     }
-    __builtin_amdgcn_wave_barrier();
     return wpos;
 }
 
 // Exact cut of the buffer to its top K by (key desc, position asc): returns
-// kappa and the position cut for wave_keep_pass.
+// kappa and the position cut for the keep passes.
 template <typename Pos>
 __device__ __forceinline__ uint32_t wave_exact_cut(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* pos_cut) {
     uint32_t ties, eq;
@@ -292,9 +333,7 @@ __device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* 
         const int hi = 32 - cp;
         const int width = hi < 8 ? hi : 8;
         const int shift = hi - width;
-        const uint32_t dmask = (1u << width) - 1u;
-        const uint32_t pm = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
-        wave_hist<false>(rb, n, 0u, pm, pv, shift, dmask);
+        wave_hist_top(rb, n, shift, width);
         uint32_t above, inb;
         const uint32_t b = wave_find_bin(rb, want, &above, &inb);
         lo_edge = pv | (b << shift);
@@ -305,7 +344,8 @@ __device__ int wave_compact(const RowBuf<Pos>& rb, int n, uint32_t K, uint32_t* 
     }
     uint32_t kappa = 0, pos_cut = 0;
     if (exact) kappa = wave_exact_cut(rb, n, K, &pos_cut);
-    const int kept = wave_keep_pass(rb, n, exact, kappa, pos_cut, lo_edge, (int32_t*)nullptr, (float*)nullptr, 0);
+    const int kept = exact ? wave_keep_inplace<true>(rb, n, kappa, pos_cut, 0u)
+                           : wave_keep_inplace<false>(rb, n, 0u, 0u, lo_edge);
     const uint32_t fl = exact ? kappa : lo_edge;
     *thr = fl == 0u ? 0u : fl - 1u;
     if (spec) *spec = !exact && want < K;
@@ -324,15 +364,13 @@ __device__ int wave_floor(const RowBuf<Pos>& rb, int n, uint32_t r, uint32_t* fl
         const int hi = 32 - cp;
         const int width = hi < 8 ? hi : 8;
         const int shift = hi - width;
-        const uint32_t dmask = (1u << width) - 1u;
-        const uint32_t pm = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
-        wave_hist<false>(rb, n, 0u, pm, pv, shift, dmask);
+        wave_hist_top(rb, n, shift, width);
         uint32_t above, inb;
         const uint32_t b = wave_find_bin(rb, r, &above, &inb);
         lo_edge = pv | (b << shift);
     }
     *floor_key = lo_edge;
-    return wave_keep_pass(rb, n, false, 0u, 0u, lo_edge, (int32_t*)nullptr, (float*)nullptr, 0);
+    return wave_keep_inplace<false>(rb, n, 0u, 0u, lo_edge);
 }
 
 // Writes the exact top K of the buffer by (key desc, position asc) -- or all
@@ -354,7 +392,7 @@ __device__ void wave_emit(const RowBuf<Pos>& rb, int n, int K, int32_t* idx, flo
     }
     uint32_t pos_cut;
     const uint32_t kappa = wave_exact_cut(rb, n, (uint32_t)K, &pos_cut);
-    wave_keep_pass<Pos, P17>(rb, n, true, kappa, pos_cut, 0u, idx, val, K);
+    wave_keep_out<Pos, P17>(rb, n, kappa, pos_cut, idx, val, K);
 }
 
 }  // namespace
