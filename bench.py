@@ -33,21 +33,21 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # HBM traffic per launch from two rocprofv3 counter passes (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch) over `bench.py --steps 2 --warmup 1
 # --no-cpu-baseline --copy-calibration`.  Each counter is scaled by what it
-# reads for a 1 GiB device-to-device copy (FETCH_SIZE 524317.4 KiB, WRITE_SIZE
+# reads for a 1 GiB device-to-device copy (FETCH_SIZE 524315.5 KiB, WRITE_SIZE
 # 1048576.0 KiB).  A record applies only while the kernel's sources hash to
 # the value it was taken at; otherwise traffic is reported as null.
-COPY_FETCH_FACTOR = 1048576.0 / 524317.4
+COPY_FETCH_FACTOR = 1048576.0 / 524315.5
 COPY_WRITE_FACTOR = 1048576.0 / 1048576.0
 _DECODE_SRC = ["csrc/decode_paged.hip", "csrc/select_row.h", "csrc/common.h", "csrc/kernels.h", "build.py"]
-_DECODE_SHA = "486482f959c2ea336bac6cb25341f2e87ba929a209b8742dc66d2be3dc34cd2b"
+_DECODE_SHA = "2e1c3a309b99f262892d2cc7f4ca31ef6c3ea26634aff37feba04cb3f117d4a8"
 COUNTERS = {
     "prefill": {"sources": ["csrc/prefill_ws.hip", "csrc/rowbuf.h", "csrc/varlen.h", "csrc/common.h", "csrc/kernels.h",
                             "build.py"],
-                "sha256": "81e18caa2c04172506961b0731c686bda3c95ad159ee43190f4fd1c7069ee931",
-                "fetch_kib": 281175.1, "write_kib": 524288.6},
+                "sha256": "154b40f3ff46fc904cbef78fa45fdc44411a0b11cf3f8c987f310bebe78b4535",
+                "fetch_kib": 255794.8, "write_kib": 524288.0},
     # main scan of one decode call (the sample kernel reads about 1/60 of it)
-    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 546046.0, "write_kib": 2381.9},
-    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 556913.8, "write_kib": 4105.3},
+    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 546095.9, "write_kib": 2378.8},
+    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 556935.9, "write_kib": 4101.5},
 }
 
 
