@@ -32,15 +32,15 @@
 //   with c = w / sqrt(D), then a cross-lane reduce-scatter leaves lane l with
 //   the score of key s0 + l.
 // Both keep a streaming top-k per wave: a per-row candidate buffer of
-// (key, position) pairs in LDS, filled in position order.  A score enters the
-// buffer only if its order-preserving key beats the row threshold.  When the
-// buffer nears capacity it is compacted: one radix digit below the buffer's
-// common key prefix locates the bin of the k-th largest key, the bin's lower
-// edge becomes the new threshold and everything below it is dropped (stable,
-// so the buffer stays in position order).  The buffer always holds every
-// entry that can still be in the row's top k.  At the end an exact radix
-// select over the buffer finds the k-th largest key and ties at that key go
-// to the lowest positions.
+// (key, position) pairs in LDS.  A score enters the buffer only if its
+// order-preserving key beats the row threshold.  When the buffer nears
+// capacity it is compacted: one radix digit below the buffer's common key
+// prefix locates the bin of the k-th largest key, the bin's lower edge
+// becomes the new threshold and everything below it is dropped.  The buffer
+// always holds every entry that can still be in the row's top k; its order
+// carries no meaning (ties are broken by the stored positions).  At the end
+// an exact radix select over the buffer finds the k-th largest key and ties
+// at that key go to the lowest positions.
 #include <type_traits>
 
 #include "common.h"
