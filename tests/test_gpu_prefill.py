@@ -170,6 +170,33 @@ def test_fused_floor_rescan_when_sample_holds_the_top(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_speculative_cut_rescan_when_early_keys_win(dtype):
+    """Key scores fall with position, so a long row's earliest keys are its
+    top k.  The sampled floor (strided chunks) is representative, but the
+    sequential scan then meets the best keys first: the buffer fills, and
+    the speculative cut -- sized for a row whose scanned keys hold k n_seen /
+    (t+1) of its top k -- drops some of them.  Fewer than k keys end above
+    the floor, the row is scanned again without speculation, and the
+    selection must still be exact."""
+    L, H, D, K = 8192, 16, 128, 2048
+    rng = np.random.default_rng(6100)
+    q0 = rng.standard_normal(D).astype(np.float32)
+    q = np.broadcast_to(q0, (1, L, H, D)).copy()
+    a = 2.0 * (1.0 - np.arange(L, dtype=np.float32) / L)
+    k = a[None, :, None] * q0[None, None, :] + 0.3 * rng.standard_normal((1, L, D)).astype(np.float32)
+    w = synth.softmax_weights(rng.standard_normal((1, L, H)))
+    if dtype == "fp8":
+        qc, qs = synth.quantize_fp8_rows(q)
+        kc, ks = synth.quantize_fp8_rows(k)
+        inp = dict(q=qc, q_scale=qs, k=kc, k_scale=ks, w=w, dtype="fp8")
+    else:
+        inp = dict(q=synth.to_bf16_bits(q), q_scale=None, k=synth.to_bf16_bits(k), k_scale=None, w=w,
+                   dtype="bf16")
+    rows = np.array([0, 2047, 2048, 4095, 4096, 6000, 7000, 8190, 8191])
+    parity(inp, K, rows=rows, name=f"early keys win {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_tie_heavy_long_rows_sampled(dtype):
     """Exact ties on long rows: ties at the k-th score go to the lowest
     positions even though the fp8 kernel scores a row's chunks out of order."""
