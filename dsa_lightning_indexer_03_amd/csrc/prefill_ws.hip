@@ -508,6 +508,32 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) slot[64 * j] = outv[j];
             };
+            // The steady-state iteration with its stage slot (i % 3) and ring
+            // slot ((i-1) % 2) known at compile time: every LDS address is a
+            // register base plus an immediate offset.
+            auto body_c = [&](int i, auto sc, auto rp) {
+                constexpr int SC = decltype(sc)::value;
+                constexpr int RP = decltype(rp)::value;
+                sb_prev = sb_cur;
+                ks_prev = ks_cur;
+                sb_cur = read_sb(SC);
+                ks_cur = read_ks(SC);
+                region(I3{}, T1{}, Bo1, sb_prev, acc, Pa, Bo0, SC, 0, false, no_extra);  // heads: chunk i-1, subtile 2
+                take(Pb, 1);
+                region(I0{}, T1{}, Bo0, sb_cur, acc, Pb, Bo1, SC, 1, false, no_extra);   // heads: chunk i-1, subtile 3
+                take(Pa, 2);
+                region(I1{}, T1{}, Bo1, sb_cur, acc, Pa, Bo0, SC, 2, false, no_extra);   // heads: chunk i, subtile 0
+                take(Pb, 3);
+                finish_scores();
+                region(I2{}, T1{}, Bo0, sb_cur, acc, Pb, Bo1, SC, 3, false,              // heads: chunk i, subtile 1
+                       [&] {
+                           float* slot = ring + (size_t)(RP * kWsRows + 2 * m) * 64 + lane;
+#pragma unroll
+                           for (int j = 0; j < 2; ++j) slot[64 * j] = outv[j];
+                       });
+                take(Pa, 0);
+                (void)i;
+            };
             auto body = [&](int i, bool pin) {
                 sb_prev = sb_cur;
                 ks_prev = ks_cur;
@@ -531,8 +557,25 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
             region(I2{}, T1{}, Bo0, sb_cur, acc, Pb, Bo1, 0, 3, true, no_extra);
             take(Pa, 0);
             __syncthreads();
-            s_cur = 1;
-            for (int i = 1; i < n_ch; ++i) {
+            // iterations 1 .. n_ch-1: six at a time (stage slots 1 2 0 1 2 0, ring
+            // slots 0 1 0 1 0 1), then the rest
+            int i = 1;
+            for (; i + 6 <= n_ch; i += 6) {
+                body_c(i, I1{}, I0{});
+                __syncthreads();
+                body_c(i + 1, I2{}, I1{});
+                __syncthreads();
+                body_c(i + 2, I0{}, I0{});
+                __syncthreads();
+                body_c(i + 3, I1{}, I1{});
+                __syncthreads();
+                body_c(i + 4, I2{}, I0{});
+                __syncthreads();
+                body_c(i + 5, I0{}, I1{});
+                __syncthreads();
+            }
+            s_cur = i % 3;
+            for (; i < n_ch; ++i) {
                 body(i, false);
                 __syncthreads();
                 s_cur = s_cur == 2 ? 0 : s_cur + 1;
