@@ -308,13 +308,18 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
     // (x % 8) ^ ((row >> 1) & 7) of that row; rows past the keys repeat key
     // Lk-1.  Wave 4 also copies the chunk's 64 adjusted scales, wave 5 its
     // E8M0 bytes (lanes 16..63 repeat them into the unused tail).
+    // Selection wave m copies pieces P and P + 2 (P = m % 2 + 4 (m / 2)):
+    // 16 rows apart, they share the swizzle, so the second piece sits 2048
+    // bytes after the first both in the chunk and in the stage, and one LDS
+    // base (M0) with an instruction offset serves both copies.
     const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(a.k);
     // this lane's two pieces: byte offset inside a 64-key chunk, and row
     uint32_t poff[2];
     int prow[2];
+    const int piece0 = (m & 1) + 4 * (m >> 1);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        const int x = 64 * (4 * r + m) + lane;
+        const int x = 64 * (piece0 + 2 * r) + lane;
         const int row = x >> 3;
         prow[r] = row;
         poff[r] = (uint32_t)(row * kD + 16 * ((x & 7) ^ ((row >> 1) & 7)));
@@ -326,11 +331,9 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
             // paged cache) plus the lane's fixed offsets
             const uint8_t* base = VARLEN ? kbytes + (size_t)a.block_table[(size_t)sg.b * a.max_pages + chunk] * (64 * kD)
                                          : kbytes + ((size_t)sg.b * a.L + (size_t)chunk * 64) * kD;
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-                __builtin_amdgcn_global_load_lds(base + poff[r],
-                                                 (__attribute__((address_space(3))) void*)(dst + 1024 * (4 * r + m)),
-                                                 16, 0, 0);
+            auto* ldst = (__attribute__((address_space(3))) void*)(dst + 1024 * piece0);
+            __builtin_amdgcn_global_load_lds(base + poff[0], ldst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(base + poff[0], ldst, 16, 2048, 0);  // piece P + 2
         } else {
             // the last chunk: rows past the keys repeat key Lk-1
 #pragma unroll
@@ -338,7 +341,7 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
                 const int rg = min(chunk * 64 + prow[r], sg.Lk - 1);
                 const uint8_t* src = kbytes + key_slot<VARLEN>(a, sg.b, rg) * kD + (poff[r] & (kD - 1));
                 __builtin_amdgcn_global_load_lds(src,
-                                                 (__attribute__((address_space(3))) void*)(dst + 1024 * (4 * r + m)),
+                                                 (__attribute__((address_space(3))) void*)(dst + 1024 * (piece0 + 2 * r)),
                                                  16, 0, 0);
             }
         }
@@ -654,17 +657,33 @@ prefill_ws_fp8_kernel(PrefillArgs a) {
                 for (int j = 0; j < 2; ++j) sc[j] = slot[64 * j];
                 fw_raw = flags[s_prev];
                 const int s = c * 64 + lane;
+                // both rows step by step, so that their dependency chains interleave
+                uint32_t wd[2];
+                bool app[2];
+                uint64_t msk[2];
+                int o[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) wd[j] = entry_word<P17>(sc[j], (uint32_t)s);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const bool valid = (s <= tp[j]) & (s < sg.Lk);
-                    const uint32_t wd = entry_word<P17>(sc[j], (uint32_t)s);
-                    const bool app = act[j] & valid & (wd > thr[j]);
-                    const uint64_t msk = wave_ballot(app);
-                    const int o = app ? nb[j] + lanes_below(msk) : CAP + lane;
-                    rb[j].key[o] = wd;
-                    rb[j].pos[o] = (Pos)s;
-                    nb[j] += __builtin_popcountll(msk);
-                    if (ROWS && act[j] && s < sg.Lk) srow[j][s] = valid ? sc[j] : -INFINITY;
+                    // last position the row appends (-1 while it is idle)
+                    const int lastp = act[j] ? min(tp[j], sg.Lk - 1) : -1;
+                    const bool above = wd[j] > thr[j], inrow = s <= lastp;
+                    app[j] = above & inrow;
+                    msk[j] = wave_ballot(above) & wave_ballot(inrow);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    int ob = nb[j] + lanes_below(msk[j]);
+                    asm volatile("" : "+v"(ob));  // computed by every lane: the select stays branch free
+                    o[j] = app[j] ? ob : CAP + lane;
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    rb[j].key[o[j]] = wd[j];
+                    rb[j].pos[o[j]] = (Pos)s;
+                    nb[j] += __builtin_popcountll(msk[j]);
+                    if (ROWS && act[j] && s < sg.Lk) srow[j][s] = s <= tp[j] ? sc[j] : -INFINITY;
                 }
                 c_sel = chunk_next(i - 1, c_sel);
             } else {
