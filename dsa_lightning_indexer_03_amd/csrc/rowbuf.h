@@ -191,6 +191,10 @@ __device__ __forceinline__ int wave_common_prefix(const RowBuf<Pos>& rb, int n, 
 // Exact `need`-th largest key of the buffer (1 <= need <= n): returns kappa;
 // *ties = how many entries equal to kappa belong to the top `need` (the rest
 // of the top are strictly greater); *eq = how many entries equal kappa.
+// Early end: when the entries of a digit's bin exactly fill the rest of the
+// top, kappa is that bin's lower edge and *ties = *eq = their count, so
+// "key > kappa, or key == kappa at any position" is again exactly the top
+// `need` (every key of the bin is >= its edge, every key below it is less).
 template <typename Pos>
 __device__ uint32_t wave_kth_key(const RowBuf<Pos>& rb, int n, uint32_t need, uint32_t* ties, uint32_t* eq) {
     uint32_t pv;
@@ -212,6 +216,7 @@ __device__ uint32_t wave_kth_key(const RowBuf<Pos>& rb, int n, uint32_t need, ui
         pv |= b << shift;
         pm |= dmask << shift;
         hi = shift;
+        if (need == inb) break;
     }
     *ties = need;
     *eq = inb;
@@ -373,8 +378,56 @@ __device__ int wave_floor(const RowBuf<Pos>& rb, int n, uint32_t r, uint32_t* fl
     return wave_keep_inplace<false>(rb, n, 0u, 0u, lo_edge);
 }
 
+// One pass that splits the buffer at the radix bin `bdig` (the value of
+// key >> shift, prefix and digit): entries above the bin -- and, with
+// `fill`, those in it -- go to the output row (idx/val from slot 0, in
+// buffer order of a step's slots); without `fill`, the bin's entries move to
+// the buffer front in place (as in wave_keep_inplace, dropped lanes writing
+// a slot of their own in the histogram words).  Returns how many moved.
+template <typename Pos, bool P17>
+__device__ int wave_split_out(const RowBuf<Pos>& rb, int n, int shift, uint32_t bdig, bool fill, int32_t* idx,
+                              float* val) {
+    const int l = lane_id();
+    uint32_t* const dk = rb.hist + l;
+    Pos* const dp = reinterpret_cast<Pos*>(rb.hist + kWave) + l;
+    int wpos = 0, opos = 0;
+    for (int j0 = 0; j0 < n; j0 += 256) {
+        const int j = j0 + 4 * l;
+        const v4u k = *reinterpret_cast<const v4u*>(rb.key + j);
+        const Pos4<Pos> p = read_pos4(rb.pos + j);
+        const bool full = j0 + 256 <= n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool in = full | (j + e < n);
+            const uint32_t d = k[e] >> shift;
+            const bool out = in & ((d > bdig) | (fill & (d == bdig)));
+            const bool keep = in & (!fill) & (d == bdig);
+            const uint64_t mo = wave_ballot(out);
+            if (out) {
+                const int o = opos + lanes_below(mo);
+                idx[o] = entry_pos<P17>(k[e], (uint32_t)p.v[e]);
+                if (val) val[o] = entry_score<P17>(k[e]);
+            }
+            opos += __builtin_popcountll(mo);
+            const uint64_t mk = wave_ballot(keep);
+            const int w = wpos + lanes_below(mk);
+            *(keep ? rb.key + w : dk) = k[e];
+            *(keep ? rb.pos + w : dp) = p.v[e];
+            wpos += __builtin_popcountll(mk);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    return wpos;
+}
+
 // Writes the exact top K of the buffer by (key desc, position asc) -- or all
 // of it when n <= K -- to the output row, then the -1 / -inf padding.
+//
+// Three passes over the buffer: the keys' common prefix, the histogram of
+// the digit below it, then one pass that writes every entry above the bin
+// holding the K-th key and gathers that bin's entries at the buffer front.
+// The rest of the row is the exact top (K - above) of the bin, selected
+// over those few entries alone.
 template <typename Pos, bool P17 = false>
 __device__ void wave_emit(const RowBuf<Pos>& rb, int n, int K, int32_t* idx, float* val) {
     const int l = lane_id();
@@ -390,9 +443,26 @@ __device__ void wave_emit(const RowBuf<Pos>& rb, int n, int K, int32_t* idx, flo
         }
         return;
     }
+    uint32_t pv;
+    const int cp = wave_common_prefix(rb, n, &pv);
+    int n2 = n;
+    uint32_t above = 0u;
+    if (cp < 32) {
+        const int hi = 32 - cp;
+        const int width = hi < 8 ? hi : 8;
+        const int shift = hi - width;
+        wave_hist_top(rb, n, shift, width);
+        uint32_t inb;
+        const uint32_t b = wave_find_bin(rb, (uint32_t)K, &above, &inb);
+        const bool fill = above + inb == (uint32_t)K;
+        n2 = wave_split_out<Pos, P17>(rb, n, shift, (pv >> shift) | b, fill, idx, val);
+        if (fill) return;
+    }
+    // all keys equal (cp == 32): the K lowest positions, over the whole buffer
+    const uint32_t need = (uint32_t)K - above;
     uint32_t pos_cut;
-    const uint32_t kappa = wave_exact_cut(rb, n, (uint32_t)K, &pos_cut);
-    wave_keep_out<Pos, P17>(rb, n, kappa, pos_cut, idx, val, K);
+    const uint32_t kappa = wave_exact_cut(rb, n2, need, &pos_cut);
+    wave_keep_out<Pos, P17>(rb, n2, kappa, pos_cut, idx + above, val ? val + above : nullptr, (int)need);
 }
 
 }  // namespace
