@@ -33,18 +33,18 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # HBM traffic per launch from two rocprofv3 counter passes (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch) over `bench.py --steps 2 --warmup 1
 # --no-cpu-baseline --copy-calibration`.  Each counter is scaled by what it
-# reads for a 1 GiB device-to-device copy (FETCH_SIZE 524315.5 KiB, WRITE_SIZE
+# reads for a 1 GiB device-to-device copy (FETCH_SIZE 524315.4 KiB, WRITE_SIZE
 # 1048576.0 KiB).  A record applies only while the kernel's sources hash to
 # the value it was taken at; otherwise traffic is reported as null.
-COPY_FETCH_FACTOR = 1048576.0 / 524315.5
+COPY_FETCH_FACTOR = 1048576.0 / 524315.4
 COPY_WRITE_FACTOR = 1048576.0 / 1048576.0
 _DECODE_SRC = ["csrc/decode_paged.hip", "csrc/select_row.h", "csrc/common.h", "csrc/kernels.h", "build.py"]
 _DECODE_SHA = "2e1c3a309b99f262892d2cc7f4ca31ef6c3ea26634aff37feba04cb3f117d4a8"
 COUNTERS = {
     "prefill": {"sources": ["csrc/prefill_ws.hip", "csrc/rowbuf.h", "csrc/varlen.h", "csrc/common.h", "csrc/kernels.h",
                             "build.py"],
-                "sha256": "4d209e237581bf6693cbe342ef201fb92c5df5dc23709ea9ccbce138a06a602b",
-                "fetch_kib": 282972.7, "write_kib": 524288.0},
+                "sha256": "2656a5a8c175dc5c49fd05abbb05ad29a4303095500848da57288ccea7aedcc3",
+                "fetch_kib": 255993.1, "write_kib": 524323.6},
     # main scan of one decode call (the sample kernel reads about 1/60 of it)
     "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 546143.8, "write_kib": 2377.3},
     "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 557011.9, "write_kib": 4109.6},
