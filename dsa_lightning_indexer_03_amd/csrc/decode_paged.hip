@@ -60,6 +60,10 @@ constexpr int kPrefixLds = 2048;   // queries whose page prefix is searched in L
 constexpr int kSampleStride = 32;                       // at most one sampled page in this many
 constexpr int kMaxSamplePages = DSAIDX_SAMPLE_PAGES;    // sampled pages of one query, at most
 constexpr int kCandBuf = 1024;     // per-wave LDS candidate buffer (score, position) pairs
+#ifndef DSAIDX_PRODUCER_PAGES
+#define DSAIDX_PRODUCER_PAGES 24
+#endif
+constexpr int kProducerPages = DSAIDX_PRODUCER_PAGES;  // fused scan: pages' worth of time spent sampling a query
 
 #ifndef DSAIDX_DECODE_NT
 #define DSAIDX_DECODE_NT 0  // 1: non-temporal (streaming) loads of the key cache
@@ -202,14 +206,15 @@ decode_prologue_kernel(DecodeArgs a) {
 }
 
 constexpr int kSfThreads = 512;  // sample-and-floor workgroup
-constexpr int kSfWaves = kSfThreads / kWave;
 
-// Bin of the 2048-bin LDS histogram h (kSfThreads threads) where the count
-// from the top reaches r; also the count in the bins above it.  With r == 0
-// it returns the total count in *above and bin -1.
+// Bin of the 2048-bin LDS histogram h (NT threads) where the count from the
+// top reaches r; also the count in the bins above it.  With r == 0 it
+// returns the total count in *above and bin -1.
+template <int NT>
 __device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint32_t* above, uint32_t* red) {
     const int t = threadIdx.x;
-    constexpr int kPer = kHistBins / kSfThreads;
+    constexpr int kSfWaves = NT / kWave;
+    constexpr int kPer = kHistBins / NT;
     const uint32_t* hl = h + kHistBins - kPer * (t + 1);  // thread t: bins from the top, ascending
     uint32_t loc = 0;
 #pragma unroll
@@ -247,28 +252,24 @@ __device__ __forceinline__ int bin_from_top(const uint32_t* h, uint32_t r, uint3
     return bin;
 }
 
-// Sample and floor of query b, one workgroup of kSfThreads per query.
-// 1. The query is staged in LDS; wave w scores the sampled pages w, w + 8,
+// Sample and floor of query b, by the calling workgroup of NT threads.
+// 1. The query is staged in LDS; wave w scores the sampled pages w, w + NW,
 //    ... (two pages of loads in flight, page ids preloaded one per lane) and
 //    keeps their score keys in LDS.
 // 2. The floor: the r-th largest valid sampled key cut to its top 22 bits
 //    (first digit by histogram, then the next 11 bits inside that bin), with
 //    r five standard deviations above the expected number of sampled scores
 //    at or above the query's k-th largest.
-// Writes the floor (word 2 of the query's counter block; 0 when the query is
-// not sampled or r exceeds its sample, so every score is a candidate) and
-// clears the candidate count (word 1) -- for every query.
-template <int HB>
-__global__ void __launch_bounds__(kSfThreads)
-decode_sample_floor_kernel(DecodeArgs a) {
-    __shared__ uint32_t skey[kMaxSamplePages * kPage];
-    __shared__ uint32_t h[kHistBins];
-    __shared__ __align__(16) uint16_t qsh[64 * kD];
-    __shared__ float csh[64];
-    __shared__ uint32_t red[kSfWaves + 2];
-    const int b = blockIdx.x, t = threadIdx.x;
+// Returns the floor key: 0 when the query is not sampled or r exceeds its
+// sample (every score is then a candidate); otherwise its low 10 bits are 0.
+// LDS: skey [kMaxSamplePages * kPage], h [kHistBins], qsh [64 * kD] bf16,
+// csh [64], red [NT / kWave + 2].
+template <int HB, int NT>
+__device__ __forceinline__ uint32_t sample_floor(const DecodeArgs& a, const int b, uint32_t* skey, uint32_t* h,
+                                                 uint16_t* qsh, float* csh, uint32_t* red) {
+    constexpr int NW = NT / kWave;
+    const int t = threadIdx.x;
     const int lane = lane_id(), wave = t / kWave;
-    uint32_t* ctrl = a.ctrl + (size_t)b * kCtrlStride;
     const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
     // The query goes to LDS once per workgroup, with coalesced 16-byte
     // loads issued before anything that depends on the context.  Row r's
@@ -276,24 +277,21 @@ decode_sample_floor_kernel(DecodeArgs a) {
     // below (16 rows, one piece column) touch distinct banks.
     constexpr int H = 16 * HB;
     constexpr int kQPieces = H * kD * 2 / 16;
-    constexpr int kQPer = (kQPieces + kSfThreads - 1) / kSfThreads;
+    constexpr int kQPer = (kQPieces + NT - 1) / NT;
     v4i qv[kQPer];
 #pragma unroll
     for (int i = 0; i < kQPer; ++i)
-        if (t + i * kSfThreads < kQPieces)
-            qv[i] = reinterpret_cast<const v4i*>(a.q + (size_t)b * H * kD)[t + i * kSfThreads];
+        if (t + i * NT < kQPieces)
+            qv[i] = reinterpret_cast<const v4i*>(a.q + (size_t)b * H * kD)[t + i * NT];
     const float wv = t < H ? a.w[(size_t)b * H + t] * a.inv_sqrt_d : 0.f;
     const SamplePlan sp = sample_plan(b, ctx, a.topk);
-    if (sp.ns == 0) {
-        if (t == 0) { ctrl[1] = 0u; ctrl[2] = 0u; }
-        return;
-    }
-    // wave w scores the sampled pages w + 8 j, j < npw; their page ids sit
+    if (sp.ns == 0) return 0u;
+    // wave w scores the sampled pages w + NW j, j < npw; their page ids sit
     // one per lane (lane j), so no page load waits on a table read
-    constexpr int kPerWave = (kMaxSamplePages + kSfWaves - 1) / kSfWaves;
+    constexpr int kPerWave = (kMaxSamplePages + NW - 1) / NW;
     static_assert(kPerWave <= kWave, "page ids must fit one per lane");
-    const int npw = wave < sp.ns ? (sp.ns - wave + kSfWaves - 1) / kSfWaves : 0;
-    const int mine = wave + kSfWaves * lane;
+    const int npw = wave < sp.ns ? (sp.ns - wave + NW - 1) / NW : 0;
+    const int mine = wave + NW * lane;
     const int pid = (lane < kPerWave && mine < sp.ns)
                         ? a.block_table[(size_t)b * a.max_pages + sp.off + (size_t)sp.stride * mine] : 0;
     const int n = lane & 15, g = lane >> 4;
@@ -307,7 +305,7 @@ decode_sample_floor_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < kQPer; ++i) {
-        const int pc = t + i * kSfThreads;
+        const int pc = t + i * NT;
         if (pc < kQPieces) reinterpret_cast<v4i*>(qsh)[(pc & ~15) | ((pc ^ (pc >> 4)) & 15)] = qv[i];
     }
     if (t < H) csh[t] = wv;
@@ -328,10 +326,10 @@ decode_sample_floor_kernel(DecodeArgs a) {
             for (int i = 0; i < 4; ++i) c[hb][i] = csh[16 * hb + 4 * g + i];
         }
         for (int j = 0;; j += 2) {
-            skey[(wave + kSfWaves * j) * kPage + lane] = score_key(page_scores<HB>(A, c, p0, k0));
+            skey[(wave + NW * j) * kPage + lane] = score_key(page_scores<HB>(A, c, p0, k0));
             if (j + 1 >= npw) break;
             load_page(a, page_at(j + 2), lane_off, lane, p0, k0);  // (again the last page past the end)
-            skey[(wave + kSfWaves * (j + 1)) * kPage + lane] = score_key(page_scores<HB>(A, c, p1, k1));
+            skey[(wave + NW * (j + 1)) * kPage + lane] = score_key(page_scores<HB>(A, c, p1, k1));
             if (j + 2 >= npw) break;
             load_page(a, page_at(j + 3), lane_off, lane, p1, k1);
         }
@@ -344,9 +342,9 @@ decode_sample_floor_kernel(DecodeArgs a) {
     // pass over the sample: histogram of digit (key >> shift) & 2047 of the
     // keys whose top bits (key >> 21) equal `sel` (all keys when sel < 0)
     auto pass = [&](int shift, int sel) {
-        for (int i = t; i < kHistBins; i += kSfThreads) h[i] = 0u;
+        for (int i = t; i < kHistBins; i += NT) h[i] = 0u;
         __syncthreads();  // (the first time: also every sampled key is in LDS)
-        for (int e = t; e < n_all; e += kSfThreads) {
+        for (int e = t; e < n_all; e += NT) {
             const uint32_t kk = skey[e];
             if (valid(e) && (sel < 0 || (int)(kk >> 21) == sel)) atomicAdd(&h[(kk >> shift) & (kHistBins - 1)], 1u);
         }
@@ -354,19 +352,42 @@ decode_sample_floor_kernel(DecodeArgs a) {
     };
     pass(21, -1);
     uint32_t m = 0;
-    bin_from_top(h, 0, &m, red);
+    bin_from_top<NT>(h, 0, &m, red);
     const float ex = (float)m * (float)a.topk / (float)ctx;
     const uint32_t r = (uint32_t)ceilf(ex + 5.f * sqrtf(ex) + 8.f);
     uint32_t fl = 0u;
     if (r < m) {
         uint32_t above1 = 0;
-        const int bin1 = bin_from_top(h, r, &above1, red);
+        const int bin1 = bin_from_top<NT>(h, r, &above1, red);
         pass(10, bin1);
         uint32_t above2 = 0;
-        const int bin2 = bin_from_top(h, r - above1, &above2, red);
+        const int bin2 = bin_from_top<NT>(h, r - above1, &above2, red);
         fl = ((uint32_t)bin1 << 21) | ((uint32_t)bin2 << 10);
     }
-    if (t == 0) { ctrl[1] = 0u; ctrl[2] = fl; }
+    return fl;
+}
+
+// Sample and floor of query b, one workgroup of kSfThreads per query (the
+// three-kernel form of the step, for batches too large for the fused scan).
+// Writes the floor (word 2 of the query's counter block) and clears the
+// candidate count (word 1) and the unfiltered-flush flag (word 3) -- for
+// every query.
+template <int HB>
+__global__ void __launch_bounds__(kSfThreads)
+decode_sample_floor_kernel(DecodeArgs a) {
+    __shared__ uint32_t skey[kMaxSamplePages * kPage];
+    __shared__ uint32_t h[kHistBins];
+    __shared__ __align__(16) uint16_t qsh[64 * kD];
+    __shared__ float csh[64];
+    __shared__ uint32_t red[kSfThreads / kWave + 2];
+    const int b = blockIdx.x;
+    const uint32_t fl = sample_floor<HB, kSfThreads>(a, b, skey, h, qsh, csh, red);
+    if (threadIdx.x == 0) {
+        uint32_t* ctrl = a.ctrl + (size_t)b * kCtrlStride;
+        ctrl[1] = 0u;
+        ctrl[2] = fl;
+        ctrl[3] = 0u;
+    }
 }
 
 // The main scan.  A persistent grid (one resident round of workgroups): the
@@ -381,10 +402,24 @@ decode_sample_floor_kernel(DecodeArgs a) {
 // buffer, flushed to the query's candidate list.  The page prefix over
 // queries is built in LDS from the context lengths (or read from the
 // prologue's output for very large batches).
-template <int HB>
+//
+// FUSED: the sampling runs inside this grid instead of a kernel before it.
+// Workgroup b < B first samples query b and publishes its floor in word 2 of
+// the query's counter block with an agent-scope atomic store (floor | 1: the
+// floor's low 10 bits are zero, bit 0 marks it published; the words were
+// cleared before the launch).  Its share of pages is smaller by about the
+// time that takes (kProducerPages).  A wave entering a query reads that word
+// with an agent-scope atomic load and, until it finds the floor published,
+// keeps every valid score in its buffer, polling once per page; once the
+// floor is there it filters the buffer in place and goes on as usual.  A
+// buffer that must be flushed (full, or the wave leaves the query) before
+// the floor is known is flushed unfiltered and the query is marked (word 3),
+// so the final kernel's verification counts only the candidates at or above
+// the floor.  Nothing ever waits on another workgroup.
+template <int HB, bool FUSED>
 __global__ void __launch_bounds__(kThreadsDec)
 decode_scan_kernel(DecodeArgs a) {
-    __shared__ uint32_t lds_wave[kThreadsDec / kWave][2 * kCandBuf];  // candidate buffer
+    __shared__ __align__(16) uint32_t lds_wave[kThreadsDec / kWave][2 * kCandBuf];  // candidate buffer
     __shared__ int32_t prefix_lds[kPrefixLds];
     __shared__ uint32_t wtot[kThreadsDec / kWave];
     constexpr int NW = kThreadsDec / kWave;
@@ -394,14 +429,40 @@ decode_scan_kernel(DecodeArgs a) {
     float* cbuf_s = reinterpret_cast<float*>(lds_wave[wave]);
     int32_t* cbuf_p = reinterpret_cast<int32_t*>(lds_wave[wave] + kCandBuf);
 
+    if constexpr (FUSED) {
+        // The producer's sample borrows the candidate buffers' LDS: keys,
+        // histogram and the staged query fill exactly its 32 KB.
+        static_assert(kMaxSamplePages * kPage + kHistBins + 64 * kD / 2 <= NW * 2 * kCandBuf, "sample LDS");
+        __shared__ float csh[64];
+        __shared__ uint32_t red[NW + 2];
+        if ((int)blockIdx.x < a.B) {
+            uint32_t* base = &lds_wave[0][0];
+            const uint32_t fl = sample_floor<HB, kThreadsDec>(a, (int)blockIdx.x, base, base + kMaxSamplePages * kPage,
+                                                              reinterpret_cast<uint16_t*>(base + kMaxSamplePages * kPage + kHistBins),
+                                                              csh, red);
+            if (threadIdx.x == 0)
+                __hip_atomic_store(a.ctrl + (size_t)blockIdx.x * kCtrlStride + 2, fl | 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();  // the LDS goes back to the candidate buffers
+        }
+    }
+
+    // FUSED: sampled queries below this workgroup's index and the next, and in all
+    __shared__ uint32_t hred[3][NW];
+    uint32_t h_lo = 0, h_hi = 0, h_all = 0;
     const bool pre_in_lds = a.B + 1 <= kPrefixLds;
     if (pre_in_lds) {
         // exclusive prefix of the per-query page counts, 256 queries a round
         int carry = 0;
         for (int b0 = 0; b0 <= a.B; b0 += kThreadsDec) {
             const int b = b0 + (int)threadIdx.x;
-            const uint32_t np = b < a.B ? (uint32_t)((clamp_ctx(a.context_lens[b], a.max_ctx) + kPage - 1) / kPage)
-                                        : 0u;
+            const int ctxb = b < a.B ? clamp_ctx(a.context_lens[b], a.max_ctx) : 0;
+            const uint32_t np = (uint32_t)((ctxb + kPage - 1) / kPage);
+            if (FUSED && b < a.B && sample_plan(b, ctxb, a.topk).ns > 0) {
+                ++h_all;
+                h_lo += b < (int)blockIdx.x;
+                h_hi += b < (int)blockIdx.x + 1;
+            }
             const uint32_t ip = wave_incl_scan(np);
             if (lane == kWave - 1) wtot[wave] = ip;
             __syncthreads();
@@ -419,8 +480,27 @@ decode_scan_kernel(DecodeArgs a) {
     auto prefix_at = [&](int i) -> int { return pre_in_lds ? prefix_lds[i] : a.prefix[i]; };
     const int P = prefix_at(a.B);
     const int64_t G = gridDim.x;
-    const int share_begin = (int)((int64_t)blockIdx.x * P / G);
-    const int share_end = (int)((int64_t)(blockIdx.x + 1) * P / G);
+    int share_begin, share_end;
+    if constexpr (FUSED) {
+        // Shares weighted 1 - d for the workgroups that sampled a query (d =
+        // kProducerPages / mean share, in 1/1024, at most 0.88), 1 for the rest:
+        // boundary j = P (j - d H_j) / (G - d H_G), H_j = sampled queries < j.
+        const uint32_t v[3] = {wave_sum(h_lo), wave_sum(h_hi), wave_sum(h_all)};
+        if (lane == 0)
+            for (int i = 0; i < 3; ++i) hred[i][wave] = v[i];
+        __syncthreads();
+        int64_t hs[3] = {0, 0, 0};
+        for (int i = 0; i < 3; ++i)
+            for (int w = 0; w < NW; ++w) hs[i] += hred[i][w];
+        int64_t dq = P > 0 ? (int64_t)kProducerPages * 1024 * G / P : 0;
+        if (dq > 900) dq = 900;
+        const int64_t den = G * 1024 - dq * hs[2];
+        share_begin = (int)((int64_t)P * ((int64_t)blockIdx.x * 1024 - dq * hs[0]) / den);
+        share_end = (int)((int64_t)P * ((int64_t)(blockIdx.x + 1) * 1024 - dq * hs[1]) / den);
+    } else {
+        share_begin = (int)((int64_t)blockIdx.x * P / G);
+        share_end = (int)((int64_t)(blockIdx.x + 1) * P / G);
+    }
     // this wave's pages: share_begin + wave + NW*k for k < nk
     const int nk = share_end - share_begin - wave > 0 ? (share_end - share_begin - wave + NW - 1) / NW : 0;
     if (nk == 0) return;
@@ -462,6 +542,39 @@ decode_scan_kernel(DecodeArgs a) {
     uint32_t floor_key = 0u;  // candidates have key >= floor_key
     int nbuf = 0;             // entries in the wave's candidate buffer
     uint32_t* cand_n = a.ctrl + 1;  // word 1 of each query's counter block
+    // FUSED: whether the current query's floor is known
+    bool fready = !FUSED;
+    auto floor_word = [&](int qb) -> uint32_t {
+        return __hip_atomic_load(a.ctrl + (size_t)qb * kCtrlStride + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // keep the buffer's entries whose key reaches fk, in place and in order
+    auto compact = [&](uint32_t fk) {
+        int o = 0;
+        for (int j0 = 0; j0 < nbuf; j0 += kWave) {
+            const int j = j0 + lane;
+            float sc = 0.f;
+            int32_t ps = 0;
+            bool keep = false;
+            if (j < nbuf) {
+                sc = cbuf_s[j];
+                ps = cbuf_p[j];
+                keep = score_key(sc) >= fk;
+            }
+            const uint64_t m = wave_ballot(keep);
+            if (keep) {
+                const int d = o + lanes_below(m);  // d <= j: every entry of this step was read above
+                cbuf_s[d] = sc;
+                cbuf_p[d] = ps;
+            }
+            o += __builtin_popcountll(m);
+        }
+        __builtin_amdgcn_wave_barrier();
+        nbuf = o;
+    };
+    // a flush before the floor is known writes every valid score: mark the query
+    auto mark_unfiltered = [&](int qb) {
+        if (FUSED && !fready && nbuf > 0 && lane == 0) a.ctrl[(size_t)qb * kCtrlStride + 3] = 1u;
+    };
     auto flush_cand = [&](int qb) {
         if (nbuf == 0) return;
         uint32_t base = 0;
@@ -489,6 +602,11 @@ decode_scan_kernel(DecodeArgs a) {
         const int i = k & 63;
         const int pb = __builtin_amdgcn_readlane(cq, i);
         const int ppos = __builtin_amdgcn_readlane(cpos, i);
+        // FUSED, floor not yet known: poll it now, read the answer after this
+        // page's scores (issued ahead of the next prefetch, so that wait covers
+        // one page fewer in flight, only on these few steps)
+        uint32_t fpoll = 0u;
+        if (FUSED && !fready && pb == qcur) fpoll = floor_word(qcur);
         {
             // Unconditional, so every path issues the same loads and the wait
             // for `cur` can leave two pages in flight; past the end of the
@@ -502,20 +620,41 @@ decode_scan_kernel(DecodeArgs a) {
             describe(k + 65, nq, npos, npid);
         }
         if (pb != qcur) {  // entering a new query
-            if (qcur >= 0) flush_cand(qcur);
+            if (qcur >= 0) {
+                mark_unfiltered(qcur);
+                flush_cand(qcur);
+            }
             qcur = pb;
             ctx_cur = clamp_ctx(a.context_lens[pb], a.max_ctx);
             load_query<HB>(a, pb, n, g, A, c);
-            floor_key = a.ctrl[(size_t)pb * kCtrlStride + 2];
+            const uint32_t fw = FUSED ? floor_word(pb) : a.ctrl[(size_t)pb * kCtrlStride + 2];
             // Settle the query loads here, on this rare path: otherwise the
             // common path after it inherits their pending count and waits
             // for every page load in flight at each step.
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            if constexpr (FUSED) {
+                fready = (fw & 1u) != 0u;
+                floor_key = fready ? (fw & ~1u) : 0u;
+            } else {
+                floor_key = fw;
+            }
         }
         const float score = page_scores<HB>(A, c, cur, ks_c);
         const int s = ppos + lane;
         const uint32_t key = score_key(score);
-        if (nbuf > kCandBuf - kWave) flush_cand(qcur);
+        if (FUSED && !fready && pb == qcur) {
+            // the asm keeps the read of the polled word (and its wait) on this path
+            asm volatile("" : "+v"(fpoll));
+            if (fpoll & 1u) {  // the floor came out: filter what is buffered
+                fready = true;
+                floor_key = fpoll & ~1u;
+                compact(floor_key);
+            }
+        }
+        if (nbuf > kCandBuf - kWave) {
+            mark_unfiltered(qcur);
+            flush_cand(qcur);
+        }
         const bool take = s < ctx_cur && key >= floor_key;
         const uint64_t m = wave_ballot(take);
         if (take) {
@@ -535,7 +674,10 @@ decode_scan_kernel(DecodeArgs a) {
         if (k + 1 < nk) step(k + 1, b1, k1, b0, k0);
         if (k + 2 < nk) step(k + 2, b2, k2, b1, k1);
     }
-    if (qcur >= 0) flush_cand(qcur);
+    if (qcur >= 0) {
+        mark_unfiltered(qcur);
+        flush_cand(qcur);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // the final page prefetches (unused) settle before exit
 }
 
@@ -556,7 +698,23 @@ decode_finish_kernel(DecodeArgs a, SelectArgs sa) {
     uint32_t* cnt = a.ctrl + (size_t)b * kCtrlStride + 1;
     const uint32_t need = (uint32_t)min(a.topk, ctx);
     int n_known = (int)*cnt;
-    if ((uint32_t)n_known < need) {
+    bool rescore = (uint32_t)n_known < need;
+    if (!rescore && a.ctrl[(size_t)b * kCtrlStride + 3] != 0u) {
+        // Some candidates were flushed before the floor was known: only
+        // those at or above the floor prove the selection exact.
+        const uint32_t fk = a.ctrl[(size_t)b * kCtrlStride + 2] & ~1u;
+        const float* cs = a.cand_score + (size_t)b * a.cand_stride;
+        uint32_t c = 0;
+        for (int j = t; j < n_known; j += sel::kThreads) c += score_key(cs[j]) >= fk ? 1u : 0u;
+        if (t == 0) sh.above = 0u;
+        __syncthreads();
+        c = wave_sum(c);
+        if (lane_id() == 0) atomicAdd(&sh.above, c);
+        __syncthreads();
+        rescore = sh.above < need;
+        __syncthreads();
+    }
+    if (rescore) {
         // the query and its head coefficients, in the selector's LDS (free until it runs)
         float* qs = reinterpret_cast<float*>(sh.cand_key);  // [H][kD]
         float* cs = reinterpret_cast<float*>(sh.cand_pos);  // [H]
@@ -616,21 +774,23 @@ __global__ void zero_u32_kernel(uint32_t* p, size_t n) {
 template <int HB>
 hipError_t launch_decode_hb(const DecodeArgs& a_in, const SelectArgs& s, int64_t max_pages, hipStream_t stream) {
     DecodeArgs a = a_in;
-    hipLaunchKernelGGL(decode_sample_floor_kernel<HB>, dim3((unsigned)a.B), dim3(kSfThreads), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     // Main scan: one resident round of workgroups (occupancy queried once
-    // per process), never more workgroups than pages.
+    // per process; both forms of the scan have the same resources), never
+    // more workgroups than pages.
     static PerDevice<int> resident_once;
     int resident = 0;
-    e = resident_once.get(
+    hipError_t e = resident_once.get(
         [](int dev, int* v) {
-            int per_cu = 0, cus = 0;
+            int per_cu = 0, per_cu_f = 0, cus = 0;
             hipError_t r = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
             if (r != hipSuccess) return r;
-            r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)decode_scan_kernel<HB>,
+            r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)decode_scan_kernel<HB, false>,
                                                              kThreadsDec, 0);
             if (r != hipSuccess) return r;
+            r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_f, (const void*)decode_scan_kernel<HB, true>,
+                                                             kThreadsDec, 0);
+            if (r != hipSuccess) return r;
+            if (per_cu_f < per_cu) per_cu = per_cu_f;
             *v = (per_cu < 1 ? 1 : per_cu) * cus;
             return hipSuccess;
         },
@@ -639,7 +799,18 @@ hipError_t launch_decode_hb(const DecodeArgs& a_in, const SelectArgs& s, int64_t
     int64_t grid = resident;
     if (grid > max_pages) grid = max_pages;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(decode_scan_kernel<HB>, dim3((unsigned)grid), dim3(kThreadsDec), 0, stream, a);
+    // The sample runs inside the scan when at most half the grid samples
+    // (workgroup b < B samples query b) and the page prefix fits in LDS;
+    // otherwise a kernel of its own goes first.
+    const bool fused = (int64_t)a.B * 2 <= grid && a.B + 1 <= kPrefixLds;
+    if (fused) {
+        if ((e = launch_zero_u32(a.ctrl, (size_t)a.B * kCtrlStride, stream)) != hipSuccess) return e;
+        hipLaunchKernelGGL((decode_scan_kernel<HB, true>), dim3((unsigned)grid), dim3(kThreadsDec), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(decode_sample_floor_kernel<HB>, dim3((unsigned)a.B), dim3(kSfThreads), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((decode_scan_kernel<HB, false>), dim3((unsigned)grid), dim3(kThreadsDec), 0, stream, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     static PerDevice<int> lds_once;
     if ((e = set_lds_limit(lds_once, (const void*)decode_finish_kernel<HB>, (int)sizeof(sel::SelShared))) !=

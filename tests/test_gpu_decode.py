@@ -212,6 +212,15 @@ def test_constant_scores_long_context():
         assert np.all(gv[b] == 0.0)
 
 
+def test_batch_beyond_fused_sampling():
+    """300 sampled queries at H=64: more than half the scan's resident grid,
+    so the sample runs as a kernel of its own before the scan."""
+    rng = np.random.default_rng(573)
+    ctx = rng.integers(5000, 12000, size=300).tolist()
+    d = synth.decode_inputs(300, ctx, 64, 128, seed=573, permute=True)
+    parity(d, 512, "B=300 sampled", queries=list(range(0, 300, 5)) + [299])
+
+
 def test_batch_beyond_lds_prefix():
     """2100 queries: the scan's page prefix over queries no longer fits its
     LDS table and comes from global memory instead."""

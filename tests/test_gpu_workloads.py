@@ -81,6 +81,13 @@ def decode_run(n):
                                           dev(d["block_table"]), dev(d["context_lens"]), K,
                                           max_context_len=mcl, workspace=ws)
         torch.cuda.synchronize()
+        # per-query counter blocks after the candidate lists: word 1 the
+        # candidate count, word 3 set when candidates were flushed before the
+        # query's floor was known (then only those at or above it count)
+        stride = -(-mcl // 64) * 64
+        ctrl = host(ws[c["B"] * stride * 8:c["B"] * stride * 8 + c["B"] * 64 * 4]).view(np.uint32).reshape(c["B"], 64)
+        say(f"  candidates per query: mean {ctrl[:, 1].mean():.0f}, max {ctrl[:, 1].max()}; "
+            f"queries with unfiltered flushes: {int((ctrl[:, 3] != 0).sum())}")
         _CACHE[n] = (d, host(gi), host(gv))
     return _CACHE[n]
 
