@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 COPY_FETCH_FACTOR = 1048576.0 / 524315.4
 COPY_WRITE_FACTOR = 1048576.0 / 1048576.0
 _DECODE_SRC = ["csrc/decode_paged.hip", "csrc/select_row.h", "csrc/common.h", "csrc/kernels.h", "build.py"]
-_DECODE_SHA = "e967f1c21d5ddc397c33edea68fc9f3fff0e8ece0bea34ccc89112d1a9a1e7d6"
+_DECODE_SHA = "80194e1c6585a515301353fe27a58b9e09260ce13a5272989a9d7aacb6f2f937"
 COUNTERS = {
     "prefill": {"sources": ["csrc/prefill_ws.hip", "csrc/rowbuf.h", "csrc/varlen.h", "csrc/common.h", "csrc/kernels.h",
                             "build.py"],

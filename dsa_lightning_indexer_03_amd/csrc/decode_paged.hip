@@ -27,16 +27,19 @@
 // per 132 B read, interleaved with the cache reads, costs about a fifth of
 // the scan.  So the scan writes only candidates:
 //
-// 1. A sample-and-floor kernel, one workgroup per query, scores a strided
-//    sample of every long query's pages (one page in kSampleStride or
-//    sparser, at most kMaxSamplePages, from a per-query offset), keeps the
-//    score keys in LDS and takes the r-th largest sampled key to 22 bits (two
-//    radix digits) as the query's floor, with r five standard deviations
-//    above the expected number of sampled scores at or above the query's
-//    k-th largest.
+// 1. The sample: a strided sample of every long query's pages (one page in
+//    kSampleStride or sparser, at most kMaxSamplePages, from a per-query
+//    offset) is scored, its keys kept in LDS, and the r-th largest sampled
+//    key to 22 bits (two radix digits) becomes the query's floor, with r
+//    five standard deviations above the expected number of sampled scores at
+//    or above the query's k-th largest.  Workgroup b of the scan does this
+//    for query b before it scans (batches up to half the scan's grid; a
+//    kernel of its own, one workgroup per query, for larger batches).
 // 2. The main scan scores every position and writes only the scores whose
-//    key reaches the query's floor, to the query's candidate list.
-// 3. Verification: if at least min(k, context) scores reached the floor,
+//    key reaches the query's floor, to the query's candidate list (while a
+//    floor is still being sampled, a wave keeps the query's scores back, see
+//    the scan kernel).
+// 3. Verification: if at least min(k, context) candidates reach the floor,
 //    the k-th largest score is among them (and so is every score tied with
 //    it, since the floor is a key threshold), so the selection over the
 //    candidates is exact.  Otherwise a repair pass rescores the query in
