@@ -21,9 +21,10 @@
 // group beat one, four and eight -- registers against loads in flight --
 // and a grid-stride loop over fewer workgroups was slower).
 // The hardware conversion rounds to nearest even; values are clamped to
-// +-448 first, so none overflows.  The quotient is a correctly rounded
-// division: a reciprocal multiply would save ~12% of the time but can land
-// on the other side of a code midpoint.  HBM bound: per key 256 bytes
+// +-448 first, so none overflows.  The quotient must be the correctly
+// rounded one (a plain reciprocal multiply can land on the other side of a
+// code midpoint): one correctly rounded reciprocal per key and two fma
+// corrections per element give it (see the kernel).  HBM bound: per key 256 bytes
 // (bf16) or 512 (f32) of key and 8 of placement read, 132 written.
 #include "common.h"
 #include "kernels.h"
@@ -99,8 +100,32 @@ kcache_append_kernel(KcacheArgs a) {
             for (int d = 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 16));
             const float scale = m > 0.f ? m / 448.f : 1.f;
             float q[8];
+            if (scale >= 0x1p-80f && scale <= 0x1p+80f) {
+                // RN(x / scale) from y = RN(1 / scale) (one correctly rounded
+                // division per key): q0 = RN(x y) lies within 1.5 ulp of
+                // x / scale; one correction q1 = RN(q0 + r0 y) with the
+                // remainder r0 = x - scale q0 taken in an fma is within half an
+                // ulp plus a few 2^-24 ulp, so faithful; the remainder of a
+                // faithful quotient is exact, and one more correction from it
+                // gives the correctly rounded quotient (Markstein's theorem for
+                // a correctly rounded reciprocal).  No step overflows (|x y| <=
+                // 448.1) and the remainders stay off the subnormal grid for
+                // |x| >= 2^-100; below that the quotient is under 2^-19, whose
+                // E4M3 code is a signed zero on any path.  The sign is put back
+                // for x = -0, which the corrections turn into +0.
+                const float y = 1.f / scale;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) q[j] = fminf(fmaxf(x[u][j] / scale, -448.f), 448.f);
+                for (int j = 0; j < 8; ++j) {
+                    const float xv = x[u][j];
+                    const float q0 = xv * y;
+                    const float q1 = fmaf(fmaf(-scale, q0, xv), y, q0);
+                    const float q2 = fmaf(fmaf(-scale, q1, xv), y, q1);
+                    q[j] = fminf(fmaxf(__builtin_copysignf(q2, xv), -448.f), 448.f);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) q[j] = fminf(fmaxf(x[u][j] / scale, -448.f), 448.f);
+            }
             int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
             w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
             int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
