@@ -393,6 +393,21 @@ decode_sample_floor_kernel(DecodeArgs a) {
     }
 }
 
+// Fused scan: the query whose floor workgroup j samples (query b goes to
+// workgroup floor(b G / B), so the samplers spread evenly over the grid), or
+// -1.  Needs 2 B <= G.
+__device__ __forceinline__ int sampled_by(int j, int G, int B) {
+    const int b = (int)(((int64_t)j * B + G - 1) / G);
+    return (b < B && (int)((int64_t)b * G / B) == j) ? b : -1;
+}
+
+// Fused scan: a sampling workgroup's share is smaller by kProducerPages, as a
+// fraction of the mean share P / G in 1/1024 (at most 0.88).
+__device__ __forceinline__ int64_t dq_share(int P, int64_t G) {
+    const int64_t dq = P > 0 ? (int64_t)kProducerPages * 1024 * G / P : 0;
+    return dq > 900 ? 900 : dq;
+}
+
 // The main scan.  A persistent grid (one resident round of workgroups): the
 // global list of (query, page) pairs, query-major, is cut into equal
 // contiguous shares, one per workgroup, so ragged context lengths leave no
@@ -407,7 +422,7 @@ decode_sample_floor_kernel(DecodeArgs a) {
 // prologue's output for very large batches).
 //
 // FUSED: the sampling runs inside this grid instead of a kernel before it.
-// Workgroup b < B first samples query b and publishes its floor in word 2 of
+// Workgroup floor(b G / B) first samples query b and publishes its floor in word 2 of
 // the query's counter block with an agent-scope atomic store (floor | 1: the
 // floor's low 10 bits are zero, bit 0 marks it published; the words were
 // cleared before the launch).  Its share of pages is smaller by about the
@@ -438,34 +453,27 @@ decode_scan_kernel(DecodeArgs a) {
         static_assert(kMaxSamplePages * kPage + kHistBins + 64 * kD / 2 <= NW * 2 * kCandBuf, "sample LDS");
         __shared__ float csh[64];
         __shared__ uint32_t red[NW + 2];
-        if ((int)blockIdx.x < a.B) {
+        const int qs = sampled_by(blockIdx.x, gridDim.x, a.B);
+        if (qs >= 0) {
             uint32_t* base = &lds_wave[0][0];
-            const uint32_t fl = sample_floor<HB, kThreadsDec>(a, (int)blockIdx.x, base, base + kMaxSamplePages * kPage,
+            const uint32_t fl = sample_floor<HB, kThreadsDec>(a, qs, base, base + kMaxSamplePages * kPage,
                                                               reinterpret_cast<uint16_t*>(base + kMaxSamplePages * kPage + kHistBins),
                                                               csh, red);
             if (threadIdx.x == 0)
-                __hip_atomic_store(a.ctrl + (size_t)blockIdx.x * kCtrlStride + 2, fl | 1u, __ATOMIC_RELAXED,
+                __hip_atomic_store(a.ctrl + (size_t)qs * kCtrlStride + 2, fl | 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();  // the LDS goes back to the candidate buffers
         }
     }
 
-    // FUSED: sampled queries below this workgroup's index and the next, and in all
-    __shared__ uint32_t hred[3][NW];
-    uint32_t h_lo = 0, h_hi = 0, h_all = 0;
     const bool pre_in_lds = a.B + 1 <= kPrefixLds;
     if (pre_in_lds) {
         // exclusive prefix of the per-query page counts, 256 queries a round
         int carry = 0;
         for (int b0 = 0; b0 <= a.B; b0 += kThreadsDec) {
             const int b = b0 + (int)threadIdx.x;
-            const int ctxb = b < a.B ? clamp_ctx(a.context_lens[b], a.max_ctx) : 0;
-            const uint32_t np = (uint32_t)((ctxb + kPage - 1) / kPage);
-            if (FUSED && b < a.B && sample_plan(b, ctxb, a.topk).ns > 0) {
-                ++h_all;
-                h_lo += b < (int)blockIdx.x;
-                h_hi += b < (int)blockIdx.x + 1;
-            }
+            const uint32_t np = b < a.B ? (uint32_t)((clamp_ctx(a.context_lens[b], a.max_ctx) + kPage - 1) / kPage)
+                                        : 0u;
             const uint32_t ip = wave_incl_scan(np);
             if (lane == kWave - 1) wtot[wave] = ip;
             __syncthreads();
@@ -485,21 +493,18 @@ decode_scan_kernel(DecodeArgs a) {
     const int64_t G = gridDim.x;
     int share_begin, share_end;
     if constexpr (FUSED) {
-        // Shares weighted 1 - d for the workgroups that sampled a query (d =
-        // kProducerPages / mean share, in 1/1024, at most 0.88), 1 for the rest:
-        // boundary j = P (j - d H_j) / (G - d H_G), H_j = sampled queries < j.
-        const uint32_t v[3] = {wave_sum(h_lo), wave_sum(h_hi), wave_sum(h_all)};
-        if (lane == 0)
-            for (int i = 0; i < 3; ++i) hred[i][wave] = v[i];
-        __syncthreads();
-        int64_t hs[3] = {0, 0, 0};
-        for (int i = 0; i < 3; ++i)
-            for (int w = 0; w < NW; ++w) hs[i] += hred[i][w];
-        int64_t dq = P > 0 ? (int64_t)kProducerPages * 1024 * G / P : 0;
-        if (dq > 900) dq = 900;
-        const int64_t den = G * 1024 - dq * hs[2];
-        share_begin = (int)((int64_t)P * ((int64_t)blockIdx.x * 1024 - dq * hs[0]) / den);
-        share_end = (int)((int64_t)P * ((int64_t)(blockIdx.x + 1) * 1024 - dq * hs[1]) / den);
+        // The sampling workgroups (every G/B-th) get weight 1 - d, d =
+        // kProducerPages over the mean share (in 1/1024, at most 0.88), the
+        // others 1 + d B / (G - B), so the weights of each run of G/B
+        // workgroups still sum to G/B and the shares around them keep their
+        // usual edges (with whole runs per query, the query boundaries).
+        auto edge = [&](int64_t j) -> int {  // start of workgroup j's share
+            const int64_t c = (j * a.B + G - 1) / G;  // sampling workgroups below j
+            const int64_t num = j * 1024 * (G - a.B) - dq_share(P, G) * (c * (G - a.B) - (j - c) * a.B);
+            return (int)((int64_t)P * num / (G * 1024 * (G - a.B)));
+        };
+        share_begin = edge(blockIdx.x);
+        share_end = blockIdx.x + 1 == G ? P : edge(blockIdx.x + 1);
     } else {
         share_begin = (int)((int64_t)blockIdx.x * P / G);
         share_end = (int)((int64_t)(blockIdx.x + 1) * P / G);
