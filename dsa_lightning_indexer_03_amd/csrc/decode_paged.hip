@@ -32,9 +32,10 @@
 //    offset) is scored, its keys kept in LDS, and the r-th largest sampled
 //    key to 22 bits (two radix digits) becomes the query's floor, with r
 //    five standard deviations above the expected number of sampled scores at
-//    or above the query's k-th largest.  Workgroup b of the scan does this
-//    for query b before it scans (batches up to half the scan's grid; a
-//    kernel of its own, one workgroup per query, for larger batches).
+//    or above the query's k-th largest.  Workgroup floor(b G / B) of the
+//    scan's G does this for query b before it scans (batches up to half the
+//    scan's grid; a kernel of its own, one workgroup per query, for larger
+//    batches).
 // 2. The main scan scores every position and writes only the scores whose
 //    key reaches the query's floor, to the query's candidate list (while a
 //    floor is still being sampled, a wave keeps the query's scores back, see
@@ -422,8 +423,8 @@ __device__ __forceinline__ int64_t dq_share(int P, int64_t G) {
 // prologue's output for very large batches).
 //
 // FUSED: the sampling runs inside this grid instead of a kernel before it.
-// Workgroup floor(b G / B) first samples query b and publishes its floor in word 2 of
-// the query's counter block with an agent-scope atomic store (floor | 1: the
+// Workgroup floor(b G / B) first samples query b and publishes its floor in
+// word 2 of the query's counter block with an agent-scope atomic store (floor | 1: the
 // floor's low 10 bits are zero, bit 0 marks it published; the words were
 // cleared before the launch).  Its share of pages is smaller by about the
 // time that takes (kProducerPages).  A wave entering a query reads that word
