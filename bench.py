@@ -627,6 +627,45 @@ def main():
             torch.cuda.empty_cache()
         result["prefill_other"] = extra
 
+        # Long sequences: the fp8 kernel at its largest L (17-bit positions) and
+        # the unstaged bf16 kernel (L > 65536).  Inputs are drawn on the device
+        # with the recipe of the L=32768 and L=8192 workloads (no needles) and
+        # timed only; their parity is tested at L = 65536 / 66000.
+        longl = {}
+        g = torch.Generator(device=dev)
+        for name, L_l, fp8 in (("fp8_L131072", 131072, True), ("bf16_L98304", 98304, False)):
+            g.manual_seed(7)
+            H_l, D_l, K_l = 64, 128, 2048
+            w_l = torch.softmax(torch.randn(1, L_l, H_l, generator=g, device=dev, dtype=torch.float64), -1).float()
+            if fp8:
+                def quant(x):
+                    sc = x.abs().amax(-1, keepdim=True) / 448.0
+                    sc = torch.where(sc > 0, sc, torch.ones_like(sc))
+                    return (x / sc).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8), sc.squeeze(-1)
+                q_l, qs_l = quant(torch.randn(1, L_l, H_l, D_l, generator=g, device=dev))
+                k_l, ks_l = quant(torch.randn(1, L_l, D_l, generator=g, device=dev))
+            else:
+                q_l = torch.randn(1, L_l, H_l, D_l, generator=g, device=dev).to(torch.bfloat16)
+                k_l = torch.randn(1, L_l, D_l, generator=g, device=dev).to(torch.bfloat16)
+                qs_l = ks_l = None
+            torch.cuda.synchronize()
+
+            def lstep_p():
+                dsa.indexer_prefill(q_l, k_l, w_l, K_l, q_scale=qs_l, k_scale=ks_l)
+
+            tl = time_calls(torch, lstep_p, 3, 1, warm_seconds=0.0, samples=5)
+            pairs_l = L_l * (L_l + 1) // 2
+            tf = 2.0 * H_l * D_l * pairs_l / (tl["mean_ms"] * 1e-3) / 1e12
+            peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+            longl[name] = {"what": f"prefill B=1 L={L_l} H={H_l} D={D_l} k={K_l} {'fp8 e4m3' if fp8 else 'bf16'}, "
+                                   f"device-drawn N(0,1) inputs, softmax head weights",
+                           "ms_per_call": tl["mean_ms"], **stats(tl), "pairs_per_s": pairs_l / (tl["mean_ms"] * 1e-3),
+                           "TFLOP/s": tf, f"frac_of_{'fp8' if fp8 else 'bf16'}_peak": tf / peak}
+            log(f"prefill {name}: {tl['mean_ms']:.2f} ms/call, {tf:.0f} TFLOP/s")
+            del q_l, k_l, w_l, qs_l, ks_l
+            torch.cuda.empty_cache()
+        result["prefill_long"] = longl
+
     # ---------------- CPU oracle baselines (rank 0, N=1) ----------------
     if not args.no_cpu_baseline and not args.decode_only:
         result["cpu_baseline"] = cpu_baseline_prefill(inp, K, gpu_idx, gpu_val, args.cpu_seconds)
