@@ -10,16 +10,17 @@
 //
 // fp8 inputs, at every supported length, run in the kernel with specialised
 // waves (prefill_ws.hip).  This file holds the bf16 kernels:
-// * L <= 65536, and chunks of bf16 queries against the paged fp8 cache: key
-//   chunks are staged through LDS once per workgroup of eight tokens, and the
-//   weighted head sum runs on the matrix cores (sections further down).
-// * beyond L = 65536 (positions need 32 bits, buffers grow): the unstaged
-//   kernel below, whose layout is:
+// * every supported length (L <= 131072; positions past 65536 in the 17-bit
+//   candidate encoding), and chunks of bf16 queries against the paged fp8
+//   cache: key chunks are staged through LDS once per workgroup of eight
+//   tokens, and the weighted head sum runs on the matrix cores (sections
+//   further down).
+// * the unstaged kernel below, used only when the staged kernel is switched
+//   off at build time (DSAIDX_PREFILL_STAGED_BF16=0); its layout:
 // * workgroup = W independent waves; wave w owns query token t = W*blk + w and
 //   all 16*HB of its heads.  Blocks are issued heaviest (largest t) first.
-//   W = 4 with 4096-entry buffers and 32-bit positions (W = 8 with
-//   3072-entry buffers and 16-bit positions for L <= 65536, reached only
-//   when the staged kernels are switched off at build time).
+//   W = 4 with 4096-entry buffers and 32-bit positions beyond L = 65536
+//   (W = 8 with 3072-entry buffers and 16-bit positions up to it).
 // * the token's queries sit in registers as MFMA A operands for the whole
 //   scan (head on M);  keys stream through registers as B operands (key on
 //   N), 16 keys per subtile, 64 keys per step.  No LDS is used for keys and
@@ -60,7 +61,7 @@ constexpr int pad64(int n) { return (n + 63) / 64 * 64; }
 #define DSAIDX_PREFILL_DEPTH 1   // key chunks in flight ahead of the one multiplied (1 or 2)
 #endif
 #ifndef DSAIDX_PREFILL_STAGED_BF16
-#define DSAIDX_PREFILL_STAGED_BF16 1  // bf16 with L <= 65536: stage keys through LDS
+#define DSAIDX_PREFILL_STAGED_BF16 1  // bf16: stage keys through LDS (0: the unstaged kernel)
 #endif
 constexpr int kPrefetch = DSAIDX_PREFILL_DEPTH >= 2 ? 2 : 1;
 
@@ -346,7 +347,7 @@ __device__ __forceinline__ uint32_t spec_rank(float ec) {
 
 // ---------------------------------------------------------------------------
 // bf16 queries, keys staged through LDS, head sums on the matrix cores: whole
-// sequences of bf16 keys (L <= 65536), and chunks of bf16 queries against
+// sequences of bf16 keys (L <= 131072), and chunks of bf16 queries against
 // the paged fp8 key cache (variable length, positions up to 131072).
 //
 // The 8 waves of a workgroup (8 consecutive query rows of one sequence, all
@@ -897,9 +898,9 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     wave_emit<Pos, P17>(rb, nb, K, a.idx_out + row_t * K, a.val_out ? a.val_out + row_t * K : nullptr);
 }
 
-constexpr bool staged_bf16_path(int dtype, int L) { return DSAIDX_PREFILL_STAGED_BF16 && dtype == 1 && L <= 65536; }
+constexpr bool staged_bf16_path(int dtype, int L) { return DSAIDX_PREFILL_STAGED_BF16 && dtype == 1 && L <= 131072; }
 
-template <int HB>
+template <int HB, bool P17>
 hipError_t launch_bf16_staged(const PrefillArgs& a_in, hipStream_t stream) {
     PrefillArgs a = a_in;
     a.Lpad = pad64(a.L);
@@ -915,12 +916,12 @@ hipError_t launch_bf16_staged(const PrefillArgs& a_in, hipStream_t stream) {
     const size_t smem = kBfStages * kBfStageBytes + (size_t)kBfWaves * kBfWaveBytes;
     static PerDevice<int> lds_once;
     {
-        hipError_t e = set_lds_limit(lds_once, (const void*)prefill_fused_bf16_staged_kernel<HB, false, false>,
+        hipError_t e = set_lds_limit(lds_once, (const void*)prefill_fused_bf16_staged_kernel<HB, false, P17>,
                                      (int)smem);
         if (e != hipSuccess) return e;
     }
     const int nblk = (a.L + kBfWaves - 1) / kBfWaves;
-    hipLaunchKernelGGL((prefill_fused_bf16_staged_kernel<HB, false, false>), dim3((unsigned)(nblk * a.B)),
+    hipLaunchKernelGGL((prefill_fused_bf16_staged_kernel<HB, false, P17>), dim3((unsigned)(nblk * a.B)),
                        dim3(kBfWaves * kWave), smem, stream, a, (const uint16_t*)kscaled);
     return hipGetLastError();
 }
@@ -958,7 +959,9 @@ hipError_t launch_bf16_varlen(const PrefillArgs& a_in, hipStream_t stream) {
 
 template <int HB>
 hipError_t launch_bf16(const PrefillArgs& a, hipStream_t stream) {
-    if (staged_bf16_path(1, a.L)) return launch_bf16_staged<HB>(a, stream);
+    // positions past 65536 take the 17-bit candidate encoding
+    if (staged_bf16_path(1, a.L))
+        return a.L > 65536 ? launch_bf16_staged<HB, true>(a, stream) : launch_bf16_staged<HB, false>(a, stream);
     return a.L <= 65536 ? launch_one<1, HB, true>(a, stream) : launch_one<1, HB, false>(a, stream);
 }
 

@@ -101,11 +101,10 @@ typedef enum {
  *
  * Supported: 1 <= B, 1 <= L <= 131072, H a multiple of 4 in [4, 64],
  * D in {32, 64, 128}, 1 <= topk <= 2048.  bf16/fp8 with D = 128 and H a
- * multiple of 16 take the fused MFMA path.  Of these, L <= 65536 stages the
- * keys through LDS and needs a workspace per key (64-padded): fp8 5 bytes,
- * 256-byte rounded (a per-key operand scale and the key scale adjusted to
- * it); bf16 260 bytes (the adjusted scale and the key scaled into [-1, 1]).
- * Longer sequences need none.
+ * multiple of 16 take the fused MFMA path, which stages the keys through LDS
+ * and needs a workspace per key (64-padded): fp8 5 bytes, 256-byte rounded
+ * (a per-key operand scale and the key scale adjusted to it); bf16 260 bytes
+ * (the adjusted scale and the key scaled into [-1, 1]).
  * Other shapes score into a B*L*L fp32 matrix (the `scores` output if
  * given, else workspace) and select from it.  The workspace is caller-owned
  * device memory, 16-byte aligned, at least indexer_prefill_workspace_bytes()

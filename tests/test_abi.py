@@ -107,7 +107,8 @@ def test_prefill_workspace_query(lib):
     # bf16 staged: fp32 adjusted scale + the scaled bf16 key, per 64-padded key
     assert lib.indexer_prefill_workspace_bytes(1, 8192, 64, 128, 2048, 1, 0) == 8192 * 260
     assert lib.indexer_prefill_workspace_bytes(2, 100, 16, 128, 64, 1, 0) == 2 * 128 * 260
-    assert lib.indexer_prefill_workspace_bytes(1, 70000, 64, 128, 2048, 1, 0) == 0
+    # beyond 65536 positions the same staged kernel (17-bit candidate encoding)
+    assert lib.indexer_prefill_workspace_bytes(1, 70000, 64, 128, 2048, 1, 0) == 70016 * 260
     assert lib.indexer_prefill_workspace_bytes(2, 256, 4, 32, 16, 0, 0) == 2 * 256 * 256 * 4
     assert lib.indexer_prefill_workspace_bytes(2, 256, 4, 32, 16, 0, 1) == 0
 

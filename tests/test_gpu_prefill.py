@@ -205,13 +205,14 @@ def test_tie_heavy_long_rows_sampled(dtype):
     parity(inp, 512, rows=rows, name="ties long rows")
 
 
-@pytest.mark.parametrize("dtype,L", [("fp8", 65536), ("fp8", 66000), ("bf16", 65536), ("bf16", 66000)])
+@pytest.mark.parametrize("dtype,L", [("fp8", 65536), ("fp8", 66000), ("fp8", 131072),
+                                     ("bf16", 65536), ("bf16", 66000), ("bf16", 131072)])
 def test_fused_long_sequences_sampled(dtype, L):
-    """Both candidate-buffer layouts (16-bit positions up to L = 65536 in the
-    staged kernels, 32-bit beyond), checked on sampled rows including the
-    first and last."""
+    """Both candidate encodings (16-bit positions up to L = 65536, the 17-bit
+    encoding beyond, up to the largest supported L), checked on sampled rows
+    including the first and last."""
     inp = synth.prefill_inputs(1, L, 16, 128, dtype, seed=5000 + L)
-    rows = np.array([0, 2046, 2047, 2048, 40000, 65535, L - 1])
+    rows = np.array(sorted(r for r in {0, 2046, 2047, 2048, 40000, 65535, 65536, 100000, L - 2, L - 1} if r < L))
     say(f"prefill long {dtype} L={L}")
     gi, gv, _ = run_prefill(inp, 2048)
     _, _, osc = indexer.prefill(inp, 2048, rows=rows, want_scores=True)
