@@ -33,21 +33,21 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # HBM traffic per launch from two rocprofv3 counter passes (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch) over `bench.py --steps 2 --warmup 1
 # --no-cpu-baseline --copy-calibration`.  Each counter is scaled by what it
-# reads for a 1 GiB device-to-device copy (FETCH_SIZE 524315.4 KiB, WRITE_SIZE
+# reads for a 1 GiB device-to-device copy (FETCH_SIZE 524315.5 KiB, WRITE_SIZE
 # 1048576.0 KiB).  A record applies only while the kernel's sources hash to
 # the value it was taken at; otherwise traffic is reported as null.
-COPY_FETCH_FACTOR = 1048576.0 / 524315.4
+COPY_FETCH_FACTOR = 1048576.0 / 524315.5
 COPY_WRITE_FACTOR = 1048576.0 / 1048576.0
 _DECODE_SRC = ["csrc/decode_paged.hip", "csrc/select_row.h", "csrc/common.h", "csrc/kernels.h", "build.py"]
-_DECODE_SHA = "80194e1c6585a515301353fe27a58b9e09260ce13a5272989a9d7aacb6f2f937"
+_DECODE_SHA = "0e5cac2abd2fbe03826632f13ff76d5226742800138db3c6e1c6444f1d9d40d2"
 COUNTERS = {
     "prefill": {"sources": ["csrc/prefill_ws.hip", "csrc/rowbuf.h", "csrc/varlen.h", "csrc/common.h", "csrc/kernels.h",
                             "build.py"],
                 "sha256": "2656a5a8c175dc5c49fd05abbb05ad29a4303095500848da57288ccea7aedcc3",
-                "fetch_kib": 255993.1, "write_kib": 524323.6},
+                "fetch_kib": 256245.9, "write_kib": 524371.7},
     # main scan of one decode call, the sample inside it (which re-reads about 1/60 of the cache)
-    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 557336.8, "write_kib": 2434.5},
-    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 570383.3, "write_kib": 4107.5},
+    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 556757.8, "write_kib": 2391.2},
+    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 570581.4, "write_kib": 4137.1},
 }
 
 

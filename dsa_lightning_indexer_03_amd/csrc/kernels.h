@@ -116,7 +116,6 @@ struct GatherLayersArgs {
     const int32_t* block_table;              // [B][max_pages] page ids, shared by the layers
     const int32_t* idx;                      // [B][K] positions, shared by the layers
     int B, K, max_pages, row_bytes, n_layers;
-    int layers_per_group;                    // set by the launcher
 };
 
 size_t topk_select_smem_bytes();

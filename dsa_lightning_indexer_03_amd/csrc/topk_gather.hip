@@ -64,10 +64,11 @@ topk_gather_kernel(GatherArgs a) {
 // computed at one layer is reused by the layers that follow it, which skip
 // their own indexer).  The consumer side of that reuse is a gather of the
 // same positions from every serving layer's latent cache.  One launch does
-// them all: a wave reads its four indices and page ids once, then moves the
-// four rows of each layer of its layer group, two layers' loads in flight
-// before their stores.  blockIdx.y is the layer group, so a small selection
-// still fills the chip when many layers share it.
+// them all: blockIdx.y is the layer, and each wave moves four rows of that
+// layer exactly as the single-layer gather does; the indices and page ids
+// are read once per layer (from L2 after the first).  A wave that moved its
+// rows for several layers in turn, the indices read only once, was 4% slower
+// (its next layer's loads queue behind the previous layer's stores).
 __global__ void __launch_bounds__(kThreads)
 topk_gather_layers_kernel(GatherLayersArgs a) {
     const int lane = threadIdx.x & 63;
@@ -75,8 +76,8 @@ topk_gather_layers_kernel(GatherLayersArgs a) {
     const int64_t total = (int64_t)a.B * a.K;
     const int64_t r0 = wave * kRowsPerWave;
     if (r0 >= total) return;
-    const int l0 = (int)blockIdx.y * a.layers_per_group;
-    const int l1 = min(a.n_layers, l0 + a.layers_per_group);
+    const uint8_t* cache = a.cache[blockIdx.y];
+    uint8_t* out = a.out[blockIdx.y];
     const int64_t limit = (int64_t)a.max_pages * kPage;
     const int pieces = a.row_bytes / 16;
     int64_t src[kRowsPerWave];
@@ -95,59 +96,24 @@ topk_gather_layers_kernel(GatherLayersArgs a) {
                              a.row_bytes
                        : 0;
     }
-    int l = l0;
-    for (; l + 1 < l1; l += 2) {
-        const uint8_t* c0 = a.cache[l];
-        const uint8_t* c1 = a.cache[l + 1];
-        uint8_t* o0 = a.out[l];
-        uint8_t* o1 = a.out[l + 1];
-        for (int c = lane; c < pieces; c += 64) {
-            v4i v[2][kRowsPerWave];
+    for (int c = lane; c < pieces; c += 64) {
+        v4i v[kRowsPerWave];
 #pragma unroll
-            for (int u = 0; u < kRowsPerWave; ++u) {
-                v[0][u] = ok[u] ? *reinterpret_cast<const v4i*>(c0 + src[u] + 16 * c) : v4i{0, 0, 0, 0};
-                v[1][u] = ok[u] ? *reinterpret_cast<const v4i*>(c1 + src[u] + 16 * c) : v4i{0, 0, 0, 0};
-            }
+        for (int u = 0; u < kRowsPerWave; ++u)
+            v[u] = ok[u] ? *reinterpret_cast<const v4i*>(cache + src[u] + 16 * c) : v4i{0, 0, 0, 0};
 #pragma unroll
-            for (int u = 0; u < kRowsPerWave; ++u)
-                if (live[u]) {
-                    *reinterpret_cast<v4i*>(o0 + (r0 + u) * a.row_bytes + 16 * c) = v[0][u];
-                    *reinterpret_cast<v4i*>(o1 + (r0 + u) * a.row_bytes + 16 * c) = v[1][u];
-                }
-        }
-    }
-    if (l < l1) {
-        const uint8_t* c0 = a.cache[l];
-        uint8_t* o0 = a.out[l];
-        for (int c = lane; c < pieces; c += 64) {
-            v4i v[kRowsPerWave];
-#pragma unroll
-            for (int u = 0; u < kRowsPerWave; ++u)
-                v[u] = ok[u] ? *reinterpret_cast<const v4i*>(c0 + src[u] + 16 * c) : v4i{0, 0, 0, 0};
-#pragma unroll
-            for (int u = 0; u < kRowsPerWave; ++u)
-                if (live[u]) *reinterpret_cast<v4i*>(o0 + (r0 + u) * a.row_bytes + 16 * c) = v[u];
-        }
+        for (int u = 0; u < kRowsPerWave; ++u)
+            if (live[u]) *reinterpret_cast<v4i*>(out + (r0 + u) * a.row_bytes + 16 * c) = v[u];
     }
 }
 
 }  // namespace
 
-hipError_t launch_topk_gather_layers(const GatherLayersArgs& a_in, hipStream_t stream) {
-    GatherLayersArgs a = a_in;
+hipError_t launch_topk_gather_layers(const GatherLayersArgs& a, hipStream_t stream) {
     const int64_t total = (int64_t)a.B * a.K;
     const int64_t waves = (total + kRowsPerWave - 1) / kRowsPerWave;
     const int64_t blocks = (waves * 64 + kThreads - 1) / kThreads;
-    // Layer groups: all layers in one group when the rows alone give enough
-    // waves; otherwise split the layers until about 8192 waves are in flight
-    // (32 per CU), so the indices are re-read only where that buys occupancy.
-    constexpr int64_t kWantWaves = 8192;
-    int64_t groups = (kWantWaves + waves - 1) / waves;
-    if (groups > a.n_layers) groups = a.n_layers;
-    if (groups < 1) groups = 1;
-    a.layers_per_group = (int)((a.n_layers + groups - 1) / groups);
-    groups = (a.n_layers + a.layers_per_group - 1) / a.layers_per_group;
-    hipLaunchKernelGGL(topk_gather_layers_kernel, dim3((unsigned)blocks, (unsigned)groups), dim3(kThreads), 0,
+    hipLaunchKernelGGL(topk_gather_layers_kernel, dim3((unsigned)blocks, (unsigned)a.n_layers), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }

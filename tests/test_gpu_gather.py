@@ -4,7 +4,7 @@ padding and out-of-table indices, several row sizes and ragged B * K, the
 paged decode's own output as the indices, and the full-size configuration
 the bench times (sampled rows).  Also Index Share's multi-layer gather
 (indexer_topk_gather_layers): every layer's output against the oracle's
-gather of that layer, with one and with several layer groups per launch."""
+gather of that layer, from 2 to 64 layers in one launch."""
 import numpy as np
 import pytest
 import torch
@@ -82,8 +82,8 @@ def test_full_size_sampled():
 @pytest.mark.parametrize("S,B,K,row", [(3, 5, 300, 656), (61, 1, 64, 1152), (64, 2, 33, 48), (2, 16, 2048, 1024)])
 def test_layers_share_one_selection(S, B, K, row):
     """Index Share: S layers gather the same selection from their own caches
-    (S=61 with 16 waves of rows splits the layers into groups; S=2 with
-    8192 waves runs all layers in one group)."""
+    in one launch (one grid row per layer), from a 16-wave selection over 61
+    layers to an 8192-wave one over 2."""
     rng = np.random.default_rng(S * 7919 + B * 131 + K + row)
     mpp, n_pages = 5, B * 5 + 2
     say(f"gather layers S={S} B={B} K={K} row={row}")
