@@ -9,30 +9,12 @@
 // causal half; D = 128 and H is a multiple of 16.
 //
 // fp8 inputs, at every supported length, run in the kernel with specialised
-// waves (prefill_ws.hip).  This file holds the bf16 kernels:
-// * every supported length (L <= 131072; positions past 65536 in the 17-bit
-//   candidate encoding), and chunks of bf16 queries against the paged fp8
-//   cache: key chunks are staged through LDS once per workgroup of eight
-//   tokens, and the weighted head sum runs on the matrix cores (sections
-//   further down).
-// * the unstaged kernel below, used only when the staged kernel is switched
-//   off at build time (DSAIDX_PREFILL_STAGED_BF16=0); its layout:
-// * workgroup = W independent waves; wave w owns query token t = W*blk + w and
-//   all 16*HB of its heads.  Blocks are issued heaviest (largest t) first.
-//   W = 4 with 4096-entry buffers and 32-bit positions beyond L = 65536
-//   (W = 8 with 3072-entry buffers and 16-bit positions up to it).
-// * the token's queries sit in registers as MFMA A operands for the whole
-//   scan (head on M);  keys stream through registers as B operands (key on
-//   N), 16 keys per subtile, 64 keys per step.  No LDS is used for keys and
-//   waves never wait for each other; the four waves of a workgroup read the
-//   same key rows close together in time, so the vector L1 serves most of it.
-// * four v_mfma_f32_16x16x32_bf16 per 16 heads x 16 keys.  The contraction
-//   dimension is split the same way on both operands: lane group g owns the
-//   dims [32g, 32g+32).
-// * epilogue in registers: c[t,h] * max(S, 0) summed over the lane's heads,
-//   with c = w / sqrt(D), then a cross-lane reduce-scatter leaves lane l with
-//   the score of key s0 + l.
-// Both keep a streaming top-k per wave: a per-row candidate buffer of
+// waves (prefill_ws.hip).  This file holds the bf16 kernel: every supported
+// length (L <= 131072; positions past 65536 in the 17-bit candidate
+// encoding), and chunks of bf16 queries against the paged fp8 cache.  Key
+// chunks are staged through LDS once per workgroup of eight tokens, and the
+// weighted head sum runs on the matrix cores (details at the kernel).
+// Each wave keeps a streaming top-k for its row: a candidate buffer of
 // (key, position) pairs in LDS.  A score enters the buffer only if its
 // order-preserving key beats the row threshold.  When the buffer nears
 // capacity it is compacted: one radix digit below the buffer's common key
@@ -56,283 +38,6 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int pad64(int n) { return (n + 63) / 64 * 64; }
-
-#ifndef DSAIDX_PREFILL_DEPTH
-#define DSAIDX_PREFILL_DEPTH 1   // key chunks in flight ahead of the one multiplied (1 or 2)
-#endif
-#ifndef DSAIDX_PREFILL_STAGED_BF16
-#define DSAIDX_PREFILL_STAGED_BF16 1  // bf16: stage keys through LDS (0: the unstaged kernel)
-#endif
-constexpr int kPrefetch = DSAIDX_PREFILL_DEPTH >= 2 ? 2 : 1;
-
-template <bool POS16>
-struct BufCfg {
-    using Pos = typename std::conditional<POS16, uint16_t, uint32_t>::type;
-    static constexpr int kWaves = POS16 ? 8 : 4;      // waves (= tokens) per workgroup
-    static constexpr int kCap = POS16 ? 3072 : 4096;  // candidates per row
-    static constexpr size_t kWaveBytes = (size_t)kCap * (4 + sizeof(Pos)) + 256 * 4;
-};
-
-__device__ __forceinline__ float reduce_scatter4(const float v[4]) {
-    auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[2]), false, false);
-    auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[1]), __float_as_uint(v[3]), false, false);
-    const float a0 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
-    const float a1 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
-    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
-    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-template <int DT>  // 1 = bf16, 2 = fp8 e4m3
-struct Operands;
-
-template <>
-struct Operands<1> {
-    // A: lane (m, g) holds, for k-step j, q[t][16hb+m][32g+8j .. +8] (bf16).
-    template <int HB>
-    struct A { v8bf a[HB][4]; };
-    template <int HB>
-    __device__ static void load_a(A<HB>& A_, const uint8_t* qrow0, int m, int g) {
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                A_.a[hb][j] = *reinterpret_cast<const v8bf*>(qrow0 + ((size_t)(16 * hb + m) * kD + 32 * g + 8 * j) * 2);
-    }
-    struct Bt { v8bf b[4]; };
-    __device__ static void load_b(Bt& b, const uint8_t* krow, int g) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b.b[j] = *reinterpret_cast<const v8bf*>(krow + (32 * g + 8 * j) * 2);
-    }
-    template <int HB>
-    __device__ static void mma(v4f (&acc)[HB], const A<HB>& A_, const Bt& b) {
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            v4f c = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_.a[hb][j], b.b[j], c, 0, 0, 0);
-            acc[hb] = c;
-        }
-    }
-    static constexpr int kRowBytes = kD * 2;
-};
-
-template <int DT, int HB, bool POS16>
-__global__ void __launch_bounds__(BufCfg<POS16>::kWaves * kWave)
-prefill_fused_kernel(PrefillArgs a) {
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    using Op = Operands<DT>;
-    using Cfg = BufCfg<POS16>;
-    using Pos = typename Cfg::Pos;
-    constexpr int W = Cfg::kWaves;
-    constexpr int CAP = Cfg::kCap;
-    constexpr int H = 16 * HB;
-    const int L = a.L;
-    const int nblk = (L + W - 1) / W;
-    const int b = blockIdx.x % a.B;
-    const int blk = nblk - 1 - (int)(blockIdx.x / a.B);  // heaviest first
-    const int wave = threadIdx.x / kWave;
-    const int t = blk * W + wave;
-    if (t >= L) return;
-    const int lane = lane_id();
-    const int n = lane & 15, g = lane >> 4;
-
-    RowBuf<Pos> rb;
-    unsigned char* wbase = smem_raw + wave * Cfg::kWaveBytes;
-    rb.key = reinterpret_cast<uint32_t*>(wbase);
-    rb.hist = reinterpret_cast<uint32_t*>(wbase + (size_t)CAP * 4);
-    rb.pos = reinterpret_cast<Pos*>(wbase + (size_t)CAP * 4 + 256 * 4);
-
-    const size_t row_t = (size_t)b * L + t;
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * L * Op::kRowBytes;
-    typename Op::template A<HB> Aq;
-    Op::template load_a<HB>(Aq, reinterpret_cast<const uint8_t*>(a.q) + row_t * H * Op::kRowBytes, n, g);
-
-    // Head coefficients of the lane's accumulator rows: c = w * q_scale / sqrt(D)
-    // (fp8) or w / sqrt(D) (bf16).  The fp8 epilogue uses the identity
-    //   sum_i c_i max(S_i, 0) = 1/2 sum_i c_i |S_i| + 1/2 sum_i c_i S_i,
-    // so its coefficients carry the 1/2.
-    constexpr float kHalf = DT == 2 ? 0.5f : 1.0f;
-    float c[HB][4];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 16 * hb + 4 * g + i;
-            float cf = a.w[row_t * H + h] * (a.inv_sqrt_d * kHalf);
-            if constexpr (DT == 2) cf *= a.q_scale[row_t * H + h];
-            c[hb][i] = cf;
-        }
-
-    // fp8: the linear half 1/2 sum_i c_i S_i = u . k with u = sum_i c_i q_i (in
-    // code units) is one more MFMA block.  u (fp32) is split into six fp8
-    // pieces with power-of-two scales, piece p = e4m3(r_p / 2^e_p), r_{p+1} =
-    // r_p - piece_p * 2^e_p; each piece shrinks the largest residual by 2^4,
-    // so the dropped remainder is below 2^-24 of max|u|.  Pieces 0..3 sit in
-    // rows 0, 4, 8, 12 of the extra A block and pieces 4, 5 in rows 1, 5, so
-    // every lane group folds at most two of them into its partial sum.
-    v8i Alin = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    float lin0 = 0.f, lin1 = 0.f;
-    if constexpr (DT == 2) {
-        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + row_t * H * kD;
-        const int tu = __builtin_amdgcn_readfirstlane((int)row_t);
-        float u0 = 0.f, u1 = 0.f;  // dims 2*lane, 2*lane+1
-        for (int h = 0; h < H; ++h) {
-            const float ch = a.w[(size_t)tu * H + h] * a.q_scale[(size_t)tu * H + h] * (a.inv_sqrt_d * 0.5f);
-            const int two = (int)*reinterpret_cast<const uint16_t*>(qrow + (size_t)h * kD + 2 * lane);
-            const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(two, false);
-            u0 = fmaf(ch, f[0], u0);
-            u1 = fmaf(ch, f[1], u1);
-        }
-        uint8_t* pieces = reinterpret_cast<uint8_t*>(rb.hist);  // 6 x 128 bytes of scratch
-        float sc[6];
-#pragma unroll
-        for (int pc = 0; pc < 6; ++pc) {
-            float m = fmaxf(fabsf(u0), fabsf(u1));
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
-            // smallest power of two >= m / 448, so every |r / scale| <= 448
-            const bool live = m > 1e-30f;  // a vanishing residual ends the pieces
-            const float scale = live ? ldexpf(1.0f, __builtin_amdgcn_frexp_expf(m * (1.0f / 448.0f))) : 0.f;
-            const float inv = live ? 1.0f / scale : 0.f;
-            const int code = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * inv, u1 * inv, 0, false);
-            const auto dec = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
-            u0 -= dec[0] * scale;
-            u1 -= dec[1] * scale;
-            *reinterpret_cast<uint16_t*>(pieces + pc * kD + 2 * lane) = (uint16_t)(code & 0xFFFF);
-            sc[pc] = scale;
-        }
-        __builtin_amdgcn_wave_barrier();
-        // lane (row n, group g) of the extra A block
-        int pc_of_row = -1;
-        if ((n & 3) == 0) pc_of_row = n >> 2;               // rows 0, 4, 8, 12 -> pieces 0..3
-        else if (n == 1 || n == 5) pc_of_row = 4 + (n >> 2);  // rows 1, 5 -> pieces 4, 5
-        if (pc_of_row >= 0) {
-            const v4i lo = *reinterpret_cast<const v4i*>(pieces + pc_of_row * kD + 32 * g);
-            const v4i hi = *reinterpret_cast<const v4i*>(pieces + pc_of_row * kD + 32 * g + 16);
-            Alin = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        // output rows 4g (piece g) and 4g+1 (piece 4+g for g < 2)
-        lin0 = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
-        lin1 = g == 0 ? sc[4] : g == 1 ? sc[5] : 0.f;
-        __builtin_amdgcn_wave_barrier();
-    }
-    (void)Alin; (void)lin0; (void)lin1;
-
-    const float* kscale = DT == 2 ? a.k_scale + (size_t)b * L : nullptr;
-    float* srow = a.scores ? a.scores + row_t * L : nullptr;
-
-    auto load_chunk = [&](int s0, typename Op::Bt (&Bk)[4], float& ksc) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int s = min(s0 + 16 * st + n, L - 1);
-            Op::load_b(Bk[st], kbase + (size_t)s * Op::kRowBytes, g);
-        }
-        if constexpr (DT == 2) {
-            ksc = kscale[min(s0 + lane, L - 1)];
-        }
-    };
-
-    int nb = 0;           // candidates in the buffer (wave-uniform)
-    uint32_t thr = 0u;    // append iff key > thr
-    const int last = t / 64;
-
-    // One step over the 64 keys of `chunk`, held in `cur`; the next chunk's
-    // keys are loaded into `nxt` first.  Called with alternating buffers.
-    auto step = [&](int chunk, typename Op::Bt (&cur)[4], float ksc, typename Op::Bt (&nxt)[4], float& ksn) {
-        const int s0 = chunk * 64;
-        if (chunk + kPrefetch <= last) load_chunk(s0 + 64 * kPrefetch, nxt, ksn);
-        float part[4];
-        if constexpr (DT == 2) {
-            v4f acc[4][HB], accl[4];
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                Op::template mma<HB>(acc[st], Aq, cur[st]);
-                const v8i bb = v8i{cur[st].lo[0], cur[st].lo[1], cur[st].lo[2], cur[st].lo[3],
-                                   cur[st].hi[0], cur[st].hi[1], cur[st].hi[2], cur[st].hi[3]};
-                accl[st] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Alin, bb, v4f{0.f, 0.f, 0.f, 0.f},
-                                                                              0, 0, 0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                float pp = fmaf(lin0, accl[st][0], lin1 * accl[st][1]);
-#pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) pp = fmaf(c[hb][i], fabsf(acc[st][hb][i]), pp);
-                part[st] = pp;
-            }
-        } else {
-            v4f acc[4][HB];
-#pragma unroll
-            for (int st = 0; st < 4; ++st) Op::template mma<HB>(acc[st], Aq, cur[st]);
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                float pp = 0.f;
-#pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) pp = fmaf(c[hb][i], relu(acc[st][hb][i]), pp);
-                part[st] = pp;
-            }
-        }
-        const float score = reduce_scatter4(part) * ksc;
-        const int s = s0 + lane;
-        const bool valid = s <= t;
-        if (srow && s < L) srow[s] = valid ? score : -INFINITY;
-        const uint32_t key = score_key(score);
-        const bool app = valid && key > thr;
-        const uint64_t m = wave_ballot(app);
-        if (app) {
-            const int o = nb + lanes_below(m);
-            rb.key[o] = key;
-            rb.pos[o] = (Pos)s;
-        }
-        nb += __builtin_popcountll(m);
-        if (nb > CAP - kWave) {
-            __builtin_amdgcn_wave_barrier();
-            nb = wave_compact(rb, nb, (uint32_t)a.topk, &thr, CAP);
-        }
-    };
-
-#if DSAIDX_PREFILL_DEPTH >= 2
-    // keys two chunks ahead are in flight: three buffers in rotation
-    typename Op::Bt bx[4], by[4], bz[4];
-    float kx = 1.f, ky = 1.f, kz = 1.f;
-    load_chunk(0, bx, kx);
-    if (last >= 1) load_chunk(64, by, ky);
-    for (int chunk = 0; chunk <= last; chunk += 3) {
-        step(chunk, bx, kx, bz, kz);
-        if (chunk + 1 <= last) step(chunk + 1, by, ky, bx, kx);
-        if (chunk + 2 <= last) step(chunk + 2, bz, kz, by, ky);
-    }
-#else
-    typename Op::Bt bx[4], by[4];
-    float kx = 1.f, ky = 1.f;
-    load_chunk(0, bx, kx);
-    for (int chunk = 0; chunk <= last; chunk += 2) {
-        step(chunk, bx, kx, by, ky);
-        if (chunk + 1 <= last) step(chunk + 1, by, ky, bx, kx);
-    }
-#endif
-    if (srow) {
-        for (int s = (last + 1) * 64 + lane; s < L; s += kWave) srow[s] = -INFINITY;
-    }
-    __builtin_amdgcn_wave_barrier();
-    wave_emit(rb, nb, a.topk, a.idx_out + row_t * a.topk, a.val_out ? a.val_out + row_t * a.topk : nullptr);
-}
-
-template <int DT, int HB, bool POS16>
-hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
-    using Cfg = BufCfg<POS16>;
-    const size_t smem = (size_t)Cfg::kWaves * Cfg::kWaveBytes;
-    static PerDevice<int> lds_once;
-    hipError_t e = set_lds_limit(lds_once, (const void*)prefill_fused_kernel<DT, HB, POS16>, (int)smem);
-    if (e != hipSuccess) return e;
-    const int nblk = (a.L + Cfg::kWaves - 1) / Cfg::kWaves;
-    hipLaunchKernelGGL((prefill_fused_kernel<DT, HB, POS16>), dim3((unsigned)(nblk * a.B)),
-                       dim3(Cfg::kWaves * kWave), smem, stream, a);
-    return hipGetLastError();
-}
 
 // Rank r of the speculative floor in a row's sample, from the expected
 // number ec of sampled keys at or above the row's k-th largest: 3.5 standard
@@ -898,7 +603,7 @@ prefill_fused_bf16_staged_kernel(PrefillArgs a, const uint16_t* kscaled) {
     wave_emit<Pos, P17>(rb, nb, K, a.idx_out + row_t * K, a.val_out ? a.val_out + row_t * K : nullptr);
 }
 
-constexpr bool staged_bf16_path(int dtype, int L) { return DSAIDX_PREFILL_STAGED_BF16 && dtype == 1 && L <= 131072; }
+constexpr bool staged_bf16_path(int dtype, int L) { return dtype == 1 && L <= 131072; }
 
 template <int HB, bool P17>
 hipError_t launch_bf16_staged(const PrefillArgs& a_in, hipStream_t stream) {
@@ -959,10 +664,9 @@ hipError_t launch_bf16_varlen(const PrefillArgs& a_in, hipStream_t stream) {
 
 template <int HB>
 hipError_t launch_bf16(const PrefillArgs& a, hipStream_t stream) {
+    if (!staged_bf16_path(1, a.L)) return hipErrorInvalidValue;
     // positions past 65536 take the 17-bit candidate encoding
-    if (staged_bf16_path(1, a.L))
-        return a.L > 65536 ? launch_bf16_staged<HB, true>(a, stream) : launch_bf16_staged<HB, false>(a, stream);
-    return a.L <= 65536 ? launch_one<1, HB, true>(a, stream) : launch_one<1, HB, false>(a, stream);
+    return a.L > 65536 ? launch_bf16_staged<HB, true>(a, stream) : launch_bf16_staged<HB, false>(a, stream);
 }
 
 }  // namespace
