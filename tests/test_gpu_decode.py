@@ -212,6 +212,17 @@ def test_constant_scores_long_context():
         assert np.all(gv[b] == 0.0)
 
 
+@pytest.mark.parametrize("B", [256, 257])
+def test_fused_sampling_at_half_grid(B):
+    """Sampled queries at H=64 around half the scan's resident grid (two
+    workgroups per CU): 256 queries sample inside the scan with every second
+    workgroup a sampler, 257 take the separate sample kernel."""
+    rng = np.random.default_rng(574 + B)
+    ctx = rng.integers(4096, 6000, size=B).tolist()
+    d = synth.decode_inputs(B, ctx, 64, 128, seed=574 + B, permute=True)
+    parity(d, 256, f"B={B} sampled", queries=list(range(0, B, 4)) + [B - 1])
+
+
 def test_batch_beyond_fused_sampling():
     """300 sampled queries at H=64: more than half the scan's resident grid,
     so the sample runs as a kernel of its own before the scan."""
