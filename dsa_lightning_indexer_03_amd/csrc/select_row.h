@@ -188,11 +188,24 @@ __device__ inline void select_row(const SelectArgs& a, const int row, SelShared&
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = j0 + u * kThreads + t;
-                if (j < n) {
-                    const uint32_t key = score_key(v[u]);
+                const bool ok = j < n;
+                const uint32_t key = score_key(v[u]);
+                if (ok) {
                     sh.cand_key[j] = key;
                     sh.cand_pos[j] = p[u];
-                    atomicAdd(&sh.hist[key >> 21], 1u);
+                }
+                // The keys of a row's candidates often share their top digit
+                // (a decode query's all lie above its floor): the lanes with the
+                // first valid lane's digit add their count in one atomic, the
+                // others one each.
+                const uint64_t mv = wave_ballot(ok);
+                if (mv != 0) {
+                    const int first = __builtin_ctzll(mv);
+                    const uint32_t d = key >> 21;
+                    const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, first);
+                    const uint64_t ms = wave_ballot(ok && d == d0);
+                    if (lane_id() == first) atomicAdd(&sh.hist[d0], (uint32_t)__builtin_popcountll(ms));
+                    if (ok && d != d0) atomicAdd(&sh.hist[d], 1u);
                 }
             }
         }
