@@ -703,6 +703,15 @@ decode_finish_kernel(DecodeArgs a, SelectArgs sa) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     sel::SelShared& sh = *reinterpret_cast<sel::SelShared*>(smem_raw);
     const int b = blockIdx.x, t = threadIdx.x;
+    // The first candidates are loaded before their count is known (inside the
+    // row's stride), so both arrive in one round trip.
+    sel::Preload pre;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = u * sel::kThreads + t;
+        pre.v[u] = j < a.cand_stride ? a.cand_score[(size_t)b * a.cand_stride + j] : 0.f;
+        pre.p[u] = j < a.cand_stride ? (uint32_t)a.cand_pos[(size_t)b * a.cand_stride + j] : 0u;
+    }
     const int ctx = clamp_ctx(a.context_lens[b], a.max_ctx);
     uint32_t* cnt = a.ctrl + (size_t)b * kCtrlStride + 1;
     const uint32_t need = (uint32_t)min(a.topk, ctx);
@@ -771,7 +780,7 @@ decode_finish_kernel(DecodeArgs a, SelectArgs sa) {
         if (t == 0) *cnt = (uint32_t)ctx;
         n_known = ctx;
     }
-    sel::select_row(sa, b, sh, n_known);
+    sel::select_row(sa, b, sh, n_known, pre, !rescore);  // a rescore rewrote the candidates
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, size_t n) {

@@ -121,9 +121,19 @@ __device__ __forceinline__ void emit(SelShared& sh, bool take, uint32_t pos, flo
     }
 }
 
+// The row's first 4 * kThreads entries, loaded by the caller before it knew
+// the row's length (lane t holds entries t + u * kThreads, inside the row's
+// stride); used only where they are below the length.
+struct Preload {
+    float v[4];
+    uint32_t p[4];
+};
+
 // Selects row `row` of `a` with the whole workgroup (kThreads threads) and
-// the LDS block `sh`.  n_known >= 0 overrides the row's entry count.
-__device__ inline void select_row(const SelectArgs& a, const int row, SelShared& sh, const int n_known) {
+// the LDS block `sh`.  n_known >= 0 overrides the row's entry count; with
+// use_pre, `pre` holds the row's first entries already loaded.
+__device__ __forceinline__ void select_row(const SelectArgs& a, const int row, SelShared& sh, const int n_known,
+                                          const Preload& pre, const bool use_pre) {
     const int t = threadIdx.x;
     const float* src = a.scores + (int64_t)row * a.row_stride;
     const int32_t* psrc = a.pos ? a.pos + (int64_t)row * a.row_stride : nullptr;
@@ -182,8 +192,13 @@ __device__ inline void select_row(const SelectArgs& a, const int row, SelShared&
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = j0 + u * kThreads + t;
-                v[u] = j < n ? src[j] : 0.f;
-                p[u] = j < n ? (psrc ? (uint32_t)psrc[j] : (uint32_t)j) : 0u;
+                if (use_pre && j0 == 0) {
+                    v[u] = pre.v[u];
+                    p[u] = pre.p[u];
+                } else {
+                    v[u] = j < n ? src[j] : 0.f;
+                    p[u] = j < n ? (psrc ? (uint32_t)psrc[j] : (uint32_t)j) : 0u;
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -313,6 +328,11 @@ __device__ inline void select_row(const SelectArgs& a, const int row, SelShared&
     }
 }
 
+
+__device__ __forceinline__ void select_row(const SelectArgs& a, const int row, SelShared& sh, const int n_known) {
+    const Preload none{};
+    select_row(a, row, sh, n_known, none, false);
+}
 
 }  // namespace sel
 }  // namespace dsaidx
