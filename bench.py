@@ -39,15 +39,15 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 COPY_FETCH_FACTOR = 1048576.0 / 524315.5
 COPY_WRITE_FACTOR = 1048576.0 / 1048576.0
 _DECODE_SRC = ["csrc/decode_paged.hip", "csrc/select_row.h", "csrc/common.h", "csrc/kernels.h", "build.py"]
-_DECODE_SHA = "63f2a85d1ad5047b89314e436c574efa32613613597ba8ac69c4ed0efdbc7772"
+_DECODE_SHA = "98816410d2ad66fc654ebd73ea1412957325d177b33375d34187322513b8bb50"
 COUNTERS = {
     "prefill": {"sources": ["csrc/prefill_ws.hip", "csrc/rowbuf.h", "csrc/varlen.h", "csrc/common.h", "csrc/kernels.h",
                             "build.py"],
                 "sha256": "8716ea67a91e407f862c95a89fba2b4518b2e0d852a0e95bb2dad72b274757d6",
-                "fetch_kib": 255832.1, "write_kib": 524314.6},
+                "fetch_kib": 256229.1, "write_kib": 524378.5},
     # main scan of one decode call, the sample inside it (which re-reads about 1/60 of the cache)
-    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 556743.1, "write_kib": 2388.0},
-    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 570511.7, "write_kib": 4133.8},
+    "decode_scan_w4": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 556828.7, "write_kib": 2382.2},
+    "decode_scan_w5": {"sources": _DECODE_SRC, "sha256": _DECODE_SHA, "fetch_kib": 570465.3, "write_kib": 4139.6},
 }
 
 
