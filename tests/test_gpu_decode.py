@@ -239,3 +239,33 @@ def test_batch_beyond_lds_prefix():
     ctx = rng.integers(1, 300, size=2100).tolist()
     d = synth.decode_inputs(2100, ctx, 16, 128, seed=572, permute=True)
     parity(d, 64, "B=2100", queries=list(range(0, 2100, 97)) + [2099])
+
+
+def test_workspace_garbage_then_reused():
+    """The caller's workspace starts as 0xFF bytes (every counter word at its
+    maximum, every floor word marked as published), and is then reused
+    unchanged by a second call with another batch: each query's counters are
+    cleared by the call itself, so both results match the oracle."""
+    K = 512
+    d1 = synth.decode_inputs(4, [20000, 9000, 4096, 700], 64, 128, seed=575, permute=True)
+    rng = np.random.default_rng(576)
+    ctx2 = rng.integers(4096, 9000, size=300).tolist()
+    d2 = synth.decode_inputs(300, ctx2, 64, 128, seed=576, permute=True)
+    # each call's counter blocks sit after its own candidate lists, so the
+    # second call's lie over the first call's candidates
+    mcl = {id(d): d["block_table"].shape[1] * 64 for d in (d1, d2)}
+    nws = max(dsa.decode_workspace_bytes(d["q"].shape[0], mcl[id(d)], 64, 128, K) for d in (d1, d2))
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda")
+    for d, name, qs in ((d1, "garbage workspace", range(4)),
+                        (d2, "reused workspace, B=300", list(range(0, 300, 6)) + [299]),
+                        (d1, "reused again, B=4", range(4))):
+        say(f"decode {name}: B={d['q'].shape[0]} K={K}")
+        gi, gv = dsa.indexer_decode_paged(dev(d["q"]), dev(d["w"]), dev(d["k_cache"]), dev(d["k_scale"]),
+                                          dev(d["block_table"]), dev(d["context_lens"]), K,
+                                          max_context_len=mcl[id(d)], workspace=ws)
+        torch.cuda.synchronize()
+        gi, gv = host(gi), host(gv)
+        for b in qs:
+            o = indexer.decode_scores(d, b)
+            check_topk_rows(gi[b:b + 1], gv[b:b + 1], o[None], [o.size], K, where=f"{name} q{b}")
+        say("  ok")

@@ -58,6 +58,17 @@ def test_generic_path_edge_lengths(dtype, L):
     parity(inp, 16, want_scores=True, name=f"generic L={L}")
 
 
+@pytest.mark.parametrize("dtype,D,H,L,K", [("f32", 128, 64, 200, 16), ("f32", 64, 60, 130, 32),
+                                           ("bf16", 128, 20, 257, 64), ("bf16", 32, 64, 100, 8),
+                                           ("fp8", 128, 36, 190, 48), ("fp8", 64, 12, 129, 128)])
+def test_generic_path_shapes(dtype, D, H, L, K):
+    """Shapes outside the fused kernels (fp32 inputs, D below 128, H not a
+    multiple of 16) at the ends of the supported ranges: every D, H up to 64,
+    several key tiles with a ragged last one, k above some rows' lengths."""
+    inp = synth.prefill_inputs(1, L, H, D, dtype, seed=1100 + D + H + L)
+    parity(inp, K, want_scores=True, name=f"generic D={D} H={H}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("L,H,K", [(1, 64, 16), (17, 64, 16), (64, 16, 16), (65, 64, 64), (1000, 64, 64),
                                    (1000, 32, 7), (5000, 16, 2048), (300, 48, 32), (3000, 48, 256)])

@@ -91,3 +91,36 @@ def test_all_k_values_small():
     s = rng.standard_normal((3, 777)).astype(np.float32)
     for K in (1, 2, 7, 64, 776, 777, 778, 2048):
         compare(s, K, name=f"K={K}")
+
+
+def test_strided_rows_and_positive_infinity():
+    """Rows read from a wider matrix (row stride 7001 floats, first column at
+    offset 3): +inf entries rank first; a row holding more +inf entries than
+    k keeps the lowest positions among them."""
+    rng = np.random.default_rng(107)
+    wide = rng.standard_normal((5, 7001)).astype(np.float32)
+    wide[0, 3 + np.arange(0, 6000, 700)] = np.inf          # fewer than k
+    wide[1, 3:3 + 6000:2] = np.inf                          # 3000 > k
+    wide[2, 3 + np.array([5, 6, 5999])] = [np.inf, -np.inf, np.inf]
+    view = dev(wide)[:, 3:6003]
+    assert view.stride(0) == 7001 and not view.is_contiguous()
+    K = 1000
+    say(f"topk_select strided: rows=5 cols=6000 row_stride=7001 K={K}")
+    idx, val = dsa.topk_select(view, K)
+    torch.cuda.synchronize()
+    gi, gv = host(idx), host(val)
+    s = wide[:, 3:6003]
+    oi, _ = indexer.topk_rows(s, None, K)
+    for r in range(5):
+        assert sorted(gi[r].tolist()) == sorted(oi[r].tolist()), r
+        assert np.array_equal(gv[r], s[r, gi[r]]), r
+    assert sorted(gi[1].tolist()) == list(range(0, 2 * K, 2))
+
+
+def test_maximum_columns():
+    """Rows of the largest supported length (4194304 columns), one of them
+    cut short by its row length; k = 2048."""
+    rng = np.random.default_rng(108)
+    s = rng.standard_normal((2, 4194304)).astype(np.float32)
+    s[1, 4194000:] = 100.0  # past row 1's length: never selected
+    compare(s, 2048, np.array([4194304, 4194000], np.int32), name="max cols")
