@@ -172,6 +172,15 @@ size_t indexer_prefill_noalloc_scratch_bytes(void);
  *   max_context_len  host-side upper bound of context_lens (sizes the launch
  *                and the workspace); <= max_pages_per_seq * page_size
  *   topk_idx     out [B][topk] int32;  topk_score out [B][topk] fp32 or NULL
+ *   workspace    indexer_decode_paged_workspace_bytes(B, max_context_len, H,
+ *                D, topk) bytes of caller-owned device memory, 16-byte
+ *                aligned: candidate scores and positions (8 bytes per
+ *                position of max_context_len, 64-padded, per query), then 256
+ *                bytes of counters per query, then B + 1 page offsets.  Its
+ *                contents on entry do not matter: the call clears its
+ *                counters before using them, so a workspace may hold anything
+ *                and may be reused by any later call.  Two calls in flight
+ *                on one workspace at once race.
  *
  * Supported: H a multiple of 16 in [16, 64], D = 128, page_size = 64,
  * 1 <= topk <= 2048, max_context_len <= 131072 (larger needs no change but
